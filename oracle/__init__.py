@@ -1,0 +1,244 @@
+"""CPU oracle for the W4A16 decode/verify matmul.
+
+TEST INFRASTRUCTURE.  Only ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` may import this package.  The HIP library
+never imports, links or calls it, and the two share no code: the only thing
+both sides consume is the seeded input generator in ``synth.py``, which holds
+none of the method's arithmetic.
+
+Contents
+  * ``unpack``, ``dequant``, ``gemm``, ``repack``, ``unrepack``: thin numpy
+    wrappers around ``oracle.c`` (fp64, plain loops), built with gcc into
+    ``liboracle.so`` next to this file.
+  * ``exact_gemm``: exact rational arithmetic (Python ``Fraction``) for tiny
+    shapes, used to pin the fp64 oracle.
+  * ``normalized_error``: the acceptance metric
+    ``max |C_gpu - C_ref| / sum|a*w|`` per output.
+  * ``bf16_bits_to_f64`` / ``f32_exact_to_bf16_bits``: exact bf16 reading,
+    and round-to-nearest-even of fp32-representable values to bf16.
+
+What is computed follows the checkpoint contract on the page "Qwen3.8-27B on
+single DGX Spark ..." (section "Quality."): symmetric GPTQ, 4-bit, group 128,
+BF16 activations, no act-order, no zero points, with the runtime judged
+against exact dequantization of its checkpoint.  The oracle is that exact
+dequantization followed by an fp64 dot product.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+from fractions import Fraction
+
+import numpy as np
+
+GROUP = 128
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "oracle.c")
+_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+_lib = None
+
+
+def build(force: bool = False) -> str:
+    """Compile oracle.c with gcc (portable x86-64, OpenMP) into liboracle.so."""
+    if force or not os.path.exists(_LIB_PATH):
+        tmp = _LIB_PATH + ".tmp"
+        cmd = ["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-std=c99",
+               "-o", tmp, _SRC, "-lm"]
+        subprocess.run(cmd, check=True)
+        os.replace(tmp, _LIB_PATH)
+    return _LIB_PATH
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        build()
+        lib = ctypes.CDLL(_LIB_PATH)
+        P = ctypes.c_void_p
+        i = ctypes.c_int
+        lib.oracle_unpack.argtypes = [P, i, i, P]
+        lib.oracle_dequant.argtypes = [P, P, i, i, P]
+        lib.oracle_gemm.argtypes = [P, P, P, i, i, i, P, i, i, P, P]
+        lib.oracle_repack.argtypes = [P, i, i, P]
+        lib.oracle_unrepack.argtypes = [P, i, i, P]
+        lib.oracle_bf16_to_f64.argtypes = [ctypes.c_uint16]
+        lib.oracle_bf16_to_f64.restype = ctypes.c_double
+        lib.oracle_max_threads.restype = ctypes.c_int
+        _lib = lib
+    return _lib
+
+
+def _ptr(a: np.ndarray):
+    return a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _check_shapes(K: int, N: int, multiple: int = GROUP):
+    if K % multiple or K <= 0 or N <= 0:
+        raise ValueError(f"oracle: K must be a positive multiple of {multiple}, N positive")
+
+
+def unpack(qweight: np.ndarray, K: int, N: int) -> np.ndarray:
+    """Codes q[k, n] in [0, 15] from GPTQ words uint32 [K/8, N] (low nibble first)."""
+    _check_shapes(K, N, 8)
+    qw = np.ascontiguousarray(qweight, dtype=np.uint32).reshape(K // 8, N)
+    out = np.empty((K, N), dtype=np.uint8)
+    _load().oracle_unpack(_ptr(qw), K, N, _ptr(out))
+    return out
+
+
+def dequant(qweight: np.ndarray, scales: np.ndarray, K: int, N: int) -> np.ndarray:
+    """W[k, n] = (q - 8) * s[k // 128, n] in fp64 (exactly fp32-representable)."""
+    _check_shapes(K, N)
+    qw = np.ascontiguousarray(qweight, dtype=np.uint32).reshape(K // 8, N)
+    sc = np.ascontiguousarray(scales, dtype=np.uint16).reshape(K // GROUP, N)
+    out = np.empty((K, N), dtype=np.float64)
+    _load().oracle_dequant(_ptr(qw), _ptr(sc), K, N, _ptr(out))
+    return out
+
+
+def gemm(A: np.ndarray, qweight: np.ndarray, scales: np.ndarray, M: int, N: int, K: int,
+         cols=None, nthreads: int = 0):
+    """fp64 reference C[M, ncols] = A . dequant(W)[:, cols] and D = sum |a*w|.
+
+    ``A`` is bf16 bits (uint16) [M, K]; ``cols`` selects output columns (all if None).
+    Returns (C, D), both float64 [M, ncols].
+    """
+    _check_shapes(K, N)
+    if not 1 <= M <= 16:
+        raise ValueError("oracle.gemm: 1 <= M <= 16")
+    a = np.ascontiguousarray(A, dtype=np.uint16).reshape(-1, K)[:M]
+    a = np.ascontiguousarray(a)
+    qw = np.ascontiguousarray(qweight, dtype=np.uint32).reshape(K // 8, N)
+    sc = np.ascontiguousarray(scales, dtype=np.uint16).reshape(K // GROUP, N)
+    if cols is None:
+        ncols = N
+        cptr = None
+    else:
+        c = np.ascontiguousarray(cols, dtype=np.int32)
+        if c.size and (c.min() < 0 or c.max() >= N):
+            raise ValueError("oracle.gemm: column index out of range")
+        ncols = int(c.size)
+        cptr = _ptr(c)
+    C = np.empty((M, ncols), dtype=np.float64)
+    D = np.empty((M, ncols), dtype=np.float64)
+    _load().oracle_gemm(_ptr(a), _ptr(qw), _ptr(sc), M, N, K, cptr, ncols, int(nthreads),
+                        _ptr(C), _ptr(D))
+    return C, D
+
+
+def repack(qweight: np.ndarray, K: int, N: int) -> np.ndarray:
+    """Tile-order blob (uint32, K*N/8 words) built from the written layout definition."""
+    _check_shapes(K, N)
+    if N % 16:
+        raise ValueError("oracle.repack: N must be a multiple of 16")
+    qw = np.ascontiguousarray(qweight, dtype=np.uint32).reshape(K // 8, N)
+    out = np.empty(K * N // 8, dtype=np.uint32)
+    _load().oracle_repack(_ptr(qw), K, N, _ptr(out))
+    return out
+
+
+def unrepack(blob: np.ndarray, K: int, N: int) -> np.ndarray:
+    """Inverse of ``repack``: GPTQ words uint32 [K/8, N]."""
+    _check_shapes(K, N)
+    b = np.ascontiguousarray(blob, dtype=np.uint32).reshape(-1)
+    if b.size != K * N // 8:
+        raise ValueError("oracle.unrepack: blob size mismatch")
+    out = np.empty((K // 8, N), dtype=np.uint32)
+    _load().oracle_unrepack(_ptr(b), K, N, _ptr(out))
+    return out
+
+
+def max_threads() -> int:
+    return int(_load().oracle_max_threads())
+
+
+# ---------------------------------------------------------------------------
+# bf16 helpers (exact reading; RNE only for values already exact in fp32)
+# ---------------------------------------------------------------------------
+
+def bf16_bits_to_f64(bits: np.ndarray) -> np.ndarray:
+    """Exact value of bf16 bit patterns: the bits are the top half of an fp32."""
+    b = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)
+    return b.view(np.float32).astype(np.float64)
+
+
+def f32_exact_to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """Round-to-nearest-even to bf16 of values that are exactly representable in fp32.
+
+    Raises if a value is not fp32-exact, so that no double rounding can hide here.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    f = x.astype(np.float32)
+    if not np.array_equal(f.astype(np.float64), x, equal_nan=True):
+        raise ValueError("f32_exact_to_bf16_bits: input is not exactly representable in fp32")
+    u = f.view(np.uint32).astype(np.uint64)
+    keep = u >> np.uint64(16)
+    rem = u & np.uint64(0xFFFF)
+    half = np.uint64(0x8000)
+    up = (rem > half) | ((rem == half) & ((keep & np.uint64(1)) == np.uint64(1)))
+    out = keep + up.astype(np.uint64)
+    return out.astype(np.uint16)
+
+
+# ---------------------------------------------------------------------------
+# Exact rational reference (tiny shapes only)
+# ---------------------------------------------------------------------------
+
+def _bf16_fraction(bits: int) -> Fraction:
+    """Exact rational value of a finite bf16 bit pattern, from its fields."""
+    sign = -1 if bits & 0x8000 else 1
+    exp = (bits >> 7) & 0xFF
+    man = bits & 0x7F
+    if exp == 0xFF:
+        raise ValueError("non-finite bf16 in exact reference")
+    if exp == 0:
+        val = Fraction(man, 1 << 7) * Fraction(1, 1 << 126)
+    else:
+        val = (1 + Fraction(man, 1 << 7)) * (Fraction(2) ** (exp - 127))
+    return sign * val
+
+
+def exact_gemm(A_bits, qweight, scales_bits, M: int, N: int, K: int):
+    """C[m][n] = sum_k a * (q - 8) * s with exact rationals, and D = sum |a*w|.
+
+    Pure-Python loops; the code of (k, n) is read with integer operations from
+    word (k // 8, n), nibble k % 8, low nibble first.
+    """
+    A_bits = np.asarray(A_bits, dtype=np.uint16).reshape(-1, K)
+    qw = np.asarray(qweight, dtype=np.uint32).reshape(K // 8, N)
+    sc = np.asarray(scales_bits, dtype=np.uint16).reshape(K // GROUP, N)
+    a = [[_bf16_fraction(int(A_bits[m, k])) for k in range(K)] for m in range(M)]
+    C = [[Fraction(0)] * N for _ in range(M)]
+    D = [[Fraction(0)] * N for _ in range(M)]
+    for n in range(N):
+        for k in range(K):
+            word = int(qw[k // 8, n])
+            q = (word >> (4 * (k % 8))) & 0xF
+            w = (q - 8) * _bf16_fraction(int(sc[k // GROUP, n]))
+            for m in range(M):
+                p = a[m][k] * w
+                C[m][n] += p
+                D[m][n] += abs(p)
+    return C, D
+
+
+# ---------------------------------------------------------------------------
+# Acceptance metric
+# ---------------------------------------------------------------------------
+
+def normalized_error(C_test: np.ndarray, C_ref: np.ndarray, D_ref: np.ndarray) -> np.ndarray:
+    """Per-output error |C_test - C_ref| / D_ref.
+
+    Where D_ref == 0 every term a*w is zero, so the exact result is zero and
+    C_test must be +-0: the error there is 0 if it is, +inf otherwise.
+    """
+    C_test = np.asarray(C_test, dtype=np.float64)
+    C_ref = np.asarray(C_ref, dtype=np.float64)
+    D_ref = np.asarray(D_ref, dtype=np.float64)
+    num = np.abs(C_test - C_ref)
+    out = np.empty_like(num)
+    nz = D_ref > 0
+    out[nz] = num[nz] / D_ref[nz]
+    out[~nz] = np.where(C_test[~nz] == 0.0, 0.0, np.inf)
+    return out

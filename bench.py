@@ -1,0 +1,312 @@
+"""Benchmark of the W4A16 decode/verify matmul on one MI355X.
+
+Default run: the QKV-shaped decode call (M=1, K=5120, N=8192, group 128,
+synthetic inputs with the distributions of the 27B workloads), repeated
+--steps times inside one HIP graph replay.  The weight blob, scales,
+activations and outputs rotate over enough distinct buffer sets (>= 1 GiB in
+total) that no call finds its weights in the 256 MiB last-level cache: every
+call streams its weights from HBM.
+
+Prints ONE JSON line:
+  value        algorithmic bytes per call / (graph replay time / steps), GB/s
+  roofline     the kernel's own average duration from per-launch HIP events
+               (eager launches on the launch stream), against 8 TB/s
+  cpu_baseline the fp64 CPU oracle on the same workload (rank 0 only)
+
+--sweep prints one JSON line per (workload, M) instead (not the contract line);
+--stack times one decode step's full sequence of linear shapes.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import synth  # noqa: E402
+
+METRIC = "achieved HBM GB/s (% of peak) for W4A16 matmul at M=1,4,8,16; µs/call"
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
+PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+LLC_BYTES = 256 << 20          # MI355X Infinity Cache
+ROTATE_BYTES = 1 << 30         # rotate over >= 1 GiB of buffer sets
+KERNEL_SOURCES = ["weight_only_int4_gptq_amd/csrc/w4a16.hip",
+                  "weight_only_int4_gptq_amd/csrc/w4a16_kernels.hpp"]
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+class Problem:
+    """Device buffers for one (K, N) shape, replicated over `sets` distinct buffer sets."""
+
+    def __init__(self, torch, w4, K, N, seed, act, sets, Mmax=16):
+        dev = torch.device("cuda:0")
+        A, qw, sc = synth.gen_problem(K, N, seed, act, Mmax)
+        self.host = (A, qw, sc)
+        q = torch.from_numpy(qw.view(np.int32)).to(dev)
+        blob = w4.repack_weights(q, K, N)
+        del q
+        s = torch.from_numpy(sc.view(np.int16)).to(dev)
+        a = torch.from_numpy(A.view(np.int16)).to(dev).view(torch.bfloat16)
+        self.blobs = [blob] + [blob.clone() for _ in range(sets - 1)]
+        self.scales = [s] + [s.clone() for _ in range(sets - 1)]
+        self.acts = [a] + [a.clone() for _ in range(sets - 1)]
+        self.outs = [torch.empty((Mmax, N), dtype=torch.bfloat16, device=dev) for _ in range(sets)]
+        self.K, self.N, self.sets = K, N, sets
+        torch.cuda.synchronize()
+
+    def call(self, w4, M, i):
+        j = i % self.sets
+        w4.gemm(self.acts[j][:M], self.blobs[j], self.scales[j], self.N, out=self.outs[j][:M])
+
+
+def sets_for(K, N, M):
+    per = synth.algorithmic_bytes(M, N, K)
+    return max(1, -(-ROTATE_BYTES // per)) if per < 4 * LLC_BYTES else 1
+
+
+def time_graph(torch, fn, steps, warmup):
+    """Warm up eagerly, capture `steps` calls in one graph, replay and time it (ms/step)."""
+    for i in range(warmup):
+        fn(i)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    stream = torch.cuda.Stream()
+    stream.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(stream):
+        with torch.cuda.graph(g, stream=stream):
+            for i in range(steps):
+                fn(i)
+    torch.cuda.synchronize()
+    g.replay()                      # warm replay
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / steps
+
+
+def time_eager_per_launch(torch, fn, launches):
+    """Average GPU duration of one call: an event pair around every launch (ms)."""
+    stream = torch.cuda.current_stream()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(launches)]
+    torch.cuda.synchronize()
+    for i, (a, b) in enumerate(evs):
+        a.record(stream)
+        fn(i)
+        b.record(stream)
+    torch.cuda.synchronize()
+    ts = sorted(a.elapsed_time(b) for a, b in evs)
+    return sum(ts) / len(ts), ts[len(ts) // 2]
+
+
+def measure(torch, w4, prob, M, steps, warmup, launches=200):
+    ms_graph = time_graph(torch, lambda i: prob.call(w4, M, i), steps, warmup)
+    ms_kern, ms_kern_med = time_eager_per_launch(torch, lambda i: prob.call(w4, M, i), launches)
+    nbytes = synth.algorithmic_bytes(M, prob.N, prob.K)
+    flops = 2.0 * M * prob.N * prob.K
+    return {
+        "ms_per_step": ms_graph,
+        "us_per_call": ms_graph * 1e3,
+        "gbs": nbytes / (ms_graph * 1e-3) / 1e9,
+        "kernel_us": ms_kern * 1e3,
+        "kernel_us_median": ms_kern_med * 1e3,
+        "kernel_gbs": nbytes / (ms_kern * 1e-3) / 1e9,
+        "bytes": nbytes,
+        "tflops": flops / (ms_kern * 1e-3) / 1e12,
+    }
+
+
+def cpu_baseline(prob, M, seconds=10.0):
+    import oracle
+
+    A, qw, sc = prob.host
+    nthreads = oracle.max_threads()
+    oracle.gemm(A, qw, sc, M, prob.N, prob.K, cols=np.arange(64))    # load + warm
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        oracle.gemm(A, qw, sc, M, prob.N, prob.K, nthreads=nthreads)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= seconds:
+            break
+    nbytes = synth.algorithmic_bytes(M, prob.N, prob.K) * reps
+    return {"value": round(nbytes / el / 1e9, 3), "unit": "GB/s", "cores": nthreads, "kind": "oracle",
+            "sample": f"{reps} full calls of the same workload (M={M}, K={prob.K}, N={prob.N}), "
+                      f"{el:.1f} s wall, fp64 C oracle with OpenMP over columns; "
+                      f"{el / reps * 1e6:.0f} us/call"}
+
+
+def traffic_record(name):
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    try:
+        with open(path) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    entry = rec.get(name)
+    if not entry or entry.get("source_hash") != kernel_source_hash():
+        return None
+    return entry.get("bytes_per_launch")
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=400)
+    ap.add_argument("--warmup", type=int, default=50)
+    ap.add_argument("--workload", default="qkv", choices=sorted(synth.WORKLOADS))
+    ap.add_argument("--m", type=int, default=1)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--sweep", action="store_true", help="one JSON line per (workload, M)")
+    ap.add_argument("--stack", action="store_true", help="full decode-step sweep of linear shapes")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py: this build measures one GPU; --gpus {args.gpus} is not supported "
+              f"(the matmul shards by columns without communication, see DESIGN.md)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import weight_only_int4_gptq_amd as w4
+
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    torch.cuda.set_device(0)
+    name = torch.cuda.get_device_name(0)
+
+    if args.sweep:
+        return sweep(torch, w4, args)
+    if args.stack:
+        return stack(torch, w4, args)
+
+    wl = synth.WORKLOADS[args.workload]
+    M = args.m
+    sets = sets_for(wl.K, wl.N, M)
+    log(f"bench: {wl.desc} M={M} on {name}; {sets} buffer sets")
+    prob = Problem(torch, w4, wl.K, wl.N, wl.seed, wl.act, sets)
+    r = measure(torch, w4, prob, M, args.steps, args.warmup)
+    plan = w4.get_plan(M, wl.N, wl.K).as_dict()
+    log(f"bench: graph {r['us_per_call']:.2f} us/call {r['gbs']:.0f} GB/s; "
+        f"kernel {r['kernel_us']:.2f} us {r['kernel_gbs']:.0f} GB/s; plan {plan}")
+
+    roof = {"bound": "hbm", "achieved": round(r["kernel_gbs"], 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+            "frac": round(r["kernel_gbs"] / PEAK_HBM_GBS, 4),
+            "traffic": traffic_record(f"{args.workload}_m{M}")}
+    out = {
+        "metric": METRIC,
+        "value": round(r["gbs"], 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(r["ms_per_step"], 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": f"{args.workload}: {wl.desc}, M={M}, group 128",
+            "M": M, "K": wl.K, "N": wl.N, "group": 128,
+            "us_per_call": round(r["us_per_call"], 3),
+            "pct_of_peak_hbm": round(100 * r["gbs"] / PEAK_HBM_GBS, 2),
+            "kernel_us_per_call": round(r["kernel_us"], 3),
+            "algorithmic_bytes_per_call": r["bytes"],
+            "buffer_sets": sets,
+            "plan": plan,
+            "timing": "value: one HIP graph of `steps` calls; roofline: event pair per eager launch",
+            "device": name,
+        },
+        "roofline": roof,
+    }
+    if M == 16:
+        out["config"]["mfma_util"] = round(r["tflops"] / PEAK_BF16_TFLOPS, 4)
+    if not args.no_cpu:
+        log("bench: timing the CPU oracle ...")
+        out["cpu_baseline"] = cpu_baseline(prob, M, args.cpu_seconds)
+    else:
+        out["cpu_baseline"] = None
+    print(json.dumps(out), flush=True)
+
+
+def sweep(torch, w4, args):
+    for wname in ("qkv", "gate_up", "down", "lm_head"):
+        wl = synth.WORKLOADS[wname]
+        Ms = sorted(set(wl.Ms) | {1, 4, 8, 16})
+        sets = sets_for(wl.K, wl.N, 1)
+        prob = Problem(torch, w4, wl.K, wl.N, wl.seed, wl.act, sets)
+        for M in Ms:
+            steps = max(20, min(args.steps, int(2e6 / synth.algorithmic_bytes(M, wl.N, wl.K) * 100)))
+            r = measure(torch, w4, prob, M, steps, min(args.warmup, 20), launches=min(100, steps))
+            rec = {"workload": wname, "M": M, "K": wl.K, "N": wl.N, "plan": w4.get_plan(M, wl.N, wl.K).as_dict(),
+                   "us_per_call": round(r["us_per_call"], 3), "GBps": round(r["gbs"], 1),
+                   "pct_peak": round(100 * r["gbs"] / PEAK_HBM_GBS, 2),
+                   "kernel_us": round(r["kernel_us"], 3), "kernel_GBps": round(r["kernel_gbs"], 1),
+                   "kernel_pct_peak": round(100 * r["kernel_gbs"] / PEAK_HBM_GBS, 2),
+                   "mfma_util": round(r["tflops"] / PEAK_BF16_TFLOPS, 4), "sets": sets}
+            print(json.dumps(rec), flush=True)
+        del prob
+        torch.cuda.empty_cache()
+
+
+def stack(torch, w4, args):
+    """One decode step: 64 layers x (attn-in, attn-out, gate/up, down) + lm_head, all resident."""
+    dev = torch.device("cuda:0")
+    for M in (1, 8):
+        probs = {}
+        for (K, N) in set(synth.STACK_LAYER_SHAPES) | {synth.LM_HEAD_SHAPE}:
+            probs[(K, N)] = Problem(torch, w4, K, N, K + N, "normal", 1)
+        # every layer gets its own weights: 64 copies of each layer shape
+        layers = []
+        for li in range(synth.STACK_LAYERS):
+            for (K, N) in synth.STACK_LAYER_SHAPES:
+                p = probs[(K, N)]
+                blob = p.blobs[0] if li == 0 else p.blobs[0].clone()
+                sc = p.scales[0] if li == 0 else p.scales[0].clone()
+                layers.append((K, N, blob, sc, p.acts[0], p.outs[0]))
+        K, N = synth.LM_HEAD_SHAPE
+        p = probs[(K, N)]
+        layers.append((K, N, p.blobs[0], p.scales[0], p.acts[0], p.outs[0]))
+        total = sum(synth.algorithmic_bytes(M, N, K) for (K, N, *_ ) in layers)
+
+        def step(_i):
+            for (K, N, blob, sc, a, o) in layers:
+                w4.gemm(a[:M], blob, sc, N, out=o[:M])
+
+        ms = time_graph(torch, step, 3, 2)
+        print(json.dumps({"stack": "64 layers x 4 linear shapes + lm_head", "M": M, "calls": len(layers),
+                          "bytes": total, "ms_per_step": round(ms, 4),
+                          "GBps": round(total / (ms * 1e-3) / 1e9, 1),
+                          "pct_peak": round(100 * total / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 2)}), flush=True)
+        del layers, probs, p
+        torch.cuda.empty_cache()
+    _ = dev
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,174 @@
+/*
+ * w4a16.h - C ABI of a gfx950 (MI355X) library for the weight-only INT4
+ * decode/verify matmul
+ *
+ *     C[M, N] = A[M, K] . dequant(Wq)[K, N],   1 <= M <= 16,
+ *
+ * with BF16 activations A, BF16 output C and weights Wq in the symmetric GPTQ
+ * 4-bit format: group size 128 along K, no zero points, no act-order.  That
+ * checkpoint contract is stated on the page "Qwen3.8-27B on single DGX Spark
+ * ..." (section "Quality."); the same page (section "How.") describes the
+ * backbone and output-projection matmuls as kernels dispatched by row count,
+ * and the page "One Config Line Made My 27B Model 2.7x Faster" (section "The
+ * fix: use the MTP head you already downloaded") explains why decode calls it
+ * with one row and speculative verify with a handful of rows.
+ *
+ * Formats
+ *   qweight  uint32 [K/8][N], N contiguous.  Nibble j of word (kb, n), i.e.
+ *            bits 4j..4j+3 (low nibble first), is the code q in [0, 15] of
+ *            row k = 8*kb + j.  The weight is w = (q - 8) * s.
+ *   scales   bf16 [K/128][N], N contiguous: s for (group floor(k/128), column n).
+ *   A        bf16 [M][K], K contiguous (row stride K).
+ *   C        bf16 [M][N], N contiguous (row stride N); fp32 accumulation,
+ *            rounded to nearest even once at the end.
+ *   blob     the repacked weights: exactly K*N/2 bytes.  Layout: 16-byte
+ *            pieces; piece (t, g, h, c) at piece index ((t*G + g)*4 + h)*16 + c
+ *            (G = K/128) holds column n = 16t + c, rows k = 128g + 32h + 8r + e
+ *            in its word r = 0..3; inside a word the code of row offset e sits
+ *            at bit 4*(e/2) for even e and 16 + 4*(e/2) for odd e.
+ *
+ * Conventions shared by every entry point
+ *   - Every pointer argument except `stream` is DEVICE memory owned by the
+ *     caller.  The library allocates nothing and keeps no state between calls
+ *     other than a lazily filled cache of device properties.
+ *   - Work is enqueued on `stream` (a hipStream_t; NULL = the null stream) and
+ *     is asynchronous: a return of W4A16_OK means the launch was accepted,
+ *     not that the kernel has finished.  Nothing synchronizes.
+ *   - Arguments are validated before any device work; an invalid call returns
+ *     a negative status and enqueues nothing.  No call aborts the process and
+ *     no unsupported case falls back silently to another path.
+ *   - Device pointers must be 16-byte aligned.  Output buffers must not
+ *     overlap any input (not checked).
+ *   - Valid shapes: 1 <= M <= 16, K a positive multiple of 128, N a positive
+ *     multiple of 16, K*N/2 < 2^40.  group must be 128.
+ */
+#ifndef W4A16_H
+#define W4A16_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes returned by every int-valued entry point. */
+#define W4A16_OK              0
+#define W4A16_ERR_NULL       -1   /* a required pointer is NULL */
+#define W4A16_ERR_SHAPE      -2   /* M, N or K outside the valid set */
+#define W4A16_ERR_GROUP      -3   /* group != 128 */
+#define W4A16_ERR_ALIGN      -4   /* a device pointer is not 16-byte aligned */
+#define W4A16_ERR_WORKSPACE  -5   /* the plan needs a workspace that is missing or too small */
+#define W4A16_ERR_DEVICE     -6   /* no HIP device, or the current device is not gfx950 */
+#define W4A16_ERR_LAUNCH     -7   /* the HIP runtime rejected a launch */
+#define W4A16_ERR_PLAN       -8   /* an explicit plan names a variant this build does not have */
+
+#define W4A16_GROUP 128
+#define W4A16_MAX_M 16
+
+/* Execution paths of the row-count dispatcher. */
+#define W4A16_PATH_AUTO 0
+#define W4A16_PATH_GEMV 1   /* VALU dot products, cross-lane reduction (small M) */
+#define W4A16_PATH_MFMA 2   /* bf16 matrix cores, 16x16x32 tiles (larger M) */
+
+/* Where the MFMA path takes its A operand from. */
+#define W4A16_ASRC_LDS    0  /* staged once per workgroup in LDS */
+#define W4A16_ASRC_GLOBAL 1  /* read per group from global memory (L1/L2) */
+
+/*
+ * A launch plan.  w4a16_gemm chooses one from (M, N, K); w4a16_gemm_plan
+ * runs an explicit one (tests force each path with it).
+ *   path    W4A16_PATH_GEMV or W4A16_PATH_MFMA
+ *   tiles   16-column tiles per wavefront (1, 2 or 4)
+ *   kwaves  wavefronts of one workgroup that split the workgroup's K range
+ *   splits  workgroups that split K for the same columns (1 = none); more
+ *           than one needs a workspace (see w4a16_workspace_bytes)
+ *   asrc    W4A16_ASRC_LDS or W4A16_ASRC_GLOBAL (MFMA path only)
+ */
+typedef struct {
+    int path;
+    int tiles;
+    int kwaves;
+    int splits;
+    int asrc;
+} w4a16_plan_t;
+
+/* Human-readable name of a status code (static storage, never NULL). */
+const char *w4a16_status_string(int status);
+
+/* Bytes of the repacked blob for a K x N matrix (= K*N/2), 0 for invalid shapes. */
+size_t w4a16_repacked_bytes(int K, int N);
+
+/*
+ * One-time repack of GPTQ words into the blob layout described above.
+ *   qweight      device, uint32 [K/8][N] as in the header comment (read only)
+ *   wq_repacked  device, w4a16_repacked_bytes(K, N) bytes (written)
+ * A pure permutation of nibbles: every code is moved, none is changed.
+ * Returns W4A16_OK or an error status.
+ */
+int w4a16_repack_weights(const void *qweight, void *wq_repacked, int K, int N, void *stream);
+
+/*
+ * The plan w4a16_gemm uses for (M, N, K): fills *plan and returns W4A16_OK,
+ * or returns an error status for invalid shapes.  Host-only, no device work.
+ */
+int w4a16_get_plan(int M, int N, int K, w4a16_plan_t *plan);
+
+/*
+ * W4A16_OK if this build can run `plan` for (M, N, K) (a kernel exists and
+ * its LDS fits), W4A16_ERR_PLAN if not, W4A16_ERR_SHAPE for invalid shapes.
+ * Host-only, no device work.
+ */
+int w4a16_check_plan(int M, int N, int K, const w4a16_plan_t *plan);
+
+/*
+ * Workspace bytes a plan needs: fp32 partials [splits][M][N] plus one 32-bit
+ * counter per column strip, or 0 when splits == 1.  plan == NULL means the
+ * plan w4a16_gemm would choose.  Returns 0 for invalid arguments.
+ * A workspace must be zero-filled before its first use; every call returns
+ * its counters to zero, so it can be reused without clearing.  Calls that
+ * share a workspace must not run concurrently.
+ */
+size_t w4a16_workspace_bytes(int M, int N, int K, const w4a16_plan_t *plan);
+
+/*
+ * C = A . dequant(blob, scales), dispatched by row count.
+ *   A            device bf16 [M][K]
+ *   wq_repacked  device blob from w4a16_repack_weights for this K, N
+ *   scales       device bf16 [K/128][N]
+ *   C            device bf16 [M][N] (written)
+ *   group        must be 128
+ *   workspace    device, at least w4a16_workspace_bytes(M, N, K, NULL) bytes,
+ *                zero-filled before first use; may be NULL when that is 0
+ * Deterministic: the same arguments give bitwise the same C.
+ */
+int w4a16_gemm(const void *A, const void *wq_repacked, const void *scales, void *C,
+               int M, int N, int K, int group, void *workspace, size_t workspace_bytes,
+               void *stream);
+
+/*
+ * As w4a16_gemm, with an explicit plan (plan == NULL: same as w4a16_gemm).
+ * Returns W4A16_ERR_PLAN when this build has no kernel for the plan.
+ */
+int w4a16_gemm_plan(const void *A, const void *wq_repacked, const void *scales, void *C,
+                    int M, int N, int K, int group, void *workspace, size_t workspace_bytes,
+                    const w4a16_plan_t *plan, void *stream);
+
+/*
+ * Test export of the device dequantization used by both GEMM paths:
+ * W[k][n] = (q - 8) * s as fp32 (exact), device fp32 [K][N] (written).
+ */
+int w4a16_dequant(const void *wq_repacked, const void *scales, float *W, int K, int N,
+                  void *stream);
+
+/*
+ * Test export of the device unpacking used by both GEMM paths:
+ * codes[k][n] = q in [0, 15], device uint8 [K][N] (written).
+ */
+int w4a16_unpack(const void *wq_repacked, uint8_t *codes, int K, int N, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* W4A16_H */

@@ -65,8 +65,8 @@ void oracle_unpack(const uint32_t *qweight, int K, int N, uint8_t *codes) {
             codes[(size_t)k * N + n] = (uint8_t)code_at(qweight, N, k, n);
 }
 
-/* W[k*N + n] = (q(k,n) - 8) * s[floor(k/128)][n], exact in fp64 (and, as
- * it happens, exactly representable in fp32 as well). */
+/* W[k*N + n] = (q(k,n) - 8) * s[floor(k/128)][n], exact in fp64 (and also
+ * exactly representable in fp32 whenever |q - 8| * s stays in fp32 range). */
 void oracle_dequant(const uint32_t *qweight, const uint16_t *scales, int K, int N,
                     double *W) {
     for (int k = 0; k < K; ++k) {

@@ -1,0 +1,133 @@
+"""C-ABI checks that need no GPU: exported symbols, argument validation, planning.
+
+Every error here is raised by the host-side checks before any device work,
+so these run on a machine without a GPU.  Compute calls are not made.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import weight_only_int4_gptq_amd as w4
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "w4a16.h")
+
+# fake, 16-byte aligned "device" addresses: never dereferenced, because every
+# call below fails its argument checks first
+P = ctypes.c_void_p(0x10000)
+P2 = ctypes.c_void_p(0x20000)
+ODD = ctypes.c_void_p(0x10008)
+NULL = ctypes.c_void_p(0)
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"\b(w4a16_[a-z_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    names = declared_functions()
+    assert len(names) >= 9
+    lib = w4.lib()
+    for name in names:
+        assert hasattr(lib, name), name
+
+
+def test_status_strings():
+    for st in range(-8, 1):
+        s = w4.status_string(st)
+        assert s and s != "unknown status"
+    assert w4.status_string(-99) == "unknown status"
+
+
+def test_repacked_bytes():
+    assert w4.repacked_bytes(5120, 8192) == 5120 * 8192 // 2
+    assert w4.repacked_bytes(100, 16) == 0
+    assert w4.repacked_bytes(128, 8) == 0
+
+
+def _gemm(A=P, wq=P, s=P, C=P2, M=1, N=1024, K=512, group=128, ws=NULL, wsb=0, plan=None):
+    L = w4.lib()
+    if plan is None:
+        return L.w4a16_gemm(A, wq, s, C, M, N, K, group, ws, wsb, NULL)
+    return L.w4a16_gemm_plan(A, wq, s, C, M, N, K, group, ws, wsb, ctypes.byref(plan), NULL)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(A=NULL), -1), (dict(wq=NULL), -1), (dict(s=NULL), -1), (dict(C=NULL), -1),
+    (dict(M=0), -2), (dict(M=17), -2), (dict(K=500), -2), (dict(K=0), -2), (dict(N=1000), -2),
+    (dict(N=-16), -2), (dict(group=64), -3), (dict(A=ODD), -4), (dict(C=ODD), -4),
+    (dict(s=ODD), -4), (dict(wq=ODD), -4),
+])
+def test_gemm_argument_errors(kw, status):
+    assert _gemm(**kw) == status
+
+
+def test_gemm_plan_errors():
+    bad = [
+        w4.make_plan(w4.PATH_GEMV, 1, 4),             # GEMV for M > 4
+        w4.make_plan(3, 1, 4),                        # unknown path
+        w4.make_plan(w4.PATH_MFMA, 3, 4),             # no such tile count
+        w4.make_plan(w4.PATH_MFMA, 1, 5),             # no such wave count
+        w4.make_plan(w4.PATH_MFMA, 1, 4, splits=0),
+        w4.make_plan(w4.PATH_MFMA, 1, 4, splits=5),   # more splits than K groups (K=512)
+        w4.make_plan(w4.PATH_MFMA, 1, 4, asrc=7),
+    ]
+    for p in bad:
+        assert _gemm(M=8, plan=p) == -8, p
+
+
+def test_split_plan_needs_workspace():
+    p = w4.make_plan(w4.PATH_MFMA, 1, 4, splits=2)
+    need = w4.workspace_bytes(8, 1024, 512, p)
+    assert need >= 2 * 8 * 1024 * 4
+    assert _gemm(M=8, plan=p) == -5
+    assert _gemm(M=8, plan=p, ws=P, wsb=need - 1) == -5
+    assert w4.workspace_bytes(8, 1024, 512) == 0       # the automatic plan never splits
+
+
+def test_no_device_is_an_error_not_a_crash():
+    # valid arguments: on a machine without a gfx950 GPU the device check fails
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present")
+    assert _gemm() == -6
+    assert w4.lib().w4a16_repack_weights(P, P2, 512, 1024, NULL) == -6
+    assert w4.lib().w4a16_dequant(P, P, P2, 512, 1024, NULL) == -6
+
+
+def test_repack_and_export_argument_errors():
+    L = w4.lib()
+    assert L.w4a16_repack_weights(NULL, P, 512, 1024, NULL) == -1
+    assert L.w4a16_repack_weights(P, P2, 500, 1024, NULL) == -2
+    assert L.w4a16_repack_weights(P, P2, 512, 1000, NULL) == -2
+    assert L.w4a16_repack_weights(ODD, P2, 512, 1024, NULL) == -4
+    assert L.w4a16_dequant(P, NULL, P2, 512, 1024, NULL) == -1
+    assert L.w4a16_unpack(P, NULL, 512, 1024, NULL) == -1
+    assert L.w4a16_unpack(P, P2, 512, 1000, NULL) == -2
+
+
+def test_row_count_dispatch():
+    # GEMV for M <= 4 while its LDS staging fits, matrix cores above
+    for M in range(1, 17):
+        p = w4.get_plan(M, 34816, 5120)
+        assert p.path == (w4.PATH_GEMV if M <= 4 else w4.PATH_MFMA), (M, p)
+        assert p.splits == 1
+    # narrow N: more wavefronts along K
+    assert w4.get_plan(1, 8192, 5120).kwaves == 8
+    assert w4.get_plan(1, 248320, 5120).tiles == 2
+    # tiny K: no more K waves than K groups
+    assert w4.get_plan(1, 1024, 512).kwaves <= 4
+    p = w4.Plan()
+    assert w4.lib().w4a16_get_plan(0, 1024, 512, ctypes.byref(p)) == -2
+
+
+def test_check_plan():
+    ok = w4.make_plan(w4.PATH_MFMA, 1, 8, 1, w4.ASRC_GLOBAL)
+    assert w4.plan_ok(16, 34816, 5120, ok)
+    # staging 16 rows of K=5120 in LDS does not fit one workgroup's budget
+    assert not w4.plan_ok(16, 34816, 5120, w4.make_plan(w4.PATH_MFMA, 1, 8, 1, w4.ASRC_LDS))
+    assert w4.plan_ok(16, 34816, 5120, w4.make_plan(w4.PATH_MFMA, 1, 8, 4, w4.ASRC_LDS))
+    assert w4.lib().w4a16_check_plan(0, 16, 128, ctypes.byref(ok)) == -2

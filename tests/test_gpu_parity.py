@@ -1,0 +1,264 @@
+"""GPU parity: the HIP path against the CPU oracle, through the C ABI.
+
+Bars (from the acceptance rule for this matmul):
+  * repack blob, unpacked codes and fp32 dequantized weights: bit-exact;
+  * C: max over outputs of |C_gpu - C_ref| / sum_k |a_k w_k| <= 2e-3, with
+    C_ref and the normalizer from the fp64 oracle on the same seeded inputs;
+  * special inputs whose exact result is representable: bitwise equal to the
+    round-to-nearest-even bf16 of the exact value;
+  * repeated calls and row prefixes: bitwise equal.
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+import weight_only_int4_gptq_amd as w4
+
+pytestmark = pytest.mark.gpu
+TOL = 2e-3
+DEV = "cuda:0"
+
+
+def note(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def to_dev(qweight, scales, A=None):
+    q = torch.from_numpy(qweight.view(np.int32)).to(DEV)
+    s = torch.from_numpy(scales.view(np.int16)).to(DEV)
+    a = None if A is None else torch.from_numpy(np.ascontiguousarray(A).view(np.int16)).to(DEV).view(torch.bfloat16)
+    return q, s, a
+
+
+def c_bits(C):
+    return C.view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def run_gemm(a, blob, s, N, M, plan=None, ws=None):
+    out = w4.gemm(a[:M].contiguous(), blob, s, N, plan=plan, workspace=ws)
+    torch.cuda.synchronize()
+    return out
+
+
+def max_err(C, Cref, Dref):
+    e = oracle.normalized_error(oracle.bf16_bits_to_f64(c_bits(C)), Cref, Dref)
+    return float(e.max())
+
+
+# ------------------------------------------------------------- plans to force
+ALL_PLANS = []
+for path in (w4.PATH_GEMV, w4.PATH_MFMA):
+    for (t, kw) in ((1, 4), (1, 8), (2, 4), (2, 8), (4, 4), (1, 1)):
+        for asrc in ((w4.ASRC_LDS,) if path == w4.PATH_GEMV else (w4.ASRC_LDS, w4.ASRC_GLOBAL)):
+            ALL_PLANS.append(w4.make_plan(path, t, kw, 1, asrc))
+
+
+def plans_for(M, N, K):
+    """Every single-split plan this build can run for (M, N, K)."""
+    return [p for p in ALL_PLANS if w4.plan_ok(M, N, K, p)]
+
+
+# ------------------------------------------------------------- bit-exact weights
+
+@pytest.mark.parametrize("K,N,seed", [(128, 16, 1), (512, 1024, 0), (1152, 592, 2), (5120, 8192, 1)])
+def test_repack_unpack_dequant_bit_exact(K, N, seed):
+    note(f"[repack/unpack/dequant] K={K} N={N} seed={seed}")
+    _, qw, sc = synth.gen_problem(K, N, seed, M=1)
+    q, s, _ = to_dev(qw, sc)
+    blob = w4.repack_weights(q, K, N)
+    codes = w4.unpack(blob, K, N)
+    W = w4.dequant(blob, s, K, N)
+    torch.cuda.synchronize()
+    ref_blob = oracle.repack(qw, K, N)
+    assert np.array_equal(blob.cpu().numpy().view(np.uint32), ref_blob)
+    assert np.array_equal(codes.cpu().numpy(), oracle.unpack(qw, K, N))
+    Wd = W.cpu().numpy().astype(np.float64)
+    assert np.array_equal(Wd, oracle.dequant(qw, sc, K, N))
+
+
+def test_dequant_subnormal_and_extreme_scales():
+    K, N = 256, 32
+    _, qw, _ = synth.gen_problem(K, N, 9, M=1)
+    sc = np.zeros((K // 128, N), dtype=np.uint16)
+    sc[0, :] = np.arange(1, N + 1, dtype=np.uint16)            # subnormal bf16
+    # large scales, just below the point where 8 * s leaves the fp32 range
+    # (above it the fp32 export correctly overflows where fp64 does not)
+    sc[1, :] = 0x7D00 + np.arange(N, dtype=np.uint16)          # about 2^123 .. 2^124
+    q, s, _ = to_dev(qw, sc)
+    blob = w4.repack_weights(q, K, N)
+    W = w4.dequant(blob, s, K, N)
+    torch.cuda.synchronize()
+    assert np.array_equal(W.cpu().numpy().astype(np.float64), oracle.dequant(qw, sc, K, N))
+
+
+# ------------------------------------------------------------- GEMM, all plans
+
+SMALL_SHAPES = [(512, 1024, 0), (1152, 592, 5), (384, 48, 6), (128, 16, 7), (2048, 272, 8)]
+
+
+@pytest.mark.parametrize("K,N,seed", SMALL_SHAPES)
+def test_gemm_parity_every_plan_every_m(K, N, seed):
+    A, qw, sc = synth.gen_problem(K, N, seed)
+    q, s, a = to_dev(qw, sc, A)
+    blob = w4.repack_weights(q, K, N)
+    Cref16, Dref16 = oracle.gemm(A, qw, sc, 16, N, K)
+    worst = 0.0
+    for M in range(1, 17):
+        cases = [None] + plans_for(M, N, K)
+        note(f"[gemm] K={K} N={N} M={M}: {len(cases)} plans")
+        for p in cases:
+            C = run_gemm(a, blob, s, N, M, plan=p)
+            e = max_err(C, Cref16[:M], Dref16[:M])
+            worst = max(worst, e)
+            assert e <= TOL, (M, p, e)
+    note(f"  worst normalized error {worst:.3e}")
+
+
+@pytest.mark.parametrize("splits", [2, 3, 5])
+def test_gemm_split_k_parity_and_reuse(splits):
+    K, N = 1280, 528
+    A, qw, sc = synth.gen_problem(K, N, 21)
+    q, s, a = to_dev(qw, sc, A)
+    blob = w4.repack_weights(q, K, N)
+    Cref, Dref = oracle.gemm(A, qw, sc, 16, N, K)
+    for M in (1, 3, 4, 8, 16):
+        for path, asrc in ((w4.PATH_GEMV, 0), (w4.PATH_MFMA, 0), (w4.PATH_MFMA, 1)):
+            if path == w4.PATH_GEMV and M > 4:
+                continue
+            for t, kw in ((1, 4), (2, 8)):
+                p = w4.make_plan(path, t, kw, splits, asrc)
+                nbytes = w4.workspace_bytes(M, N, K, p)
+                assert nbytes > 0
+                ws = torch.zeros(nbytes, dtype=torch.uint8, device=DEV)
+                note(f"[split-k] M={M} plan={p}")
+                C1 = run_gemm(a, blob, s, N, M, plan=p, ws=ws)
+                C2 = run_gemm(a, blob, s, N, M, plan=p, ws=ws)   # counters were reset
+                assert max_err(C1, Cref[:M], Dref[:M]) <= TOL
+                assert torch.equal(C1.view(torch.int16), C2.view(torch.int16))
+                cnt_off = (splits * M * N * 4 + 255) // 256 * 256
+                assert int(ws[cnt_off:].view(torch.int32).abs().sum()) == 0
+
+
+# ------------------------------------------------------------- exact special inputs
+
+def _pow2_bf16(e):
+    return ((127 + e) & 0xFF) << 7
+
+
+@pytest.mark.parametrize("word,colsum", [(0x76543210, -36), (0xFEDCBA98, 28), (0xFFFFFFFF, 56),
+                                          (0x00000000, -64), (0x88888888, 0)])
+def test_gemm_exact_ones(word, colsum):
+    # A = ones, s = 2^-3: C = 2^-3 * (K/8) * colsum exactly (an integer < 2^24 times 2^-3)
+    K, N = 2048, 64
+    A = np.full((16, K), 0x3F80, dtype=np.uint16)
+    qw = np.full((K // 8, N), word, dtype=np.uint32)
+    sc = np.full((K // 128, N), _pow2_bf16(-3), dtype=np.uint16)
+    q, s, a = to_dev(qw, sc, A)
+    blob = w4.repack_weights(q, K, N)
+    exact = colsum * (K // 8) * 2.0 ** -3
+    expect = int(oracle.f32_exact_to_bf16_bits(np.array([exact]))[0])
+    for M in (1, 2, 4, 8, 16):
+        for p in [None] + plans_for(M, N, K):
+            C = run_gemm(a, blob, s, N, M, plan=p)
+            assert np.all(c_bits(C) == expect), (M, p)
+
+
+def test_gemm_exact_one_hot_rows_and_groups():
+    # q-8 = k % 8 everywhere; s[g, n] = 2^(g - n % 3); row m of A is one-hot at k_m
+    K, N = 1024, 48
+    qw = np.full((K // 8, N), 0xFEDCBA98, dtype=np.uint32)
+    sc = np.array([[_pow2_bf16(g - n % 3) for n in range(N)] for g in range(K // 128)], dtype=np.uint16)
+    ks = [0, 5, 127, 128, 129, 255, 300, 511, 512, 640, 777, 895, 896, 1000, 1022, 1023]
+    A = np.zeros((16, K), dtype=np.uint16)
+    for m, k in enumerate(ks):
+        A[m, k] = 0x3F80
+    q, s, a = to_dev(qw, sc, A)
+    blob = w4.repack_weights(q, K, N)
+    expect = np.array([[(k % 8) * 2.0 ** (k // 128 - n % 3) for n in range(N)] for k in ks])
+    ebits = oracle.f32_exact_to_bf16_bits(expect)
+    for M in (1, 4, 9, 16):
+        for p in [None] + plans_for(M, N, K):
+            C = run_gemm(a, blob, s, N, M, plan=p)
+            assert np.array_equal(c_bits(C), ebits[:M]), (M, p)
+
+
+def test_gemm_zero_weights_give_signed_zero_free_exact_zero():
+    K, N = 512, 32
+    A, _, sc = synth.gen_problem(K, N, 3)
+    qw = np.full((K // 8, N), 0x88888888, dtype=np.uint32)
+    q, s, a = to_dev(qw, sc, A)
+    blob = w4.repack_weights(q, K, N)
+    for M in (1, 4, 16):
+        C = run_gemm(a, blob, s, N, M)
+        assert np.all(oracle.bf16_bits_to_f64(c_bits(C)) == 0.0)
+
+
+# ------------------------------------------------------------- determinism
+
+def test_determinism_and_row_prefix():
+    K, N = 5120, 2048
+    A, qw, sc = synth.gen_problem(K, N, 31)
+    q, s, a = to_dev(qw, sc, A)
+    blob = w4.repack_weights(q, K, N)
+    for p in plans_for(16, N, K):
+        C16 = run_gemm(a, blob, s, N, 16, plan=p)
+        C16b = run_gemm(a, blob, s, N, 16, plan=p)
+        assert torch.equal(C16.view(torch.int16), C16b.view(torch.int16)), p
+        for M in (5, 8, 9):
+            CM = run_gemm(a, blob, s, N, M, plan=p)
+            assert torch.equal(CM.view(torch.int16), C16[:M].view(torch.int16)), (M, p)
+    for M in (1, 2, 3, 4):
+        C1 = run_gemm(a, blob, s, N, M)
+        C2 = run_gemm(a, blob, s, N, M)
+        assert torch.equal(C1.view(torch.int16), C2.view(torch.int16))
+
+
+# ------------------------------------------------------------- full workload sizes
+
+@pytest.mark.parametrize("name", ["tiny", "qkv", "gate_up", "down"])
+def test_workload_parity_full(name):
+    wl = synth.WORKLOADS[name]
+    K, N = wl.K, wl.N
+    note(f"[workload] {name} K={K} N={N} Ms={wl.Ms}")
+    A, qw, sc = synth.gen_workload(name)
+    q, s, a = to_dev(qw, sc, A)
+    blob = w4.repack_weights(q, K, N)
+    torch.cuda.synchronize()
+    assert np.array_equal(blob.cpu().numpy().view(np.uint32), oracle.repack(qw, K, N))
+    Ms = sorted(set(wl.Ms) | {1})
+    Cref, Dref = oracle.gemm(A, qw, sc, max(Ms), N, K)
+    for M in Ms:
+        C = run_gemm(a, blob, s, N, M)
+        e = max_err(C, Cref[:M], Dref[:M])
+        note(f"  M={M} plan={w4.get_plan(M, N, K)} max normalized error {e:.3e}")
+        assert e <= TOL
+
+
+def test_workload_parity_lm_head_sampled():
+    wl = synth.WORKLOADS["lm_head"]
+    K, N = wl.K, wl.N
+    A, qw, sc = synth.gen_workload("lm_head")
+    q, s, a = to_dev(qw, sc, A)
+    blob = w4.repack_weights(q, K, N)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(99)
+    tiles = np.unique(np.concatenate([[0, 1, N // 16 - 1], rng.integers(0, N // 16, 61)]))
+    hb = blob.view(torch.int32)
+    G = K // 128
+    for t in tiles:     # each 16-column tile's chunks are self-contained in the layout
+        sub = oracle.repack(np.ascontiguousarray(qw[:, 16 * t:16 * t + 16]), K, 16)
+        got = hb[t * G * 256:(t + 1) * G * 256].cpu().numpy().view(np.uint32)
+        assert np.array_equal(got, sub), t
+    cols = np.unique(np.concatenate([np.arange(16), np.arange(N - 16, N), rng.integers(0, N, 2000)]))
+    Cref, Dref = oracle.gemm(A, qw, sc, 16, N, K, cols=cols)
+    for M in (1, 8, 16):
+        C = run_gemm(a, blob, s, N, M)
+        Cs = C[:, torch.from_numpy(cols).to(DEV)]
+        e = max_err(Cs, Cref[:M], Dref[:M])
+        note(f"  lm_head M={M} plan={w4.get_plan(M, N, K)} max normalized error {e:.3e}")
+        assert e <= TOL

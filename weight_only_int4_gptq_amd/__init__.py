@@ -1,0 +1,154 @@
+"""Python binding of the gfx950 W4A16 decode/verify matmul library.
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels of ``libw4a16.so`` (built from ``csrc/``), called through its C ABI
+(``include/w4a16.h``).  PyTorch supplies device memory and the current
+stream.  If the library is not built, or a call returns an error status,
+the functions raise: there is no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libw4a16.so")
+
+OK = 0
+PATH_AUTO, PATH_GEMV, PATH_MFMA = 0, 1, 2
+ASRC_LDS, ASRC_GLOBAL = 0, 1
+GROUP = 128
+
+
+class W4A16Error(RuntimeError):
+    def __init__(self, status: int, what: str):
+        super().__init__(f"{what}: {status_string(status)} (status {status})")
+        self.status = status
+
+
+class Plan(ctypes.Structure):
+    _fields_ = [("path", ctypes.c_int), ("tiles", ctypes.c_int), ("kwaves", ctypes.c_int),
+                ("splits", ctypes.c_int), ("asrc", ctypes.c_int)]
+
+    def as_dict(self):
+        return {f: getattr(self, f) for f, _ in self._fields_}
+
+    def __repr__(self):
+        return f"Plan({self.as_dict()})"
+
+
+_lib = None
+
+
+def lib():
+    """The loaded libw4a16.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is not built; run __graft_entry__.build()")
+        L = ctypes.CDLL(LIB_PATH)
+        P, I, S = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
+        L.w4a16_status_string.argtypes = [I]
+        L.w4a16_status_string.restype = ctypes.c_char_p
+        L.w4a16_repacked_bytes.argtypes = [I, I]
+        L.w4a16_repacked_bytes.restype = S
+        L.w4a16_repack_weights.argtypes = [P, P, I, I, P]
+        L.w4a16_get_plan.argtypes = [I, I, I, ctypes.POINTER(Plan)]
+        L.w4a16_check_plan.argtypes = [I, I, I, ctypes.POINTER(Plan)]
+        L.w4a16_check_plan.restype = I
+        L.w4a16_workspace_bytes.argtypes = [I, I, I, ctypes.POINTER(Plan)]
+        L.w4a16_workspace_bytes.restype = S
+        L.w4a16_gemm.argtypes = [P, P, P, P, I, I, I, I, P, S, P]
+        L.w4a16_gemm_plan.argtypes = [P, P, P, P, I, I, I, I, P, S, ctypes.POINTER(Plan), P]
+        L.w4a16_dequant.argtypes = [P, P, P, I, I, P]
+        L.w4a16_unpack.argtypes = [P, P, I, I, P]
+        for f in ("w4a16_repack_weights", "w4a16_get_plan", "w4a16_gemm", "w4a16_gemm_plan",
+                  "w4a16_dequant", "w4a16_unpack"):
+            getattr(L, f).restype = I
+        _lib = L
+    return _lib
+
+
+def status_string(status: int) -> str:
+    return lib().w4a16_status_string(int(status)).decode()
+
+
+def _check(status: int, what: str):
+    if status != OK:
+        raise W4A16Error(status, what)
+
+
+def _stream(t: torch.Tensor):
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
+
+
+def repacked_bytes(K: int, N: int) -> int:
+    return int(lib().w4a16_repacked_bytes(K, N))
+
+
+def repack_weights(qweight: torch.Tensor, K: int, N: int, out: torch.Tensor | None = None):
+    """GPTQ words (int32/uint32 device tensor [K/8, N]) -> repacked blob (uint8 [K*N/2])."""
+    nbytes = repacked_bytes(K, N)
+    if out is None:
+        out = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=qweight.device)
+    _check(lib().w4a16_repack_weights(_ptr(qweight), _ptr(out), K, N, _stream(qweight)),
+           "w4a16_repack_weights")
+    return out
+
+
+def get_plan(M: int, N: int, K: int) -> Plan:
+    p = Plan()
+    _check(lib().w4a16_get_plan(M, N, K, ctypes.byref(p)), "w4a16_get_plan")
+    return p
+
+
+def make_plan(path: int, tiles: int, kwaves: int, splits: int = 1, asrc: int = ASRC_LDS) -> Plan:
+    return Plan(path, tiles, kwaves, splits, asrc)
+
+
+def plan_ok(M: int, N: int, K: int, plan: Plan) -> bool:
+    """True if this build can run `plan` for (M, N, K)."""
+    return lib().w4a16_check_plan(M, N, K, ctypes.byref(plan)) == OK
+
+
+def workspace_bytes(M: int, N: int, K: int, plan: Plan | None = None) -> int:
+    return int(lib().w4a16_workspace_bytes(M, N, K, ctypes.byref(plan) if plan else None))
+
+
+def gemm(A: torch.Tensor, blob: torch.Tensor, scales: torch.Tensor, N: int,
+         out: torch.Tensor | None = None, plan: Plan | None = None,
+         workspace: torch.Tensor | None = None, group: int = GROUP):
+    """C[M, N] = A[M, K] . dequant(blob, scales); A and C bf16 device tensors."""
+    M, K = A.shape
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.bfloat16, device=A.device)
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    if plan is None:
+        st = lib().w4a16_gemm(_ptr(A), _ptr(blob), _ptr(scales), _ptr(out), M, N, K, group,
+                              _ptr(workspace), ws_bytes, _stream(A))
+    else:
+        st = lib().w4a16_gemm_plan(_ptr(A), _ptr(blob), _ptr(scales), _ptr(out), M, N, K, group,
+                                   _ptr(workspace), ws_bytes, ctypes.byref(plan), _stream(A))
+    _check(st, "w4a16_gemm")
+    return out
+
+
+def dequant(blob: torch.Tensor, scales: torch.Tensor, K: int, N: int) -> torch.Tensor:
+    """Test export: fp32 W[K, N] = (q - 8) * s from the device dequantization."""
+    W = torch.empty((K, N), dtype=torch.float32, device=blob.device)
+    _check(lib().w4a16_dequant(_ptr(blob), _ptr(scales), _ptr(W), K, N, _stream(blob)),
+           "w4a16_dequant")
+    return W
+
+
+def unpack(blob: torch.Tensor, K: int, N: int) -> torch.Tensor:
+    """Test export: codes uint8 [K, N] from the device unpacking."""
+    codes = torch.empty((K, N), dtype=torch.uint8, device=blob.device)
+    _check(lib().w4a16_unpack(_ptr(blob), _ptr(codes), K, N, _stream(blob)), "w4a16_unpack")
+    return codes

@@ -1,0 +1,319 @@
+// C ABI, argument checks and row-count dispatcher of the W4A16 library.
+//
+// The backbone and output-projection matmuls of the decode engine described on
+// the page "Qwen3.8-27B on single DGX Spark ..." (section "How.") are
+// dispatched by row count; here the row count M picks between a VALU path
+// (v_dot2_f32_bf16 with a cross-lane reduction) and a matrix-core path
+// (v_mfma_f32_16x16x32_bf16), and (M, N, K) pick the work decomposition.
+// Everything is launched on the caller's stream; nothing is allocated.
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cstdint>
+#include <cstring>
+
+#include "w4a16.h"
+#include "w4a16_kernels.hpp"
+
+namespace {
+
+using namespace w4a16;
+
+constexpr int kLdsBudget = 64 * 1024;   // per workgroup: at least two workgroups per CU
+
+// ---------------------------------------------------------------- kernel table
+
+using KernelFn = void (*)(GemmArgs);
+
+struct Variant {
+    int path, mm, tiles, kwaves, asrc;   // mm: GEMV rows (1..4), 0 for MFMA
+    KernelFn fn;
+};
+
+#define GEMV_V(MM, T, KW, D) {PATH_GEMV, MM, T, KW, ASRC_LDS, gemm_kernel<PATH_GEMV, MM, T, KW, D, ASRC_LDS>}
+#define GEMV_ALL_M(T, KW, D) GEMV_V(1, T, KW, D), GEMV_V(2, T, KW, D), GEMV_V(3, T, KW, D), GEMV_V(4, T, KW, D)
+#define MFMA_V(T, KW, D, AS) {PATH_MFMA, 0, T, KW, AS, gemm_kernel<PATH_MFMA, 0, T, KW, D, AS>}
+
+const Variant kVariants[] = {
+    GEMV_ALL_M(1, 4, 8), GEMV_ALL_M(1, 8, 8), GEMV_ALL_M(2, 4, 4), GEMV_ALL_M(2, 8, 4),
+    GEMV_ALL_M(4, 4, 2), GEMV_ALL_M(1, 1, 8),
+    MFMA_V(1, 4, 8, ASRC_LDS), MFMA_V(1, 8, 8, ASRC_LDS), MFMA_V(2, 4, 4, ASRC_LDS),
+    MFMA_V(2, 8, 4, ASRC_LDS), MFMA_V(4, 4, 2, ASRC_LDS), MFMA_V(1, 1, 8, ASRC_LDS),
+    MFMA_V(1, 4, 4, ASRC_GLOBAL), MFMA_V(1, 8, 4, ASRC_GLOBAL), MFMA_V(2, 4, 4, ASRC_GLOBAL),
+    MFMA_V(2, 8, 4, ASRC_GLOBAL), MFMA_V(4, 4, 2, ASRC_GLOBAL), MFMA_V(1, 1, 4, ASRC_GLOBAL),
+};
+
+const Variant *find_variant(const w4a16_plan_t &p, int M) {
+    const int mm = (p.path == W4A16_PATH_GEMV) ? M : 0;
+    const int asrc = (p.path == W4A16_PATH_GEMV) ? ASRC_LDS : p.asrc;
+    for (const Variant &v : kVariants)
+        if (v.path == p.path && v.mm == mm && v.tiles == p.tiles && v.kwaves == p.kwaves &&
+            v.asrc == asrc)
+            return &v;
+    return nullptr;
+}
+
+// ---------------------------------------------------------------- checks
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int check_shape(int M, int N, int K) {
+    if (M < 1 || M > W4A16_MAX_M) return W4A16_ERR_SHAPE;
+    if (K <= 0 || (K % W4A16_GROUP) != 0) return W4A16_ERR_SHAPE;
+    if (N <= 0 || (N % 16) != 0) return W4A16_ERR_SHAPE;
+    if ((unsigned long long)K * (unsigned long long)N / 2ull >= (1ull << 40)) return W4A16_ERR_SHAPE;
+    return W4A16_OK;
+}
+
+int check_weight_shape(int K, int N) { return check_shape(1, N, K); }
+
+// Current device must be a gfx950; answers are cached per device id.
+int check_device() {
+    static std::atomic<int> cache[64];   // 0 unknown, 1 gfx950, -1 other
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0) return W4A16_ERR_DEVICE;
+    if (dev >= 64) return W4A16_ERR_DEVICE;
+    int v = cache[dev].load(std::memory_order_relaxed);
+    if (v == 0) {
+        hipDeviceProp_t prop;
+        if (hipGetDeviceProperties(&prop, dev) != hipSuccess)
+            v = -1;
+        else
+            v = (std::strncmp(prop.gcnArchName, "gfx950", 6) == 0) ? 1 : -1;
+        cache[dev].store(v, std::memory_order_relaxed);
+    }
+    return v == 1 ? W4A16_OK : W4A16_ERR_DEVICE;
+}
+
+// ---------------------------------------------------------------- planning
+
+int plan_lds(const w4a16_plan_t &p, int M, int G) {
+    const int Gwg = (G + p.splits - 1) / p.splits;
+    const int asrc = (p.path == W4A16_PATH_GEMV) ? ASRC_LDS : p.asrc;
+    return lds_layout(p.path, asrc, M, Gwg, p.tiles, p.kwaves).total;
+}
+
+int validate_plan(const w4a16_plan_t &p, int M, int N, int K) {
+    const int G = K / W4A16_GROUP;
+    if (p.path != W4A16_PATH_GEMV && p.path != W4A16_PATH_MFMA) return W4A16_ERR_PLAN;
+    if (p.path == W4A16_PATH_GEMV && M > 4) return W4A16_ERR_PLAN;
+    if (p.splits < 1 || p.splits > G) return W4A16_ERR_PLAN;
+    if (p.asrc != W4A16_ASRC_LDS && p.asrc != W4A16_ASRC_GLOBAL) return W4A16_ERR_PLAN;
+    if (!find_variant(p, M)) return W4A16_ERR_PLAN;
+    if (plan_lds(p, M, G) > kLdsBudget) return W4A16_ERR_PLAN;
+    const long long nstrips = (N / 16 + p.tiles - 1) / p.tiles;
+    if (nstrips * p.splits >= (1ll << 31)) return W4A16_ERR_PLAN;
+    (void)N;
+    return W4A16_OK;
+}
+
+// The row-count dispatcher.
+//   path:   GEMV for M <= 4 (VALU dot products; cost grows with M), MFMA above
+//           (matrix cores; the weight-side cost does not grow with M).
+//   tiles:  2 for wide N (halves A/LDS traffic per weight byte), else 1.
+//   kwaves: split K across 8 wavefronts when there are few column strips, so
+//           narrow-N shapes still put thousands of wavefronts in flight.
+//   asrc:   stage A in LDS when the workgroup's A slice fits, else read it
+//           from L1/L2 per group.
+void auto_plan(int M, int N, int K, w4a16_plan_t *out) {
+    const int NT = N / 16, G = K / W4A16_GROUP;
+    w4a16_plan_t p;
+    p.path = (M <= 4) ? W4A16_PATH_GEMV : W4A16_PATH_MFMA;
+    p.tiles = (NT >= 2048) ? 2 : 1;
+    const int strips = (NT + p.tiles - 1) / p.tiles;
+    p.kwaves = (strips >= 1024) ? 4 : 8;
+    if (p.kwaves > G) p.kwaves = (G >= 4) ? 4 : 1;
+    p.splits = 1;
+    p.asrc = W4A16_ASRC_LDS;
+    if (p.path == W4A16_PATH_GEMV && plan_lds(p, M, G) > kLdsBudget) p.path = W4A16_PATH_MFMA;
+    if (p.path == W4A16_PATH_MFMA && plan_lds(p, M, G) > kLdsBudget) p.asrc = W4A16_ASRC_GLOBAL;
+    *out = p;
+}
+
+size_t workspace_for(const w4a16_plan_t &p, int M, int N) {
+    if (p.splits <= 1) return 0;
+    const size_t nstrips = (size_t)((N / 16 + p.tiles - 1) / p.tiles);
+    const size_t part = (size_t)p.splits * (size_t)M * (size_t)N * sizeof(float);
+    const size_t part_aligned = (part + 255) & ~(size_t)255;
+    return part_aligned + nstrips * sizeof(uint32_t);
+}
+
+hipError_t launch(const void *fn, unsigned grid, unsigned block, size_t lds, hipStream_t stream,
+                  void **args) {
+    return hipLaunchKernel(fn, dim3(grid), dim3(block), args, lds, stream);
+}
+
+int run_gemm(const void *A, const void *wq, const void *scales, void *C, int M, int N, int K,
+             int group, void *workspace, size_t workspace_bytes, const w4a16_plan_t *user,
+             void *stream) {
+    if (!A || !wq || !scales || !C) return W4A16_ERR_NULL;
+    int st = check_shape(M, N, K);
+    if (st != W4A16_OK) return st;
+    if (group != W4A16_GROUP) return W4A16_ERR_GROUP;
+    if (!aligned16(A) || !aligned16(wq) || !aligned16(scales) || !aligned16(C))
+        return W4A16_ERR_ALIGN;
+    w4a16_plan_t p;
+    if (user) {
+        p = *user;
+        st = validate_plan(p, M, N, K);
+        if (st != W4A16_OK) return st;
+    } else {
+        auto_plan(M, N, K, &p);
+    }
+    const size_t need = workspace_for(p, M, N);
+    if (need > 0) {
+        if (!workspace || workspace_bytes < need) return W4A16_ERR_WORKSPACE;
+        if (!aligned16(workspace)) return W4A16_ERR_ALIGN;
+    }
+    st = check_device();
+    if (st != W4A16_OK) return st;
+
+    const Variant *v = find_variant(p, M);
+    if (!v) return W4A16_ERR_PLAN;
+    GemmArgs a;
+    a.A = static_cast<const uint16_t *>(A);
+    a.blob = static_cast<const u32x4 *>(wq);
+    a.scales = static_cast<const uint16_t *>(scales);
+    a.C = static_cast<uint16_t *>(C);
+    a.M = M;
+    a.N = N;
+    a.K = K;
+    a.G = K / W4A16_GROUP;
+    a.S = p.splits;
+    a.NT = N / 16;
+    a.nstrips = (a.NT + p.tiles - 1) / p.tiles;
+    a.nunits = a.nstrips * a.S;
+    if (need > 0) {
+        const size_t part = (size_t)p.splits * (size_t)M * (size_t)N * sizeof(float);
+        a.part = static_cast<float *>(workspace);
+        a.count = reinterpret_cast<uint32_t *>(static_cast<char *>(workspace) +
+                                               ((part + 255) & ~(size_t)255));
+    } else {
+        a.part = nullptr;
+        a.count = nullptr;
+    }
+    const int lds = plan_lds(p, M, a.G);
+    void *args[] = {&a};
+    const hipError_t e = launch(reinterpret_cast<const void *>(v->fn), (unsigned)a.nunits,
+                                64u * (unsigned)p.kwaves, (size_t)lds,
+                                static_cast<hipStream_t>(stream), args);
+    return e == hipSuccess ? W4A16_OK : W4A16_ERR_LAUNCH;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *w4a16_status_string(int status) {
+    switch (status) {
+        case W4A16_OK: return "ok";
+        case W4A16_ERR_NULL: return "null pointer argument";
+        case W4A16_ERR_SHAPE: return "invalid shape (need 1<=M<=16, K%128==0, N%16==0)";
+        case W4A16_ERR_GROUP: return "group size must be 128";
+        case W4A16_ERR_ALIGN: return "device pointer not 16-byte aligned";
+        case W4A16_ERR_WORKSPACE: return "workspace missing or too small";
+        case W4A16_ERR_DEVICE: return "no gfx950 HIP device";
+        case W4A16_ERR_LAUNCH: return "kernel launch failed";
+        case W4A16_ERR_PLAN: return "plan not available in this build";
+        default: return "unknown status";
+    }
+}
+
+size_t w4a16_repacked_bytes(int K, int N) {
+    if (check_weight_shape(K, N) != W4A16_OK) return 0;
+    return (size_t)K * (size_t)N / 2;
+}
+
+int w4a16_repack_weights(const void *qweight, void *wq_repacked, int K, int N, void *stream) {
+    if (!qweight || !wq_repacked) return W4A16_ERR_NULL;
+    int st = check_weight_shape(K, N);
+    if (st != W4A16_OK) return st;
+    if (!aligned16(qweight) || !aligned16(wq_repacked)) return W4A16_ERR_ALIGN;
+    st = check_device();
+    if (st != W4A16_OK) return st;
+    const long long npieces = (long long)K * N / 32;
+    const unsigned grid = (unsigned)((npieces + 255) / 256);
+    const uint32_t *q = static_cast<const uint32_t *>(qweight);
+    u32x4 *b = static_cast<u32x4 *>(wq_repacked);
+    int n = N, g = K / W4A16_GROUP;
+    long long np = npieces;
+    void *args[] = {&q, &b, &n, &g, &np};
+    const hipError_t e = launch(reinterpret_cast<const void *>(repack_kernel), grid, 256, 0,
+                                static_cast<hipStream_t>(stream), args);
+    return e == hipSuccess ? W4A16_OK : W4A16_ERR_LAUNCH;
+}
+
+int w4a16_get_plan(int M, int N, int K, w4a16_plan_t *plan) {
+    if (!plan) return W4A16_ERR_NULL;
+    const int st = check_shape(M, N, K);
+    if (st != W4A16_OK) return st;
+    auto_plan(M, N, K, plan);
+    return W4A16_OK;
+}
+
+int w4a16_check_plan(int M, int N, int K, const w4a16_plan_t *plan) {
+    if (!plan) return W4A16_ERR_NULL;
+    const int st = check_shape(M, N, K);
+    if (st != W4A16_OK) return st;
+    return validate_plan(*plan, M, N, K);
+}
+
+size_t w4a16_workspace_bytes(int M, int N, int K, const w4a16_plan_t *plan) {
+    if (check_shape(M, N, K) != W4A16_OK) return 0;
+    w4a16_plan_t p;
+    if (plan) {
+        p = *plan;
+        if (validate_plan(p, M, N, K) != W4A16_OK) return 0;
+    } else {
+        auto_plan(M, N, K, &p);
+    }
+    return workspace_for(p, M, N);
+}
+
+int w4a16_gemm(const void *A, const void *wq_repacked, const void *scales, void *C, int M, int N,
+               int K, int group, void *workspace, size_t workspace_bytes, void *stream) {
+    return run_gemm(A, wq_repacked, scales, C, M, N, K, group, workspace, workspace_bytes, nullptr,
+                    stream);
+}
+
+int w4a16_gemm_plan(const void *A, const void *wq_repacked, const void *scales, void *C, int M,
+                    int N, int K, int group, void *workspace, size_t workspace_bytes,
+                    const w4a16_plan_t *plan, void *stream) {
+    return run_gemm(A, wq_repacked, scales, C, M, N, K, group, workspace, workspace_bytes, plan,
+                    stream);
+}
+
+static int run_export(const void *wq, const void *scales, float *W, uint8_t *codes, int K, int N,
+                      void *stream) {
+    int st = check_weight_shape(K, N);
+    if (st != W4A16_OK) return st;
+    if (!aligned16(wq) || (scales && !aligned16(scales)) || (W && !aligned16(W)) ||
+        (codes && !aligned16(codes)))
+        return W4A16_ERR_ALIGN;
+    st = check_device();
+    if (st != W4A16_OK) return st;
+    const long long npieces = (long long)K * N / 32;
+    const unsigned grid = (unsigned)((npieces + 255) / 256);
+    const u32x4 *b = static_cast<const u32x4 *>(wq);
+    const uint16_t *s = static_cast<const uint16_t *>(scales);
+    int n = N, g = K / W4A16_GROUP;
+    long long np = npieces;
+    void *args[] = {&b, &s, &W, &codes, &n, &g, &np};
+    const void *fn = codes ? reinterpret_cast<const void *>(export_kernel<true>)
+                           : reinterpret_cast<const void *>(export_kernel<false>);
+    const hipError_t e = launch(fn, grid, 256, 0, static_cast<hipStream_t>(stream), args);
+    return e == hipSuccess ? W4A16_OK : W4A16_ERR_LAUNCH;
+}
+
+int w4a16_dequant(const void *wq_repacked, const void *scales, float *W, int K, int N,
+                  void *stream) {
+    if (!wq_repacked || !scales || !W) return W4A16_ERR_NULL;
+    return run_export(wq_repacked, scales, W, nullptr, K, N, stream);
+}
+
+int w4a16_unpack(const void *wq_repacked, uint8_t *codes, int K, int N, void *stream) {
+    if (!wq_repacked || !codes) return W4A16_ERR_NULL;
+    return run_export(wq_repacked, nullptr, nullptr, codes, K, N, stream);
+}
+
+}  // extern "C"

@@ -1,0 +1,507 @@
+// Device code of the W4A16 decode/verify matmul for gfx950 (CDNA4, wave64).
+//
+// C[M,N] = A[M,K] . W[K,N] with W[k,n] = (q[k,n] - 8) * s[k/128, n]: symmetric
+// GPTQ 4-bit codes, group 128 along K, bf16 activations and scales (checkpoint
+// contract on the page "Qwen3.8-27B on single DGX Spark ...", section
+// "Quality.").  Decode is bound by the bytes of the weights (page "One Config
+// Line Made My 27B Model 2.7x Faster", section "Gotcha #2"), so everything
+// here is arranged around one streaming read of the repacked blob.
+//
+// Dequantization without a subtraction per weight: OR-ing a 4-bit code q into
+// the low mantissa bits of bf16 128.0 (0x4300) gives exactly the bf16 value
+// 128 + q.  The contraction runs on these biased values, and the bias is
+// removed once per group and row:
+//     sum_k a_k (q_k - 8) = sum_k a_k (128 + q_k) - 136 * sum_k a_k.
+// The per-group sum of a is column independent, so it is computed once per
+// workgroup (LDS staging) or once per group and wavefront (MFMA with a
+// constant operand), never per weight.  The group scale multiplies the
+// group's partial sum, so no dequantized weight is ever rounded.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <utility>
+
+namespace w4a16 {
+
+constexpr int kGroup = 128;
+constexpr uint32_t kMagicPair = 0x43004300u;   // bf16 pair (128.0, 128.0)
+constexpr uint32_t kNeg136Pair = 0xC308C308u;  // bf16 pair (-136.0, -136.0)
+constexpr float kBias = 136.0f;                // 128 (magic) + 8 (code midpoint)
+constexpr int kXcds = 8;                       // MI355X: 8 XCDs, 32 CUs each
+constexpr int kRowPad = 16;                    // bytes of padding per staged A row
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+enum { PATH_GEMV = 1, PATH_MFMA = 2 };
+enum { ASRC_LDS = 0, ASRC_GLOBAL = 1 };
+
+struct GemmArgs {
+    const uint16_t *A;       // bf16 [M][K]
+    const u32x4 *blob;       // repacked weights, 64 pieces of 16 B per (tile, group)
+    const uint16_t *scales;  // bf16 [G][N]
+    uint16_t *C;             // bf16 [M][N]
+    float *part;             // split-K partials [S][M][N] (S > 1 only)
+    uint32_t *count;         // split-K arrival counters [nstrips] (S > 1 only)
+    int M, N, K, G;          // G = K / 128
+    int S;                   // workgroups along K per column strip
+    int NT;                  // 16-column tiles = N / 16
+    int nstrips;             // column strips = ceil(NT / tiles)
+    int nunits;              // nstrips * S = grid size
+};
+
+// ---------------------------------------------------------------- LDS plan
+// Shared by host (sizing) and device (carving).  Offsets in bytes.
+struct LdsLayout {
+    int a;      // staged A rows [M][Gwg*128 bf16 + pad]
+    int csum;   // -136 * (sum of each 32-row quarter of a group) [M][Gwg][4] fp32
+    int corr;   // MFMA: -136 * (sum over each group) [Gwg][16 rows] fp32
+    int red;    // cross-wavefront reduction [KW][T*M*16] fp32
+    int total;
+    int row;    // bytes per staged A row
+};
+
+__host__ __device__ inline LdsLayout lds_layout(int path, int asrc, int M, int Gwg, int T, int KW) {
+    LdsLayout L;
+    const bool stage = (path == PATH_GEMV) || (asrc == ASRC_LDS);
+    L.row = Gwg * kGroup * 2 + kRowPad;
+    int off = 0;
+    L.a = off;
+    if (stage) off += M * L.row;
+    L.csum = off;
+    if (stage) off += M * Gwg * 4 * 4;
+    L.corr = off;
+    if (path == PATH_MFMA && asrc == ASRC_LDS) off += Gwg * 16 * 4;
+    L.red = off;
+    if (KW > 1) off += KW * T * M * 16 * 4;
+    L.total = off;
+    return L;
+}
+
+// ---------------------------------------------------------------- helpers
+
+// One repacked word (codes of 8 consecutive rows e = 0..7; even e in bits
+// 0..15, odd e in bits 16..31, 4 bits each) -> four bf16 pairs
+// (128 + q_e, 128 + q_{e+1}) for e = 0, 2, 4, 6: seven VALU operations.
+__device__ __forceinline__ void word_to_bf16x4(uint32_t w, uint32_t (&b)[4]) {
+    b[0] = (w & 0x000F000Fu) | kMagicPair;
+    b[1] = ((w >> 4) & 0x000F000Fu) | kMagicPair;
+    b[2] = ((w >> 8) & 0x000F000Fu) | kMagicPair;
+    b[3] = ((w >> 12) & 0x000F000Fu) | kMagicPair;
+}
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t bits16) {
+    return __uint_as_float(bits16 << 16);
+}
+// bf16 scale of column c from the dword holding columns (c & ~1, c | 1).
+__device__ __forceinline__ float scale_of(uint32_t dword, int c) {
+    return __uint_as_float((c & 1) ? (dword & 0xFFFF0000u) : (dword << 16));
+}
+__device__ __forceinline__ float pair_lo(uint32_t pair) { return __uint_as_float(pair << 16); }
+__device__ __forceinline__ float pair_hi(uint32_t pair) { return __uint_as_float(pair & 0xFFFF0000u); }
+
+// fp32 -> bf16, round to nearest even (NaN stays a quiet NaN).
+__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7FFFFFFFu) > 0x7F800000u) return (uint16_t)((u >> 16) | 0x0040u);
+    u += 0x7FFFu + ((u >> 16) & 1u);
+    return (uint16_t)(u >> 16);
+}
+
+// Workgroups are dispatched to the 8 XCDs round robin (block b -> XCD b % 8).
+// Give each XCD one contiguous range of work units, so the column strips that
+// share scale cache lines, and the K splits of one strip, meet in one L2.
+__device__ __forceinline__ int xcd_unit(int b, int nunits) {
+    const int q = nunits / kXcds, r = nunits % kXcds;
+    const int x = b % kXcds, slot = b / kXcds;
+    return x * q + (x < r ? x : r) + slot;
+}
+
+__device__ __forceinline__ f32x4 mfma16x16x32(u32x4 a, u32x4 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                  __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+
+__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a),
+                                           __builtin_bit_cast(bf16x2, b), c, false);
+}
+
+// Sum of a value over the 4 lanes l, l^16, l^32, l^48 (the four K quarters of
+// one column in the GEMV lane layout), in the fixed order
+// (x[l] + x[l^32]) + (x[l^16] + x[l^16^32]); every one of the 4 lanes gets
+// bitwise the same result.
+__device__ __forceinline__ float sum_quarters(float x) {
+    uint32_t u = __float_as_uint(x);
+    auto s32 = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+    float y = __uint_as_float(s32[0]) + __uint_as_float(s32[1]);
+    uint32_t v = __float_as_uint(y);
+    auto s16 = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+    return __uint_as_float(s16[0]) + __uint_as_float(s16[1]);
+}
+
+// ---------------------------------------------------------------- repack
+// One thread per 16-byte piece of the blob (see the layout in w4a16.h).
+__device__ __forceinline__ uint32_t gptq_word_to_tile_word(uint32_t x) {
+    uint32_t out = 0;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        const uint32_t q = (x >> (4 * j)) & 0xFu;
+        const int pos = (j & 1) ? 16 + 4 * (j >> 1) : 4 * (j >> 1);
+        out |= q << pos;
+    }
+    return out;
+}
+
+__global__ void __launch_bounds__(256) repack_kernel(const uint32_t *__restrict__ qweight,
+                                                     u32x4 *__restrict__ blob, int N, int G,
+                                                     long long npieces) {
+    const long long pc = (long long)blockIdx.x * 256 + threadIdx.x;
+    if (pc >= npieces) return;
+    const int c = (int)(pc & 15), h = (int)((pc >> 4) & 3);
+    const long long tg = pc >> 6;
+    const int g = (int)(tg % G);
+    const long long t = tg / G;
+    const long long n = t * 16 + c;
+    u32x4 out;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        const long long kb = (long long)g * 16 + h * 4 + r;
+        out[r] = gptq_word_to_tile_word(qweight[kb * N + n]);
+    }
+    blob[pc] = out;
+}
+
+// Test exports: the same word_to_bf16x4 the GEMM kernels use.
+template <bool CODES>
+__global__ void __launch_bounds__(256) export_kernel(const u32x4 *__restrict__ blob,
+                                                     const uint16_t *__restrict__ scales,
+                                                     float *__restrict__ W, uint8_t *__restrict__ codes,
+                                                     int N, int G, long long npieces) {
+    const long long pc = (long long)blockIdx.x * 256 + threadIdx.x;
+    if (pc >= npieces) return;
+    const int c = (int)(pc & 15), h = (int)((pc >> 4) & 3);
+    const long long tg = pc >> 6;
+    const int g = (int)(tg % G);
+    const long long t = tg / G;
+    const long long n = t * 16 + c;
+    const u32x4 w = blob[pc];
+    const float s = CODES ? 0.0f : bf16_bits_to_f32(scales[(long long)g * N + n]);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        uint32_t b[4];
+        word_to_bf16x4(w[r], b);
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+            const long long k = (long long)g * kGroup + h * 32 + r * 8 + 2 * v;
+            const float lo = pair_lo(b[v]), hi = pair_hi(b[v]);
+            if (CODES) {
+                codes[k * N + n] = (uint8_t)(int)(lo - 128.0f);
+                codes[(k + 1) * N + n] = (uint8_t)(int)(hi - 128.0f);
+            } else {
+                W[k * N + n] = (lo - kBias) * s;
+                W[(k + 1) * N + n] = (hi - kBias) * s;
+            }
+        }
+    }
+}
+
+// ---------------------------------------------------------------- GEMM
+//
+// Work decomposition.  A workgroup owns one column strip of T 16-column tiles
+// and one of S contiguous ranges of K groups; its KW wavefronts split that
+// range further.  Every wavefront streams, for each of its groups, T pieces
+// of 1 KiB (one 16-byte load per lane, the whole 1 KiB contiguous) plus the
+// 16 scales of each tile, through a D-deep register ring, so D*T KiB per
+// wavefront are in flight from the start.
+//
+// Lane l of a wavefront owns column c = l % 16 of each tile and quarter
+// h = l / 16 of each group (32 rows, 4 words).  In the MFMA path these are
+// exactly the B operands of four v_mfma_f32_16x16x32_bf16 (lane l holds
+// B[8*(l/16) + e][l % 16], e = 0..7, word r feeding instruction r), A rows
+// are lanes l % 16, and the 16x16 fp32 result puts row 4*(l/16)+v of column
+// l % 16 in register v.  In the GEMV path each lane forms dot products of its
+// 32 rows with v_dot2_f32_bf16, and the four quarters of a column are summed
+// across lanes at the very end.
+//
+// The partial sums of the KW wavefronts meet in LDS and are added in a fixed
+// order; with S > 1 the workgroups of one strip meet in the workspace, where
+// the last one to arrive adds the S partials in a fixed order.  No float
+// atomics: the result does not depend on timing.
+template <int PATH, int MM, int T, int KW, int D, int ASRC>
+__global__ void __launch_bounds__(64 * KW) gemm_kernel(GemmArgs p) {
+    extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+    __shared__ int s_last;
+
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int M = (PATH == PATH_GEMV) ? MM : p.M;
+    const int c = lane & 15, h = lane >> 4;
+    const int arow_m = min(c, M - 1);   // MFMA A-operand row of this lane
+
+    const int u = xcd_unit(blockIdx.x, p.nunits);
+    const int strip = u / p.S, z = u - (u / p.S) * p.S;
+    const int gw0 = (p.G * z) / p.S, gw1 = (p.G * (z + 1)) / p.S;
+    const int Gwg = gw1 - gw0;
+    const int gk0 = gw0 + (Gwg * wave) / KW, gk1 = gw0 + (Gwg * (wave + 1)) / KW;
+    const int ng = gk1 - gk0;
+    const LdsLayout L = lds_layout(PATH, ASRC, M, Gwg, T, KW);
+
+    int tl[T];
+#pragma unroll
+    for (int t = 0; t < T; ++t) tl[t] = min(strip * T + t, p.NT - 1);
+
+    // ---- register ring, prefetched before anything else
+    u32x4 wv[D][T];
+    uint32_t sv[D][T];
+    u32x4 av[(ASRC == ASRC_GLOBAL && PATH == PATH_MFMA) ? D : 1][4];
+
+    auto load_group = [&](auto jc, int g) {
+        constexpr int j = decltype(jc)::value;
+#pragma unroll
+        for (int t = 0; t < T; ++t) {
+            wv[j][t] = __builtin_nontemporal_load(&p.blob[((size_t)tl[t] * p.G + g) * 64 + lane]);
+            // the aligned dword that holds this lane's bf16 scale (a 16-bit
+            // load would be re-extended at the loop latch, which stalls the ring)
+            sv[j][t] = reinterpret_cast<const uint32_t *>(p.scales)[((size_t)g * p.N + tl[t] * 16 + c) >> 1];
+        }
+        if constexpr (ASRC == ASRC_GLOBAL && PATH == PATH_MFMA) {
+            // A rows >= M repeat row M-1: their results land in output rows
+            // that are never written, and the loads stay branch free
+            const u32x4 *ap = reinterpret_cast<const u32x4 *>(
+                p.A + (size_t)arow_m * p.K + (size_t)g * kGroup + h * 32);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) av[j][r] = ap[r];   // rows 32h + 8r .. +8: 16 B
+        }
+    };
+
+    if (ng > 0) {
+        // issue in ring order (slot 0 first, weights then scale per slot), as
+        // the main loop does, so the wait counts of both paths agree
+        [&]<int... J>(std::integer_sequence<int, J...>) {
+            ((load_group(std::integral_constant<int, J>{}, min(gk0 + J, gk1 - 1)),
+              __builtin_amdgcn_sched_barrier(0)),
+             ...);
+        }(std::make_integer_sequence<int, D>{});
+    }
+
+    // ---- stage this workgroup's K range of A in LDS, with bias corrections
+    constexpr bool kStage = (PATH == PATH_GEMV) || (ASRC == ASRC_LDS);
+    if constexpr (kStage) {
+        const int nblk = M * Gwg * 4;
+        for (int b = threadIdx.x; b < nblk; b += 64 * KW) {
+            const int m = b / (Gwg * 4);
+            const int rem = b - m * Gwg * 4;
+            const int gl = rem >> 2, hq = rem & 3;
+            const u32x4 *src = reinterpret_cast<const u32x4 *>(
+                p.A + (size_t)m * p.K + (size_t)(gw0 + gl) * kGroup + hq * 32);
+            u32x4 x[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) x[i] = src[i];
+            u32x4 *dst = reinterpret_cast<u32x4 *>(smem + L.a + m * L.row + (gl * kGroup + hq * 32) * 2);
+            float s = 0.0f;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                dst[i] = x[i];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    s += pair_lo(x[i][e]);
+                    s += pair_hi(x[i][e]);
+                }
+            }
+            reinterpret_cast<float *>(smem + L.csum)[(m * Gwg + gl) * 4 + hq] = -kBias * s;
+        }
+        __syncthreads();
+        if constexpr (PATH == PATH_MFMA) {
+            const float *cs = reinterpret_cast<const float *>(smem + L.csum);
+            float *corr = reinterpret_cast<float *>(smem + L.corr);
+            for (int e = threadIdx.x; e < Gwg * 16; e += 64 * KW) {
+                const int gl = e >> 4, m = e & 15;
+                float v = 0.0f;
+                if (m < M) {
+                    const float *q = cs + (m * Gwg + gl) * 4;
+                    v = (q[0] + q[1]) + (q[2] + q[3]);
+                }
+                corr[e] = v;
+            }
+            __syncthreads();
+        }
+    }
+
+    // ---- main loop over this wavefront's groups
+    constexpr int NACC = (PATH == PATH_GEMV) ? MM : 4;
+    float acc[T][NACC];
+#pragma unroll
+    for (int t = 0; t < T; ++t)
+#pragma unroll
+        for (int i = 0; i < NACC; ++i) acc[t][i] = 0.0f;
+
+    auto compute_group = [&](auto jc, int g) {
+        constexpr int j = decltype(jc)::value;
+        const int gl = g - gw0;
+        if constexpr (PATH == PATH_MFMA) {
+            u32x4 a[4];
+            f32x4 cinit;
+            if constexpr (ASRC == ASRC_LDS) {
+                const uint8_t *arow = smem + L.a + arow_m * L.row + (gl * kGroup + h * 32) * 2;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) a[r] = reinterpret_cast<const u32x4 *>(arow)[r];
+                cinit = reinterpret_cast<const f32x4 *>(smem + L.corr)[gl * 4 + h];
+            } else {
+                const u32x4 neg = {kNeg136Pair, kNeg136Pair, kNeg136Pair, kNeg136Pair};
+                cinit = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    a[r] = av[j][r];
+                    cinit = mfma16x16x32(a[r], neg, cinit);
+                }
+            }
+#pragma unroll
+            for (int t = 0; t < T; ++t) {
+                f32x4 P = cinit;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    uint32_t b[4];
+                    word_to_bf16x4(wv[j][t][r], b);
+                    const u32x4 bv = {b[0], b[1], b[2], b[3]};
+                    P = mfma16x16x32(a[r], bv, P);
+                }
+                const float s = scale_of(sv[j][t], c);
+#pragma unroll
+                for (int v = 0; v < 4; ++v) acc[t][v] = __builtin_fmaf(s, P[v], acc[t][v]);
+            }
+        } else {
+            u32x4 ar[MM][4];
+            float corr[MM];
+#pragma unroll
+            for (int m = 0; m < MM; ++m) {
+                const uint8_t *arow = smem + L.a + m * L.row + (gl * kGroup + h * 32) * 2;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) ar[m][r] = reinterpret_cast<const u32x4 *>(arow)[r];
+                corr[m] = reinterpret_cast<const float *>(smem + L.csum)[(m * Gwg + gl) * 4 + h];
+            }
+#pragma unroll
+            for (int t = 0; t < T; ++t) {
+                float part[MM];
+#pragma unroll
+                for (int m = 0; m < MM; ++m) part[m] = corr[m];
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    uint32_t b[4];
+                    word_to_bf16x4(wv[j][t][r], b);
+#pragma unroll
+                    for (int v = 0; v < 4; ++v)
+#pragma unroll
+                        for (int m = 0; m < MM; ++m) part[m] = dot2_bf16(b[v], ar[m][r][v], part[m]);
+                }
+                const float s = scale_of(sv[j][t], c);
+#pragma unroll
+                for (int m = 0; m < MM; ++m) acc[t][m] = __builtin_fmaf(s, part[m], acc[t][m]);
+            }
+        }
+    };
+
+    if (ng > 0) {
+        for (int base = 0; base < ng; base += D) {
+            [&]<int... J>(std::integer_sequence<int, J...>) {
+                // compute group j of the ring, then refill slot j with the group D ahead:
+                // D - 1 groups stay in flight while one is being computed
+                ((base + J < ng ? compute_group(std::integral_constant<int, J>{}, gk0 + base + J)
+                                : void(),
+                  load_group(std::integral_constant<int, J>{}, min(gk0 + base + J + D, gk1 - 1))),
+                 ...);
+            }(std::make_integer_sequence<int, D>{});
+        }
+    }
+
+    // ---- GEMV: sum the four K quarters of each column across lanes
+    if constexpr (PATH == PATH_GEMV) {
+#pragma unroll
+        for (int t = 0; t < T; ++t)
+#pragma unroll
+            for (int m = 0; m < MM; ++m) acc[t][m] = sum_quarters(acc[t][m]);
+    }
+
+    // ---- epilogue: fixed-order reduction over wavefronts, then C or partials
+    const int NV = T * M * 16;   // values (t, m, c) of this workgroup
+    auto emit = [&](int t, int m, int cc, float val) {
+        const int tile = strip * T + t;
+        if (tile >= p.NT) return;
+        const size_t n = (size_t)tile * 16 + cc;
+        if (p.S == 1)
+            p.C[(size_t)m * p.N + n] = f32_to_bf16_rne(val);
+        else
+            p.part[((size_t)z * M + m) * p.N + n] = val;
+    };
+
+    if constexpr (KW == 1) {
+#pragma unroll
+        for (int t = 0; t < T; ++t) {
+            if constexpr (PATH == PATH_MFMA) {
+#pragma unroll
+                for (int v = 0; v < 4; ++v)
+                    if (4 * h + v < M) emit(t, 4 * h + v, c, acc[t][v]);
+            } else {
+                if (h == 0) {
+#pragma unroll
+                    for (int m = 0; m < MM; ++m) emit(t, m, c, acc[t][m]);
+                }
+            }
+        }
+    } else {
+        float *red = reinterpret_cast<float *>(smem + L.red);
+        float *mine = red + wave * NV;
+#pragma unroll
+        for (int t = 0; t < T; ++t) {
+            if constexpr (PATH == PATH_MFMA) {
+#pragma unroll
+                for (int v = 0; v < 4; ++v)
+                    if (4 * h + v < M) mine[(t * M + 4 * h + v) * 16 + c] = acc[t][v];
+            } else {
+                if (h == 0) {
+#pragma unroll
+                    for (int m = 0; m < MM; ++m) mine[(t * MM + m) * 16 + c] = acc[t][m];
+                }
+            }
+        }
+        __syncthreads();
+        for (int e = threadIdx.x; e < NV; e += 64 * KW) {
+            float s = red[e];
+#pragma unroll
+            for (int w = 1; w < KW; ++w) s += red[w * NV + e];
+            const int t = e / (16 * M), m = (e >> 4) - t * M, cc = e & 15;
+            emit(t, m, cc, s);
+        }
+    }
+
+    if (p.S > 1) {
+        // Publish this workgroup's partials, count arrivals, and let the last
+        // workgroup of the strip add all S partials in order z = 0..S-1.
+        __threadfence();
+        __syncthreads();
+        if (threadIdx.x == 0) {
+            const uint32_t prev = atomicAdd(&p.count[strip], 1u);
+            s_last = (prev == (uint32_t)(p.S - 1));
+        }
+        __syncthreads();
+        if (s_last) {
+            __threadfence();
+            for (int e = threadIdx.x; e < NV; e += 64 * KW) {
+                const int t = e / (16 * M), m = (e >> 4) - t * M, cc = e & 15;
+                const int tile = strip * T + t;
+                if (tile >= p.NT) continue;
+                const size_t n = (size_t)tile * 16 + cc;
+                float s = 0.0f;
+                for (int zz = 0; zz < p.S; ++zz) s += __builtin_nontemporal_load(&p.part[((size_t)zz * M + m) * p.N + n]);
+                p.C[(size_t)m * p.N + n] = f32_to_bf16_rne(s);
+            }
+            if (threadIdx.x == 0) atomicExch(&p.count[strip], 0u);
+        }
+    }
+}
+
+}  // namespace w4a16

@@ -11,11 +11,14 @@
 // the low mantissa bits of bf16 128.0 (0x4300) gives exactly the bf16 value
 // 128 + q.  The contraction runs on these biased values, and the bias is
 // removed once per group and row:
-//     sum_k a_k (q_k - 8) = sum_k a_k (128 + q_k) - 136 * sum_k a_k.
-// The per-group sum of a is column independent, so it is computed once per
-// workgroup (LDS staging) or once per group and wavefront (MFMA with a
-// constant operand), never per weight.  The group scale multiplies the
-// group's partial sum, so no dequantized weight is ever rounded.
+//     sum_k a_k (q_k - 8) = sum_k a_k (128 + q_k) - sum_k a_k * 136.
+// The bias sum is column independent, so it is formed once per group (per
+// workgroup in the GEMV path, per wavefront in the MFMA path), never per
+// weight.  It is formed by the very instruction sequence that forms the
+// weight sum, in the same order, with every code replaced by 8: a group whose
+// codes are all 8 therefore contributes exactly zero, as it must.  The group
+// scale multiplies the group's partial sum, so no dequantized weight is ever
+// rounded.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -27,7 +30,7 @@ namespace w4a16 {
 
 constexpr int kGroup = 128;
 constexpr uint32_t kMagicPair = 0x43004300u;   // bf16 pair (128.0, 128.0)
-constexpr uint32_t kNeg136Pair = 0xC308C308u;  // bf16 pair (-136.0, -136.0)
+constexpr uint32_t kBiasPair = 0x43084308u;    // bf16 pair (136.0, 136.0) = codes of 8
 constexpr float kBias = 136.0f;                // 128 (magic) + 8 (code midpoint)
 constexpr int kXcds = 8;                       // MI355X: 8 XCDs, 32 CUs each
 constexpr int kRowPad = 16;                    // bytes of padding per staged A row
@@ -58,8 +61,7 @@ struct GemmArgs {
 // Shared by host (sizing) and device (carving).  Offsets in bytes.
 struct LdsLayout {
     int a;      // staged A rows [M][Gwg*128 bf16 + pad]
-    int csum;   // -136 * (sum of each 32-row quarter of a group) [M][Gwg][4] fp32
-    int corr;   // MFMA: -136 * (sum over each group) [Gwg][16 rows] fp32
+    int csum;   // GEMV: bias sum of each 32-row quarter of a group [M][Gwg][4] fp32
     int red;    // cross-wavefront reduction [KW][T*M*16] fp32
     int total;
     int row;    // bytes per staged A row
@@ -73,9 +75,7 @@ __host__ __device__ inline LdsLayout lds_layout(int path, int asrc, int M, int G
     L.a = off;
     if (stage) off += M * L.row;
     L.csum = off;
-    if (stage) off += M * Gwg * 4 * 4;
-    L.corr = off;
-    if (path == PATH_MFMA && asrc == ASRC_LDS) off += Gwg * 16 * 4;
+    if (path == PATH_GEMV) off += M * Gwg * 4 * 4;
     L.red = off;
     if (KW > 1) off += KW * T * M * 16 * 4;
     L.total = off;
@@ -289,7 +289,7 @@ __global__ void __launch_bounds__(64 * KW) gemm_kernel(GemmArgs p) {
         }(std::make_integer_sequence<int, D>{});
     }
 
-    // ---- stage this workgroup's K range of A in LDS, with bias corrections
+    // ---- stage this workgroup's K range of A in LDS (GEMV: with bias sums)
     constexpr bool kStage = (PATH == PATH_GEMV) || (ASRC == ASRC_LDS);
     if constexpr (kStage) {
         const int nblk = M * Gwg * 4;
@@ -303,33 +303,19 @@ __global__ void __launch_bounds__(64 * KW) gemm_kernel(GemmArgs p) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) x[i] = src[i];
             u32x4 *dst = reinterpret_cast<u32x4 *>(smem + L.a + m * L.row + (gl * kGroup + hq * 32) * 2);
-            float s = 0.0f;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                dst[i] = x[i];
+            for (int i = 0; i < 4; ++i) dst[i] = x[i];
+            if constexpr (PATH == PATH_GEMV) {
+                // the GEMV lane's dot2 chain of this quarter, with every code 8
+                float cs = 0.0f;
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    s += pair_lo(x[i][e]);
-                    s += pair_hi(x[i][e]);
-                }
+                for (int i = 0; i < 4; ++i)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) cs = dot2_bf16(kBiasPair, x[i][e], cs);
+                reinterpret_cast<float *>(smem + L.csum)[(m * Gwg + gl) * 4 + hq] = cs;
             }
-            reinterpret_cast<float *>(smem + L.csum)[(m * Gwg + gl) * 4 + hq] = -kBias * s;
         }
         __syncthreads();
-        if constexpr (PATH == PATH_MFMA) {
-            const float *cs = reinterpret_cast<const float *>(smem + L.csum);
-            float *corr = reinterpret_cast<float *>(smem + L.corr);
-            for (int e = threadIdx.x; e < Gwg * 16; e += 64 * KW) {
-                const int gl = e >> 4, m = e & 15;
-                float v = 0.0f;
-                if (m < M) {
-                    const float *q = cs + (m * Gwg + gl) * 4;
-                    v = (q[0] + q[1]) + (q[2] + q[3]);
-                }
-                corr[e] = v;
-            }
-            __syncthreads();
-        }
     }
 
     // ---- main loop over this wavefront's groups
@@ -345,24 +331,22 @@ __global__ void __launch_bounds__(64 * KW) gemm_kernel(GemmArgs p) {
         const int gl = g - gw0;
         if constexpr (PATH == PATH_MFMA) {
             u32x4 a[4];
-            f32x4 cinit;
             if constexpr (ASRC == ASRC_LDS) {
                 const uint8_t *arow = smem + L.a + arow_m * L.row + (gl * kGroup + h * 32) * 2;
 #pragma unroll
                 for (int r = 0; r < 4; ++r) a[r] = reinterpret_cast<const u32x4 *>(arow)[r];
-                cinit = reinterpret_cast<const f32x4 *>(smem + L.corr)[gl * 4 + h];
             } else {
-                const u32x4 neg = {kNeg136Pair, kNeg136Pair, kNeg136Pair, kNeg136Pair};
-                cinit = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    a[r] = av[j][r];
-                    cinit = mfma16x16x32(a[r], neg, cinit);
-                }
+                for (int r = 0; r < 4; ++r) a[r] = av[j][r];
             }
+            // bias: the same four-MFMA chain with every code 8
+            const u32x4 bias = {kBiasPair, kBiasPair, kBiasPair, kBiasPair};
+            f32x4 Q = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+            for (int r = 0; r < 4; ++r) Q = mfma16x16x32(a[r], bias, Q);
 #pragma unroll
             for (int t = 0; t < T; ++t) {
-                f32x4 P = cinit;
+                f32x4 P = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     uint32_t b[4];
@@ -372,7 +356,7 @@ __global__ void __launch_bounds__(64 * KW) gemm_kernel(GemmArgs p) {
                 }
                 const float s = scale_of(sv[j][t], c);
 #pragma unroll
-                for (int v = 0; v < 4; ++v) acc[t][v] = __builtin_fmaf(s, P[v], acc[t][v]);
+                for (int v = 0; v < 4; ++v) acc[t][v] = __builtin_fmaf(s, P[v] - Q[v], acc[t][v]);
             }
         } else {
             u32x4 ar[MM][4];
@@ -388,7 +372,7 @@ __global__ void __launch_bounds__(64 * KW) gemm_kernel(GemmArgs p) {
             for (int t = 0; t < T; ++t) {
                 float part[MM];
 #pragma unroll
-                for (int m = 0; m < MM; ++m) part[m] = corr[m];
+                for (int m = 0; m < MM; ++m) part[m] = 0.0f;
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     uint32_t b[4];
@@ -400,7 +384,7 @@ __global__ void __launch_bounds__(64 * KW) gemm_kernel(GemmArgs p) {
                 }
                 const float s = scale_of(sv[j][t], c);
 #pragma unroll
-                for (int m = 0; m < MM; ++m) acc[t][m] = __builtin_fmaf(s, part[m], acc[t][m]);
+                for (int m = 0; m < MM; ++m) acc[t][m] = __builtin_fmaf(s, part[m] - corr[m], acc[t][m]);
             }
         }
     };

@@ -64,7 +64,7 @@ class Problem:
         q = torch.from_numpy(qw.view(np.int32)).to(dev)
         blob = w4.repack_weights(q, K, N)
         del q
-        s = torch.from_numpy(sc.view(np.int16)).to(dev)
+        s = w4.repack_scales(torch.from_numpy(sc.view(np.int16)).to(dev), K, N)
         a = torch.from_numpy(A.view(np.int16)).to(dev).view(torch.bfloat16)
         self.blobs = [blob] + [blob.clone() for _ in range(sets - 1)]
         self.scales = [s] + [s.clone() for _ in range(sets - 1)]

@@ -18,6 +18,9 @@
  *            bits 4j..4j+3 (low nibble first), is the code q in [0, 15] of
  *            row k = 8*kb + j.  The weight is w = (q - 8) * s.
  *   scales   bf16 [K/128][N], N contiguous: s for (group floor(k/128), column n).
+ *            The GEMM reads them repacked (w4a16_repack_scales): the scale of
+ *            (g, n) at index (t*G + g)*16 + c with t = n/16, c = n%16, so one
+ *            tile's scales follow each other in the order the kernel reads them.
  *   A        bf16 [M][K], K contiguous (row stride K).
  *   C        bf16 [M][N], N contiguous (row stride N); fp32 accumulation,
  *            rounded to nearest even once at the end.
@@ -108,6 +111,17 @@ size_t w4a16_repacked_bytes(int K, int N);
  */
 int w4a16_repack_weights(const void *qweight, void *wq_repacked, int K, int N, void *stream);
 
+/* Bytes of the repacked scales (= (K/128)*N*2), 0 for invalid shapes. */
+size_t w4a16_repacked_scale_bytes(int K, int N);
+
+/*
+ * One-time repack of the bf16 scales [K/128][N] into the tile order above.
+ *   scales           device, bf16 [K/128][N] (read only)
+ *   scales_repacked  device, w4a16_repacked_scale_bytes(K, N) bytes (written)
+ * A pure permutation.  Returns W4A16_OK or an error status.
+ */
+int w4a16_repack_scales(const void *scales, void *scales_repacked, int K, int N, void *stream);
+
 /*
  * The plan w4a16_gemm uses for (M, N, K): fills *plan and returns W4A16_OK,
  * or returns an error status for invalid shapes.  Host-only, no device work.
@@ -135,7 +149,7 @@ size_t w4a16_workspace_bytes(int M, int N, int K, const w4a16_plan_t *plan);
  * C = A . dequant(blob, scales), dispatched by row count.
  *   A            device bf16 [M][K]
  *   wq_repacked  device blob from w4a16_repack_weights for this K, N
- *   scales       device bf16 [K/128][N]
+ *   scales       device, repacked scales from w4a16_repack_scales
  *   C            device bf16 [M][N] (written)
  *   group        must be 128
  *   workspace    device, at least w4a16_workspace_bytes(M, N, K, NULL) bytes,
@@ -156,7 +170,8 @@ int w4a16_gemm_plan(const void *A, const void *wq_repacked, const void *scales, 
 
 /*
  * Test export of the device dequantization used by both GEMM paths:
- * W[k][n] = (q - 8) * s as fp32 (exact), device fp32 [K][N] (written).
+ * W[k][n] = (q - 8) * s as fp32 (exact), device fp32 [K][N] (written);
+ * `scales` are the repacked scales.
  */
 int w4a16_dequant(const void *wq_repacked, const void *scales, float *W, int K, int N,
                   void *stream);

@@ -7,7 +7,8 @@ both sides consume is the seeded input generator in ``synth.py``, which holds
 none of the method's arithmetic.
 
 Contents
-  * ``unpack``, ``dequant``, ``gemm``, ``repack``, ``unrepack``: thin numpy
+  * ``unpack``, ``dequant``, ``gemm``, ``repack``, ``unrepack``,
+    ``repack_scales``: thin numpy
     wrappers around ``oracle.c`` (fp64, plain loops), built with gcc into
     ``liboracle.so`` next to this file.
   * ``exact_gemm``: exact rational arithmetic (Python ``Fraction``) for tiny
@@ -62,6 +63,7 @@ def _load():
         lib.oracle_gemm.argtypes = [P, P, P, i, i, i, P, i, i, P, P]
         lib.oracle_repack.argtypes = [P, i, i, P]
         lib.oracle_unrepack.argtypes = [P, i, i, P]
+        lib.oracle_repack_scales.argtypes = [P, i, i, P]
         lib.oracle_bf16_to_f64.argtypes = [ctypes.c_uint16]
         lib.oracle_bf16_to_f64.restype = ctypes.c_double
         lib.oracle_max_threads.restype = ctypes.c_int
@@ -146,6 +148,17 @@ def unrepack(blob: np.ndarray, K: int, N: int) -> np.ndarray:
         raise ValueError("oracle.unrepack: blob size mismatch")
     out = np.empty((K // 8, N), dtype=np.uint32)
     _load().oracle_unrepack(_ptr(b), K, N, _ptr(out))
+    return out
+
+
+def repack_scales(scales: np.ndarray, K: int, N: int) -> np.ndarray:
+    """Tile-order scales (uint16 bf16 bits, (K/128)*N values) from the layout definition."""
+    _check_shapes(K, N)
+    if N % 16:
+        raise ValueError("oracle.repack_scales: N must be a multiple of 16")
+    sc = np.ascontiguousarray(scales, dtype=np.uint16).reshape(K // GROUP, N)
+    out = np.empty((K // GROUP) * N, dtype=np.uint16)
+    _load().oracle_repack_scales(_ptr(sc), K, N, _ptr(out))
     return out
 
 

@@ -107,6 +107,10 @@ def test_repack_and_export_argument_errors():
     assert L.w4a16_dequant(P, NULL, P2, 512, 1024, NULL) == -1
     assert L.w4a16_unpack(P, NULL, 512, 1024, NULL) == -1
     assert L.w4a16_unpack(P, P2, 512, 1000, NULL) == -2
+    assert L.w4a16_repack_scales(NULL, P, 512, 1024, NULL) == -1
+    assert L.w4a16_repack_scales(P, P2, 512, 1000, NULL) == -2
+    assert L.w4a16_repack_scales(ODD, P2, 512, 1024, NULL) == -4
+    assert L.w4a16_repacked_scale_bytes(512, 1024) == 4 * 1024 * 2
 
 
 def test_row_count_dispatch():

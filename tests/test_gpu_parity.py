@@ -29,8 +29,11 @@ def note(*a):
 
 
 def to_dev(qweight, scales, A=None):
+    """Device copies: GPTQ words, scales repacked by the HIP path, bf16 A."""
     q = torch.from_numpy(qweight.view(np.int32)).to(DEV)
-    s = torch.from_numpy(scales.view(np.int16)).to(DEV)
+    K, N = qweight.shape[0] * 8, qweight.shape[1]
+    s_raw = torch.from_numpy(np.ascontiguousarray(scales).view(np.int16)).to(DEV)
+    s = w4.repack_scales(s_raw, K, N)
     a = None if A is None else torch.from_numpy(np.ascontiguousarray(A).view(np.int16)).to(DEV).view(torch.bfloat16)
     return q, s, a
 
@@ -76,6 +79,7 @@ def test_repack_unpack_dequant_bit_exact(K, N, seed):
     torch.cuda.synchronize()
     ref_blob = oracle.repack(qw, K, N)
     assert np.array_equal(blob.cpu().numpy().view(np.uint32), ref_blob)
+    assert np.array_equal(s.cpu().numpy().view(np.uint16), oracle.repack_scales(sc, K, N))
     assert np.array_equal(codes.cpu().numpy(), oracle.unpack(qw, K, N))
     Wd = W.cpu().numpy().astype(np.float64)
     assert np.array_equal(Wd, oracle.dequant(qw, sc, K, N))

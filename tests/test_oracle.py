@@ -261,6 +261,20 @@ def test_repack_is_a_bijection_preserving_nibbles():
         assert np.array_equal(hist_q, hist_b)
 
 
+def test_repack_scales_literal_positions_and_bijection():
+    # index of (g, n) = (t*G + g)*16 + c, t = n // 16, c = n % 16; K=384 (G=3), N=48
+    K, N = 384, 48
+    sc = np.arange(3 * 48, dtype=np.uint16).reshape(3, 48)      # value = g*48 + n
+    out = oracle.repack_scales(sc, K, N)
+    assert out.size == 3 * 48
+    assert out[0] == 0 and out[15] == 15          # (g=0, n=0..15)
+    assert out[16] == 48                          # (g=1, n=0)
+    assert out[47] == 2 * 48 + 15                 # (g=2, n=15)
+    assert out[48] == 16                          # (g=0, n=16): tile 1 starts
+    assert out[(2 * 3 + 1) * 16 + 5] == 48 + 37   # (g=1, n=37): t=2, c=5
+    assert sorted(out.tolist()) == list(range(3 * 48))
+
+
 # ---------------------------------------------------------------- metric
 
 def test_normalized_error():

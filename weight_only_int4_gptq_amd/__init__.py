@@ -55,6 +55,10 @@ def lib():
         L.w4a16_repacked_bytes.argtypes = [I, I]
         L.w4a16_repacked_bytes.restype = S
         L.w4a16_repack_weights.argtypes = [P, P, I, I, P]
+        L.w4a16_repacked_scale_bytes.argtypes = [I, I]
+        L.w4a16_repacked_scale_bytes.restype = S
+        L.w4a16_repack_scales.argtypes = [P, P, I, I, P]
+        L.w4a16_repack_scales.restype = I
         L.w4a16_get_plan.argtypes = [I, I, I, ctypes.POINTER(Plan)]
         L.w4a16_check_plan.argtypes = [I, I, I, ctypes.POINTER(Plan)]
         L.w4a16_check_plan.restype = I
@@ -102,6 +106,20 @@ def repack_weights(qweight: torch.Tensor, K: int, N: int, out: torch.Tensor | No
     return out
 
 
+def repack_scales(scales: torch.Tensor, K: int, N: int, out: torch.Tensor | None = None):
+    """bf16 scales (16-bit device tensor [K/128, N]) -> tile-order scales (int16 [K/128 * N])."""
+    if out is None:
+        out = torch.empty(max((K // GROUP) * N, 1), dtype=torch.int16, device=scales.device)
+    _check(lib().w4a16_repack_scales(_ptr(scales), _ptr(out), K, N, _stream(scales)),
+           "w4a16_repack_scales")
+    return out
+
+
+def repack(qweight: torch.Tensor, scales: torch.Tensor, K: int, N: int):
+    """Both one-time repacks: (blob, repacked scales)."""
+    return repack_weights(qweight, K, N), repack_scales(scales, K, N)
+
+
 def get_plan(M: int, N: int, K: int) -> Plan:
     p = Plan()
     _check(lib().w4a16_get_plan(M, N, K, ctypes.byref(p)), "w4a16_get_plan")
@@ -124,7 +142,10 @@ def workspace_bytes(M: int, N: int, K: int, plan: Plan | None = None) -> int:
 def gemm(A: torch.Tensor, blob: torch.Tensor, scales: torch.Tensor, N: int,
          out: torch.Tensor | None = None, plan: Plan | None = None,
          workspace: torch.Tensor | None = None, group: int = GROUP):
-    """C[M, N] = A[M, K] . dequant(blob, scales); A and C bf16 device tensors."""
+    """C[M, N] = A[M, K] . dequant(blob, scales); A and C bf16 device tensors.
+
+    ``blob`` and ``scales`` come from ``repack`` (weights and scales repacked once).
+    """
     M, K = A.shape
     if out is None:
         out = torch.empty((M, N), dtype=torch.bfloat16, device=A.device)
@@ -140,7 +161,7 @@ def gemm(A: torch.Tensor, blob: torch.Tensor, scales: torch.Tensor, N: int,
 
 
 def dequant(blob: torch.Tensor, scales: torch.Tensor, K: int, N: int) -> torch.Tensor:
-    """Test export: fp32 W[K, N] = (q - 8) * s from the device dequantization."""
+    """Test export: fp32 W[K, N] = (q - 8) * s from the device dequantization (repacked scales)."""
     W = torch.empty((K, N), dtype=torch.float32, device=blob.device)
     _check(lib().w4a16_dequant(_ptr(blob), _ptr(scales), _ptr(W), K, N, _stream(blob)),
            "w4a16_dequant")

@@ -243,6 +243,30 @@ int w4a16_repack_weights(const void *qweight, void *wq_repacked, int K, int N, v
     return e == hipSuccess ? W4A16_OK : W4A16_ERR_LAUNCH;
 }
 
+size_t w4a16_repacked_scale_bytes(int K, int N) {
+    if (check_weight_shape(K, N) != W4A16_OK) return 0;
+    return (size_t)(K / W4A16_GROUP) * (size_t)N * 2;
+}
+
+int w4a16_repack_scales(const void *scales, void *scales_repacked, int K, int N, void *stream) {
+    if (!scales || !scales_repacked) return W4A16_ERR_NULL;
+    int st = check_weight_shape(K, N);
+    if (st != W4A16_OK) return st;
+    if (!aligned16(scales) || !aligned16(scales_repacked)) return W4A16_ERR_ALIGN;
+    st = check_device();
+    if (st != W4A16_OK) return st;
+    const long long count = (long long)(K / W4A16_GROUP) * N;
+    const unsigned grid = (unsigned)((count + 255) / 256);
+    const uint16_t *in = static_cast<const uint16_t *>(scales);
+    uint16_t *out = static_cast<uint16_t *>(scales_repacked);
+    int n = N, g = K / W4A16_GROUP;
+    long long cnt = count;
+    void *args[] = {&in, &out, &n, &g, &cnt};
+    const hipError_t e = launch(reinterpret_cast<const void *>(repack_scales_kernel), grid, 256, 0,
+                                static_cast<hipStream_t>(stream), args);
+    return e == hipSuccess ? W4A16_OK : W4A16_ERR_LAUNCH;
+}
+
 int w4a16_get_plan(int M, int N, int K, w4a16_plan_t *plan) {
     if (!plan) return W4A16_ERR_NULL;
     const int st = check_shape(M, N, K);

@@ -30,6 +30,7 @@ namespace w4a16 {
 
 constexpr int kGroup = 128;
 constexpr uint32_t kMagicPair = 0x43004300u;   // bf16 pair (128.0, 128.0)
+constexpr uint32_t kNibblePair = 0x000F000Fu;  // the low nibble of each half
 constexpr uint32_t kBiasPair = 0x43084308u;    // bf16 pair (136.0, 136.0) = codes of 8
 constexpr float kBias = 136.0f;                // 128 (magic) + 8 (code midpoint)
 constexpr int kXcds = 8;                       // MI355X: 8 XCDs, 32 CUs each
@@ -46,7 +47,7 @@ enum { ASRC_LDS = 0, ASRC_GLOBAL = 1 };
 struct GemmArgs {
     const uint16_t *A;       // bf16 [M][K]
     const u32x4 *blob;       // repacked weights, 64 pieces of 16 B per (tile, group)
-    const uint16_t *scales;  // bf16 [G][N]
+    const uint16_t *scales;  // repacked bf16 scales: [tile][group][16 columns]
     uint16_t *C;             // bf16 [M][N]
     float *part;             // split-K partials [S][M][N] (S > 1 only)
     uint32_t *count;         // split-K arrival counters [nstrips] (S > 1 only)
@@ -84,14 +85,37 @@ __host__ __device__ inline LdsLayout lds_layout(int path, int asrc, int M, int G
 
 // ---------------------------------------------------------------- helpers
 
+// Register-held constants of the dequantization.  gfx9-family VOP3
+// instructions take no 32-bit literal, so v_and_or_b32 needs its mask and
+// magic in registers; made opaque once per kernel, they stay there (with
+// literal constants the compiler would split each into v_and + v_or).
+struct DequantConsts {
+    uint32_t nib;     // SGPR: 0x000F000F
+    uint32_t magic;   // VGPR: 0x43004300
+};
+
+__device__ __forceinline__ DequantConsts dequant_consts() {
+    DequantConsts k;
+    asm volatile("s_mov_b32 %0, 0x000f000f" : "=s"(k.nib));
+    asm volatile("v_mov_b32 %0, 0x43004300" : "=v"(k.magic));
+    return k;
+}
+
+// Plain C on purpose: the compiler selects v_and_or_b32 from it (the operands
+// are registers) and so knows the instruction when it places the wait states
+// an MFMA reading its result needs.
+__device__ __forceinline__ uint32_t and_or(uint32_t x, uint32_t nib, uint32_t magic) {
+    return (x & nib) | magic;
+}
+
 // One repacked word (codes of 8 consecutive rows e = 0..7; even e in bits
 // 0..15, odd e in bits 16..31, 4 bits each) -> four bf16 pairs
 // (128 + q_e, 128 + q_{e+1}) for e = 0, 2, 4, 6: seven VALU operations.
-__device__ __forceinline__ void word_to_bf16x4(uint32_t w, uint32_t (&b)[4]) {
-    b[0] = (w & 0x000F000Fu) | kMagicPair;
-    b[1] = ((w >> 4) & 0x000F000Fu) | kMagicPair;
-    b[2] = ((w >> 8) & 0x000F000Fu) | kMagicPair;
-    b[3] = ((w >> 12) & 0x000F000Fu) | kMagicPair;
+__device__ __forceinline__ void word_to_bf16x4(uint32_t w, const DequantConsts &k, uint32_t (&b)[4]) {
+    b[0] = and_or(w, k.nib, k.magic);
+    b[1] = and_or(w >> 4, k.nib, k.magic);
+    b[2] = and_or(w >> 8, k.nib, k.magic);
+    b[3] = and_or(w >> 12, k.nib, k.magic);
 }
 
 __device__ __forceinline__ float bf16_bits_to_f32(uint32_t bits16) {
@@ -113,8 +137,8 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
 }
 
 // Workgroups are dispatched to the 8 XCDs round robin (block b -> XCD b % 8).
-// Give each XCD one contiguous range of work units, so the column strips that
-// share scale cache lines, and the K splits of one strip, meet in one L2.
+// Give each XCD one contiguous range of work units, so the K splits of one
+// strip meet in one L2.
 __device__ __forceinline__ int xcd_unit(int b, int nunits) {
     const int q = nunits / kXcds, r = nunits % kXcds;
     const int x = b % kXcds, slot = b / kXcds;
@@ -142,6 +166,39 @@ __device__ __forceinline__ float sum_quarters(float x) {
     uint32_t v = __float_as_uint(y);
     auto s16 = __builtin_amdgcn_permlane16_swap(v, v, false, false);
     return __uint_as_float(s16[0]) + __uint_as_float(s16[1]);
+}
+
+// s_waitcnt immediates (gfx9 encoding): vmcnt <= n only; LDS/scalar only.
+constexpr int waitcnt_vm(int n) { return (n & 15) | (7 << 4) | (15 << 8) | ((n >> 4) << 14); }
+constexpr int kWaitLgkm0 = 15 | (7 << 4) | (0 << 8) | (3 << 14);
+
+// Barrier for LDS traffic only: unlike __syncthreads() it does not wait for
+// outstanding global loads, so the weight ring stays in flight across it.
+__device__ __forceinline__ void lds_barrier() {
+    __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+    __builtin_amdgcn_s_barrier();
+}
+
+// 16 bytes per lane from global memory straight into LDS: lane l's bytes land
+// at lds_base + 16*l (lds_base wave-uniform).  Written as inline assembly so
+// that the compiler's wait insertion does not track it: the caller waits for
+// it explicitly (it is older than every load issued after it).
+// M0 is a reserved register to the compiler; nothing else in these kernels
+// uses it (no LDS-DMA builtins, messages or relative register moves), so
+// setting it here cannot disturb compiler-generated code.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void lds_dma16(const void *gsrc, uint32_t lds_base) {
+    // one wait state between the SALU write of M0 and the LDS-DMA load reading it
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+                 :
+                 : "v"(gsrc), "s"(lds_base)
+                 : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
+__device__ __forceinline__ uint32_t lds_addr(const void *p) {
+    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void *)p;
 }
 
 // ---------------------------------------------------------------- repack
@@ -176,7 +233,20 @@ __global__ void __launch_bounds__(256) repack_kernel(const uint32_t *__restrict_
     blob[pc] = out;
 }
 
-// Test exports: the same word_to_bf16x4 the GEMM kernels use.
+// Scales [G][N] -> [tile][group][16]: one thread per scale.
+__global__ void __launch_bounds__(256) repack_scales_kernel(const uint16_t *__restrict__ scales,
+                                                            uint16_t *__restrict__ out, int N, int G,
+                                                            long long count) {
+    const long long i = (long long)blockIdx.x * 256 + threadIdx.x;
+    if (i >= count) return;
+    const int c = (int)(i & 15);
+    const long long tg = i >> 4;
+    const int g = (int)(tg % G);
+    const long long t = tg / G;
+    out[i] = scales[(long long)g * N + t * 16 + c];
+}
+
+// Test exports: the same word_to_bf16x4 and scale layout the GEMM kernels use.
 template <bool CODES>
 __global__ void __launch_bounds__(256) export_kernel(const u32x4 *__restrict__ blob,
                                                      const uint16_t *__restrict__ scales,
@@ -190,11 +260,12 @@ __global__ void __launch_bounds__(256) export_kernel(const u32x4 *__restrict__ b
     const long long t = tg / G;
     const long long n = t * 16 + c;
     const u32x4 w = blob[pc];
-    const float s = CODES ? 0.0f : bf16_bits_to_f32(scales[(long long)g * N + n]);
+    const DequantConsts kc = dequant_consts();
+    const float s = CODES ? 0.0f : bf16_bits_to_f32(scales[tg * 16 + c]);
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
         uint32_t b[4];
-        word_to_bf16x4(w[r], b);
+        word_to_bf16x4(w[r], kc, b);
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
             const long long k = (long long)g * kGroup + h * 32 + r * 8 + 2 * v;
@@ -219,6 +290,12 @@ __global__ void __launch_bounds__(256) export_kernel(const u32x4 *__restrict__ b
 // 16 scales of each tile, through a D-deep register ring, so D*T KiB per
 // wavefront are in flight from the start.
 //
+// Issue order at start: first the asynchronous LDS fill of A (global -> LDS
+// without passing through registers), then the weight ring.  Memory
+// operations complete in order, so waiting for the A fill does not wait for
+// any weight load, and the first group can be computed as soon as its own
+// bytes arrive.  At the end, no load is issued past the last group.
+//
 // Lane l of a wavefront owns column c = l % 16 of each tile and quarter
 // h = l / 16 of each group (32 rows, 4 words).  In the MFMA path these are
 // exactly the B operands of four v_mfma_f32_16x16x32_bf16 (lane l holds
@@ -237,6 +314,10 @@ __global__ void __launch_bounds__(64 * KW) gemm_kernel(GemmArgs p) {
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
     __shared__ int s_last;
 
+    constexpr bool kGlobalA = (PATH == PATH_MFMA && ASRC == ASRC_GLOBAL);
+    constexpr bool kStage = !kGlobalA;
+    constexpr int kLoadsPerGroup = 2 * T + (kGlobalA ? 4 : 0);
+
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int M = (PATH == PATH_GEMV) ? MM : p.M;
@@ -250,26 +331,44 @@ __global__ void __launch_bounds__(64 * KW) gemm_kernel(GemmArgs p) {
     const int gk0 = gw0 + (Gwg * wave) / KW, gk1 = gw0 + (Gwg * (wave + 1)) / KW;
     const int ng = gk1 - gk0;
     const LdsLayout L = lds_layout(PATH, ASRC, M, Gwg, T, KW);
+    const DequantConsts kc = dequant_consts();
 
     int tl[T];
 #pragma unroll
     for (int t = 0; t < T; ++t) tl[t] = min(strip * T + t, p.NT - 1);
 
-    // ---- register ring, prefetched before anything else
+    // ---- 1. asynchronous LDS fill of this workgroup's K range of A
+    if constexpr (kStage) {
+        const int rowbytes = Gwg * kGroup * 2;
+        const int chunks_per_row = (rowbytes + 1023) >> 10;
+        for (int x = wave; x < M * chunks_per_row; x += KW) {
+            const int m = x / chunks_per_row, q = x - m * chunks_per_row;
+            const int off = (q << 10) + lane * 16;
+            const uint32_t dst = __builtin_amdgcn_readfirstlane(lds_addr(smem + L.a + m * L.row + (q << 10)));
+            if (off < rowbytes) {
+                const uint8_t *src = reinterpret_cast<const uint8_t *>(p.A + (size_t)m * p.K +
+                                                                       (size_t)gw0 * kGroup) + off;
+                lds_dma16(src, dst);
+            }
+        }
+    }
+
+    // ---- 2. weight ring, D groups deep, issued in slot order
     u32x4 wv[D][T];
     uint32_t sv[D][T];
-    u32x4 av[(ASRC == ASRC_GLOBAL && PATH == PATH_MFMA) ? D : 1][4];
+    u32x4 av[kGlobalA ? D : 1][4];
 
     auto load_group = [&](auto jc, int g) {
         constexpr int j = decltype(jc)::value;
 #pragma unroll
         for (int t = 0; t < T; ++t) {
-            wv[j][t] = __builtin_nontemporal_load(&p.blob[((size_t)tl[t] * p.G + g) * 64 + lane]);
+            const size_t tg = (size_t)tl[t] * p.G + g;
+            wv[j][t] = __builtin_nontemporal_load(&p.blob[tg * 64 + lane]);
             // the aligned dword that holds this lane's bf16 scale (a 16-bit
             // load would be re-extended at the loop latch, which stalls the ring)
-            sv[j][t] = reinterpret_cast<const uint32_t *>(p.scales)[((size_t)g * p.N + tl[t] * 16 + c) >> 1];
+            sv[j][t] = reinterpret_cast<const uint32_t *>(p.scales)[(tg * 16 + c) >> 1];
         }
-        if constexpr (ASRC == ASRC_GLOBAL && PATH == PATH_MFMA) {
+        if constexpr (kGlobalA) {
             // A rows >= M repeat row M-1: their results land in output rows
             // that are never written, and the loads stay branch free
             const u32x4 *ap = reinterpret_cast<const u32x4 *>(
@@ -278,47 +377,45 @@ __global__ void __launch_bounds__(64 * KW) gemm_kernel(GemmArgs p) {
             for (int r = 0; r < 4; ++r) av[j][r] = ap[r];   // rows 32h + 8r .. +8: 16 B
         }
     };
+    auto gidx = [&](int i) { return gk0 + min(i, ng - 1); };
 
     if (ng > 0) {
-        // issue in ring order (slot 0 first, weights then scale per slot), as
-        // the main loop does, so the wait counts of both paths agree
         [&]<int... J>(std::integer_sequence<int, J...>) {
-            ((load_group(std::integral_constant<int, J>{}, min(gk0 + J, gk1 - 1)),
+            ((load_group(std::integral_constant<int, J>{}, gidx(J)),
               __builtin_amdgcn_sched_barrier(0)),
              ...);
         }(std::make_integer_sequence<int, D>{});
     }
 
-    // ---- stage this workgroup's K range of A in LDS (GEMV: with bias sums)
-    constexpr bool kStage = (PATH == PATH_GEMV) || (ASRC == ASRC_LDS);
+    // ---- 3. A is in LDS once every wavefront's fill has landed
     if constexpr (kStage) {
-        const int nblk = M * Gwg * 4;
-        for (int b = threadIdx.x; b < nblk; b += 64 * KW) {
-            const int m = b / (Gwg * 4);
-            const int rem = b - m * Gwg * 4;
-            const int gl = rem >> 2, hq = rem & 3;
-            const u32x4 *src = reinterpret_cast<const u32x4 *>(
-                p.A + (size_t)m * p.K + (size_t)(gw0 + gl) * kGroup + hq * 32);
-            u32x4 x[4];
+        // this wavefront's fill is older than its ring loads (ng == 0: no ring)
+        if (ng > 0)
+            __builtin_amdgcn_s_waitcnt(waitcnt_vm(D * kLoadsPerGroup));
+        else
+            __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+        __builtin_amdgcn_s_barrier();
+        if constexpr (PATH == PATH_GEMV) {
+            // bias of every 32-row quarter: the GEMV lane's dot2 chain with every code 8
+            float *cs = reinterpret_cast<float *>(smem + L.csum);
+            for (int b = threadIdx.x; b < M * Gwg * 4; b += 64 * KW) {
+                const int m = b / (Gwg * 4);
+                const int rem = b - m * Gwg * 4;
+                const u32x4 *src = reinterpret_cast<const u32x4 *>(smem + L.a + m * L.row + rem * 64);
+                float s = 0.0f;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) x[i] = src[i];
-            u32x4 *dst = reinterpret_cast<u32x4 *>(smem + L.a + m * L.row + (gl * kGroup + hq * 32) * 2);
+                for (int i = 0; i < 4; ++i) {
+                    const u32x4 x = src[i];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) dst[i] = x[i];
-            if constexpr (PATH == PATH_GEMV) {
-                // the GEMV lane's dot2 chain of this quarter, with every code 8
-                float cs = 0.0f;
-#pragma unroll
-                for (int i = 0; i < 4; ++i)
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) cs = dot2_bf16(kBiasPair, x[i][e], cs);
-                reinterpret_cast<float *>(smem + L.csum)[(m * Gwg + gl) * 4 + hq] = cs;
+                    for (int e = 0; e < 4; ++e) s = dot2_bf16(kBiasPair, x[e], s);
+                }
+                cs[b] = s;
             }
+            lds_barrier();
         }
-        __syncthreads();
     }
 
-    // ---- main loop over this wavefront's groups
+    // ---- 4. main loop over this wavefront's groups
     constexpr int NACC = (PATH == PATH_GEMV) ? MM : 4;
     float acc[T][NACC];
 #pragma unroll
@@ -331,7 +428,7 @@ __global__ void __launch_bounds__(64 * KW) gemm_kernel(GemmArgs p) {
         const int gl = g - gw0;
         if constexpr (PATH == PATH_MFMA) {
             u32x4 a[4];
-            if constexpr (ASRC == ASRC_LDS) {
+            if constexpr (!kGlobalA) {
                 const uint8_t *arow = smem + L.a + arow_m * L.row + (gl * kGroup + h * 32) * 2;
 #pragma unroll
                 for (int r = 0; r < 4; ++r) a[r] = reinterpret_cast<const u32x4 *>(arow)[r];
@@ -350,7 +447,7 @@ __global__ void __launch_bounds__(64 * KW) gemm_kernel(GemmArgs p) {
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     uint32_t b[4];
-                    word_to_bf16x4(wv[j][t][r], b);
+                    word_to_bf16x4(wv[j][t][r], kc, b);
                     const u32x4 bv = {b[0], b[1], b[2], b[3]};
                     P = mfma16x16x32(a[r], bv, P);
                 }
@@ -376,7 +473,7 @@ __global__ void __launch_bounds__(64 * KW) gemm_kernel(GemmArgs p) {
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     uint32_t b[4];
-                    word_to_bf16x4(wv[j][t][r], b);
+                    word_to_bf16x4(wv[j][t][r], kc, b);
 #pragma unroll
                     for (int v = 0; v < 4; ++v)
 #pragma unroll
@@ -390,16 +487,33 @@ __global__ void __launch_bounds__(64 * KW) gemm_kernel(GemmArgs p) {
     };
 
     if (ng > 0) {
-        for (int base = 0; base < ng; base += D) {
+        int base = 0;
+        // steady state: compute slot j, then refill it with the group D ahead
+        // (every refill is a real group); D - 1 groups stay in flight
+        for (; base + 2 * D <= ng; base += D) {
             [&]<int... J>(std::integer_sequence<int, J...>) {
-                // compute group j of the ring, then refill slot j with the group D ahead:
-                // D - 1 groups stay in flight while one is being computed
-                ((base + J < ng ? compute_group(std::integral_constant<int, J>{}, gk0 + base + J)
-                                : void(),
-                  load_group(std::integral_constant<int, J>{}, min(gk0 + base + J + D, gk1 - 1))),
+                ((compute_group(std::integral_constant<int, J>{}, gk0 + base + J),
+                  load_group(std::integral_constant<int, J>{}, gk0 + base + J + D),
+                  __builtin_amdgcn_sched_barrier(0)),
                  ...);
             }(std::make_integer_sequence<int, D>{});
         }
+        // one round whose refills stop at the last group
+        if (base + D < ng) {
+            [&]<int... J>(std::integer_sequence<int, J...>) {
+                ((compute_group(std::integral_constant<int, J>{}, gk0 + base + J),
+                  base + J + D < ng ? load_group(std::integral_constant<int, J>{}, gk0 + base + J + D)
+                                    : void(),
+                  __builtin_amdgcn_sched_barrier(0)),
+                 ...);
+            }(std::make_integer_sequence<int, D>{});
+            base += D;
+        }
+        // last round: no more loads
+        [&]<int... J>(std::integer_sequence<int, J...>) {
+            ((base + J < ng ? compute_group(std::integral_constant<int, J>{}, gk0 + base + J) : void()),
+             ...);
+        }(std::make_integer_sequence<int, D>{});
     }
 
     // ---- GEMV: sum the four K quarters of each column across lanes
@@ -410,7 +524,7 @@ __global__ void __launch_bounds__(64 * KW) gemm_kernel(GemmArgs p) {
             for (int m = 0; m < MM; ++m) acc[t][m] = sum_quarters(acc[t][m]);
     }
 
-    // ---- epilogue: fixed-order reduction over wavefronts, then C or partials
+    // ---- 5. epilogue: fixed-order reduction over wavefronts, then C or partials
     const int NV = T * M * 16;   // values (t, m, c) of this workgroup
     auto emit = [&](int t, int m, int cc, float val) {
         const int tile = strip * T + t;
@@ -480,7 +594,7 @@ __global__ void __launch_bounds__(64 * KW) gemm_kernel(GemmArgs p) {
                 if (tile >= p.NT) continue;
                 const size_t n = (size_t)tile * 16 + cc;
                 float s = 0.0f;
-                for (int zz = 0; zz < p.S; ++zz) s += __builtin_nontemporal_load(&p.part[((size_t)zz * M + m) * p.N + n]);
+                for (int zz = 0; zz < p.S; ++zz) s += p.part[((size_t)zz * M + m) * p.N + n];
                 p.C[(size_t)m * p.N + n] = f32_to_bf16_rne(s);
             }
             if (threadIdx.x == 0) atomicExch(&p.count[strip], 0u);

@@ -87,6 +87,8 @@ extern "C" {
  *   splits  workgroups that split K for the same columns (1 = none); more
  *           than one needs a workspace (see w4a16_workspace_bytes)
  *   asrc    W4A16_ASRC_LDS or W4A16_ASRC_GLOBAL (MFMA path only)
+ *   depth   K groups each wavefront keeps in flight (0 = the default for
+ *           `tiles`: 8, 4, 2 for 1, 2, 4 tiles)
  */
 typedef struct {
     int path;
@@ -94,6 +96,7 @@ typedef struct {
     int kwaves;
     int splits;
     int asrc;
+    int depth;
 } w4a16_plan_t;
 
 /* Human-readable name of a status code (static storage, never NULL). */

@@ -26,29 +26,38 @@ constexpr int kLdsBudget = 64 * 1024;   // per workgroup: at least two workgroup
 using KernelFn = void (*)(GemmArgs);
 
 struct Variant {
-    int path, mm, tiles, kwaves, asrc;   // mm: GEMV rows (1..4), 0 for MFMA
+    int path, mm, tiles, kwaves, depth, asrc;   // mm: compile-time row count (0: run time)
     KernelFn fn;
 };
 
-#define GEMV_V(MM, T, KW, D) {PATH_GEMV, MM, T, KW, ASRC_LDS, gemm_kernel<PATH_GEMV, MM, T, KW, D, ASRC_LDS>}
-#define GEMV_ALL_M(T, KW, D) GEMV_V(1, T, KW, D), GEMV_V(2, T, KW, D), GEMV_V(3, T, KW, D), GEMV_V(4, T, KW, D)
-#define MFMA_V(T, KW, D, AS) {PATH_MFMA, 0, T, KW, AS, gemm_kernel<PATH_MFMA, 0, T, KW, D, AS>}
+// (tiles, kwaves, depth) shapes instantiated for every path / row count
+#define W4A16_SHAPES(X, P, MM, AS) \
+    X(P, MM, 1, 1, 8, AS) X(P, MM, 1, 4, 8, AS) X(P, MM, 1, 8, 4, AS) X(P, MM, 1, 8, 8, AS) \
+    X(P, MM, 2, 4, 4, AS) X(P, MM, 2, 8, 4, AS) X(P, MM, 2, 4, 8, AS) X(P, MM, 4, 4, 2, AS) \
+    X(P, MM, 4, 4, 4, AS)
+#define W4A16_V(P, MM, T, KW, D, AS) {P, MM, T, KW, D, AS, gemm_kernel<P, MM, T, KW, D, AS>},
 
 const Variant kVariants[] = {
-    GEMV_ALL_M(1, 4, 8), GEMV_ALL_M(1, 8, 8), GEMV_ALL_M(2, 4, 4), GEMV_ALL_M(2, 8, 4),
-    GEMV_ALL_M(4, 4, 2), GEMV_ALL_M(1, 1, 8),
-    MFMA_V(1, 4, 8, ASRC_LDS), MFMA_V(1, 8, 8, ASRC_LDS), MFMA_V(2, 4, 4, ASRC_LDS),
-    MFMA_V(2, 8, 4, ASRC_LDS), MFMA_V(4, 4, 2, ASRC_LDS), MFMA_V(1, 1, 8, ASRC_LDS),
-    MFMA_V(1, 4, 4, ASRC_GLOBAL), MFMA_V(1, 8, 4, ASRC_GLOBAL), MFMA_V(2, 4, 4, ASRC_GLOBAL),
-    MFMA_V(2, 8, 4, ASRC_GLOBAL), MFMA_V(4, 4, 2, ASRC_GLOBAL), MFMA_V(1, 1, 4, ASRC_GLOBAL),
+    W4A16_SHAPES(W4A16_V, PATH_GEMV, 1, ASRC_LDS) W4A16_SHAPES(W4A16_V, PATH_GEMV, 2, ASRC_LDS)
+    W4A16_SHAPES(W4A16_V, PATH_GEMV, 3, ASRC_LDS) W4A16_SHAPES(W4A16_V, PATH_GEMV, 4, ASRC_LDS)
+    W4A16_SHAPES(W4A16_V, PATH_MFMA, 0, ASRC_LDS) W4A16_SHAPES(W4A16_V, PATH_MFMA, 0, ASRC_GLOBAL)
+    W4A16_SHAPES(W4A16_V, PATH_MFMA, 1, ASRC_LDS) W4A16_SHAPES(W4A16_V, PATH_MFMA, 1, ASRC_GLOBAL)
+    W4A16_SHAPES(W4A16_V, PATH_MFMA, 2, ASRC_LDS) W4A16_SHAPES(W4A16_V, PATH_MFMA, 2, ASRC_GLOBAL)
+    W4A16_SHAPES(W4A16_V, PATH_MFMA, 3, ASRC_LDS) W4A16_SHAPES(W4A16_V, PATH_MFMA, 3, ASRC_GLOBAL)
+    W4A16_SHAPES(W4A16_V, PATH_MFMA, 4, ASRC_LDS) W4A16_SHAPES(W4A16_V, PATH_MFMA, 4, ASRC_GLOBAL)
 };
 
+int default_depth(int tiles) { return tiles == 1 ? 8 : (tiles == 2 ? 4 : 2); }
+
+// The kernel for a plan: GEMV kernels are compiled per row count (1..4);
+// MFMA kernels too for M <= 4, and take M at run time above.
 const Variant *find_variant(const w4a16_plan_t &p, int M) {
-    const int mm = (p.path == W4A16_PATH_GEMV) ? M : 0;
+    const int mm = (p.path == W4A16_PATH_GEMV || M <= 4) ? M : 0;
     const int asrc = (p.path == W4A16_PATH_GEMV) ? ASRC_LDS : p.asrc;
+    const int depth = p.depth ? p.depth : default_depth(p.tiles);
     for (const Variant &v : kVariants)
         if (v.path == p.path && v.mm == mm && v.tiles == p.tiles && v.kwaves == p.kwaves &&
-            v.asrc == asrc)
+            v.depth == depth && v.asrc == asrc)
             return &v;
     return nullptr;
 }
@@ -99,6 +108,7 @@ int validate_plan(const w4a16_plan_t &p, int M, int N, int K) {
     if (p.path == W4A16_PATH_GEMV && M > 4) return W4A16_ERR_PLAN;
     if (p.splits < 1 || p.splits > G) return W4A16_ERR_PLAN;
     if (p.asrc != W4A16_ASRC_LDS && p.asrc != W4A16_ASRC_GLOBAL) return W4A16_ERR_PLAN;
+    if (p.depth < 0) return W4A16_ERR_PLAN;
     if (!find_variant(p, M)) return W4A16_ERR_PLAN;
     if (plan_lds(p, M, G) > kLdsBudget) return W4A16_ERR_PLAN;
     const long long nstrips = (N / 16 + p.tiles - 1) / p.tiles;
@@ -125,6 +135,7 @@ void auto_plan(int M, int N, int K, w4a16_plan_t *out) {
     if (p.kwaves > G) p.kwaves = (G >= 4) ? 4 : 1;
     p.splits = 1;
     p.asrc = W4A16_ASRC_LDS;
+    p.depth = 0;
     if (p.path == W4A16_PATH_GEMV && plan_lds(p, M, G) > kLdsBudget) p.path = W4A16_PATH_MFMA;
     if (p.path == W4A16_PATH_MFMA && plan_lds(p, M, G) > kLdsBudget) p.asrc = W4A16_ASRC_GLOBAL;
     *out = p;

@@ -62,7 +62,8 @@ struct GemmArgs {
 // Shared by host (sizing) and device (carving).  Offsets in bytes.
 struct LdsLayout {
     int a;      // staged A rows [M][Gwg*128 bf16 + pad]
-    int csum;   // GEMV: bias sum of each 32-row quarter of a group [M][Gwg][4] fp32
+    int bias;   // GEMV: bias of each 32-row quarter [M][Gwg][4] fp32;
+                // MFMA with staged A: bias tile rows [Gwg][16] fp32
     int red;    // cross-wavefront reduction [KW][T*M*16] fp32
     int total;
     int row;    // bytes per staged A row
@@ -75,8 +76,9 @@ __host__ __device__ inline LdsLayout lds_layout(int path, int asrc, int M, int G
     int off = 0;
     L.a = off;
     if (stage) off += M * L.row;
-    L.csum = off;
+    L.bias = off;
     if (path == PATH_GEMV) off += M * Gwg * 4 * 4;
+    else if (stage) off += Gwg * 16 * 4;
     L.red = off;
     if (KW > 1) off += KW * T * M * 16 * 4;
     L.total = off;
@@ -288,13 +290,15 @@ __global__ void __launch_bounds__(256) export_kernel(const u32x4 *__restrict__ b
 // range further.  Every wavefront streams, for each of its groups, T pieces
 // of 1 KiB (one 16-byte load per lane, the whole 1 KiB contiguous) plus the
 // 16 scales of each tile, through a D-deep register ring, so D*T KiB per
-// wavefront are in flight from the start.
+// wavefront are in flight from the start.  All addresses are a wave-uniform
+// base (scalar registers) plus a fixed per-lane offset, so the stream costs
+// no vector instructions for address arithmetic.
 //
 // Issue order at start: first the asynchronous LDS fill of A (global -> LDS
 // without passing through registers), then the weight ring.  Memory
 // operations complete in order, so waiting for the A fill does not wait for
 // any weight load, and the first group can be computed as soon as its own
-// bytes arrive.  At the end, no load is issued past the last group.
+// bytes arrive.
 //
 // Lane l of a wavefront owns column c = l % 16 of each tile and quarter
 // h = l / 16 of each group (32 rows, 4 words).  In the MFMA path these are
@@ -304,6 +308,10 @@ __global__ void __launch_bounds__(256) export_kernel(const u32x4 *__restrict__ b
 // l % 16 in register v.  In the GEMV path each lane forms dot products of its
 // 32 rows with v_dot2_f32_bf16, and the four quarters of a column are summed
 // across lanes at the very end.
+//
+// MM is the row count when it is known at compile time (1..4; the GEMV path
+// always has it): then only the live rows are scaled and accumulated.  MM = 0
+// (MFMA only) takes M at run time, up to 16.
 //
 // The partial sums of the KW wavefronts meet in LDS and are added in a fixed
 // order; with S > 1 the workgroups of one strip meet in the workspace, where
@@ -317,10 +325,12 @@ __global__ void __launch_bounds__(64 * KW) gemm_kernel(GemmArgs p) {
     constexpr bool kGlobalA = (PATH == PATH_MFMA && ASRC == ASRC_GLOBAL);
     constexpr bool kStage = !kGlobalA;
     constexpr int kLoadsPerGroup = 2 * T + (kGlobalA ? 4 : 0);
+    // rows of the 4-row block held by lane group h that are ever stored
+    constexpr int kRowsV = (MM >= 1 && MM <= 4) ? MM : 4;
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int M = (PATH == PATH_GEMV) ? MM : p.M;
+    const int M = (MM >= 1) ? MM : p.M;
     const int c = lane & 15, h = lane >> 4;
     const int arow_m = min(c, M - 1);   // MFMA A-operand row of this lane
 
@@ -333,9 +343,20 @@ __global__ void __launch_bounds__(64 * KW) gemm_kernel(GemmArgs p) {
     const LdsLayout L = lds_layout(PATH, ASRC, M, Gwg, T, KW);
     const DequantConsts kc = dequant_consts();
 
-    int tl[T];
+    // wave-uniform bases (scalar) and per-lane byte offsets (vector, fixed)
+    const uint8_t *wbase[T];
+    const uint8_t *sbase[T];
 #pragma unroll
-    for (int t = 0; t < T; ++t) tl[t] = min(strip * T + t, p.NT - 1);
+    for (int t = 0; t < T; ++t) {
+        const size_t tile = (size_t)min(strip * T + t, p.NT - 1);
+        wbase[t] = reinterpret_cast<const uint8_t *>(p.blob) + tile * (size_t)p.G * 1024;
+        sbase[t] = reinterpret_cast<const uint8_t *>(p.scales) + tile * (size_t)p.G * 32;
+    }
+    const uint32_t w_lane = (uint32_t)lane * 16;             // this lane's 16 B of a 1 KiB piece
+    const uint32_t s_lane = (uint32_t)(c >> 1) * 4;          // dword holding this column's scale
+    const uint32_t s_shift = (c & 1) ? 0u : 16u;             // bring the scale to the high half
+    const uint8_t *abase = reinterpret_cast<const uint8_t *>(p.A) +
+                           ((size_t)arow_m * p.K + (size_t)h * 32) * 2;   // MFMA A from global
 
     // ---- 1. asynchronous LDS fill of this workgroup's K range of A
     if constexpr (kStage) {
@@ -362,17 +383,16 @@ __global__ void __launch_bounds__(64 * KW) gemm_kernel(GemmArgs p) {
         constexpr int j = decltype(jc)::value;
 #pragma unroll
         for (int t = 0; t < T; ++t) {
-            const size_t tg = (size_t)tl[t] * p.G + g;
-            wv[j][t] = __builtin_nontemporal_load(&p.blob[tg * 64 + lane]);
+            wv[j][t] = __builtin_nontemporal_load(
+                reinterpret_cast<const u32x4 *>(wbase[t] + (size_t)g * 1024 + w_lane));
             // the aligned dword that holds this lane's bf16 scale (a 16-bit
             // load would be re-extended at the loop latch, which stalls the ring)
-            sv[j][t] = reinterpret_cast<const uint32_t *>(p.scales)[(tg * 16 + c) >> 1];
+            sv[j][t] = *reinterpret_cast<const uint32_t *>(sbase[t] + (size_t)g * 32 + s_lane);
         }
         if constexpr (kGlobalA) {
             // A rows >= M repeat row M-1: their results land in output rows
             // that are never written, and the loads stay branch free
-            const u32x4 *ap = reinterpret_cast<const u32x4 *>(
-                p.A + (size_t)arow_m * p.K + (size_t)g * kGroup + h * 32);
+            const u32x4 *ap = reinterpret_cast<const u32x4 *>(abase + (size_t)g * kGroup * 2);
 #pragma unroll
             for (int r = 0; r < 4; ++r) av[j][r] = ap[r];   // rows 32h + 8r .. +8: 16 B
         }
@@ -387,7 +407,8 @@ __global__ void __launch_bounds__(64 * KW) gemm_kernel(GemmArgs p) {
         }(std::make_integer_sequence<int, D>{});
     }
 
-    // ---- 3. A is in LDS once every wavefront's fill has landed
+    // ---- 3. A is in LDS once every wavefront's fill has landed; then the
+    //         bias of every group, formed once per workgroup
     if constexpr (kStage) {
         // this wavefront's fill is older than its ring loads (ng == 0: no ring)
         if (ng > 0)
@@ -395,9 +416,9 @@ __global__ void __launch_bounds__(64 * KW) gemm_kernel(GemmArgs p) {
         else
             __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
         __builtin_amdgcn_s_barrier();
+        float *bias = reinterpret_cast<float *>(smem + L.bias);
         if constexpr (PATH == PATH_GEMV) {
-            // bias of every 32-row quarter: the GEMV lane's dot2 chain with every code 8
-            float *cs = reinterpret_cast<float *>(smem + L.csum);
+            // each 32-row quarter: the GEMV lane's dot2 chain with every code 8
             for (int b = threadIdx.x; b < M * Gwg * 4; b += 64 * KW) {
                 const int m = b / (Gwg * 4);
                 const int rem = b - m * Gwg * 4;
@@ -409,14 +430,27 @@ __global__ void __launch_bounds__(64 * KW) gemm_kernel(GemmArgs p) {
 #pragma unroll
                     for (int e = 0; e < 4; ++e) s = dot2_bf16(kBiasPair, x[e], s);
                 }
-                cs[b] = s;
+                bias[b] = s;
             }
-            lds_barrier();
+        } else {
+            // each group: the MFMA lanes' four-instruction chain with every code
+            // 8, exactly as the main loop would form it; rows 4h..4h+3 of column
+            // 0 are stored (all 16 columns are equal)
+            const u32x4 bconst = {kBiasPair, kBiasPair, kBiasPair, kBiasPair};
+            for (int gl = wave; gl < Gwg; gl += KW) {
+                const uint8_t *arow = smem + L.a + arow_m * L.row + (gl * kGroup + h * 32) * 2;
+                f32x4 Q = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    Q = mfma16x16x32(reinterpret_cast<const u32x4 *>(arow)[r], bconst, Q);
+                if (c == 0) reinterpret_cast<f32x4 *>(bias)[gl * 4 + h] = Q;
+            }
         }
+        lds_barrier();
     }
 
     // ---- 4. main loop over this wavefront's groups
-    constexpr int NACC = (PATH == PATH_GEMV) ? MM : 4;
+    constexpr int NACC = (PATH == PATH_GEMV) ? MM : kRowsV;
     float acc[T][NACC];
 #pragma unroll
     for (int t = 0; t < T; ++t)
@@ -428,19 +462,21 @@ __global__ void __launch_bounds__(64 * KW) gemm_kernel(GemmArgs p) {
         const int gl = g - gw0;
         if constexpr (PATH == PATH_MFMA) {
             u32x4 a[4];
+            f32x4 Q;
             if constexpr (!kGlobalA) {
                 const uint8_t *arow = smem + L.a + arow_m * L.row + (gl * kGroup + h * 32) * 2;
 #pragma unroll
                 for (int r = 0; r < 4; ++r) a[r] = reinterpret_cast<const u32x4 *>(arow)[r];
+                Q = reinterpret_cast<const f32x4 *>(smem + L.bias)[gl * 4 + h];
             } else {
 #pragma unroll
                 for (int r = 0; r < 4; ++r) a[r] = av[j][r];
-            }
-            // bias: the same four-MFMA chain with every code 8
-            const u32x4 bias = {kBiasPair, kBiasPair, kBiasPair, kBiasPair};
-            f32x4 Q = {0.0f, 0.0f, 0.0f, 0.0f};
+                // bias: the same four-MFMA chain with every code 8
+                const u32x4 bconst = {kBiasPair, kBiasPair, kBiasPair, kBiasPair};
+                Q = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-            for (int r = 0; r < 4; ++r) Q = mfma16x16x32(a[r], bias, Q);
+                for (int r = 0; r < 4; ++r) Q = mfma16x16x32(a[r], bconst, Q);
+            }
 #pragma unroll
             for (int t = 0; t < T; ++t) {
                 f32x4 P = {0.0f, 0.0f, 0.0f, 0.0f};
@@ -451,69 +487,63 @@ __global__ void __launch_bounds__(64 * KW) gemm_kernel(GemmArgs p) {
                     const u32x4 bv = {b[0], b[1], b[2], b[3]};
                     P = mfma16x16x32(a[r], bv, P);
                 }
-                const float s = scale_of(sv[j][t], c);
+                const float s = __uint_as_float((sv[j][t] << s_shift) & 0xFFFF0000u);
 #pragma unroll
-                for (int v = 0; v < 4; ++v) acc[t][v] = __builtin_fmaf(s, P[v] - Q[v], acc[t][v]);
+                for (int v = 0; v < kRowsV; ++v) acc[t][v] = __builtin_fmaf(s, P[v] - Q[v], acc[t][v]);
             }
         } else {
-            u32x4 ar[MM][4];
-            float corr[MM];
+            // r outermost: one 16-byte A sub-block per row is live at a time.
+            // Per (tile, row) the dot2 chain runs r = 0..3, v = 0..3, the same
+            // order the bias was formed in.
+            float part[T][MM];
 #pragma unroll
-            for (int m = 0; m < MM; ++m) {
-                const uint8_t *arow = smem + L.a + m * L.row + (gl * kGroup + h * 32) * 2;
+            for (int t = 0; t < T; ++t)
 #pragma unroll
-                for (int r = 0; r < 4; ++r) ar[m][r] = reinterpret_cast<const u32x4 *>(arow)[r];
-                corr[m] = reinterpret_cast<const float *>(smem + L.csum)[(m * Gwg + gl) * 4 + h];
-            }
+                for (int m = 0; m < MM; ++m) part[t][m] = 0.0f;
 #pragma unroll
-            for (int t = 0; t < T; ++t) {
-                float part[MM];
+            for (int r = 0; r < 4; ++r) {
+                u32x4 ar[MM];
 #pragma unroll
-                for (int m = 0; m < MM; ++m) part[m] = 0.0f;
+                for (int m = 0; m < MM; ++m)
+                    ar[m] = reinterpret_cast<const u32x4 *>(smem + L.a + m * L.row +
+                                                           (gl * kGroup + h * 32) * 2)[r];
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
+                for (int t = 0; t < T; ++t) {
                     uint32_t b[4];
                     word_to_bf16x4(wv[j][t][r], kc, b);
 #pragma unroll
                     for (int v = 0; v < 4; ++v)
 #pragma unroll
-                        for (int m = 0; m < MM; ++m) part[m] = dot2_bf16(b[v], ar[m][r][v], part[m]);
+                        for (int m = 0; m < MM; ++m) part[t][m] = dot2_bf16(b[v], ar[m][v], part[t][m]);
                 }
-                const float s = scale_of(sv[j][t], c);
+            }
 #pragma unroll
-                for (int m = 0; m < MM; ++m) acc[t][m] = __builtin_fmaf(s, part[m] - corr[m], acc[t][m]);
+            for (int t = 0; t < T; ++t) {
+                const float s = __uint_as_float((sv[j][t] << s_shift) & 0xFFFF0000u);
+#pragma unroll
+                for (int m = 0; m < MM; ++m) {
+                    const float corr = reinterpret_cast<const float *>(smem + L.bias)[(m * Gwg + gl) * 4 + h];
+                    acc[t][m] = __builtin_fmaf(s, part[t][m] - corr, acc[t][m]);
+                }
             }
         }
     };
 
     if (ng > 0) {
-        int base = 0;
-        // steady state: compute slot j, then refill it with the group D ahead
-        // (every refill is a real group); D - 1 groups stay in flight
-        for (; base + 2 * D <= ng; base += D) {
+        // compute slot j, then refill it with the group D ahead, so D - 1
+        // groups stay in flight.  Past the last group the refill re-reads the
+        // last group (clamped): it is in flight or in L2 already, so it costs
+        // no HBM traffic, and every iteration issues the same loads, which
+        // keeps the wait counts static (a data-dependent skip would make the
+        // compiler wait for every load in flight at each slot).
+        for (int base = 0; base < ng; base += D) {
             [&]<int... J>(std::integer_sequence<int, J...>) {
-                ((compute_group(std::integral_constant<int, J>{}, gk0 + base + J),
-                  load_group(std::integral_constant<int, J>{}, gk0 + base + J + D),
+                ((base + J < ng ? compute_group(std::integral_constant<int, J>{}, gk0 + base + J) : void(),
+                  load_group(std::integral_constant<int, J>{}, gidx(base + J + D)),
                   __builtin_amdgcn_sched_barrier(0)),
                  ...);
             }(std::make_integer_sequence<int, D>{});
         }
-        // one round whose refills stop at the last group
-        if (base + D < ng) {
-            [&]<int... J>(std::integer_sequence<int, J...>) {
-                ((compute_group(std::integral_constant<int, J>{}, gk0 + base + J),
-                  base + J + D < ng ? load_group(std::integral_constant<int, J>{}, gk0 + base + J + D)
-                                    : void(),
-                  __builtin_amdgcn_sched_barrier(0)),
-                 ...);
-            }(std::make_integer_sequence<int, D>{});
-            base += D;
-        }
-        // last round: no more loads
-        [&]<int... J>(std::integer_sequence<int, J...>) {
-            ((base + J < ng ? compute_group(std::integral_constant<int, J>{}, gk0 + base + J) : void()),
-             ...);
-        }(std::make_integer_sequence<int, D>{});
     }
 
     // ---- GEMV: sum the four K quarters of each column across lanes
@@ -532,8 +562,9 @@ __global__ void __launch_bounds__(64 * KW) gemm_kernel(GemmArgs p) {
         const size_t n = (size_t)tile * 16 + cc;
         if (p.S == 1)
             p.C[(size_t)m * p.N + n] = f32_to_bf16_rne(val);
-        else
-            p.part[((size_t)z * M + m) * p.N + n] = val;
+        else   // device-coherent store (the XCDs' L2s are not coherent with each other)
+            __hip_atomic_store(&p.part[((size_t)z * M + m) * p.N + n], val, __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
     };
 
     if constexpr (KW == 1) {
@@ -541,7 +572,7 @@ __global__ void __launch_bounds__(64 * KW) gemm_kernel(GemmArgs p) {
         for (int t = 0; t < T; ++t) {
             if constexpr (PATH == PATH_MFMA) {
 #pragma unroll
-                for (int v = 0; v < 4; ++v)
+                for (int v = 0; v < kRowsV; ++v)
                     if (4 * h + v < M) emit(t, 4 * h + v, c, acc[t][v]);
             } else {
                 if (h == 0) {
@@ -557,7 +588,7 @@ __global__ void __launch_bounds__(64 * KW) gemm_kernel(GemmArgs p) {
         for (int t = 0; t < T; ++t) {
             if constexpr (PATH == PATH_MFMA) {
 #pragma unroll
-                for (int v = 0; v < 4; ++v)
+                for (int v = 0; v < kRowsV; ++v)
                     if (4 * h + v < M) mine[(t * M + 4 * h + v) * 16 + c] = acc[t][v];
             } else {
                 if (h == 0) {
@@ -566,7 +597,7 @@ __global__ void __launch_bounds__(64 * KW) gemm_kernel(GemmArgs p) {
                 }
             }
         }
-        __syncthreads();
+        lds_barrier();   // LDS only: the clamped refills still in flight need no wait
         for (int e = threadIdx.x; e < NV; e += 64 * KW) {
             float s = red[e];
 #pragma unroll
@@ -577,27 +608,33 @@ __global__ void __launch_bounds__(64 * KW) gemm_kernel(GemmArgs p) {
     }
 
     if (p.S > 1) {
-        // Publish this workgroup's partials, count arrivals, and let the last
-        // workgroup of the strip add all S partials in order z = 0..S-1.
-        __threadfence();
-        __syncthreads();
+        // Hand-off between the S workgroups of a strip without flushing any
+        // L2: partials go out with device-coherent stores, every thread waits
+        // for its own stores to complete, then one counter increment per
+        // workgroup; the last to arrive reads the S partials with
+        // device-coherent loads and adds them in the fixed order z = 0..S-1.
+        __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+        __builtin_amdgcn_s_barrier();
         if (threadIdx.x == 0) {
-            const uint32_t prev = atomicAdd(&p.count[strip], 1u);
+            const uint32_t prev = __hip_atomic_fetch_add(&p.count[strip], 1u, __ATOMIC_RELAXED,
+                                                         __HIP_MEMORY_SCOPE_AGENT);
             s_last = (prev == (uint32_t)(p.S - 1));
         }
-        __syncthreads();
+        lds_barrier();
         if (s_last) {
-            __threadfence();
             for (int e = threadIdx.x; e < NV; e += 64 * KW) {
                 const int t = e / (16 * M), m = (e >> 4) - t * M, cc = e & 15;
                 const int tile = strip * T + t;
                 if (tile >= p.NT) continue;
                 const size_t n = (size_t)tile * 16 + cc;
                 float s = 0.0f;
-                for (int zz = 0; zz < p.S; ++zz) s += p.part[((size_t)zz * M + m) * p.N + n];
+                for (int zz = 0; zz < p.S; ++zz)
+                    s += __hip_atomic_load(&p.part[((size_t)zz * M + m) * p.N + n], __ATOMIC_RELAXED,
+                                           __HIP_MEMORY_SCOPE_AGENT);
                 p.C[(size_t)m * p.N + n] = f32_to_bf16_rne(s);
             }
-            if (threadIdx.x == 0) atomicExch(&p.count[strip], 0u);
+            if (threadIdx.x == 0)
+                __hip_atomic_store(&p.count[strip], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
     }
 }

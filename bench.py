@@ -9,8 +9,8 @@ call streams its weights from HBM.
 
 Prints ONE JSON line:
   value        algorithmic bytes per call / (graph replay time / steps), GB/s
-  roofline     the kernel's own average duration from per-launch HIP events
-               (eager launches on the launch stream), against 8 TB/s
+  roofline     the same per-launch duration (timed region / steps, one kernel
+               launch per step) against MI355X's 8 TB/s
   cpu_baseline the fp64 CPU oracle on the same workload (rank 0 only)
 
 --sweep prints one JSON line per (workload, M) instead (not the contract line);
@@ -107,36 +107,29 @@ def time_graph(torch, fn, steps, warmup):
     return e0.elapsed_time(e1) / steps
 
 
-def time_eager_per_launch(torch, fn, launches):
-    """Average GPU duration of one call: an event pair around every launch (ms)."""
-    stream = torch.cuda.current_stream()
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(launches)]
-    torch.cuda.synchronize()
-    for i, (a, b) in enumerate(evs):
-        a.record(stream)
-        fn(i)
-        b.record(stream)
-    torch.cuda.synchronize()
-    ts = sorted(a.elapsed_time(b) for a, b in evs)
-    return sum(ts) / len(ts), ts[len(ts) // 2]
-
-
-def measure(torch, w4, prob, M, steps, warmup, launches=200):
+def measure(torch, w4, prob, M, steps, warmup):
     ms_graph = time_graph(torch, lambda i: prob.call(w4, M, i), steps, warmup)
-    ms_kern, ms_kern_med = time_eager_per_launch(torch, lambda i: prob.call(w4, M, i), launches)
     nbytes = synth.algorithmic_bytes(M, prob.N, prob.K)
     flops = 2.0 * M * prob.N * prob.K
     return {
         "ms_per_step": ms_graph,
         "us_per_call": ms_graph * 1e3,
         "gbs": nbytes / (ms_graph * 1e-3) / 1e9,
-        "kernel_us": ms_kern * 1e3,
-        "kernel_us_median": ms_kern_med * 1e3,
-        "kernel_gbs": nbytes / (ms_kern * 1e-3) / 1e9,
         "bytes": nbytes,
-        "tflops": flops / (ms_kern * 1e-3) / 1e12,
+        "tflops": flops / (ms_graph * 1e-3) / 1e12,
     }
+
+
+def copy_calibration(torch, mib, reps=4):
+    """Plain device-to-device copies of a known size (a reference for the HBM byte counters)."""
+    n = mib << 20
+    src = torch.empty(n, dtype=torch.uint8, device="cuda:0").fill_(1)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    log(f"bench: {reps} copies of {mib} MiB (read {n} B, write {n} B each)")
 
 
 def cpu_baseline(prob, M, seconds=10.0):
@@ -183,6 +176,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--sweep", action="store_true", help="one JSON line per (workload, M)")
     ap.add_argument("--stack", action="store_true", help="full decode-step sweep of linear shapes")
+    ap.add_argument("--copy-calib", type=int, default=0, metavar="MIB",
+                    help="after timing, copy MIB MiB a few times (reference for byte counters)")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -211,11 +206,13 @@ def main():
     prob = Problem(torch, w4, wl.K, wl.N, wl.seed, wl.act, sets)
     r = measure(torch, w4, prob, M, args.steps, args.warmup)
     plan = w4.get_plan(M, wl.N, wl.K).as_dict()
-    log(f"bench: graph {r['us_per_call']:.2f} us/call {r['gbs']:.0f} GB/s; "
-        f"kernel {r['kernel_us']:.2f} us {r['kernel_gbs']:.0f} GB/s; plan {plan}")
+    log(f"bench: {r['us_per_call']:.3f} us/call {r['gbs']:.0f} GB/s; plan {plan}")
+    if args.copy_calib:
+        copy_calibration(torch, args.copy_calib)
 
-    roof = {"bound": "hbm", "achieved": round(r["kernel_gbs"], 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-            "frac": round(r["kernel_gbs"] / PEAK_HBM_GBS, 4),
+    # one launch per step: the per-launch duration is the timed region / steps
+    roof = {"bound": "hbm", "achieved": round(r["gbs"], 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+            "frac": round(r["gbs"] / PEAK_HBM_GBS, 4),
             "traffic": traffic_record(f"{args.workload}_m{M}")}
     out = {
         "metric": METRIC,
@@ -235,11 +232,10 @@ def main():
             "M": M, "K": wl.K, "N": wl.N, "group": 128,
             "us_per_call": round(r["us_per_call"], 3),
             "pct_of_peak_hbm": round(100 * r["gbs"] / PEAK_HBM_GBS, 2),
-            "kernel_us_per_call": round(r["kernel_us"], 3),
             "algorithmic_bytes_per_call": r["bytes"],
             "buffer_sets": sets,
             "plan": plan,
-            "timing": "value: one HIP graph of `steps` calls; roofline: event pair per eager launch",
+            "timing": "HIP events around one graph replay of `steps` dependent calls on the launch stream",
             "device": name,
         },
         "roofline": roof,
@@ -262,12 +258,10 @@ def sweep(torch, w4, args):
         prob = Problem(torch, w4, wl.K, wl.N, wl.seed, wl.act, sets)
         for M in Ms:
             steps = max(20, min(args.steps, int(2e6 / synth.algorithmic_bytes(M, wl.N, wl.K) * 100)))
-            r = measure(torch, w4, prob, M, steps, min(args.warmup, 20), launches=min(100, steps))
+            r = measure(torch, w4, prob, M, steps, min(args.warmup, 20))
             rec = {"workload": wname, "M": M, "K": wl.K, "N": wl.N, "plan": w4.get_plan(M, wl.N, wl.K).as_dict(),
                    "us_per_call": round(r["us_per_call"], 3), "GBps": round(r["gbs"], 1),
                    "pct_peak": round(100 * r["gbs"] / PEAK_HBM_GBS, 2),
-                   "kernel_us": round(r["kernel_us"], 3), "kernel_GBps": round(r["kernel_gbs"], 1),
-                   "kernel_pct_peak": round(100 * r["kernel_gbs"] / PEAK_HBM_GBS, 2),
                    "mfma_util": round(r["tflops"] / PEAK_BF16_TFLOPS, 4), "sets": sets}
             print(json.dumps(rec), flush=True)
         del prob

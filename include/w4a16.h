@@ -84,8 +84,9 @@ extern "C" {
  *   path    W4A16_PATH_GEMV or W4A16_PATH_MFMA
  *   tiles   16-column tiles per wavefront (1, 2 or 4)
  *   kwaves  wavefronts of one workgroup that split the workgroup's K range
- *   splits  workgroups that split K for the same columns (1 = none); more
- *           than one needs a workspace (see w4a16_workspace_bytes)
+ *   splits  workgroups that split K for the same columns: 1 (none), 2, 4, 8, ...
+ *           (a power of two); more than one needs a workspace (see
+ *           w4a16_workspace_bytes)
  *   asrc    W4A16_ASRC_LDS or W4A16_ASRC_GLOBAL (MFMA path only)
  *   depth   K groups each wavefront keeps in flight (0 = the default for
  *           `tiles`: 8, 4, 2 for 1, 2, 4 tiles)

@@ -72,7 +72,8 @@ def test_gemm_plan_errors():
         w4.make_plan(w4.PATH_MFMA, 3, 4),             # no such tile count
         w4.make_plan(w4.PATH_MFMA, 1, 5),             # no such wave count
         w4.make_plan(w4.PATH_MFMA, 1, 4, splits=0),
-        w4.make_plan(w4.PATH_MFMA, 1, 4, splits=5),   # more splits than K groups (K=512)
+        w4.make_plan(w4.PATH_MFMA, 1, 4, splits=8),   # more splits than K groups (K=512)
+        w4.make_plan(w4.PATH_MFMA, 1, 4, splits=3),   # not a power of two
         w4.make_plan(w4.PATH_MFMA, 1, 4, asrc=7),
     ]
     for p in bad:
@@ -85,7 +86,8 @@ def test_split_plan_needs_workspace():
     assert need >= 2 * 8 * 1024 * 4
     assert _gemm(M=8, plan=p) == -5
     assert _gemm(M=8, plan=p, ws=P, wsb=need - 1) == -5
-    assert w4.workspace_bytes(8, 1024, 512) == 0       # the automatic plan never splits
+    assert w4.workspace_bytes(8, 1024, 512) == 0       # short K: the automatic plan does not split
+    assert w4.workspace_bytes(16, 5120, 17408) > 0     # long K, few strips: it does
 
 
 def test_no_device_is_an_error_not_a_crash():
@@ -114,16 +116,27 @@ def test_repack_and_export_argument_errors():
 
 
 def test_row_count_dispatch():
-    # GEMV for M <= 4 while its LDS staging fits, matrix cores above
+    # one row: the dot2 GEMV kernel; two and more: matrix cores
     for M in range(1, 17):
         p = w4.get_plan(M, 34816, 5120)
-        assert p.path == (w4.PATH_GEMV if M <= 4 else w4.PATH_MFMA), (M, p)
+        assert p.path == (w4.PATH_GEMV if M == 1 else w4.PATH_MFMA), (M, p)
         assert p.splits == 1
-    # narrow N: more wavefronts along K
-    assert w4.get_plan(1, 8192, 5120).kwaves == 8
+        # A staged in LDS up to four rows, read from global memory above
+        if M >= 2:
+            assert p.asrc == (w4.ASRC_LDS if M <= 4 else w4.ASRC_GLOBAL), (M, p)
+    # long K with few column strips: split K (two rows and more)
+    assert w4.get_plan(1, 5120, 17408).splits == 1
+    assert w4.get_plan(4, 5120, 17408).splits == 4
+    assert w4.get_plan(16, 5120, 17408).splits == 2
+    assert w4.get_plan(1, 5120, 17408).kwaves == 8
     assert w4.get_plan(1, 248320, 5120).tiles == 2
     # tiny K: no more K waves than K groups
     assert w4.get_plan(1, 1024, 512).kwaves <= 4
+    assert w4.get_plan(1, 1024, 256).kwaves == 1
+    for M in (1, 2, 5, 16):
+        for K in (128, 256, 512, 5120, 17408):
+            for N in (16, 1024, 8192, 34816):
+                assert w4.plan_ok(M, N, K, w4.get_plan(M, N, K)), (M, N, K)
     p = w4.Plan()
     assert w4.lib().w4a16_get_plan(0, 1024, 512, ctypes.byref(p)) == -2
 

@@ -123,7 +123,7 @@ def test_gemm_parity_every_plan_every_m(K, N, seed):
     note(f"  worst normalized error {worst:.3e}")
 
 
-@pytest.mark.parametrize("splits", [2, 3, 5])
+@pytest.mark.parametrize("splits", [2, 4, 8])
 def test_gemm_split_k_parity_and_reuse(splits):
     K, N = 1280, 528
     A, qw, sc = synth.gen_problem(K, N, 21)

@@ -140,6 +140,24 @@ def workspace_bytes(M: int, N: int, K: int, plan: Plan | None = None) -> int:
     return int(lib().w4a16_workspace_bytes(M, N, K, ctypes.byref(plan) if plan else None))
 
 
+_workspaces: dict = {}
+
+
+def _shared_workspace(device, nbytes: int) -> torch.Tensor:
+    """A zero-filled split-K workspace per device, grown on demand.
+
+    Every call leaves its counters at zero again, so one buffer serves all
+    calls issued in order on one stream; calls that run concurrently need
+    their own (pass ``workspace=``).
+    """
+    key = str(device)
+    ws = _workspaces.get(key)
+    if ws is None or ws.numel() < nbytes:
+        ws = torch.zeros(nbytes, dtype=torch.uint8, device=device)
+        _workspaces[key] = ws
+    return ws
+
+
 def gemm(A: torch.Tensor, blob: torch.Tensor, scales: torch.Tensor, N: int,
          out: torch.Tensor | None = None, plan: Plan | None = None,
          workspace: torch.Tensor | None = None, group: int = GROUP):
@@ -150,6 +168,10 @@ def gemm(A: torch.Tensor, blob: torch.Tensor, scales: torch.Tensor, N: int,
     M, K = A.shape
     if out is None:
         out = torch.empty((M, N), dtype=torch.bfloat16, device=A.device)
+    if workspace is None:
+        need = workspace_bytes(M, N, K, plan)
+        if need:
+            workspace = _shared_workspace(A.device, need)
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     if plan is None:
         st = lib().w4a16_gemm(_ptr(A), _ptr(blob), _ptr(scales), _ptr(out), M, N, K, group,

@@ -37,7 +37,15 @@ struct Variant {
     X(P, MM, 4, 4, 4, AS)
 #define W4A16_V(P, MM, T, KW, D, AS) {P, MM, T, KW, D, AS, gemm_kernel<P, MM, T, KW, D, AS>},
 
+// one-shot shapes (the ring covers a wavefront's whole K range) for one row
+#define W4A16_ONESHOT(X, P, MM, AS) \
+    X(P, MM, 2, 4, 10, AS) X(P, MM, 2, 4, 5, AS) X(P, MM, 4, 4, 5, AS) X(P, MM, 4, 8, 5, AS) \
+    X(P, MM, 1, 4, 10, AS) X(P, MM, 2, 2, 10, AS) X(P, MM, 4, 2, 5, AS) X(P, MM, 1, 8, 17, AS) \
+    X(P, MM, 2, 8, 17, AS) X(P, MM, 2, 4, 17, AS) X(P, MM, 4, 4, 10, AS) X(P, MM, 2, 2, 17, AS)
+
 const Variant kVariants[] = {
+    W4A16_ONESHOT(W4A16_V, PATH_GEMV, 1, ASRC_LDS) W4A16_ONESHOT(W4A16_V, PATH_MFMA, 1, ASRC_LDS)
+    W4A16_ONESHOT(W4A16_V, PATH_MFMA, 1, ASRC_GLOBAL)
     W4A16_SHAPES(W4A16_V, PATH_GEMV, 1, ASRC_LDS) W4A16_SHAPES(W4A16_V, PATH_GEMV, 2, ASRC_LDS)
     W4A16_SHAPES(W4A16_V, PATH_GEMV, 3, ASRC_LDS) W4A16_SHAPES(W4A16_V, PATH_GEMV, 4, ASRC_LDS)
     W4A16_SHAPES(W4A16_V, PATH_MFMA, 0, ASRC_LDS) W4A16_SHAPES(W4A16_V, PATH_MFMA, 0, ASRC_GLOBAL)
@@ -106,7 +114,7 @@ int validate_plan(const w4a16_plan_t &p, int M, int N, int K) {
     const int G = K / W4A16_GROUP;
     if (p.path != W4A16_PATH_GEMV && p.path != W4A16_PATH_MFMA) return W4A16_ERR_PLAN;
     if (p.path == W4A16_PATH_GEMV && M > 4) return W4A16_ERR_PLAN;
-    if (p.splits < 1 || p.splits > G) return W4A16_ERR_PLAN;
+    if (p.splits < 1 || p.splits > G || (p.splits & (p.splits - 1)) != 0) return W4A16_ERR_PLAN;
     if (p.asrc != W4A16_ASRC_LDS && p.asrc != W4A16_ASRC_GLOBAL) return W4A16_ERR_PLAN;
     if (p.depth < 0) return W4A16_ERR_PLAN;
     if (!find_variant(p, M)) return W4A16_ERR_PLAN;
@@ -125,19 +133,55 @@ int validate_plan(const w4a16_plan_t &p, int M, int N, int K) {
 //           narrow-N shapes still put thousands of wavefronts in flight.
 //   asrc:   stage A in LDS when the workgroup's A slice fits, else read it
 //           from L1/L2 per group.
+// Plan choice, from graph-replayed timings of every compiled plan on MI355X
+// (cold weights) over the decoder shapes K x N = 5120 x 8192, 6144 x 5120,
+// 5120 x 34816, 17408 x 5120 and 5120 x 248320, M = 1..16:
+//  * M = 1: the GEMV kernel, two tiles per workgroup, four wavefronts along K
+//    (eight for long K), ring depth 4 (5 for wide N);
+//  * M = 2..4: matrix cores with A staged in LDS; four tiles and depth 2 for
+//    wide N, else two tiles and depth 4, with K split four ways for long K;
+//  * M >= 5: matrix cores with A read from global memory (it no longer fits
+//    LDS next to the ring at these widths); long K splits two ways.
+// "Wide" is N >= 32768 (2048 tiles), "long" K >= 16384 (128 groups).
 void auto_plan(int M, int N, int K, w4a16_plan_t *out) {
     const int NT = N / 16, G = K / W4A16_GROUP;
+    const bool wide = NT >= 2048, deep = G >= 128;
     w4a16_plan_t p;
-    p.path = (M <= 4) ? W4A16_PATH_GEMV : W4A16_PATH_MFMA;
-    p.tiles = (NT >= 2048) ? 2 : 1;
-    const int strips = (NT + p.tiles - 1) / p.tiles;
-    p.kwaves = (strips >= 1024) ? 4 : 8;
-    if (p.kwaves > G) p.kwaves = (G >= 4) ? 4 : 1;
+    p.kwaves = 4;
     p.splits = 1;
     p.asrc = W4A16_ASRC_LDS;
-    p.depth = 0;
-    if (p.path == W4A16_PATH_GEMV && plan_lds(p, M, G) > kLdsBudget) p.path = W4A16_PATH_MFMA;
-    if (p.path == W4A16_PATH_MFMA && plan_lds(p, M, G) > kLdsBudget) p.asrc = W4A16_ASRC_GLOBAL;
+    if (M == 1) {
+        p.path = W4A16_PATH_GEMV;
+        p.tiles = 2;
+        if (deep) p.kwaves = 8;
+        p.depth = (wide && !deep) ? 5 : 4;
+    } else if (M <= 4) {
+        p.path = W4A16_PATH_MFMA;
+        p.tiles = wide ? 4 : 2;
+        p.depth = wide ? 2 : 4;
+        if (deep && !wide) p.splits = 4;
+    } else {
+        p.path = W4A16_PATH_MFMA;
+        p.asrc = W4A16_ASRC_GLOBAL;
+        p.tiles = (wide || deep) ? 4 : 2;
+        p.depth = (wide || deep) ? 2 : 4;
+        if (deep && !wide) p.splits = 2;
+    }
+    // short K: no more wavefronts along K than groups per workgroup
+    if (p.kwaves * p.splits > G) {
+        p.splits = 1;
+        if (p.kwaves > G) {
+            p.tiles = 1;
+            p.kwaves = 1;
+            p.depth = 8;
+        }
+    }
+    if (p.path == W4A16_PATH_GEMV && plan_lds(p, M, G) > kLdsBudget) {
+        p.path = W4A16_PATH_MFMA;
+        p.depth = 0;
+    }
+    if (p.path == W4A16_PATH_MFMA && p.asrc == W4A16_ASRC_LDS && plan_lds(p, M, G) > kLdsBudget)
+        p.asrc = W4A16_ASRC_GLOBAL;
     *out = p;
 }
 
@@ -191,6 +235,8 @@ int run_gemm(const void *A, const void *wq, const void *scales, void *C, int M, 
     a.K = K;
     a.G = K / W4A16_GROUP;
     a.S = p.splits;
+    a.Slog2 = 0;
+    while ((1 << a.Slog2) < a.S) ++a.Slog2;
     a.NT = N / 16;
     a.nstrips = (a.NT + p.tiles - 1) / p.tiles;
     a.nunits = a.nstrips * a.S;

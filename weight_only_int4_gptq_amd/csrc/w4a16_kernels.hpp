@@ -52,7 +52,8 @@ struct GemmArgs {
     float *part;             // split-K partials [S][M][N] (S > 1 only)
     uint32_t *count;         // split-K arrival counters [nstrips] (S > 1 only)
     int M, N, K, G;          // G = K / 128
-    int S;                   // workgroups along K per column strip
+    int S;                   // workgroups along K per column strip (a power of two)
+    int Slog2;               // log2(S)
     int NT;                  // 16-column tiles = N / 16
     int nstrips;             // column strips = ceil(NT / tiles)
     int nunits;              // nstrips * S = grid size
@@ -335,8 +336,8 @@ __global__ void __launch_bounds__(64 * KW) gemm_kernel(GemmArgs p) {
     const int arow_m = min(c, M - 1);   // MFMA A-operand row of this lane
 
     const int u = xcd_unit(blockIdx.x, p.nunits);
-    const int strip = u / p.S, z = u - (u / p.S) * p.S;
-    const int gw0 = (p.G * z) / p.S, gw1 = (p.G * (z + 1)) / p.S;
+    const int strip = u >> p.Slog2, z = u & (p.S - 1);
+    const int gw0 = (p.G * z) >> p.Slog2, gw1 = (p.G * (z + 1)) >> p.Slog2;
     const int Gwg = gw1 - gw0;
     const int gk0 = gw0 + (Gwg * wave) / KW, gk1 = gw0 + (Gwg * (wave + 1)) / KW;
     const int ng = gk1 - gk0;
@@ -362,16 +363,17 @@ __global__ void __launch_bounds__(64 * KW) gemm_kernel(GemmArgs p) {
     if constexpr (kStage) {
         const int rowbytes = Gwg * kGroup * 2;
         const int chunks_per_row = (rowbytes + 1023) >> 10;
-        for (int x = wave; x < M * chunks_per_row; x += KW) {
-            const int m = x / chunks_per_row, q = x - m * chunks_per_row;
-            const int off = (q << 10) + lane * 16;
-            const uint32_t dst = __builtin_amdgcn_readfirstlane(lds_addr(smem + L.a + m * L.row + (q << 10)));
-            if (off < rowbytes) {
-                const uint8_t *src = reinterpret_cast<const uint8_t *>(p.A + (size_t)m * p.K +
-                                                                       (size_t)gw0 * kGroup) + off;
-                lds_dma16(src, dst);
+        for (int m = 0; m < M; ++m)
+            for (int q = wave; q < chunks_per_row; q += KW) {
+                const int off = (q << 10) + lane * 16;
+                const uint32_t dst =
+                    __builtin_amdgcn_readfirstlane(lds_addr(smem + L.a + m * L.row + (q << 10)));
+                if (off < rowbytes) {
+                    const uint8_t *src = reinterpret_cast<const uint8_t *>(p.A + (size_t)m * p.K +
+                                                                           (size_t)gw0 * kGroup) + off;
+                    lds_dma16(src, dst);
+                }
             }
-        }
     }
 
     // ---- 2. weight ring, D groups deep, issued in slot order
@@ -419,9 +421,9 @@ __global__ void __launch_bounds__(64 * KW) gemm_kernel(GemmArgs p) {
         float *bias = reinterpret_cast<float *>(smem + L.bias);
         if constexpr (PATH == PATH_GEMV) {
             // each 32-row quarter: the GEMV lane's dot2 chain with every code 8
-            for (int b = threadIdx.x; b < M * Gwg * 4; b += 64 * KW) {
-                const int m = b / (Gwg * 4);
-                const int rem = b - m * Gwg * 4;
+            for (int m = 0; m < M; ++m)
+            for (int rem = threadIdx.x; rem < Gwg * 4; rem += 64 * KW) {
+                const int b = m * Gwg * 4 + rem;
                 const u32x4 *src = reinterpret_cast<const u32x4 *>(smem + L.a + m * L.row + rem * 64);
                 float s = 0.0f;
 #pragma unroll
@@ -436,14 +438,32 @@ __global__ void __launch_bounds__(64 * KW) gemm_kernel(GemmArgs p) {
             // each group: the MFMA lanes' four-instruction chain with every code
             // 8, exactly as the main loop would form it; rows 4h..4h+3 of column
             // 0 are stored (all 16 columns are equal)
+            // Four groups per pass so that four independent chains fill the
+            // matrix pipeline; a pass past the last group repeats it and
+            // skips the store.
             const u32x4 bconst = {kBiasPair, kBiasPair, kBiasPair, kBiasPair};
-            for (int gl = wave; gl < Gwg; gl += KW) {
-                const uint8_t *arow = smem + L.a + arow_m * L.row + (gl * kGroup + h * 32) * 2;
-                f32x4 Q = {0.0f, 0.0f, 0.0f, 0.0f};
+            constexpr int kB = 4;
+            for (int gb = wave; gb < Gwg; gb += kB * KW) {
+                u32x4 a[kB][4];
+#pragma unroll
+                for (int i = 0; i < kB; ++i) {
+                    const int gl = min(gb + i * KW, Gwg - 1);
+                    const uint8_t *arow = smem + L.a + arow_m * L.row + (gl * kGroup + h * 32) * 2;
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) a[i][r] = reinterpret_cast<const u32x4 *>(arow)[r];
+                }
+                f32x4 Q[kB];
+#pragma unroll
+                for (int i = 0; i < kB; ++i) Q[i] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
                 for (int r = 0; r < 4; ++r)
-                    Q = mfma16x16x32(reinterpret_cast<const u32x4 *>(arow)[r], bconst, Q);
-                if (c == 0) reinterpret_cast<f32x4 *>(bias)[gl * 4 + h] = Q;
+#pragma unroll
+                    for (int i = 0; i < kB; ++i) Q[i] = mfma16x16x32(a[i][r], bconst, Q[i]);
+#pragma unroll
+                for (int i = 0; i < kB; ++i) {
+                    const int gl = gb + i * KW;
+                    if (c == 0 && gl < Gwg) reinterpret_cast<f32x4 *>(bias)[gl * 4 + h] = Q[i];
+                }
             }
         }
         lds_barrier();
@@ -530,19 +550,33 @@ __global__ void __launch_bounds__(64 * KW) gemm_kernel(GemmArgs p) {
     };
 
     if (ng > 0) {
-        // compute slot j, then refill it with the group D ahead, so D - 1
-        // groups stay in flight.  Past the last group the refill re-reads the
-        // last group (clamped): it is in flight or in L2 already, so it costs
-        // no HBM traffic, and every iteration issues the same loads, which
-        // keeps the wait counts static (a data-dependent skip would make the
-        // compiler wait for every load in flight at each slot).
-        for (int base = 0; base < ng; base += D) {
+        if (ng % D == 0) {
+            // exact: every refill is a real group; the last round loads nothing
+            int base = 0;
+            for (; base + D < ng; base += D) {
+                [&]<int... J>(std::integer_sequence<int, J...>) {
+                    ((compute_group(std::integral_constant<int, J>{}, gk0 + base + J),
+                      load_group(std::integral_constant<int, J>{}, gk0 + base + J + D),
+                      __builtin_amdgcn_sched_barrier(0)),
+                     ...);
+                }(std::make_integer_sequence<int, D>{});
+            }
             [&]<int... J>(std::integer_sequence<int, J...>) {
-                ((base + J < ng ? compute_group(std::integral_constant<int, J>{}, gk0 + base + J) : void(),
-                  load_group(std::integral_constant<int, J>{}, gidx(base + J + D)),
-                  __builtin_amdgcn_sched_barrier(0)),
-                 ...);
+                (compute_group(std::integral_constant<int, J>{}, gk0 + base + J), ...);
             }(std::make_integer_sequence<int, D>{});
+        } else {
+            // ragged: past the last group the refill re-reads the last group
+            // (clamped; it is in flight or in L2 already), so every iteration
+            // issues the same loads and the wait counts stay static
+            for (int base = 0; base < ng; base += D) {
+                [&]<int... J>(std::integer_sequence<int, J...>) {
+                    ((base + J < ng ? compute_group(std::integral_constant<int, J>{}, gk0 + base + J)
+                                    : void(),
+                      load_group(std::integral_constant<int, J>{}, gidx(base + J + D)),
+                      __builtin_amdgcn_sched_barrier(0)),
+                     ...);
+                }(std::make_integer_sequence<int, D>{});
+            }
         }
     }
 
@@ -598,13 +632,15 @@ __global__ void __launch_bounds__(64 * KW) gemm_kernel(GemmArgs p) {
             }
         }
         lds_barrier();   // LDS only: the clamped refills still in flight need no wait
-        for (int e = threadIdx.x; e < NV; e += 64 * KW) {
-            float s = red[e];
 #pragma unroll
-            for (int w = 1; w < KW; ++w) s += red[w * NV + e];
-            const int t = e / (16 * M), m = (e >> 4) - t * M, cc = e & 15;
-            emit(t, m, cc, s);
-        }
+        for (int t = 0; t < T; ++t)
+            for (int mc = threadIdx.x; mc < M * 16; mc += 64 * KW) {
+                const int e = t * M * 16 + mc;
+                float s = red[e];
+#pragma unroll
+                for (int w = 1; w < KW; ++w) s += red[w * NV + e];
+                emit(t, mc >> 4, mc & 15, s);
+            }
     }
 
     if (p.S > 1) {
@@ -622,17 +658,19 @@ __global__ void __launch_bounds__(64 * KW) gemm_kernel(GemmArgs p) {
         }
         lds_barrier();
         if (s_last) {
-            for (int e = threadIdx.x; e < NV; e += 64 * KW) {
-                const int t = e / (16 * M), m = (e >> 4) - t * M, cc = e & 15;
-                const int tile = strip * T + t;
-                if (tile >= p.NT) continue;
-                const size_t n = (size_t)tile * 16 + cc;
-                float s = 0.0f;
-                for (int zz = 0; zz < p.S; ++zz)
-                    s += __hip_atomic_load(&p.part[((size_t)zz * M + m) * p.N + n], __ATOMIC_RELAXED,
-                                           __HIP_MEMORY_SCOPE_AGENT);
-                p.C[(size_t)m * p.N + n] = f32_to_bf16_rne(s);
-            }
+#pragma unroll
+            for (int t = 0; t < T; ++t)
+                for (int mc = threadIdx.x; mc < M * 16; mc += 64 * KW) {
+                    const int m = mc >> 4, cc = mc & 15;
+                    const int tile = strip * T + t;
+                    if (tile >= p.NT) continue;
+                    const size_t n = (size_t)tile * 16 + cc;
+                    float s = 0.0f;
+                    for (int zz = 0; zz < p.S; ++zz)
+                        s += __hip_atomic_load(&p.part[((size_t)zz * M + m) * p.N + n], __ATOMIC_RELAXED,
+                                               __HIP_MEMORY_SCOPE_AGENT);
+                    p.C[(size_t)m * p.N + n] = f32_to_bf16_rne(s);
+                }
             if (threadIdx.x == 0)
                 __hip_atomic_store(&p.count[strip], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }

@@ -15,6 +15,7 @@ Prints ONE JSON line:
 
 --sweep prints one JSON line per (workload, M) instead (not the contract line);
 --stack times one decode step's full sequence of linear shapes.
+--ceiling measures a plain streaming read at the same byte counts.
 """
 from __future__ import annotations
 
@@ -165,6 +166,90 @@ def traffic_record(name):
     return entry.get("bytes_per_launch")
 
 
+def _csv_rows(path):
+    import csv
+    with open(path) as f:
+        return list(csv.DictReader(f))
+
+
+def summarize_profiles(args):
+    """Turn rocprofv3 output (kernel trace + FETCH_SIZE/WRITE_SIZE passes) into profiles/.
+
+    Writes profiles/traffic.json (HBM bytes per launch of the matmul kernel,
+    each counter scaled by what it reads for a plain copy of known size) and
+    two short text summaries named for the kernel and workload.
+    """
+    import statistics as st
+    trace_dir, fetch_dir, write_dir = args.summarize
+    wname, M, mib = args.workload, args.m, args.copy_calib
+    wl = synth.WORKLOADS[wname]
+    tag = f"{wname}_m{M}"
+    copy_kib = float(mib << 10)
+
+    def counter(d):
+        rows = _csv_rows(os.path.join(d, "run_counter_collection.csv"))
+        gemm = [float(r["Counter_Value"]) for r in rows if "gemm_kernel" in r["Kernel_Name"]]
+        kname = next(r["Kernel_Name"] for r in rows if "gemm_kernel" in r["Kernel_Name"])
+        # the calibration copies are the copy dispatches near the reference size
+        cp = [float(r["Counter_Value"]) for r in rows if "copyBuffer" in r["Kernel_Name"]
+              and float(r["Counter_Value"]) > 0.25 * copy_kib]
+        return kname, st.median(gemm), len(gemm), st.median(cp), len(cp)
+
+    kname, f_kib, nf, f_copy, ncf = counter(fetch_dir)
+    _, w_kib, nw, w_copy, ncw = counter(write_dir)
+    f_fac, w_fac = copy_kib / f_copy, copy_kib / w_copy
+    nbytes = round((f_kib * f_fac + w_kib * w_fac) * 1024)
+    algo = synth.algorithmic_bytes(M, wl.N, wl.K)
+    cmd_f = (f"rocprofv3 --pmc FETCH_SIZE -d {fetch_dir} -o run --output-format csv -- "
+             f"python3 bench.py --workload {wname} --m {M} --steps 20 --warmup 5 --no-cpu --copy-calib {mib}")
+    cmd_w = cmd_f.replace("FETCH_SIZE", "WRITE_SIZE").replace(fetch_dir, write_dir)
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    try:
+        with open(path) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        rec = {}
+    rec[tag] = {"kernel": kname, "source_hash": kernel_source_hash(), "bytes_per_launch": nbytes,
+                "algorithmic_bytes": algo, "fetch_kib": f_kib, "write_kib": w_kib,
+                "fetch_factor": round(f_fac, 5), "write_factor": round(w_fac, 5),
+                "reference": f"plain device copy of {mib} MiB (reads and writes {mib} MiB)",
+                "commands": [cmd_f, cmd_w]}
+    with open(path, "w") as f:
+        json.dump(rec, f, indent=1, sort_keys=True)
+        f.write("\n")
+
+    kshort = kname.split("(")[0].replace("void ", "").replace("w4a16::", "")
+    with open(os.path.join(ROOT, "profiles", f"gemm_kernel_{tag}_hbm_bytes.md"), "w") as f:
+        f.write(f"# HBM bytes per launch: {kshort}, {wl.desc}, M={M}\n\n")
+        f.write("Commands (repo root, TMPDIR=/tmp):\n\n")
+        f.write(f"    {cmd_f}\n    {cmd_w}\n\n")
+        f.write("| counter | matmul kernel, median KiB/dispatch | dispatches | "
+                f"copy of {mib} MiB, median KiB | copies | scale |\n|---|---|---|---|---|---|\n")
+        f.write(f"| FETCH_SIZE | {f_kib:.1f} | {nf} | {f_copy:.1f} | {ncf} | {f_fac:.4f} |\n")
+        f.write(f"| WRITE_SIZE | {w_kib:.1f} | {nw} | {w_copy:.1f} | {ncw} | {w_fac:.4f} |\n\n")
+        f.write(f"Scaled HBM traffic per launch: {nbytes} B; algorithmic bytes: {algo} B "
+                f"(ratio {nbytes / algo:.4f}).\n")
+        f.write(f"Kernel source hash: {kernel_source_hash()}\n")
+
+    rows = [r for r in _csv_rows(os.path.join(trace_dir, "run_kernel_trace.csv")) if "gemm_kernel" in r["Kernel_Name"]]
+    d = [int(r["End_Timestamp"]) - int(r["Start_Timestamp"]) for r in rows]
+    stats = _csv_rows(os.path.join(trace_dir, "run_kernel_stats.csv"))
+    with open(os.path.join(ROOT, "profiles", f"gemm_kernel_{tag}_kernel_trace.md"), "w") as f:
+        f.write(f"# Kernel trace: {wl.desc}, M={M} (the default bench run)\n\n")
+        f.write(f"Command (repo root, TMPDIR=/tmp):\n\n    rocprofv3 --kernel-trace --stats -d {trace_dir} "
+                f"-o run --output-format csv -- python3 bench.py\n\n")
+        f.write("rocprofv3 --stats summary (run_kernel_stats.csv):\n\n| kernel | calls | average ns | min ns | max ns |\n|---|---|---|---|---|\n")
+        for r in stats:
+            f.write(f"| {r['Name'][:90]} | {r['Calls']} | {float(r['AverageNs']):.0f} | {r['MinNs']} | {r['MaxNs']} |\n")
+        if len(d) >= args.warmup + 2 * args.steps:
+            w, a, b = args.warmup, args.warmup + args.steps, args.warmup + 2 * args.steps
+            f.write(f"\nMatmul kernel by phase: {w} eager warm-up launches average {st.mean(d[:w]):.0f} ns; "
+                    f"warm graph replay average {st.mean(d[w:a]):.0f} ns; timed graph replay average "
+                    f"{st.mean(d[a:b]):.0f} ns over {args.steps} launches.\n")
+        f.write(f"Kernel source hash: {kernel_source_hash()}\n")
+    print(json.dumps(rec[tag]))
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -176,9 +261,15 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--sweep", action="store_true", help="one JSON line per (workload, M)")
     ap.add_argument("--stack", action="store_true", help="full decode-step sweep of linear shapes")
+    ap.add_argument("--ceiling", action="store_true",
+                    help="plain streaming-read bandwidth at the matmul byte counts (probe kernel)")
     ap.add_argument("--copy-calib", type=int, default=0, metavar="MIB",
                     help="after timing, copy MIB MiB a few times (reference for byte counters)")
+    ap.add_argument("--summarize", nargs=3, metavar=("TRACE_DIR", "FETCH_DIR", "WRITE_DIR"),
+                    help="write profiles/ from rocprofv3 output of the bench (no GPU use)")
     args = ap.parse_args()
+    if args.summarize:
+        return summarize_profiles(args)
 
     if args.gpus != 1:
         print(f"bench.py: this build measures one GPU; --gpus {args.gpus} is not supported "
@@ -198,6 +289,8 @@ def main():
         return sweep(torch, w4, args)
     if args.stack:
         return stack(torch, w4, args)
+    if args.ceiling:
+        return ceiling(torch, w4, args)
 
     wl = synth.WORKLOADS[args.workload]
     M = args.m
@@ -265,6 +358,54 @@ def sweep(torch, w4, args):
                    "mfma_util": round(r["tflops"] / PEAK_BF16_TFLOPS, 4), "sets": sets}
             print(json.dumps(rec), flush=True)
         del prob
+        torch.cuda.empty_cache()
+
+
+def ceiling(torch, w4, args):
+    """Best plain streaming-read bandwidth at the byte counts of the matmul calls.
+
+    The read-only probe kernel (libw4a16_probe.so) is swept over launch shapes;
+    buffers rotate over >= 1 GiB like the matmul timing, so every read comes
+    from HBM.  One JSON line per byte count.
+    """
+    import ctypes
+    lib = ctypes.CDLL(os.path.join(ROOT, "weight_only_int4_gptq_amd", "libw4a16_probe.so"))
+    lib.w4a16_probe_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_longlong, ctypes.c_int, ctypes.c_int,
+                                            ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    dev = torch.device("cuda:0")
+    sink = torch.zeros(8192 * 1024, dtype=torch.int32, device=dev)
+    sizes = [("qkv_m1", synth.algorithmic_bytes(1, 8192, 5120)),
+             ("down_m1", synth.algorithmic_bytes(1, 5120, 17408)),
+             ("gate_up_m1", synth.algorithmic_bytes(1, 34816, 5120)),
+             ("lm_head_m1", synth.algorithmic_bytes(1, 248320, 5120)),
+             ("2GiB", 2 << 30)]
+    for tag, nbytes in sizes:
+        nbytes = (nbytes + 15) // 16 * 16
+        nbuf = max(1, -(-ROTATE_BYTES // nbytes)) if nbytes < 4 * LLC_BYTES else 1
+        bufs = [torch.empty(nbytes, dtype=torch.uint8, device=dev) for _ in range(nbuf)]
+        best = None
+        for blocks in (512, 1024, 2048, 4096, 8192):
+            for threads in (256, 512, 1024):
+                for unroll in (1, 4, 8):
+                    if blocks * threads > sink.numel() or nbytes // 16 < blocks * threads // 4:
+                        continue
+
+                    def call(i, b=blocks, t=threads, u=unroll):
+                        st = lib.w4a16_probe_stream_read(bufs[i % nbuf].data_ptr(), nbytes, b, t, u,
+                                                         sink.data_ptr(), torch.cuda.current_stream().cuda_stream)
+                        if st != 0:
+                            raise RuntimeError(f"probe launch failed ({st})")
+
+                    steps = 100 if nbytes < 1e8 else (20 if nbytes < 1e9 else 5)
+                    ms = time_graph(torch, call, steps, 3)
+                    if best is None or ms < best[0]:
+                        best = (ms, blocks, threads, unroll)
+        ms, b, t, u = best
+        print(json.dumps({"ceiling": tag, "bytes": nbytes, "us_per_call": round(ms * 1e3, 3),
+                          "GBps": round(nbytes / (ms * 1e-3) / 1e9, 1),
+                          "pct_peak": round(100 * nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 2),
+                          "launch": {"blocks": b, "threads": t, "unroll": u}, "buffer_sets": nbuf}), flush=True)
+        del bufs
         torch.cuda.empty_cache()
 
 

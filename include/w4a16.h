@@ -140,12 +140,23 @@ int w4a16_get_plan(int M, int N, int K, w4a16_plan_t *plan);
 int w4a16_check_plan(int M, int N, int K, const w4a16_plan_t *plan);
 
 /*
- * Workspace bytes a plan needs: fp32 partials [splits][M][N] plus one 32-bit
- * counter per column strip, or 0 when splits == 1.  plan == NULL means the
- * plan w4a16_gemm would choose.  Returns 0 for invalid arguments.
- * A workspace must be zero-filled before its first use; every call returns
- * its counters to zero, so it can be reused without clearing.  Calls that
- * share a workspace must not run concurrently.
+ * Split-K workspace layout, the same for every shape and plan:
+ *   bytes [0, W4A16_SPLIT_COUNTER_BYTES)   32-bit arrival counters, one per
+ *                                          column strip (strip s at index s)
+ *   bytes [W4A16_SPLIT_COUNTER_BYTES, ...) fp32 partials [splits][M][N]
+ * A plan with splits > 1 may have at most W4A16_SPLIT_COUNTER_BYTES / 4
+ * column strips (ceil(N / 16 / tiles)).
+ */
+#define W4A16_SPLIT_COUNTER_BYTES 65536
+
+/*
+ * Workspace bytes a plan needs: W4A16_SPLIT_COUNTER_BYTES plus
+ * 4 * splits * M * N, or 0 when splits == 1.  plan == NULL means the plan
+ * w4a16_gemm would choose.  Returns 0 for invalid arguments.
+ * A workspace must be zero-filled before its first use.  Every call leaves
+ * the counter region zero again and writes partials only after it, so one
+ * workspace serves calls of any shape and plan issued one after another
+ * (stream order); calls that share a workspace must not run concurrently.
  */
 size_t w4a16_workspace_bytes(int M, int N, int K, const w4a16_plan_t *plan);
 

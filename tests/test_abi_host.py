@@ -83,7 +83,7 @@ def test_gemm_plan_errors():
 def test_split_plan_needs_workspace():
     p = w4.make_plan(w4.PATH_MFMA, 1, 4, splits=2)
     need = w4.workspace_bytes(8, 1024, 512, p)
-    assert need >= 2 * 8 * 1024 * 4
+    assert need == 65536 + 2 * 8 * 1024 * 4
     assert _gemm(M=8, plan=p) == -5
     assert _gemm(M=8, plan=p, ws=P, wsb=need - 1) == -5
     assert w4.workspace_bytes(8, 1024, 512) == 0       # short K: the automatic plan does not split
@@ -139,6 +139,15 @@ def test_row_count_dispatch():
                 assert w4.plan_ok(M, N, K, w4.get_plan(M, N, K)), (M, N, K)
     p = w4.Plan()
     assert w4.lib().w4a16_get_plan(0, 1024, 512, ctypes.byref(p)) == -2
+
+
+def test_split_plan_strip_limit():
+    # split plans keep one counter per column strip in a fixed 64 KiB region
+    ok = w4.make_plan(w4.PATH_MFMA, 1, 4, 2, w4.ASRC_GLOBAL)
+    assert w4.plan_ok(8, 16384 * 16, 5120, ok)
+    assert not w4.plan_ok(8, 16385 * 16, 5120, ok)
+    assert w4.plan_ok(8, 16385 * 16, 5120, w4.make_plan(w4.PATH_MFMA, 2, 4, 2, w4.ASRC_GLOBAL))
+    assert w4.plan_ok(8, 16385 * 16, 5120, w4.make_plan(w4.PATH_MFMA, 1, 4, 1, w4.ASRC_GLOBAL))
 
 
 def test_check_plan():

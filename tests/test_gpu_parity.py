@@ -54,11 +54,15 @@ def max_err(C, Cref, Dref):
 
 
 # ------------------------------------------------------------- plans to force
+# every (path, tiles, kwaves, A source, ring depth) combination a build might
+# hold; plan_ok keeps the ones this build compiled (depth 0 = its default)
 ALL_PLANS = []
 for path in (w4.PATH_GEMV, w4.PATH_MFMA):
-    for (t, kw) in ((1, 4), (1, 8), (2, 4), (2, 8), (4, 4), (1, 1)):
-        for asrc in ((w4.ASRC_LDS,) if path == w4.PATH_GEMV else (w4.ASRC_LDS, w4.ASRC_GLOBAL)):
-            ALL_PLANS.append(w4.make_plan(path, t, kw, 1, asrc))
+    for t in (1, 2, 4):
+        for kw in (1, 2, 4, 5, 8, 10, 16):
+            for asrc in ((w4.ASRC_LDS,) if path == w4.PATH_GEMV else (w4.ASRC_LDS, w4.ASRC_GLOBAL)):
+                for depth in (0, 2, 4, 5, 8, 10, 17):
+                    ALL_PLANS.append(w4.make_plan(path, t, kw, 1, asrc, depth))
 
 
 def plans_for(M, N, K):
@@ -123,6 +127,24 @@ def test_gemm_parity_every_plan_every_m(K, N, seed):
     note(f"  worst normalized error {worst:.3e}")
 
 
+@pytest.mark.parametrize("K,N,seed", [(5120, 96, 9), (17408, 48, 10)])
+def test_gemm_parity_every_plan_long_k(K, N, seed):
+    # K = 5120 (40 groups) and 17408 (136 groups): wavefront group counts that
+    # are multiples of the ring depth (every refill real, last round loads
+    # nothing) and ones that are not (clamped refills), for every depth
+    A, qw, sc = synth.gen_problem(K, N, seed)
+    q, s, a = to_dev(qw, sc, A)
+    blob = w4.repack_weights(q, K, N)
+    Cref16, Dref16 = oracle.gemm(A, qw, sc, 16, N, K)
+    for M in (1, 2, 4, 5, 16):
+        cases = [None] + plans_for(M, N, K)
+        note(f"[gemm long K] K={K} N={N} M={M}: {len(cases)} plans")
+        for p in cases:
+            C = run_gemm(a, blob, s, N, M, plan=p)
+            e = max_err(C, Cref16[:M], Dref16[:M])
+            assert e <= TOL, (M, p, e)
+
+
 @pytest.mark.parametrize("splits", [2, 4, 8])
 def test_gemm_split_k_parity_and_reuse(splits):
     K, N = 1280, 528
@@ -144,8 +166,34 @@ def test_gemm_split_k_parity_and_reuse(splits):
                 C2 = run_gemm(a, blob, s, N, M, plan=p, ws=ws)   # counters were reset
                 assert max_err(C1, Cref[:M], Dref[:M]) <= TOL
                 assert torch.equal(C1.view(torch.int16), C2.view(torch.int16))
-                cnt_off = (splits * M * N * 4 + 255) // 256 * 256
-                assert int(ws[cnt_off:].view(torch.int32).abs().sum()) == 0
+                assert int(ws[:65536].view(torch.int32).abs().sum()) == 0
+
+
+def test_split_k_workspace_shared_across_shapes():
+    # one zero-filled workspace serves split calls of different M, N, splits
+    # and tiles in stream order: each call's partials stay clear of the
+    # counter region every call leaves at zero
+    cases = []
+    for (K, N, seed) in ((17408, 48, 10), (1280, 528, 21), (2048, 272, 8)):
+        A, qw, sc = synth.gen_problem(K, N, seed)
+        q, s, a = to_dev(qw, sc, A)
+        blob = w4.repack_weights(q, K, N)
+        Cref, Dref = oracle.gemm(A, qw, sc, 16, N, K)
+        cases.append((K, N, a, blob, s, Cref, Dref))
+    plans = [w4.make_plan(w4.PATH_MFMA, 2, 4, 4, w4.ASRC_LDS), w4.make_plan(w4.PATH_MFMA, 4, 4, 2, w4.ASRC_GLOBAL),
+             w4.make_plan(w4.PATH_GEMV, 1, 4, 8), w4.make_plan(w4.PATH_MFMA, 1, 8, 2, w4.ASRC_GLOBAL)]
+    need = max(w4.workspace_bytes(16, N, K, p) for (K, N, *_) in cases for p in plans)
+    ws = torch.zeros(need, dtype=torch.uint8, device=DEV)
+    for rnd in range(2):
+        for (K, N, a, blob, s, Cref, Dref) in cases:
+            for M in (4, 5, 2, 16, 1):
+                for p in [None] + plans:
+                    if p is not None and (not w4.plan_ok(M, N, K, p)):
+                        continue
+                    C = run_gemm(a, blob, s, N, M, plan=p, ws=ws)
+                    e = max_err(C, Cref[:M], Dref[:M])
+                    assert e <= TOL, (rnd, K, N, M, p, e)
+    assert int(ws[:65536].view(torch.int32).abs().sum()) == 0
 
 
 # ------------------------------------------------------------- exact special inputs

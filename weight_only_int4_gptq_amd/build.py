@@ -1,4 +1,9 @@
-"""Build the gfx950 HIP library libw4a16.so in-tree with hipcc."""
+"""Build the gfx950 HIP libraries in-tree with hipcc.
+
+libw4a16.so        the matmul path (repack, GEMV and MFMA kernels, C ABI)
+libw4a16_probe.so  a plain streaming-read kernel, used only by bench.py to
+                   measure the read bandwidth the box reaches at a byte count
+"""
 from __future__ import annotations
 
 import os
@@ -9,6 +14,8 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 LIB = os.path.join(PKG, "libw4a16.so")
 SOURCES = [os.path.join(PKG, "csrc", "w4a16.hip")]
+PROBE_LIB = os.path.join(PKG, "libw4a16_probe.so")
+PROBE_SOURCES = [os.path.join(PKG, "csrc", "probe_stream.hip")]
 DEPENDS = SOURCES + [os.path.join(PKG, "csrc", "w4a16_kernels.hpp"),
                      os.path.join(ROOT, "include", "w4a16.h")]
 
@@ -20,15 +27,12 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found")
 
 
-def build(force: bool = True, verbose: bool = False) -> str:
-    """Compile libw4a16.so for gfx950 (always, unless force=False and it exists)."""
-    if not force and os.path.exists(LIB):
-        return LIB
-    tmp = LIB + ".tmp"
+def _compile(out: str, sources: list, verbose: bool) -> str:
+    tmp = out + ".tmp"
     cmd = [hipcc(), "--offload-arch=gfx950", "-O3", "-std=c++20", "-fPIC", "-shared",
            # packed fp32 VALU forms stay off: plain fp32 ops only
            "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-           "-I", os.path.join(ROOT, "include"), "-o", tmp] + SOURCES
+           "-I", os.path.join(ROOT, "include"), "-o", tmp] + sources
     res = subprocess.run(cmd, capture_output=True, text=True)
     noise = "is not a recognized feature for this target"
     err = "\n".join(l for l in (res.stderr or "").splitlines() if noise not in l)
@@ -36,8 +40,18 @@ def build(force: bool = True, verbose: bool = False) -> str:
         raise RuntimeError(f"hipcc failed ({res.returncode}):\n{err}")
     if verbose and err.strip():
         print(err)
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, out)
+    return out
+
+
+def build(force: bool = True, verbose: bool = False) -> str:
+    """Compile libw4a16.so and libw4a16_probe.so for gfx950 (always, unless
+    force=False and they exist).  Returns the path of libw4a16.so."""
+    if force or not os.path.exists(PROBE_LIB):
+        _compile(PROBE_LIB, PROBE_SOURCES, verbose)
+    if not force and os.path.exists(LIB):
+        return LIB
+    return _compile(LIB, SOURCES, verbose)
 
 
 if __name__ == "__main__":

@@ -121,21 +121,14 @@ int validate_plan(const w4a16_plan_t &p, int M, int N, int K) {
     if (plan_lds(p, M, G) > kLdsBudget) return W4A16_ERR_PLAN;
     const long long nstrips = (N / 16 + p.tiles - 1) / p.tiles;
     if (nstrips * p.splits >= (1ll << 31)) return W4A16_ERR_PLAN;
-    (void)N;
+    if (p.splits > 1 && nstrips > W4A16_SPLIT_COUNTER_BYTES / 4) return W4A16_ERR_PLAN;
     return W4A16_OK;
 }
 
-// The row-count dispatcher.
-//   path:   GEMV for M <= 4 (VALU dot products; cost grows with M), MFMA above
-//           (matrix cores; the weight-side cost does not grow with M).
-//   tiles:  2 for wide N (halves A/LDS traffic per weight byte), else 1.
-//   kwaves: split K across 8 wavefronts when there are few column strips, so
-//           narrow-N shapes still put thousands of wavefronts in flight.
-//   asrc:   stage A in LDS when the workgroup's A slice fits, else read it
-//           from L1/L2 per group.
-// Plan choice, from graph-replayed timings of every compiled plan on MI355X
-// (cold weights) over the decoder shapes K x N = 5120 x 8192, 6144 x 5120,
-// 5120 x 34816, 17408 x 5120 and 5120 x 248320, M = 1..16:
+// The row-count dispatcher.  Plan choice, from graph-replayed timings of
+// every compiled plan on MI355X (cold weights) over the decoder shapes
+// K x N = 5120 x 8192, 6144 x 5120, 5120 x 34816, 17408 x 5120 and
+// 5120 x 248320, M = 1..16:
 //  * M = 1: the GEMV kernel, two tiles per workgroup, four wavefronts along K
 //    (eight for long K), ring depth 4 (5 for wide N);
 //  * M = 2..4: matrix cores with A staged in LDS; four tiles and depth 2 for
@@ -187,10 +180,7 @@ void auto_plan(int M, int N, int K, w4a16_plan_t *out) {
 
 size_t workspace_for(const w4a16_plan_t &p, int M, int N) {
     if (p.splits <= 1) return 0;
-    const size_t nstrips = (size_t)((N / 16 + p.tiles - 1) / p.tiles);
-    const size_t part = (size_t)p.splits * (size_t)M * (size_t)N * sizeof(float);
-    const size_t part_aligned = (part + 255) & ~(size_t)255;
-    return part_aligned + nstrips * sizeof(uint32_t);
+    return (size_t)W4A16_SPLIT_COUNTER_BYTES + (size_t)p.splits * (size_t)M * (size_t)N * sizeof(float);
 }
 
 hipError_t launch(const void *fn, unsigned grid, unsigned block, size_t lds, hipStream_t stream,
@@ -241,10 +231,8 @@ int run_gemm(const void *A, const void *wq, const void *scales, void *C, int M, 
     a.nstrips = (a.NT + p.tiles - 1) / p.tiles;
     a.nunits = a.nstrips * a.S;
     if (need > 0) {
-        const size_t part = (size_t)p.splits * (size_t)M * (size_t)N * sizeof(float);
-        a.part = static_cast<float *>(workspace);
-        a.count = reinterpret_cast<uint32_t *>(static_cast<char *>(workspace) +
-                                               ((part + 255) & ~(size_t)255));
+        a.count = static_cast<uint32_t *>(workspace);
+        a.part = reinterpret_cast<float *>(static_cast<char *>(workspace) + W4A16_SPLIT_COUNTER_BYTES);
     } else {
         a.part = nullptr;
         a.count = nullptr;

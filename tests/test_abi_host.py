@@ -130,6 +130,7 @@ def test_row_count_dispatch():
     assert w4.get_plan(16, 5120, 17408).splits == 2
     assert w4.get_plan(1, 5120, 17408).kwaves == 8
     assert w4.get_plan(1, 248320, 5120).tiles == 2
+    assert w4.get_plan(16, 248320, 5120).tiles == 8
     # tiny K: no more K waves than K groups
     assert w4.get_plan(1, 1024, 512).kwaves <= 4
     assert w4.get_plan(1, 1024, 256).kwaves == 1

@@ -38,6 +38,10 @@ struct Variant {
 #define W4A16_V(P, MM, T, KW, D, AS) {P, MM, T, KW, D, AS, gemm_kernel<P, MM, T, KW, D, AS>},
 
 // one-shot shapes (the ring covers a wavefront's whole K range) for one row
+// eight-tile strips: A read once per eight tiles (matrix-core paths)
+#define W4A16_WIDE(X, P, MM, AS) \
+    X(P, MM, 8, 4, 2, AS) X(P, MM, 8, 2, 2, AS) X(P, MM, 8, 2, 4, AS) X(P, MM, 8, 1, 4, AS)
+
 #define W4A16_ONESHOT(X, P, MM, AS) \
     X(P, MM, 2, 4, 10, AS) X(P, MM, 2, 4, 5, AS) X(P, MM, 4, 4, 5, AS) X(P, MM, 4, 8, 5, AS) \
     X(P, MM, 1, 4, 10, AS) X(P, MM, 2, 2, 10, AS) X(P, MM, 4, 2, 5, AS) X(P, MM, 1, 8, 17, AS) \
@@ -48,6 +52,9 @@ const Variant kVariants[] = {
     W4A16_ONESHOT(W4A16_V, PATH_MFMA, 1, ASRC_GLOBAL)
     W4A16_SHAPES(W4A16_V, PATH_GEMV, 1, ASRC_LDS) W4A16_SHAPES(W4A16_V, PATH_GEMV, 2, ASRC_LDS)
     W4A16_SHAPES(W4A16_V, PATH_GEMV, 3, ASRC_LDS) W4A16_SHAPES(W4A16_V, PATH_GEMV, 4, ASRC_LDS)
+    W4A16_WIDE(W4A16_V, PATH_MFMA, 0, ASRC_LDS) W4A16_WIDE(W4A16_V, PATH_MFMA, 0, ASRC_GLOBAL)
+    W4A16_WIDE(W4A16_V, PATH_MFMA, 2, ASRC_LDS) W4A16_WIDE(W4A16_V, PATH_MFMA, 3, ASRC_LDS)
+    W4A16_WIDE(W4A16_V, PATH_MFMA, 4, ASRC_LDS)
     W4A16_SHAPES(W4A16_V, PATH_MFMA, 0, ASRC_LDS) W4A16_SHAPES(W4A16_V, PATH_MFMA, 0, ASRC_GLOBAL)
     W4A16_SHAPES(W4A16_V, PATH_MFMA, 1, ASRC_LDS) W4A16_SHAPES(W4A16_V, PATH_MFMA, 1, ASRC_GLOBAL)
     W4A16_SHAPES(W4A16_V, PATH_MFMA, 2, ASRC_LDS) W4A16_SHAPES(W4A16_V, PATH_MFMA, 2, ASRC_GLOBAL)
@@ -134,7 +141,9 @@ int validate_plan(const w4a16_plan_t &p, int M, int N, int K) {
 //  * M = 2..4: matrix cores with A staged in LDS; four tiles and depth 2 for
 //    wide N, else two tiles and depth 4, with K split four ways for long K;
 //  * M >= 5: matrix cores with A read from global memory (it no longer fits
-//    LDS next to the ring at these widths); long K splits two ways.
+//    LDS next to the ring at these widths); long K splits two ways; from
+//    M = 8 on very wide N (>= 8192 tiles), one wavefront owns eight tiles so
+//    each A fragment it loads serves eight times the weights.
 // "Wide" is N >= 32768 (2048 tiles), "long" K >= 16384 (128 groups).
 void auto_plan(int M, int N, int K, w4a16_plan_t *out) {
     const int NT = N / 16, G = K / W4A16_GROUP;
@@ -159,6 +168,11 @@ void auto_plan(int M, int N, int K, w4a16_plan_t *out) {
         p.tiles = (wide || deep) ? 4 : 2;
         p.depth = (wide || deep) ? 2 : 4;
         if (deep && !wide) p.splits = 2;
+        if (NT >= 8192 && M >= 8) {   // very wide N: one wavefront per eight tiles
+            p.tiles = 8;
+            p.kwaves = 1;
+            p.depth = 4;
+        }
     }
     // short K: no more wavefronts along K than groups per workgroup
     if (p.kwaves * p.splits > G) {

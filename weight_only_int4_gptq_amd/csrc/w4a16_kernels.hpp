@@ -111,22 +111,45 @@ __device__ __forceinline__ uint32_t and_or(uint32_t x, uint32_t nib, uint32_t ma
     return (x & nib) | magic;
 }
 
-// One repacked word (codes of 8 consecutive rows e = 0..7; even e in bits
-// 0..15, odd e in bits 16..31, 4 bits each) -> four bf16 pairs
-// (128 + q_e, 128 + q_{e+1}) for e = 0, 2, 4, 6: seven VALU operations.
-__device__ __forceinline__ void word_to_bf16x4(uint32_t w, const DequantConsts &k, uint32_t (&b)[4]) {
-    b[0] = and_or(w, k.nib, k.magic);
-    b[1] = and_or(w >> 4, k.nib, k.magic);
-    b[2] = and_or(w >> 8, k.nib, k.magic);
-    b[3] = and_or(w >> 12, k.nib, k.magic);
+// Two repacked words (each: codes of 8 consecutive rows e = 0..7; even e in
+// bits 0..15, odd e in bits 16..31, 4 bits each) -> four bf16 pairs
+// (128 + q_e, 128 + q_{e+1}), e = 0, 2, 4, 6, per word.
+//
+// SHIFT64: the words share their shifts: one v_lshrrev_b64 by 4 moves both,
+// and the bits it carries from w1 into the low word land in bits 28..31,
+// which the mask drops (eleven VALU operations for sixteen codes).  The shift
+// is written out because the compiler otherwise splits it into a funnel shift
+// and a 32-bit shift; only kernels without matrix-core instructions use this
+// form, since the compiler cannot see an inline-asm write when it places the
+// wait states that protect registers an in-flight MFMA still reads.
+// Without SHIFT64 the compiler forms the shifts (fourteen operations).
+template <bool SHIFT64>
+__device__ __forceinline__ void words_to_bf16x8(uint32_t w0, uint32_t w1, const DequantConsts &k,
+                                                uint32_t (&b0)[4], uint32_t (&b1)[4]) {
+    uint64_t x = ((uint64_t)w1 << 32) | w0;
+    b0[0] = and_or(w0, k.nib, k.magic);
+    b1[0] = and_or(w1, k.nib, k.magic);
+#pragma unroll
+    for (int v = 1; v < 4; ++v) {
+        if constexpr (SHIFT64)
+            asm("v_lshrrev_b64 %0, 4, %1" : "=v"(x) : "v"(x));
+        else
+            x >>= 4;
+        b0[v] = and_or((uint32_t)x, k.nib, k.magic);
+        b1[v] = and_or((uint32_t)(x >> 32), k.nib, k.magic);
+    }
+}
+
+// Byte selector for v_perm_b32 that moves a lane's bf16 scale (low half of
+// the dword for even columns, high half for odd) to the top of an fp32 with
+// zero low bits.
+__device__ __forceinline__ uint32_t scale_selector(int c) { return (c & 1) ? 0x03020C0Cu : 0x01000C0Cu; }
+__device__ __forceinline__ float scale_from(uint32_t dword, uint32_t sel) {
+    return __uint_as_float(__builtin_amdgcn_perm(dword, dword, sel));
 }
 
 __device__ __forceinline__ float bf16_bits_to_f32(uint32_t bits16) {
     return __uint_as_float(bits16 << 16);
-}
-// bf16 scale of column c from the dword holding columns (c & ~1, c | 1).
-__device__ __forceinline__ float scale_of(uint32_t dword, int c) {
-    return __uint_as_float((c & 1) ? (dword & 0xFFFF0000u) : (dword << 16));
 }
 __device__ __forceinline__ float pair_lo(uint32_t pair) { return __uint_as_float(pair << 16); }
 __device__ __forceinline__ float pair_hi(uint32_t pair) { return __uint_as_float(pair & 0xFFFF0000u); }
@@ -249,7 +272,7 @@ __global__ void __launch_bounds__(256) repack_scales_kernel(const uint16_t *__re
     out[i] = scales[(long long)g * N + t * 16 + c];
 }
 
-// Test exports: the same word_to_bf16x4 and scale layout the GEMM kernels use.
+// Test exports: the same words_to_bf16x8 and scale layout the GEMM kernels use.
 template <bool CODES>
 __global__ void __launch_bounds__(256) export_kernel(const u32x4 *__restrict__ blob,
                                                      const uint16_t *__restrict__ scales,
@@ -265,10 +288,12 @@ __global__ void __launch_bounds__(256) export_kernel(const u32x4 *__restrict__ b
     const u32x4 w = blob[pc];
     const DequantConsts kc = dequant_consts();
     const float s = CODES ? 0.0f : bf16_bits_to_f32(scales[tg * 16 + c]);
+    uint32_t bw[4][4];
+    words_to_bf16x8<true>(w[0], w[1], kc, bw[0], bw[1]);
+    words_to_bf16x8<true>(w[2], w[3], kc, bw[2], bw[3]);
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-        uint32_t b[4];
-        word_to_bf16x4(w[r], kc, b);
+        const uint32_t (&b)[4] = bw[r];
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
             const long long k = (long long)g * kGroup + h * 32 + r * 8 + 2 * v;
@@ -355,7 +380,7 @@ __global__ void __launch_bounds__(64 * KW) gemm_kernel(GemmArgs p) {
     }
     const uint32_t w_lane = (uint32_t)lane * 16;             // this lane's 16 B of a 1 KiB piece
     const uint32_t s_lane = (uint32_t)(c >> 1) * 4;          // dword holding this column's scale
-    const uint32_t s_shift = (c & 1) ? 0u : 16u;             // bring the scale to the high half
+    const uint32_t s_sel = scale_selector(c);                  // this column's half of the dword
     const uint8_t *abase = reinterpret_cast<const uint8_t *>(p.A) +
                            ((size_t)arow_m * p.K + (size_t)h * 32) * 2;   // MFMA A from global
 
@@ -501,45 +526,52 @@ __global__ void __launch_bounds__(64 * KW) gemm_kernel(GemmArgs p) {
             for (int t = 0; t < T; ++t) {
                 f32x4 P = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    uint32_t b[4];
-                    word_to_bf16x4(wv[j][t][r], kc, b);
-                    const u32x4 bv = {b[0], b[1], b[2], b[3]};
-                    P = mfma16x16x32(a[r], bv, P);
+                for (int rp = 0; rp < 2; ++rp) {
+                    uint32_t b0[4], b1[4];
+                    words_to_bf16x8<false>(wv[j][t][2 * rp], wv[j][t][2 * rp + 1], kc, b0, b1);
+                    P = mfma16x16x32(a[2 * rp], u32x4{b0[0], b0[1], b0[2], b0[3]}, P);
+                    P = mfma16x16x32(a[2 * rp + 1], u32x4{b1[0], b1[1], b1[2], b1[3]}, P);
                 }
-                const float s = __uint_as_float((sv[j][t] << s_shift) & 0xFFFF0000u);
+                const float s = scale_from(sv[j][t], s_sel);
 #pragma unroll
                 for (int v = 0; v < kRowsV; ++v) acc[t][v] = __builtin_fmaf(s, P[v] - Q[v], acc[t][v]);
             }
         } else {
-            // r outermost: one 16-byte A sub-block per row is live at a time.
-            // Per (tile, row) the dot2 chain runs r = 0..3, v = 0..3, the same
-            // order the bias was formed in.
+            // Word pairs outermost (they share their shifts), then r: one
+            // 16-byte A sub-block per row is live at a time.  Per (tile, row)
+            // the dot2 chain runs r = 0..3, v = 0..3, the same order the bias
+            // was formed in.
             float part[T][MM];
 #pragma unroll
             for (int t = 0; t < T; ++t)
 #pragma unroll
                 for (int m = 0; m < MM; ++m) part[t][m] = 0.0f;
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                u32x4 ar[MM];
+            for (int rp = 0; rp < 2; ++rp) {
+                uint32_t b[T][2][4];
 #pragma unroll
-                for (int m = 0; m < MM; ++m)
-                    ar[m] = reinterpret_cast<const u32x4 *>(smem + L.a + m * L.row +
-                                                           (gl * kGroup + h * 32) * 2)[r];
+                for (int t = 0; t < T; ++t)
+                    words_to_bf16x8<true>(wv[j][t][2 * rp], wv[j][t][2 * rp + 1], kc, b[t][0], b[t][1]);
 #pragma unroll
-                for (int t = 0; t < T; ++t) {
-                    uint32_t b[4];
-                    word_to_bf16x4(wv[j][t][r], kc, b);
+                for (int rr = 0; rr < 2; ++rr) {
+                    const int r = 2 * rp + rr;
+                    u32x4 ar[MM];
 #pragma unroll
-                    for (int v = 0; v < 4; ++v)
+                    for (int m = 0; m < MM; ++m)
+                        ar[m] = reinterpret_cast<const u32x4 *>(smem + L.a + m * L.row +
+                                                               (gl * kGroup + h * 32) * 2)[r];
 #pragma unroll
-                        for (int m = 0; m < MM; ++m) part[t][m] = dot2_bf16(b[v], ar[m][v], part[t][m]);
+                    for (int t = 0; t < T; ++t)
+#pragma unroll
+                        for (int v = 0; v < 4; ++v)
+#pragma unroll
+                            for (int m = 0; m < MM; ++m)
+                                part[t][m] = dot2_bf16(b[t][rr][v], ar[m][v], part[t][m]);
                 }
             }
 #pragma unroll
             for (int t = 0; t < T; ++t) {
-                const float s = __uint_as_float((sv[j][t] << s_shift) & 0xFFFF0000u);
+                const float s = scale_from(sv[j][t], s_sel);
 #pragma unroll
                 for (int m = 0; m < MM; ++m) {
                     const float corr = reinterpret_cast<const float *>(smem + L.bias)[(m * Gwg + gl) * 4 + h];

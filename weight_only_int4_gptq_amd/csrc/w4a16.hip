@@ -19,7 +19,8 @@ namespace {
 
 using namespace w4a16;
 
-constexpr int kLdsBudget = 64 * 1024;   // per workgroup: at least two workgroups per CU
+constexpr int kLdsBudget = 64 * 1024;    // automatic plans: at least two workgroups per CU
+constexpr int kLdsMax = 160 * 1024;      // explicit plans: gfx950's LDS per workgroup
 
 // ---------------------------------------------------------------- kernel table
 
@@ -92,21 +93,26 @@ int check_shape(int M, int N, int K) {
 int check_weight_shape(int K, int N) { return check_shape(1, N, K); }
 
 // Current device must be a gfx950; answers are cached per device id.
-int check_device() {
-    static std::atomic<int> cache[64];   // 0 unknown, 1 gfx950, -1 other
+// Current device: W4A16_OK if it is a gfx950, with its LDS bytes per
+// workgroup in *lds_max (cached per device).
+int check_device(int *lds_max = nullptr) {
+    static std::atomic<int> cache[64];   // 0 unknown, -1 not gfx950, else LDS bytes per workgroup
     int dev = -1;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0) return W4A16_ERR_DEVICE;
     if (dev >= 64) return W4A16_ERR_DEVICE;
     int v = cache[dev].load(std::memory_order_relaxed);
     if (v == 0) {
         hipDeviceProp_t prop;
-        if (hipGetDeviceProperties(&prop, dev) != hipSuccess)
+        if (hipGetDeviceProperties(&prop, dev) != hipSuccess ||
+            std::strncmp(prop.gcnArchName, "gfx950", 6) != 0)
             v = -1;
         else
-            v = (std::strncmp(prop.gcnArchName, "gfx950", 6) == 0) ? 1 : -1;
+            v = (int)prop.sharedMemPerBlock > 0 ? (int)prop.sharedMemPerBlock : 65536;
         cache[dev].store(v, std::memory_order_relaxed);
     }
-    return v == 1 ? W4A16_OK : W4A16_ERR_DEVICE;
+    if (v < 0) return W4A16_ERR_DEVICE;
+    if (lds_max) *lds_max = v;
+    return W4A16_OK;
 }
 
 // ---------------------------------------------------------------- planning
@@ -125,7 +131,7 @@ int validate_plan(const w4a16_plan_t &p, int M, int N, int K) {
     if (p.asrc != W4A16_ASRC_LDS && p.asrc != W4A16_ASRC_GLOBAL) return W4A16_ERR_PLAN;
     if (p.depth < 0) return W4A16_ERR_PLAN;
     if (!find_variant(p, M)) return W4A16_ERR_PLAN;
-    if (plan_lds(p, M, G) > kLdsBudget) return W4A16_ERR_PLAN;
+    if (plan_lds(p, M, G) + 256 > kLdsMax) return W4A16_ERR_PLAN;
     const long long nstrips = (N / 16 + p.tiles - 1) / p.tiles;
     if (nstrips * p.splits >= (1ll << 31)) return W4A16_ERR_PLAN;
     if (p.splits > 1 && nstrips > W4A16_SPLIT_COUNTER_BYTES / 4) return W4A16_ERR_PLAN;
@@ -224,11 +230,28 @@ int run_gemm(const void *A, const void *wq, const void *scales, void *C, int M, 
         if (!workspace || workspace_bytes < need) return W4A16_ERR_WORKSPACE;
         if (!aligned16(workspace)) return W4A16_ERR_ALIGN;
     }
-    st = check_device();
+    int lds_max = 0;
+    st = check_device(&lds_max);
     if (st != W4A16_OK) return st;
 
     const Variant *v = find_variant(p, M);
     if (!v) return W4A16_ERR_PLAN;
+    const int lds = plan_lds(p, M, K / W4A16_GROUP);
+    if (lds + 256 > lds_max) return W4A16_ERR_PLAN;   // 256: the kernel's static LDS
+    if (lds > 65536) {
+        // above 64 KiB the kernel must be allowed its dynamic LDS first (once)
+        static std::atomic<uint8_t> raised[sizeof(kVariants) / sizeof(kVariants[0])];
+        const size_t vi = (size_t)(v - kVariants);
+        if (!raised[vi].load(std::memory_order_relaxed)) {
+            const void *fn = reinterpret_cast<const void *>(v->fn);
+            hipFuncAttributes fa;
+            if (hipFuncGetAttributes(&fa, fn) != hipSuccess ||
+                hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                    lds_max - (int)fa.sharedSizeBytes) != hipSuccess)
+                return W4A16_ERR_LAUNCH;
+            raised[vi].store(1, std::memory_order_relaxed);
+        }
+    }
     GemmArgs a;
     a.A = static_cast<const uint16_t *>(A);
     a.blob = static_cast<const u32x4 *>(wq);
@@ -251,7 +274,6 @@ int run_gemm(const void *A, const void *wq, const void *scales, void *C, int M, 
         a.part = nullptr;
         a.count = nullptr;
     }
-    const int lds = plan_lds(p, M, a.G);
     void *args[] = {&a};
     const hipError_t e = launch(reinterpret_cast<const void *>(v->fn), (unsigned)a.nunits,
                                 64u * (unsigned)p.kwaves, (size_t)lds,

@@ -424,7 +424,8 @@ __global__ void __launch_bounds__(64 * KW) gemm_kernel(GemmArgs p) {
             for (int r = 0; r < 4; ++r) av[j][r] = ap[r];   // rows 32h + 8r .. +8: 16 B
         }
     };
-    auto gidx = [&](int i) { return gk0 + min(i, ng - 1); };
+    auto gat = [&](int i) { return gk0 + i; };
+    auto gidx = [&](int i) { return gat(min(i, ng - 1)); };
 
     if (ng > 0) {
         [&]<int... J>(std::integer_sequence<int, J...>) {
@@ -587,14 +588,14 @@ __global__ void __launch_bounds__(64 * KW) gemm_kernel(GemmArgs p) {
             int base = 0;
             for (; base + D < ng; base += D) {
                 [&]<int... J>(std::integer_sequence<int, J...>) {
-                    ((compute_group(std::integral_constant<int, J>{}, gk0 + base + J),
-                      load_group(std::integral_constant<int, J>{}, gk0 + base + J + D),
+                    ((compute_group(std::integral_constant<int, J>{}, gat(base + J)),
+                      load_group(std::integral_constant<int, J>{}, gat(base + J + D)),
                       __builtin_amdgcn_sched_barrier(0)),
                      ...);
                 }(std::make_integer_sequence<int, D>{});
             }
             [&]<int... J>(std::integer_sequence<int, J...>) {
-                (compute_group(std::integral_constant<int, J>{}, gk0 + base + J), ...);
+                (compute_group(std::integral_constant<int, J>{}, gat(base + J)), ...);
             }(std::make_integer_sequence<int, D>{});
         } else {
             // ragged: past the last group the refill re-reads the last group
@@ -602,7 +603,7 @@ __global__ void __launch_bounds__(64 * KW) gemm_kernel(GemmArgs p) {
             // issues the same loads and the wait counts stay static
             for (int base = 0; base < ng; base += D) {
                 [&]<int... J>(std::integer_sequence<int, J...>) {
-                    ((base + J < ng ? compute_group(std::integral_constant<int, J>{}, gk0 + base + J)
+                    ((base + J < ng ? compute_group(std::integral_constant<int, J>{}, gat(base + J))
                                     : void(),
                       load_group(std::integral_constant<int, J>{}, gidx(base + J + D)),
                       __builtin_amdgcn_sched_barrier(0)),

@@ -77,6 +77,7 @@ extern "C" {
 /* Where the MFMA path takes its A operand from. */
 #define W4A16_ASRC_LDS    0  /* staged once per workgroup in LDS */
 #define W4A16_ASRC_GLOBAL 1  /* read per group from global memory (L1/L2) */
+#define W4A16_ASRC_RING   2  /* per group through a per-wavefront LDS ring (DMA) */
 
 /*
  * A launch plan.  w4a16_gemm chooses one from (M, N, K); w4a16_gemm_plan
@@ -87,7 +88,8 @@ extern "C" {
  *   splits  workgroups that split K for the same columns: 1 (none), 2, 4, 8, ...
  *           (a power of two); more than one needs a workspace (see
  *           w4a16_workspace_bytes)
- *   asrc    W4A16_ASRC_LDS or W4A16_ASRC_GLOBAL (MFMA path only)
+ *   asrc    W4A16_ASRC_LDS, W4A16_ASRC_GLOBAL or W4A16_ASRC_RING (the last
+ *           two on the MFMA path only)
  *   depth   K groups each wavefront keeps in flight (0 = the default for
  *           `tiles`: 8, 4, 2 for 1, 2, 4 tiles)
  */

@@ -39,6 +39,12 @@ struct Variant {
 #define W4A16_V(P, MM, T, KW, D, AS) {P, MM, T, KW, D, AS, gemm_kernel<P, MM, T, KW, D, AS>},
 
 // one-shot shapes (the ring covers a wavefront's whole K range) for one row
+// A streamed per group through a per-wavefront LDS ring (matrix-core path)
+#define W4A16_RINGS(X, P, MM, AS) \
+    X(P, MM, 1, 4, 4, AS) X(P, MM, 1, 8, 4, AS) X(P, MM, 2, 4, 2, AS) X(P, MM, 2, 4, 4, AS) \
+    X(P, MM, 4, 4, 2, AS) X(P, MM, 4, 2, 2, AS) X(P, MM, 4, 4, 4, AS) X(P, MM, 8, 1, 4, AS) \
+    X(P, MM, 8, 2, 2, AS) X(P, MM, 8, 4, 2, AS)
+
 // eight-tile strips: A read once per eight tiles (matrix-core paths)
 #define W4A16_WIDE(X, P, MM, AS) \
     X(P, MM, 8, 4, 2, AS) X(P, MM, 8, 2, 2, AS) X(P, MM, 8, 2, 4, AS) X(P, MM, 8, 1, 4, AS)
@@ -53,6 +59,7 @@ const Variant kVariants[] = {
     W4A16_ONESHOT(W4A16_V, PATH_MFMA, 1, ASRC_GLOBAL)
     W4A16_SHAPES(W4A16_V, PATH_GEMV, 1, ASRC_LDS) W4A16_SHAPES(W4A16_V, PATH_GEMV, 2, ASRC_LDS)
     W4A16_SHAPES(W4A16_V, PATH_GEMV, 3, ASRC_LDS) W4A16_SHAPES(W4A16_V, PATH_GEMV, 4, ASRC_LDS)
+    W4A16_RINGS(W4A16_V, PATH_MFMA, 0, ASRC_RING)
     W4A16_WIDE(W4A16_V, PATH_MFMA, 0, ASRC_LDS) W4A16_WIDE(W4A16_V, PATH_MFMA, 0, ASRC_GLOBAL)
     W4A16_WIDE(W4A16_V, PATH_MFMA, 2, ASRC_LDS) W4A16_WIDE(W4A16_V, PATH_MFMA, 3, ASRC_LDS)
     W4A16_WIDE(W4A16_V, PATH_MFMA, 4, ASRC_LDS)
@@ -66,9 +73,11 @@ const Variant kVariants[] = {
 int default_depth(int tiles) { return tiles == 1 ? 8 : (tiles == 2 ? 4 : 2); }
 
 // The kernel for a plan: GEMV kernels are compiled per row count (1..4);
-// MFMA kernels too for M <= 4, and take M at run time above.
+// MFMA kernels too for M <= 4 (LDS or global A), and take M at run time
+// above and with ring A.
 const Variant *find_variant(const w4a16_plan_t &p, int M) {
-    const int mm = (p.path == W4A16_PATH_GEMV || M <= 4) ? M : 0;
+    // ring A kernels take M at run time for every row count
+    const int mm = (p.path == W4A16_PATH_GEMV || (M <= 4 && p.asrc != W4A16_ASRC_RING)) ? M : 0;
     const int asrc = (p.path == W4A16_PATH_GEMV) ? ASRC_LDS : p.asrc;
     const int depth = p.depth ? p.depth : default_depth(p.tiles);
     for (const Variant &v : kVariants)
@@ -120,7 +129,8 @@ int check_device(int *lds_max = nullptr) {
 int plan_lds(const w4a16_plan_t &p, int M, int G) {
     const int Gwg = (G + p.splits - 1) / p.splits;
     const int asrc = (p.path == W4A16_PATH_GEMV) ? ASRC_LDS : p.asrc;
-    return lds_layout(p.path, asrc, M, Gwg, p.tiles, p.kwaves).total;
+    const int depth = p.depth ? p.depth : default_depth(p.tiles);
+    return lds_layout(p.path, asrc, M, Gwg, p.tiles, p.kwaves, depth).total;
 }
 
 int validate_plan(const w4a16_plan_t &p, int M, int N, int K) {
@@ -128,7 +138,8 @@ int validate_plan(const w4a16_plan_t &p, int M, int N, int K) {
     if (p.path != W4A16_PATH_GEMV && p.path != W4A16_PATH_MFMA) return W4A16_ERR_PLAN;
     if (p.path == W4A16_PATH_GEMV && M > 4) return W4A16_ERR_PLAN;
     if (p.splits < 1 || p.splits > G || (p.splits & (p.splits - 1)) != 0) return W4A16_ERR_PLAN;
-    if (p.asrc != W4A16_ASRC_LDS && p.asrc != W4A16_ASRC_GLOBAL) return W4A16_ERR_PLAN;
+    if (p.asrc != W4A16_ASRC_LDS && p.asrc != W4A16_ASRC_GLOBAL && p.asrc != W4A16_ASRC_RING)
+        return W4A16_ERR_PLAN;
     if (p.depth < 0) return W4A16_ERR_PLAN;
     if (!find_variant(p, M)) return W4A16_ERR_PLAN;
     if (plan_lds(p, M, G) + 256 > kLdsMax) return W4A16_ERR_PLAN;
@@ -146,10 +157,14 @@ int validate_plan(const w4a16_plan_t &p, int M, int N, int K) {
 //    (eight for long K), ring depth 4 (5 for wide N);
 //  * M = 2..4: matrix cores with A staged in LDS; four tiles and depth 2 for
 //    wide N, else two tiles and depth 4, with K split four ways for long K;
-//  * M >= 5: matrix cores with A read from global memory (it no longer fits
-//    LDS next to the ring at these widths); long K splits two ways; from
-//    M = 8 on very wide N (>= 8192 tiles), one wavefront owns eight tiles so
-//    each A fragment it loads serves eight times the weights.
+//  * M >= 5: matrix cores with A read per group (a whole K range of A no
+//    longer fits LDS next to the ring at these widths):
+//      - from global memory for M = 5..7 (long K splits two ways) and for
+//        wide N below M = 12;
+//      - through the per-wavefront LDS ring (contiguous DMA loads) from
+//        M = 8 on narrow N and from M = 12 on wide N;
+//      - on very wide N (>= 8192 tiles) from M = 8, one wavefront owns eight
+//        tiles, so each A fragment it loads serves eight times the weights.
 // "Wide" is N >= 32768 (2048 tiles), "long" K >= 16384 (128 groups).
 void auto_plan(int M, int N, int K, w4a16_plan_t *out) {
     const int NT = N / 16, G = K / W4A16_GROUP;
@@ -174,10 +189,17 @@ void auto_plan(int M, int N, int K, w4a16_plan_t *out) {
         p.tiles = (wide || deep) ? 4 : 2;
         p.depth = (wide || deep) ? 2 : 4;
         if (deep && !wide) p.splits = 2;
-        if (NT >= 8192 && M >= 8) {   // very wide N: one wavefront per eight tiles
+        if (NT >= 8192 && M >= 8) {          // very wide N: one wavefront per eight tiles
             p.tiles = 8;
             p.kwaves = 1;
             p.depth = 4;
+        } else if (M >= 8 && !wide) {        // A through the LDS ring, no split
+            p.asrc = W4A16_ASRC_RING;
+            p.tiles = 2;
+            p.depth = 4;
+            p.splits = 1;
+        } else if (M >= 12 && wide) {        // wide N, many rows: ring A, four tiles
+            p.asrc = W4A16_ASRC_RING;
         }
     }
     // short K: no more wavefronts along K than groups per workgroup
@@ -195,6 +217,8 @@ void auto_plan(int M, int N, int K, w4a16_plan_t *out) {
     }
     if (p.path == W4A16_PATH_MFMA && p.asrc == W4A16_ASRC_LDS && plan_lds(p, M, G) > kLdsBudget)
         p.asrc = W4A16_ASRC_GLOBAL;
+    // ring A has fewer compiled shapes (none for the short-K fallback)
+    if (p.asrc == W4A16_ASRC_RING && !find_variant(p, M)) p.asrc = W4A16_ASRC_GLOBAL;
     *out = p;
 }
 

@@ -35,6 +35,7 @@ constexpr uint32_t kBiasPair = 0x43084308u;    // bf16 pair (136.0, 136.0) = cod
 constexpr float kBias = 136.0f;                // 128 (magic) + 8 (code midpoint)
 constexpr int kXcds = 8;                       // MI355X: 8 XCDs, 32 CUs each
 constexpr int kRowPad = 16;                    // bytes of padding per staged A row
+constexpr int kRingSlotBytes = 16 * kGroup * 2; // one group of A, 16 rows, in the LDS ring
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
@@ -42,7 +43,7 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 enum { PATH_GEMV = 1, PATH_MFMA = 2 };
-enum { ASRC_LDS = 0, ASRC_GLOBAL = 1 };
+enum { ASRC_LDS = 0, ASRC_GLOBAL = 1, ASRC_RING = 2 };
 
 struct GemmArgs {
     const uint16_t *A;       // bf16 [M][K]
@@ -62,7 +63,7 @@ struct GemmArgs {
 // ---------------------------------------------------------------- LDS plan
 // Shared by host (sizing) and device (carving).  Offsets in bytes.
 struct LdsLayout {
-    int a;      // staged A rows [M][Gwg*128 bf16 + pad]
+    int a;      // staged A rows [M][Gwg*128 bf16 + pad]; ring: [KW][D][16 rows][256 B]
     int bias;   // GEMV: bias of each 32-row quarter [M][Gwg][4] fp32;
                 // MFMA with staged A: bias tile rows [Gwg][16] fp32
     int red;    // cross-wavefront reduction [KW][T*M*16] fp32
@@ -70,13 +71,14 @@ struct LdsLayout {
     int row;    // bytes per staged A row
 };
 
-__host__ __device__ inline LdsLayout lds_layout(int path, int asrc, int M, int Gwg, int T, int KW) {
+__host__ __device__ inline LdsLayout lds_layout(int path, int asrc, int M, int Gwg, int T, int KW, int D) {
     LdsLayout L;
     const bool stage = (path == PATH_GEMV) || (asrc == ASRC_LDS);
     L.row = Gwg * kGroup * 2 + kRowPad;
     int off = 0;
     L.a = off;
     if (stage) off += M * L.row;
+    else if (path == PATH_MFMA && asrc == ASRC_RING) off += KW * D * kRingSlotBytes;
     L.bias = off;
     if (path == PATH_GEMV) off += M * Gwg * 4 * 4;
     else if (stage) off += Gwg * 16 * 4;
@@ -349,8 +351,9 @@ __global__ void __launch_bounds__(64 * KW) gemm_kernel(GemmArgs p) {
     __shared__ int s_last;
 
     constexpr bool kGlobalA = (PATH == PATH_MFMA && ASRC == ASRC_GLOBAL);
-    constexpr bool kStage = !kGlobalA;
-    constexpr int kLoadsPerGroup = 2 * T + (kGlobalA ? 4 : 0);
+    constexpr bool kRingA = (PATH == PATH_MFMA && ASRC == ASRC_RING);
+    constexpr bool kStage = !kGlobalA && !kRingA;
+    constexpr int kLoadsPerGroup = 2 * T + (kGlobalA ? 4 : 0);   // loads the compiler sees
     // rows of the 4-row block held by lane group h that are ever stored
     constexpr int kRowsV = (MM >= 1 && MM <= 4) ? MM : 4;
 
@@ -366,7 +369,7 @@ __global__ void __launch_bounds__(64 * KW) gemm_kernel(GemmArgs p) {
     const int Gwg = gw1 - gw0;
     const int gk0 = gw0 + (Gwg * wave) / KW, gk1 = gw0 + (Gwg * (wave + 1)) / KW;
     const int ng = gk1 - gk0;
-    const LdsLayout L = lds_layout(PATH, ASRC, M, Gwg, T, KW);
+    const LdsLayout L = lds_layout(PATH, ASRC, M, Gwg, T, KW, D);
     const DequantConsts kc = dequant_consts();
 
     // wave-uniform bases (scalar) and per-lane byte offsets (vector, fixed)
@@ -406,8 +409,24 @@ __global__ void __launch_bounds__(64 * KW) gemm_kernel(GemmArgs p) {
     uint32_t sv[D][T];
     u32x4 av[kGlobalA ? D : 1][4];
 
+    // Ring A: the group's rows go to this wavefront's LDS slot as contiguous
+    // 1 KiB DMA loads (four rows each; rows >= M repeat row M-1).  Inside a
+    // row the 16-byte pieces are XOR-swizzled by the row index, so the
+    // matrix-core reads below (16 rows, one piece each) hit distinct banks.
+    const int nd = (M + 3) >> 2;                             // DMA loads per group
+    auto ring_slot = [&](int j) { return L.a + (wave * D + j) * kRingSlotBytes; };
+
     auto load_group = [&](auto jc, int g) {
         constexpr int j = decltype(jc)::value;
+        if constexpr (kRingA) {
+            const uint32_t dst0 = __builtin_amdgcn_readfirstlane(lds_addr(smem + ring_slot(j)));
+            for (int i = 0; i < nd; ++i) {
+                const int row = min(4 * i + h, M - 1);
+                const uint8_t *src = reinterpret_cast<const uint8_t *>(p.A) +
+                                     ((size_t)row * p.K + (size_t)g * kGroup) * 2 + ((c ^ (row & 15)) << 4);
+                lds_dma16(src, dst0 + (i << 10));
+            }
+        }
 #pragma unroll
         for (int t = 0; t < T; ++t) {
             wv[j][t] = __builtin_nontemporal_load(
@@ -503,20 +522,32 @@ __global__ void __launch_bounds__(64 * KW) gemm_kernel(GemmArgs p) {
 #pragma unroll
         for (int i = 0; i < NACC; ++i) acc[t][i] = 0.0f;
 
-    auto compute_group = [&](auto jc, int g) {
+    auto compute_group = [&](auto jc, int g, auto final_) {
         constexpr int j = decltype(jc)::value;
         const int gl = g - gw0;
         if constexpr (PATH == PATH_MFMA) {
             u32x4 a[4];
             f32x4 Q;
-            if constexpr (!kGlobalA) {
+            if constexpr (kStage) {
                 const uint8_t *arow = smem + L.a + arow_m * L.row + (gl * kGroup + h * 32) * 2;
 #pragma unroll
                 for (int r = 0; r < 4; ++r) a[r] = reinterpret_cast<const u32x4 *>(arow)[r];
                 Q = reinterpret_cast<const f32x4 *>(smem + L.bias)[gl * 4 + h];
             } else {
+                if constexpr (kRingA) {
+                    // the compiler does not see the DMA loads: wait for this
+                    // slot's explicitly (every load issued after them counted
+                    // as if each later group had one DMA load: never fewer)
+                    constexpr int later = decltype(final_)::value ? D - 1 - j : D - 1;
+                    __builtin_amdgcn_s_waitcnt(waitcnt_vm(2 * T + later * (2 * T + 1)));
+                    const uint8_t *slot = smem + ring_slot(j) + c * (kGroup * 2);
 #pragma unroll
-                for (int r = 0; r < 4; ++r) a[r] = av[j][r];
+                    for (int r = 0; r < 4; ++r)
+                        a[r] = *reinterpret_cast<const u32x4 *>(slot + (((h * 4 + r) ^ c) << 4));
+                } else {
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) a[r] = av[j][r];
+                }
                 // bias: the same four-MFMA chain with every code 8
                 const u32x4 bconst = {kBiasPair, kBiasPair, kBiasPair, kBiasPair};
                 Q = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
@@ -588,14 +619,14 @@ __global__ void __launch_bounds__(64 * KW) gemm_kernel(GemmArgs p) {
             int base = 0;
             for (; base + D < ng; base += D) {
                 [&]<int... J>(std::integer_sequence<int, J...>) {
-                    ((compute_group(std::integral_constant<int, J>{}, gat(base + J)),
+                    ((compute_group(std::integral_constant<int, J>{}, gat(base + J), std::false_type{}),
                       load_group(std::integral_constant<int, J>{}, gat(base + J + D)),
                       __builtin_amdgcn_sched_barrier(0)),
                      ...);
                 }(std::make_integer_sequence<int, D>{});
             }
             [&]<int... J>(std::integer_sequence<int, J...>) {
-                (compute_group(std::integral_constant<int, J>{}, gat(base + J)), ...);
+                (compute_group(std::integral_constant<int, J>{}, gat(base + J), std::true_type{}), ...);
             }(std::make_integer_sequence<int, D>{});
         } else {
             // ragged: past the last group the refill re-reads the last group
@@ -603,7 +634,7 @@ __global__ void __launch_bounds__(64 * KW) gemm_kernel(GemmArgs p) {
             // issues the same loads and the wait counts stay static
             for (int base = 0; base < ng; base += D) {
                 [&]<int... J>(std::integer_sequence<int, J...>) {
-                    ((base + J < ng ? compute_group(std::integral_constant<int, J>{}, gat(base + J))
+                    ((base + J < ng ? compute_group(std::integral_constant<int, J>{}, gat(base + J), std::false_type{})
                                     : void(),
                       load_group(std::integral_constant<int, J>{}, gidx(base + J + D)),
                       __builtin_amdgcn_sched_barrier(0)),

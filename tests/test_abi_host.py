@@ -87,7 +87,7 @@ def test_split_plan_needs_workspace():
     assert _gemm(M=8, plan=p) == -5
     assert _gemm(M=8, plan=p, ws=P, wsb=need - 1) == -5
     assert w4.workspace_bytes(8, 1024, 512) == 0       # short K: the automatic plan does not split
-    assert w4.workspace_bytes(4, 5120, 17408) > 0      # long K, few strips: it does
+    assert w4.workspace_bytes(6, 5120, 17408) > 0      # long K, few strips: it does
 
 
 def test_no_device_is_an_error_not_a_crash():
@@ -121,18 +121,22 @@ def test_row_count_dispatch():
         p = w4.get_plan(M, 34816, 5120)
         assert p.path == (w4.PATH_GEMV if M == 1 else w4.PATH_MFMA), (M, p)
         assert p.splits == 1
-        # A staged in LDS up to four rows, then read per group: from global
-        # memory, and through the LDS ring from 12 rows on wide N
+        # wide N: A staged in LDS up to four rows, then read per group: from
+        # global memory, and through the LDS ring from 12 rows
         if M >= 2:
             want = w4.ASRC_LDS if M <= 4 else (w4.ASRC_GLOBAL if M < 12 else w4.ASRC_RING)
             assert p.asrc == want, (M, p)
+    # narrow N: all of A in LDS up to 12 rows, the ring above
+    assert w4.get_plan(8, 8192, 5120).asrc == w4.ASRC_LDS
+    assert w4.get_plan(12, 8192, 5120).kwaves == 8
+    assert w4.get_plan(16, 8192, 5120).asrc == w4.ASRC_RING
     # long K with few column strips: split K (two rows and more)
     assert w4.get_plan(1, 5120, 17408).splits == 1
-    assert w4.get_plan(4, 5120, 17408).splits == 4
-    assert w4.get_plan(6, 5120, 17408).splits == 2
+    assert w4.get_plan(4, 5120, 17408).splits == 1           # whole K of A in LDS
+    assert w4.get_plan(4, 5120, 17408).kwaves == 8
+    assert w4.get_plan(6, 5120, 17408).splits == 4
     assert w4.get_plan(16, 5120, 17408).splits == 1           # ring A
     assert w4.get_plan(16, 5120, 17408).asrc == w4.ASRC_RING
-    assert w4.get_plan(8, 8192, 5120).asrc == w4.ASRC_RING
     assert w4.get_plan(1, 5120, 17408).kwaves == 8
     assert w4.get_plan(1, 248320, 5120).tiles == 2
     assert w4.get_plan(16, 248320, 5120).tiles == 8

@@ -19,7 +19,7 @@ namespace {
 
 using namespace w4a16;
 
-constexpr int kLdsBudget = 64 * 1024;    // automatic plans: at least two workgroups per CU
+constexpr int kLdsBudget = 64 * 1024;    // automatic GEMV plans: at least two workgroups per CU
 constexpr int kLdsMax = 160 * 1024;      // explicit plans: gfx950's LDS per workgroup
 
 // ---------------------------------------------------------------- kernel table
@@ -155,16 +155,20 @@ int validate_plan(const w4a16_plan_t &p, int M, int N, int K) {
 // 5120 x 248320, M = 1..16:
 //  * M = 1: the GEMV kernel, two tiles per workgroup, four wavefronts along K
 //    (eight for long K), ring depth 4 (5 for wide N);
-//  * M = 2..4: matrix cores with A staged in LDS; four tiles and depth 2 for
-//    wide N, else two tiles and depth 4, with K split four ways for long K;
-//  * M >= 5: matrix cores with A read per group (a whole K range of A no
-//    longer fits LDS next to the ring at these widths):
-//      - from global memory for M = 5..7 (long K splits two ways) and for
-//        wide N below M = 12;
-//      - through the per-wavefront LDS ring (contiguous DMA loads) from
-//        M = 8 on narrow N and from M = 12 on wide N;
-//      - on very wide N (>= 8192 tiles) from M = 8, one wavefront owns eight
-//        tiles, so each A fragment it loads serves eight times the weights.
+//  * M = 2..4: matrix cores with A staged in LDS (the bias formed in the
+//    loop); four tiles and depth 2 for wide N at M = 2 and for very wide N,
+//    else two tiles and depth 4; for long K eight wavefronts stage the whole
+//    K range of A (up to the full 160 KiB of LDS, one workgroup per CU);
+//  * M >= 5, matrix cores:
+//      - very wide N (>= 8192 tiles) from M = 8: one wavefront owns eight
+//        tiles (A from global memory), so each A fragment it loads serves
+//        eight times the weights;
+//      - wide N: four tiles, A per group from global memory below M = 12,
+//        through the per-wavefront LDS ring (contiguous DMA loads) above;
+//      - long K: A through the ring from M = 8; below, a quarter of K of A
+//        staged in LDS (split four ways);
+//      - otherwise all of A staged in LDS with eight wavefronts along K up
+//        to M = 12, the ring above.
 // "Wide" is N >= 32768 (2048 tiles), "long" K >= 16384 (128 groups).
 void auto_plan(int M, int N, int K, w4a16_plan_t *out) {
     const int NT = N / 16, G = K / W4A16_GROUP;
@@ -180,26 +184,46 @@ void auto_plan(int M, int N, int K, w4a16_plan_t *out) {
         p.depth = (wide && !deep) ? 5 : 4;
     } else if (M <= 4) {
         p.path = W4A16_PATH_MFMA;
-        p.tiles = wide ? 4 : 2;
-        p.depth = wide ? 2 : 4;
-        if (deep && !wide) p.splits = 4;
+        if (deep && !wide) {                 // the whole long K range of A in LDS
+            p.tiles = 2;
+            p.kwaves = 8;
+            p.depth = 4;
+        } else if (wide && (M == 2 || NT >= 8192)) {
+            p.tiles = 4;
+            p.depth = 2;
+        } else {
+            p.tiles = 2;
+            p.depth = 4;
+        }
     } else {
         p.path = W4A16_PATH_MFMA;
-        p.asrc = W4A16_ASRC_GLOBAL;
-        p.tiles = (wide || deep) ? 4 : 2;
-        p.depth = (wide || deep) ? 2 : 4;
-        if (deep && !wide) p.splits = 2;
         if (NT >= 8192 && M >= 8) {          // very wide N: one wavefront per eight tiles
+            p.asrc = W4A16_ASRC_GLOBAL;
             p.tiles = 8;
             p.kwaves = 1;
             p.depth = 4;
-        } else if (M >= 8 && !wide) {        // A through the LDS ring, no split
-            p.asrc = W4A16_ASRC_RING;
+        } else if (wide) {
+            p.asrc = M >= 12 ? W4A16_ASRC_RING : W4A16_ASRC_GLOBAL;
+            p.tiles = 4;
+            p.depth = 2;
+        } else if (deep) {
             p.tiles = 2;
             p.depth = 4;
-            p.splits = 1;
-        } else if (M >= 12 && wide) {        // wide N, many rows: ring A, four tiles
-            p.asrc = W4A16_ASRC_RING;
+            if (M >= 8) {
+                p.asrc = W4A16_ASRC_RING;
+            } else {                         // a quarter of K of A in LDS
+                p.asrc = W4A16_ASRC_LDS;
+                p.splits = 4;
+            }
+        } else {
+            p.tiles = 2;
+            p.depth = 4;
+            if (M <= 12) {                   // all of A in LDS, eight wavefronts along K
+                p.asrc = W4A16_ASRC_LDS;
+                p.kwaves = 8;
+            } else {
+                p.asrc = W4A16_ASRC_RING;
+            }
         }
     }
     // short K: no more wavefronts along K than groups per workgroup
@@ -215,8 +239,12 @@ void auto_plan(int M, int N, int K, w4a16_plan_t *out) {
         p.path = W4A16_PATH_MFMA;
         p.depth = 0;
     }
-    if (p.path == W4A16_PATH_MFMA && p.asrc == W4A16_ASRC_LDS && plan_lds(p, M, G) > kLdsBudget)
-        p.asrc = W4A16_ASRC_GLOBAL;
+    // staged A may take a whole workgroup's LDS (one workgroup per CU);
+    // beyond that A streams through the ring
+    if (p.path == W4A16_PATH_MFMA && p.asrc == W4A16_ASRC_LDS && plan_lds(p, M, G) + 256 > kLdsMax) {
+        p.asrc = M >= 5 ? W4A16_ASRC_RING : W4A16_ASRC_GLOBAL;
+        p.splits = 1;
+    }
     // ring A has fewer compiled shapes (none for the short-K fallback)
     if (p.asrc == W4A16_ASRC_RING && !find_variant(p, M)) p.asrc = W4A16_ASRC_GLOBAL;
     *out = p;

@@ -354,6 +354,11 @@ __global__ void __launch_bounds__(64 * KW) gemm_kernel(GemmArgs p) {
     constexpr bool kRingA = (PATH == PATH_MFMA && ASRC == ASRC_RING);
     constexpr bool kStage = !kGlobalA && !kRingA;
     constexpr int kLoadsPerGroup = 2 * T + (kGlobalA ? 4 : 0);   // loads the compiler sees
+    // Matrix-core bias: formed in the loop from the A fragments already
+    // loaded (four more MFMAs per group, shared by the T tiles), except for
+    // four-tile strips of one or two rows, where one pass over the staged A
+    // before the loop measures faster.
+    constexpr bool kBiasInLoop = PATH == PATH_MFMA && !(kStage && MM >= 1 && MM <= 2 && T >= 4);
     // rows of the 4-row block held by lane group h that are ever stored
     constexpr int kRowsV = (MM >= 1 && MM <= 4) ? MM : 4;
 
@@ -479,7 +484,7 @@ __global__ void __launch_bounds__(64 * KW) gemm_kernel(GemmArgs p) {
                 }
                 bias[b] = s;
             }
-        } else {
+        } else if constexpr (!kBiasInLoop) {
             // each group: the MFMA lanes' four-instruction chain with every code
             // 8, exactly as the main loop would form it; rows 4h..4h+3 of column
             // 0 are stored (all 16 columns are equal)
@@ -532,7 +537,14 @@ __global__ void __launch_bounds__(64 * KW) gemm_kernel(GemmArgs p) {
                 const uint8_t *arow = smem + L.a + arow_m * L.row + (gl * kGroup + h * 32) * 2;
 #pragma unroll
                 for (int r = 0; r < 4; ++r) a[r] = reinterpret_cast<const u32x4 *>(arow)[r];
-                Q = reinterpret_cast<const f32x4 *>(smem + L.bias)[gl * 4 + h];
+                if constexpr (kBiasInLoop) {
+                    const u32x4 bconst = {kBiasPair, kBiasPair, kBiasPair, kBiasPair};
+                    Q = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) Q = mfma16x16x32(a[r], bconst, Q);
+                } else {
+                    Q = reinterpret_cast<const f32x4 *>(smem + L.bias)[gl * 4 + h];
+                }
             } else {
                 if constexpr (kRingA) {
                     // the compiler does not see the DMA loads: wait for this

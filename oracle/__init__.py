@@ -240,6 +240,63 @@ def exact_gemm(A_bits, qweight, scales_bits, M: int, N: int, K: int):
 # Acceptance metric
 # ---------------------------------------------------------------------------
 
+def silu(x) -> np.ndarray:
+    """silu(x) = x / (1 + exp(-x)) in fp64.
+
+    For x < 0 the equal form x * e^x / (1 + e^x) is used, so exp never
+    overflows for finite x (silu(-1e6) is -0, not NaN).
+    """
+    x = np.asarray(x, dtype=np.float64)
+    out = np.empty_like(x)
+    pos = x >= 0
+    out[pos] = x[pos] / (1.0 + np.exp(-x[pos]))
+    e = np.exp(x[~pos])
+    out[~pos] = x[~pos] * e / (1.0 + e)
+    return out
+
+
+def silu_derivative(x) -> np.ndarray:
+    """d/dx silu(x) = s(x) * (1 + x * (1 - s(x))) with s the logistic function."""
+    x = np.asarray(x, dtype=np.float64)
+    s = np.empty_like(x)
+    pos = x >= 0
+    s[pos] = 1.0 / (1.0 + np.exp(-x[pos]))
+    e = np.exp(x[~pos])
+    s[~pos] = e / (1.0 + e)
+    return s * (1.0 + x * (1.0 - s))
+
+
+def gemm_silu_mul(A: np.ndarray, qweight: np.ndarray, scales: np.ndarray, M: int, N: int, K: int,
+                  js=None, nthreads: int = 0):
+    """fp64 reference of the gate/up matmul with its activation:
+
+        H[m, j] = silu(C[m, j]) * C[m, j + N/2],   C = A . dequant(W)  (fp64, as ``gemm``)
+
+    Reading taken (the pages name gate, up and down linears per MLP but not
+    the activation or the column order): the first N/2 columns of the fused
+    weight are the gate linear, the last N/2 the up linear, and the gating
+    is SiLU.  ``js`` selects columns j of H (all N/2 if None).
+
+    Returns (H, E), float64 [M, len(js)].  E = |silu'(g)| |u| D_g + |silu(g)| D_u
+    is the first-order change of H when the gate and up sums move by at most
+    their own sum |a*w| (D_g, D_u): the GEMM's normalized error bound
+    carried through the activation.
+    """
+    if N % 32:
+        raise ValueError("oracle.gemm_silu_mul: N must be a multiple of 32")
+    half = N // 2
+    j = np.arange(half, dtype=np.int64) if js is None else np.asarray(js, dtype=np.int64)
+    if j.size and (j.min() < 0 or j.max() >= half):
+        raise ValueError("oracle.gemm_silu_mul: column index out of range")
+    cols = np.concatenate([j, j + half])
+    C, D = gemm(A, qweight, scales, M, N, K, cols=cols, nthreads=nthreads)
+    g, u = C[:, :j.size], C[:, j.size:]
+    dg, du = D[:, :j.size], D[:, j.size:]
+    H = silu(g) * u
+    E = np.abs(silu_derivative(g)) * np.abs(u) * dg + np.abs(silu(g)) * du
+    return H, E
+
+
 def normalized_error(C_test: np.ndarray, C_ref: np.ndarray, D_ref: np.ndarray) -> np.ndarray:
     """Per-output error |C_test - C_ref| / D_ref.
 

@@ -6,6 +6,7 @@ special cases that reduce to a library routine, and invariants of the repack
 permutation.  A plausible slip anywhere in the oracle (nibble order, sign of
 the offset, group index, transposed operand, dropped term) fails one of them.
 """
+import math
 import os
 from fractions import Fraction
 
@@ -303,3 +304,69 @@ def test_geometry_matches_kv_cache_figure():
     assert (24 + 2 * 4) * 256 == synth.WORKLOADS["qkv"].N
     assert 2 * 17408 == synth.WORKLOADS["gate_up"].N
     assert synth.WORKLOADS["lm_head"].N == 248320
+
+
+# ----------------------------------------------------------------- gate/up activation
+
+def test_silu_closed_forms_and_identity():
+    # silu(x) - silu(-x) = x (x s(x) + x s(-x) = x since s(x) + s(-x) = 1)
+    x = np.linspace(-30.0, 30.0, 241)
+    assert np.allclose(oracle.silu(x) - oracle.silu(-x), x, rtol=0, atol=1e-12)
+    # s(ln 3) = 3/4 exactly in the reals
+    assert abs(oracle.silu(np.array([math.log(3.0)]))[0] - 0.75 * math.log(3.0)) < 1e-15
+    assert oracle.silu(np.array([0.0]))[0] == 0.0
+    # no overflow at finite extremes
+    big = oracle.silu(np.array([-1e6, 1e6, -700.0, 700.0]))
+    assert big[0] == 0.0 and big[1] == 1e6 and abs(big[2]) < 1e-290 and big[3] == 700.0
+    # derivative against a central difference
+    h = 1e-6
+    xs = np.array([-5.0, -1.0, 0.0, 0.5, 3.0])
+    num = (oracle.silu(xs + h) - oracle.silu(xs - h)) / (2 * h)
+    assert np.allclose(oracle.silu_derivative(xs), num, rtol=0, atol=1e-8)
+
+
+def test_gemm_silu_mul_halves_are_gate_then_up():
+    # one-hot A on row k, scales 1: C[0, n] = q[k, n] - 8 exactly, so
+    # H[0, j] = silu(q[k, j] - 8) * (q[k, j + N/2] - 8)
+    K, N, k = 256, 64, 131
+    rng = np.random.default_rng(5)
+    qw = rng.integers(0, 2 ** 32, size=(K // 8, N), dtype=np.uint32)
+    sc = np.full((K // 128, N), 0x3F80, dtype=np.uint16)            # 1.0
+    A = np.zeros((1, K), dtype=np.uint16)
+    A[0, k] = 0x3F80
+    H, E = oracle.gemm_silu_mul(A, qw, sc, 1, N, K)
+    q = oracle.unpack(qw, K, N)[k].astype(np.int64) - 8
+    for j in range(N // 2):
+        g, u = float(q[j]), float(q[j + N // 2])
+        want = g / (1.0 + math.exp(-g)) * u
+        assert abs(H[0, j] - want) <= 1e-12 * max(1.0, abs(want)), (j, H[0, j], want)
+    # zero gate codes (8) give exact zeros whatever the up half holds, and
+    # not the other way round
+    qw_gate0 = qw.copy()
+    qw_gate0[:, : N // 2] = 0x88888888
+    H0, E0 = oracle.gemm_silu_mul(A, qw_gate0, sc, 1, N, K)
+    assert np.all(H0 == 0.0)
+    qw_up0 = qw.copy()
+    qw_up0[:, N // 2:] = 0x88888888
+    H1, _ = oracle.gemm_silu_mul(A, qw_up0, sc, 1, N, K)
+    assert np.all(H1 == 0.0)
+    qw_swapped = np.concatenate([qw[:, N // 2:], qw[:, : N // 2]], axis=1)
+    Hs, _ = oracle.gemm_silu_mul(A, qw_swapped, sc, 1, N, K)
+    assert not np.allclose(Hs, H)
+
+
+def test_gemm_silu_mul_column_subset_and_bound():
+    K, N = 384, 96
+    A, qw, sc = synth.gen_problem(K, N, 12)
+    H, E = oracle.gemm_silu_mul(A, qw, sc, 3, N, K)
+    js = np.array([0, 7, 47, 20])
+    Hs, Es = oracle.gemm_silu_mul(A, qw, sc, 3, N, K, js=js)
+    assert np.array_equal(Hs, H[:, js]) and np.array_equal(Es, E[:, js])
+    assert np.all(E >= 0)
+    # moving g and u by at most 1e-6 of their D changes H by at most about 1e-6 E
+    C, D = oracle.gemm(A, qw, sc, 3, N, K)
+    g, u = C[:, : N // 2], C[:, N // 2:]
+    dg, du = D[:, : N // 2], D[:, N // 2:]
+    eps = 1e-6
+    H2 = oracle.silu(g + eps * dg) * (u - eps * du)
+    assert np.all(np.abs(H2 - H) <= eps * E * 1.01 + 1e-15)

@@ -71,6 +71,9 @@ class Problem:
         self.scales = [s] + [s.clone() for _ in range(sets - 1)]
         self.acts = [a] + [a.clone() for _ in range(sets - 1)]
         self.outs = [torch.empty((Mmax, N), dtype=torch.bfloat16, device=dev) for _ in range(sets)]
+        # gate/up outputs H[Mmax, N/2], contiguous, in the first half of each C buffer
+        self.houts = ([o.view(-1)[: Mmax * (N // 2)].view(Mmax, N // 2) for o in self.outs]
+                      if N % 32 == 0 else None)
         self.K, self.N, self.sets = K, N, sets
         torch.cuda.synchronize()
 
@@ -357,6 +360,20 @@ def sweep(torch, w4, args):
                    "pct_peak": round(100 * r["gbs"] / PEAK_HBM_GBS, 2),
                    "mfma_util": round(r["tflops"] / PEAK_BF16_TFLOPS, 4), "sets": sets}
             print(json.dumps(rec), flush=True)
+        if wname == "gate_up":
+            # the same weights with the SiLU(gate) * up epilogue: H[M, N/2]
+            for M in Ms:
+                def fcall(i, M=M):
+                    j = i % prob.sets
+                    w4.gemm_silu_mul(prob.acts[j][:M], prob.blobs[j], prob.scales[j], prob.N,
+                                     out=prob.houts[j][:M])
+                steps = max(20, min(args.steps, int(2e6 / synth.algorithmic_bytes(M, wl.N, wl.K) * 100)))
+                ms = time_graph(torch, fcall, steps, min(args.warmup, 20))
+                nb = synth.algorithmic_bytes_silu_mul(M, wl.N, wl.K)
+                print(json.dumps({"workload": "gate_up_silu_mul", "M": M, "K": wl.K, "N": wl.N,
+                                  "us_per_call": round(ms * 1e3, 3), "GBps": round(nb / (ms * 1e-3) / 1e9, 1),
+                                  "pct_peak": round(100 * nb / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 2),
+                                  "sets": sets}), flush=True)
         del prob
         torch.cuda.empty_cache()
 

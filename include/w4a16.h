@@ -186,6 +186,39 @@ int w4a16_gemm_plan(const void *A, const void *wq_repacked, const void *scales, 
                     const w4a16_plan_t *plan, void *stream);
 
 /*
+ * Gate/up matmul with the MLP activation in its epilogue:
+ *
+ *     C = A . dequant(blob, scales)              (C[M][N], never stored)
+ *     H[m][j] = silu(C[m][j]) * C[m][j + N/2],   0 <= j < N/2,
+ *     silu(x) = x / (1 + exp(-x)),
+ *
+ * for a fused gate/up weight whose first N/2 columns are the gate linear and
+ * last N/2 the up linear of one MLP (each layer's MLP has gate, up and down
+ * linears: page "SuperQwen3.8-27b-abliterated-NVFP4-2xDGX", the structural
+ * verification of its packed tensors; the pages do not name the activation,
+ * and SiLU-gated is the reading taken).  H feeds the down projection.
+ * silu and the product are formed in fp32 on the fp32 sums; H is rounded to
+ * bf16 (nearest even) once.
+ *   H            device bf16 [M][N/2] (written)
+ *   N            the fused width, a multiple of 32
+ *   other arguments as w4a16_gemm (blob and scales of the [K][N] fused
+ *   weight; workspace at least w4a16_workspace_bytes(M, N, K, NULL)).
+ * The plan w4a16_gemm would choose is used with an even tile count (gate
+ * and up tiles of the same columns in one workgroup).
+ */
+int w4a16_gemm_silu_mul(const void *A, const void *wq_repacked, const void *scales, void *H,
+                        int M, int N, int K, int group, void *workspace, size_t workspace_bytes,
+                        void *stream);
+
+/*
+ * As w4a16_gemm_silu_mul with an explicit plan, whose tile count must be
+ * even (W4A16_ERR_PLAN otherwise).
+ */
+int w4a16_gemm_silu_mul_plan(const void *A, const void *wq_repacked, const void *scales, void *H,
+                             int M, int N, int K, int group, void *workspace,
+                             size_t workspace_bytes, const w4a16_plan_t *plan, void *stream);
+
+/*
  * Test export of the device dequantization used by both GEMM paths:
  * W[k][n] = (q - 8) * s as fp32 (exact), device fp32 [K][N] (written);
  * `scales` are the repacked scales.

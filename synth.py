@@ -109,6 +109,11 @@ def gen_workload(name: str, M: int = M_MAX):
     return gen_problem(w.K, w.N, w.seed, w.act, M)
 
 
+def algorithmic_bytes_silu_mul(M: int, N: int, K: int) -> int:
+    """Bytes of the gate/up call with its activation: codes, scales, A, and H[M, N/2] written."""
+    return K * N // 2 + (K // GROUP) * N * 2 + M * K * 2 + M * (N // 2) * 2
+
+
 def algorithmic_bytes(M: int, N: int, K: int) -> int:
     """Bytes one call must move at least: int4 codes, bf16 scales, bf16 A, bf16 C."""
     return K * N // 2 + (K // GROUP) * N * 2 + M * K * 2 + M * N * 2

@@ -167,3 +167,28 @@ def test_check_plan():
     assert not w4.plan_ok(16, 34816, 5120, w4.make_plan(w4.PATH_MFMA, 1, 8, 1, w4.ASRC_LDS))
     assert w4.plan_ok(16, 34816, 5120, w4.make_plan(w4.PATH_MFMA, 1, 8, 4, w4.ASRC_LDS))
     assert w4.lib().w4a16_check_plan(0, 16, 128, ctypes.byref(ok)) == -2
+
+
+def _silu_mul(A=P, wq=P, s=P, H=P2, M=1, N=1024, K=512, group=128, ws=NULL, wsb=0, plan=None):
+    L = w4.lib()
+    if plan is None:
+        return L.w4a16_gemm_silu_mul(A, wq, s, H, M, N, K, group, ws, wsb, NULL)
+    return L.w4a16_gemm_silu_mul_plan(A, wq, s, H, M, N, K, group, ws, wsb, ctypes.byref(plan), NULL)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(A=NULL), -1), (dict(H=NULL), -1), (dict(M=0), -2), (dict(M=17), -2),
+    (dict(N=1008), -2),            # a multiple of 16 but not of 32: halves are not whole tiles
+    (dict(K=500), -2), (dict(group=64), -3), (dict(H=ODD), -4),
+    (dict(plan=w4.make_plan(w4.PATH_MFMA, 1, 4)), -8),       # odd tile count: no gate/up pairs
+])
+def test_silu_mul_argument_errors(kw, status):
+    assert _silu_mul(**kw) == status
+
+
+def test_silu_mul_without_device():
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present")
+    assert _silu_mul() == -6
+    assert _silu_mul(plan=w4.make_plan(w4.PATH_MFMA, 2, 4)) == -6

@@ -318,3 +318,87 @@ def test_workload_parity_lm_head_sampled():
         e = max_err(Cs, Cref[:M], Dref[:M])
         note(f"  lm_head M={M} plan={w4.get_plan(M, N, K)} max normalized error {e:.3e}")
         assert e <= TOL
+
+
+# ------------------------------------------------------------- gate/up activation epilogue
+
+def silu_mul_check(H, Href, E, what):
+    """|H - Href| <= 2e-3 E (the GEMM bound carried through silu * up) plus one
+    bf16 rounding of H (at most 2^-8 |H|)."""
+    got = oracle.bf16_bits_to_f64(c_bits(H))
+    err = np.abs(got - Href)
+    bound = TOL * E * 1.01 + 2.0 ** -8 * np.abs(Href) * (1 + 1e-6)
+    bad = err > bound
+    assert not bad.any(), (what, int(bad.sum()), float((err - bound).max()))
+
+
+EVEN_PLANS = [p for p in ALL_PLANS if p.tiles % 2 == 0]
+
+
+@pytest.mark.parametrize("K,N,seed", [(512, 1024, 30), (1152, 608, 31), (384, 64, 32), (2048, 288, 33)])
+def test_silu_mul_parity_every_even_plan(K, N, seed):
+    A, qw, sc = synth.gen_problem(K, N, seed)
+    q, s, a = to_dev(qw, sc, A)
+    blob = w4.repack_weights(q, K, N)
+    Href16, E16 = oracle.gemm_silu_mul(A, qw, sc, 16, N, K)
+    for M in (1, 2, 3, 4, 5, 8, 16):
+        cases = [None] + [p for p in EVEN_PLANS if w4.plan_ok(M, N, K, p)]
+        note(f"[silu-mul] K={K} N={N} M={M}: {len(cases)} plans")
+        for p in cases:
+            H = w4.gemm_silu_mul(a[:M].contiguous(), blob, s, N, plan=p)
+            torch.cuda.synchronize()
+            silu_mul_check(H, Href16[:M], E16[:M], (M, p))
+
+
+@pytest.mark.parametrize("splits", [2, 4])
+def test_silu_mul_split_k(splits):
+    K, N = 1280, 544
+    A, qw, sc = synth.gen_problem(K, N, 34)
+    q, s, a = to_dev(qw, sc, A)
+    blob = w4.repack_weights(q, K, N)
+    Href, E = oracle.gemm_silu_mul(A, qw, sc, 16, N, K)
+    for M in (1, 4, 9, 16):
+        for path, asrc in ((w4.PATH_GEMV, 0), (w4.PATH_MFMA, 0), (w4.PATH_MFMA, 1), (w4.PATH_MFMA, 2)):
+            if path == w4.PATH_GEMV and M > 4:
+                continue
+            p = w4.make_plan(path, 2, 4, splits, asrc)
+            if not w4.plan_ok(M, N, K, p):
+                continue
+            ws = torch.zeros(w4.workspace_bytes(M, N, K, p), dtype=torch.uint8, device=DEV)
+            note(f"[silu-mul split] M={M} plan={p}")
+            H1 = w4.gemm_silu_mul(a[:M].contiguous(), blob, s, N, plan=p, workspace=ws)
+            H2 = w4.gemm_silu_mul(a[:M].contiguous(), blob, s, N, plan=p, workspace=ws)
+            torch.cuda.synchronize()
+            silu_mul_check(H1, Href[:M], E[:M], (M, p))
+            assert torch.equal(H1.view(torch.int16), H2.view(torch.int16))
+
+
+def test_silu_mul_zero_gate_is_exact_zero_and_odd_tiles_rejected():
+    K, N = 512, 256
+    A, qw, sc = synth.gen_problem(K, N, 35)
+    qw = qw.copy()
+    qw[:, : N // 2] = 0x88888888                       # gate weights zero
+    q, s, a = to_dev(qw, sc, A)
+    blob = w4.repack_weights(q, K, N)
+    for M in (1, 4, 16):
+        H = w4.gemm_silu_mul(a[:M].contiguous(), blob, s, N)
+        torch.cuda.synchronize()
+        assert int((H.view(torch.int16) & 0x7FFF).abs().sum()) == 0
+    with pytest.raises(w4.W4A16Error):
+        w4.gemm_silu_mul(a[:1].contiguous(), blob, s, N, plan=w4.make_plan(w4.PATH_GEMV, 1, 4))
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("M", [1, 2, 4, 8, 9, 16])
+def test_silu_mul_gate_up_workload(M):
+    wl = synth.WORKLOADS["gate_up"]
+    K, N = wl.K, wl.N
+    A, qw, sc = synth.gen_workload("gate_up")
+    q, s, a = to_dev(qw, sc, A)
+    blob = w4.repack_weights(q, K, N)
+    js = np.random.default_rng(36).choice(N // 2, size=2048, replace=False)
+    Href, E = oracle.gemm_silu_mul(A, qw, sc, M, N, K, js=js)
+    H = w4.gemm_silu_mul(a[:M].contiguous(), blob, s, N)
+    torch.cuda.synchronize()
+    note(f"[silu-mul gate_up] M={M} plan={w4.get_plan(M, N, K).as_dict()}")
+    silu_mul_check(H[:, torch.from_numpy(js).to(DEV)], Href, E, M)

@@ -260,12 +260,28 @@ hipError_t launch(const void *fn, unsigned grid, unsigned block, size_t lds, hip
     return hipLaunchKernel(fn, dim3(grid), dim3(block), args, lds, stream);
 }
 
+// The gate/up epilogue needs strips of gate/up tile pairs: an even tile
+// count.  The automatic plan is moved to two tiles when it has one.
+void fuse_plan(int M, w4a16_plan_t *p) {
+    if (p->tiles % 2 == 0) return;
+    w4a16_plan_t q = *p;
+    q.tiles = 2;
+    q.depth = 0;
+    if (!find_variant(q, M)) {
+        q.kwaves = 4;
+        if (!find_variant(q, M)) q.asrc = W4A16_ASRC_GLOBAL;
+    }
+    *p = q;
+}
+
+// fuse: 0 plain C[M][N]; 1 the gate/up epilogue, C is H[M][N/2]
 int run_gemm(const void *A, const void *wq, const void *scales, void *C, int M, int N, int K,
              int group, void *workspace, size_t workspace_bytes, const w4a16_plan_t *user,
-             void *stream) {
+             void *stream, int fuse = 0) {
     if (!A || !wq || !scales || !C) return W4A16_ERR_NULL;
     int st = check_shape(M, N, K);
     if (st != W4A16_OK) return st;
+    if (fuse && N % 32 != 0) return W4A16_ERR_SHAPE;
     if (group != W4A16_GROUP) return W4A16_ERR_GROUP;
     if (!aligned16(A) || !aligned16(wq) || !aligned16(scales) || !aligned16(C))
         return W4A16_ERR_ALIGN;
@@ -274,8 +290,10 @@ int run_gemm(const void *A, const void *wq, const void *scales, void *C, int M, 
         p = *user;
         st = validate_plan(p, M, N, K);
         if (st != W4A16_OK) return st;
+        if (fuse && p.tiles % 2 != 0) return W4A16_ERR_PLAN;
     } else {
         auto_plan(M, N, K, &p);
+        if (fuse) fuse_plan(M, &p);
     }
     const size_t need = workspace_for(p, M, N);
     if (need > 0) {
@@ -319,6 +337,7 @@ int run_gemm(const void *A, const void *wq, const void *scales, void *C, int M, 
     a.NT = N / 16;
     a.nstrips = (a.NT + p.tiles - 1) / p.tiles;
     a.nunits = a.nstrips * a.S;
+    a.fuse = fuse;
     if (need > 0) {
         a.count = static_cast<uint32_t *>(workspace);
         a.part = reinterpret_cast<float *>(static_cast<char *>(workspace) + W4A16_SPLIT_COUNTER_BYTES);
@@ -438,6 +457,20 @@ int w4a16_gemm_plan(const void *A, const void *wq_repacked, const void *scales, 
                     const w4a16_plan_t *plan, void *stream) {
     return run_gemm(A, wq_repacked, scales, C, M, N, K, group, workspace, workspace_bytes, plan,
                     stream);
+}
+
+int w4a16_gemm_silu_mul(const void *A, const void *wq_repacked, const void *scales, void *H, int M,
+                        int N, int K, int group, void *workspace, size_t workspace_bytes,
+                        void *stream) {
+    return run_gemm(A, wq_repacked, scales, H, M, N, K, group, workspace, workspace_bytes, nullptr,
+                    stream, 1);
+}
+
+int w4a16_gemm_silu_mul_plan(const void *A, const void *wq_repacked, const void *scales, void *H,
+                             int M, int N, int K, int group, void *workspace,
+                             size_t workspace_bytes, const w4a16_plan_t *plan, void *stream) {
+    return run_gemm(A, wq_repacked, scales, H, M, N, K, group, workspace, workspace_bytes, plan,
+                    stream, 1);
 }
 
 static int run_export(const void *wq, const void *scales, float *W, uint8_t *codes, int K, int N,

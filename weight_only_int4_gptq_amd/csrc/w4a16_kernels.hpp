@@ -58,6 +58,7 @@ struct GemmArgs {
     int NT;                  // 16-column tiles = N / 16
     int nstrips;             // column strips = ceil(NT / tiles)
     int nunits;              // nstrips * S = grid size
+    int fuse;                // 1: the gate/up epilogue (see below), 0: plain C
 };
 
 // ---------------------------------------------------------------- LDS plan
@@ -377,12 +378,24 @@ __global__ void __launch_bounds__(64 * KW) gemm_kernel(GemmArgs p) {
     const LdsLayout L = lds_layout(PATH, ASRC, M, Gwg, T, KW, D);
     const DequantConsts kc = dequant_consts();
 
+    // Tiles of this strip.  Plain: T consecutive tiles.  Gate/up epilogue
+    // (T even): the first T/2 slots hold gate tiles strip*T/2 + t, the last
+    // T/2 the up tiles of the same columns, NT/2 tiles further on.
+    constexpr int kHalfT = T / 2;
+    auto tile_of = [&](int t) {
+        if (p.fuse) return t < kHalfT ? strip * kHalfT + t : (p.NT >> 1) + strip * kHalfT + (t - kHalfT);
+        return strip * T + t;
+    };
+    auto tile_ok = [&](int t) {
+        return p.fuse ? strip * kHalfT + (t < kHalfT ? t : t - kHalfT) < (p.NT >> 1) : strip * T + t < p.NT;
+    };
+
     // wave-uniform bases (scalar) and per-lane byte offsets (vector, fixed)
     const uint8_t *wbase[T];
     const uint8_t *sbase[T];
 #pragma unroll
     for (int t = 0; t < T; ++t) {
-        const size_t tile = (size_t)min(strip * T + t, p.NT - 1);
+        const size_t tile = (size_t)min(tile_of(t), p.NT - 1);
         wbase[t] = reinterpret_cast<const uint8_t *>(p.blob) + tile * (size_t)p.G * 1024;
         sbase[t] = reinterpret_cast<const uint8_t *>(p.scales) + tile * (size_t)p.G * 32;
     }
@@ -664,31 +677,50 @@ __global__ void __launch_bounds__(64 * KW) gemm_kernel(GemmArgs p) {
             for (int m = 0; m < MM; ++m) acc[t][m] = sum_quarters(acc[t][m]);
     }
 
-    // ---- 5. epilogue: fixed-order reduction over wavefronts, then C or partials
+    // ---- 5. epilogue: fixed-order reduction over wavefronts, then C, the
+    //         gate/up output, or split-K partials
+    //
+    // Gate/up epilogue: H[m][j] = silu(C[m][j]) * C[m][j + N/2] for
+    // j < N/2, silu(x) = x / (1 + exp(-x)), on the fp32 sums, one bf16
+    // rounding at the end; H has N/2 columns.
     const int NV = T * M * 16;   // values (t, m, c) of this workgroup
-    auto emit = [&](int t, int m, int cc, float val) {
-        const int tile = strip * T + t;
-        if (tile >= p.NT) return;
-        const size_t n = (size_t)tile * 16 + cc;
-        if (p.S == 1)
-            p.C[(size_t)m * p.N + n] = f32_to_bf16_rne(val);
-        else   // device-coherent store (the XCDs' L2s are not coherent with each other)
-            __hip_atomic_store(&p.part[((size_t)z * M + m) * p.N + n], val, __ATOMIC_RELAXED,
-                               __HIP_MEMORY_SCOPE_AGENT);
+    auto col_of = [&](int t, int cc) { return (size_t)tile_of(t) * 16 + cc; };
+    auto emit_c = [&](int t, int m, int cc, float val) {      // plain, one split
+        p.C[(size_t)m * p.N + col_of(t, cc)] = f32_to_bf16_rne(val);
+    };
+    auto emit_h = [&](int t, int m, int cc, float g, float u) {   // gate/up, one split
+        const float hv = g / (1.0f + expf(-g)) * u;
+        p.C[(size_t)m * (p.N >> 1) + col_of(t, cc)] = f32_to_bf16_rne(hv);
+    };
+    auto emit_part = [&](int t, int m, int cc, float val) {   // split-K partial
+        // device-coherent store (the XCDs' L2s are not coherent with each other)
+        __hip_atomic_store(&p.part[((size_t)z * M + m) * p.N + col_of(t, cc)], val, __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
     };
 
     if constexpr (KW == 1) {
+        // lane (c, h) holds rows 4h + v (MFMA) or, in lanes h == 0, all rows (GEMV)
+        auto row_val = [&](int t, int i) { return acc[t][i]; };
+        constexpr int kRows = (PATH == PATH_MFMA) ? kRowsV : MM;
+        const bool holder = (PATH == PATH_MFMA) || h == 0;
+        auto row_of = [&](int i) { return PATH == PATH_MFMA ? 4 * h + i : i; };
+        if (holder) {
+            if (p.S > 1 || !p.fuse) {
 #pragma unroll
-        for (int t = 0; t < T; ++t) {
-            if constexpr (PATH == PATH_MFMA) {
+                for (int t = 0; t < T; ++t)
 #pragma unroll
-                for (int v = 0; v < kRowsV; ++v)
-                    if (4 * h + v < M) emit(t, 4 * h + v, c, acc[t][v]);
+                    for (int i = 0; i < kRows; ++i)
+                        if (row_of(i) < M && tile_ok(t)) {
+                            if (p.S > 1) emit_part(t, row_of(i), c, row_val(t, i));
+                            else emit_c(t, row_of(i), c, row_val(t, i));
+                        }
             } else {
-                if (h == 0) {
 #pragma unroll
-                    for (int m = 0; m < MM; ++m) emit(t, m, c, acc[t][m]);
-                }
+                for (int t = 0; t < kHalfT; ++t)
+#pragma unroll
+                    for (int i = 0; i < kRows; ++i)
+                        if (row_of(i) < M && tile_ok(t))
+                            emit_h(t, row_of(i), c, row_val(t, i), row_val(t + kHalfT, i));
             }
         }
     } else {
@@ -708,15 +740,30 @@ __global__ void __launch_bounds__(64 * KW) gemm_kernel(GemmArgs p) {
             }
         }
         lds_barrier();   // LDS only: the clamped refills still in flight need no wait
+        auto reduced = [&](int t, int mc) {
+            const int e = t * M * 16 + mc;
+            float s = red[e];
 #pragma unroll
-        for (int t = 0; t < T; ++t)
-            for (int mc = threadIdx.x; mc < M * 16; mc += 64 * KW) {
-                const int e = t * M * 16 + mc;
-                float s = red[e];
+            for (int w = 1; w < KW; ++w) s += red[w * NV + e];
+            return s;
+        };
+        if (p.S > 1 || !p.fuse) {
 #pragma unroll
-                for (int w = 1; w < KW; ++w) s += red[w * NV + e];
-                emit(t, mc >> 4, mc & 15, s);
-            }
+            for (int t = 0; t < T; ++t)
+                for (int mc = threadIdx.x; mc < M * 16; mc += 64 * KW) {
+                    if (!tile_ok(t)) continue;
+                    const float s = reduced(t, mc);
+                    if (p.S > 1) emit_part(t, mc >> 4, mc & 15, s);
+                    else emit_c(t, mc >> 4, mc & 15, s);
+                }
+        } else {
+#pragma unroll
+            for (int t = 0; t < kHalfT; ++t)
+                for (int mc = threadIdx.x; mc < M * 16; mc += 64 * KW) {
+                    if (!tile_ok(t)) continue;
+                    emit_h(t, mc >> 4, mc & 15, reduced(t, mc), reduced(t + kHalfT, mc));
+                }
+        }
     }
 
     if (p.S > 1) {
@@ -734,19 +781,29 @@ __global__ void __launch_bounds__(64 * KW) gemm_kernel(GemmArgs p) {
         }
         lds_barrier();
         if (s_last) {
+            auto summed = [&](int t, int m, int cc) {
+                float s = 0.0f;
+                for (int zz = 0; zz < p.S; ++zz)
+                    s += __hip_atomic_load(&p.part[((size_t)zz * M + m) * p.N + col_of(t, cc)],
+                                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                return s;
+            };
+            if (!p.fuse) {
 #pragma unroll
-            for (int t = 0; t < T; ++t)
-                for (int mc = threadIdx.x; mc < M * 16; mc += 64 * KW) {
-                    const int m = mc >> 4, cc = mc & 15;
-                    const int tile = strip * T + t;
-                    if (tile >= p.NT) continue;
-                    const size_t n = (size_t)tile * 16 + cc;
-                    float s = 0.0f;
-                    for (int zz = 0; zz < p.S; ++zz)
-                        s += __hip_atomic_load(&p.part[((size_t)zz * M + m) * p.N + n], __ATOMIC_RELAXED,
-                                               __HIP_MEMORY_SCOPE_AGENT);
-                    p.C[(size_t)m * p.N + n] = f32_to_bf16_rne(s);
-                }
+                for (int t = 0; t < T; ++t)
+                    for (int mc = threadIdx.x; mc < M * 16; mc += 64 * KW) {
+                        if (!tile_ok(t)) continue;
+                        emit_c(t, mc >> 4, mc & 15, summed(t, mc >> 4, mc & 15));
+                    }
+            } else {
+#pragma unroll
+                for (int t = 0; t < kHalfT; ++t)
+                    for (int mc = threadIdx.x; mc < M * 16; mc += 64 * KW) {
+                        if (!tile_ok(t)) continue;
+                        const int m = mc >> 4, cc = mc & 15;
+                        emit_h(t, m, cc, summed(t, m, cc), summed(t + kHalfT, m, cc));
+                    }
+            }
             if (threadIdx.x == 0)
                 __hip_atomic_store(&p.count[strip], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }

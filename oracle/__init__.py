@@ -297,6 +297,12 @@ def gemm_silu_mul(A: np.ndarray, qweight: np.ndarray, scales: np.ndarray, M: int
     return H, E
 
 
+def row_argmax(C: np.ndarray) -> np.ndarray:
+    """Column of each row's largest value, the lowest one among equal values
+    (numpy's argmax returns the first occurrence; -0 and +0 compare equal)."""
+    return np.argmax(np.asarray(C, dtype=np.float64), axis=1)
+
+
 def normalized_error(C_test: np.ndarray, C_ref: np.ndarray, D_ref: np.ndarray) -> np.ndarray:
     """Per-output error |C_test - C_ref| / D_ref.
 

@@ -370,3 +370,28 @@ def test_gemm_silu_mul_column_subset_and_bound():
     eps = 1e-6
     H2 = oracle.silu(g + eps * dg) * (u - eps * du)
     assert np.all(np.abs(H2 - H) <= eps * E * 1.01 + 1e-15)
+
+
+# ----------------------------------------------------------------- greedy pick
+
+def test_row_argmax_ties_and_signed_zero():
+    C = np.array([[1.0, 3.0, 3.0, 2.0],
+                  [-0.0, 0.0, -1.0, -0.0],
+                  [-5.0, -4.0, -4.0, -7.0],
+                  [np.nan, 1.0, 2.0, 0.5]])
+    got = oracle.row_argmax(C)
+    assert got[0] == 1          # lowest of the equal maxima
+    assert got[1] == 0          # -0 == +0: the first of them
+    assert got[2] == 1
+    assert got.dtype.kind == "i"
+    # on the gemm: a one-hot A picks row k of W, so the argmax is the column
+    # of the largest (q - 8) * s in that row
+    K, N, k = 256, 48, 77
+    rng = np.random.default_rng(9)
+    qw = rng.integers(0, 2 ** 32, size=(K // 8, N), dtype=np.uint32)
+    sc = oracle.f32_exact_to_bf16_bits(np.abs(rng.standard_normal((K // 128, N))).astype(np.float32))
+    A = np.zeros((1, K), dtype=np.uint16)
+    A[0, k] = 0x3F80
+    C, _ = oracle.gemm(A, qw, sc, 1, N, K)
+    W = oracle.dequant(qw, sc, K, N)
+    assert oracle.row_argmax(C)[0] == int(np.argmax(W[k]))

@@ -374,6 +374,19 @@ def sweep(torch, w4, args):
                                   "us_per_call": round(ms * 1e3, 3), "GBps": round(nb / (ms * 1e-3) / 1e9, 1),
                                   "pct_peak": round(100 * nb / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 2),
                                   "sets": sets}), flush=True)
+        if wname == "lm_head":
+            # the same weights with the row-argmax epilogue (the greedy pick)
+            for M in Ms:
+                def acall(i, M=M):
+                    j = i % prob.sets
+                    w4.gemm_argmax(prob.acts[j][:M], prob.blobs[j], prob.scales[j], prob.N)
+                steps = max(20, min(args.steps, int(2e6 / synth.algorithmic_bytes(M, wl.N, wl.K) * 100)))
+                ms = time_graph(torch, acall, steps, min(args.warmup, 20))
+                nb = synth.algorithmic_bytes_argmax(M, wl.N, wl.K)
+                print(json.dumps({"workload": "lm_head_argmax", "M": M, "K": wl.K, "N": wl.N,
+                                  "us_per_call": round(ms * 1e3, 3), "GBps": round(nb / (ms * 1e-3) / 1e9, 1),
+                                  "pct_peak": round(100 * nb / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 2),
+                                  "sets": sets}), flush=True)
         del prob
         torch.cuda.empty_cache()
 

@@ -219,6 +219,40 @@ int w4a16_gemm_silu_mul_plan(const void *A, const void *wq_repacked, const void 
                              size_t workspace_bytes, const w4a16_plan_t *plan, void *stream);
 
 /*
+ * Output projection with the greedy pick in its epilogue: for each row m,
+ *
+ *     idx[m] = the column n of the largest C[m][n] = (A . dequant)[m][n]
+ *              (the lowest such n among equal values; -0 equals +0),
+ *     val[m] = that C[m][n] as fp32,
+ *
+ * the model's greedy token for each verified position.  The output
+ * projection is one of the row-count dispatched kernels (page "Qwen3.8-27B
+ * on single DGX Spark ...", section "How."); a drafted token is kept only if
+ * the full model agrees with it (page "One Config Line Made My 27B Model
+ * 2.7x Faster", section "Three caveats worth stating plainly"), which under
+ * greedy decoding means it equals this argmax.  C is never stored.
+ * The decision is taken on the kernel's fp32 sums.
+ *   idx, val     device int32 [M] and fp32 [M] (written), 4-byte aligned
+ *   workspace    device, at least W4A16_ARGMAX_WORKSPACE_BYTES, zero-filled
+ *                before its first use.  The call uses only the counter region
+ *                (see the split-K layout) and leaves it zero again, so one
+ *                workspace serves argmax and split-K calls alike in stream
+ *                order (not calls that run concurrently)
+ *   other arguments as w4a16_gemm.  Plans must have splits == 1.
+ * Two kernels are enqueued: the matmul, whose workgroups leave their row
+ * maxima in the workspace, and a one-workgroup fold that writes idx and val.
+ */
+#define W4A16_ARGMAX_WORKSPACE_BYTES W4A16_SPLIT_COUNTER_BYTES   /* its counter region only */
+int w4a16_gemm_argmax(const void *A, const void *wq_repacked, const void *scales, int *idx,
+                      float *val, int M, int N, int K, int group, void *workspace,
+                      size_t workspace_bytes, void *stream);
+
+/* As w4a16_gemm_argmax with an explicit plan (splits must be 1). */
+int w4a16_gemm_argmax_plan(const void *A, const void *wq_repacked, const void *scales, int *idx,
+                           float *val, int M, int N, int K, int group, void *workspace,
+                           size_t workspace_bytes, const w4a16_plan_t *plan, void *stream);
+
+/*
  * Test export of the device dequantization used by both GEMM paths:
  * W[k][n] = (q - 8) * s as fp32 (exact), device fp32 [K][N] (written);
  * `scales` are the repacked scales.

@@ -114,6 +114,11 @@ def algorithmic_bytes_silu_mul(M: int, N: int, K: int) -> int:
     return K * N // 2 + (K // GROUP) * N * 2 + M * K * 2 + M * (N // 2) * 2
 
 
+def algorithmic_bytes_argmax(M: int, N: int, K: int) -> int:
+    """Bytes of the output projection with its row argmax: codes, scales, A, and M (index, value) pairs."""
+    return K * N // 2 + (K // GROUP) * N * 2 + M * K * 2 + M * 8
+
+
 def algorithmic_bytes(M: int, N: int, K: int) -> int:
     """Bytes one call must move at least: int4 codes, bf16 scales, bf16 A, bf16 C."""
     return K * N // 2 + (K // GROUP) * N * 2 + M * K * 2 + M * N * 2

@@ -192,3 +192,27 @@ def test_silu_mul_without_device():
         pytest.skip("a GPU is present")
     assert _silu_mul() == -6
     assert _silu_mul(plan=w4.make_plan(w4.PATH_MFMA, 2, 4)) == -6
+
+
+def _argmax(A=P, wq=P, s=P, idx=P2, val=P2, M=1, N=1008, K=512, group=128, ws=P, wsb=65536, plan=None):
+    L = w4.lib()
+    if plan is None:
+        return L.w4a16_gemm_argmax(A, wq, s, idx, val, M, N, K, group, ws, wsb, NULL)
+    return L.w4a16_gemm_argmax_plan(A, wq, s, idx, val, M, N, K, group, ws, wsb, ctypes.byref(plan), NULL)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(idx=NULL), -1), (dict(val=NULL), -1), (dict(A=NULL), -1), (dict(M=17), -2), (dict(N=1000), -2),
+    (dict(group=64), -3), (dict(idx=ctypes.c_void_p(0x20002)), -4),
+    (dict(wsb=65535), -5), (dict(ws=NULL), -5),
+    (dict(plan=w4.make_plan(w4.PATH_MFMA, 1, 4, 2)), -8),      # splits must be 1
+])
+def test_argmax_argument_errors(kw, status):
+    assert _argmax(**kw) == status
+
+
+def test_argmax_without_device():
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present")
+    assert _argmax() == -6          # N = 1008: a multiple of 16 is enough here

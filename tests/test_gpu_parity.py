@@ -402,3 +402,106 @@ def test_silu_mul_gate_up_workload(M):
     torch.cuda.synchronize()
     note(f"[silu-mul gate_up] M={M} plan={w4.get_plan(M, N, K).as_dict()}")
     silu_mul_check(H[:, torch.from_numpy(js).to(DEV)], Href, E, M)
+
+
+# ------------------------------------------------------------- greedy pick (row argmax)
+
+def argmax_check(idx, val, C, D, what):
+    """Validity where several columns are within rounding of the maximum: the
+    chosen column's exact value is within the GEMM bound of the exact maximum,
+    the reported value within the bound of the chosen column's exact value;
+    and the exact winner is required wherever the top two are separated by
+    more than their bounds."""
+    idx = idx.cpu().numpy().astype(np.int64)
+    val = val.cpu().numpy().astype(np.float64)
+    best = oracle.row_argmax(C)
+    rows = np.arange(C.shape[0])
+    cg, cb = C[rows, idx], C[rows, best]
+    dg, db = D[rows, idx], D[rows, best]
+    assert np.all(cg >= cb - TOL * (dg + db)), (what, idx, best)
+    assert np.all(np.abs(val - cg) <= TOL * dg + 1e-30), (what, val, cg)
+    srt = np.sort(C, axis=1)
+    second = srt[:, -2]
+    d2 = np.take_along_axis(D, np.argsort(C, axis=1)[:, -2:-1], axis=1)[:, 0]
+    clear = (cb - second) > TOL * (db + d2)
+    assert np.array_equal(idx[clear], best[clear]), (what, idx, best)
+    return int(clear.sum())
+
+
+@pytest.mark.parametrize("K,N,seed", [(512, 1024, 40), (1152, 608, 41), (5120, 8192, 42)])
+def test_argmax_parity(K, N, seed):
+    A, qw, sc = synth.gen_problem(K, N, seed)
+    q, s, a = to_dev(qw, sc, A)
+    blob = w4.repack_weights(q, K, N)
+    C16, D16 = oracle.gemm(A, qw, sc, 16, N, K)
+    plans = [None] + [p for p in ALL_PLANS if p.splits == 1][::3]
+    for M in (1, 2, 4, 5, 9, 16):
+        cases = [p for p in plans if p is None or w4.plan_ok(M, N, K, p)]
+        note(f"[argmax] K={K} N={N} M={M}: {len(cases)} plans")
+        for p in cases:
+            idx, val = w4.gemm_argmax(a[:M].contiguous(), blob, s, N, plan=p)
+            torch.cuda.synchronize()
+            argmax_check(idx, val, C16[:M], D16[:M], (M, p))
+
+
+def test_argmax_planted_lm_head_unique_and_tie():
+    # lm_head geometry; row m's maximum is planted at column target[m] (its
+    # codes follow the signs of A[m], scale 1 against 0.01 elsewhere: a
+    # margin of thousands of units); row 0's is planted twice, identically,
+    # at two columns of different strips: the lower must win.
+    wl = synth.WORKLOADS["lm_head"]
+    K, N, M = wl.K, wl.N, 9
+    A, qw, sc = synth.gen_workload("lm_head", M)
+    qw = qw.copy()
+    sc = sc.copy()
+    rng = np.random.default_rng(43)
+    target = rng.choice(N, size=M, replace=False)
+    tie = int(target[0]) + 4096 * 16 + 3              # another strip, same row-0 pattern
+    a_val = oracle.bf16_bits_to_f64(A)
+    for m, n in list(enumerate(target)) + [(0, tie)]:
+        codes = np.where(a_val[m] > 0, 15, 0).astype(np.uint32)       # +7 / -8
+        words = np.zeros(K // 8, dtype=np.uint32)
+        for j in range(8):
+            words |= codes[j::8] << np.uint32(4 * j)
+        qw[:, n] = words
+        sc[:, n] = 0x3F80
+    q, s, a = to_dev(qw, sc, A)
+    blob = w4.repack_weights(q, K, N)
+    note(f"[argmax lm_head] targets={target.tolist()} tie={tie}")
+    for Mi in (1, 4, 9):
+        for rep in range(2):
+            idx, val = w4.gemm_argmax(a[:Mi].contiguous(), blob, s, N)
+            torch.cuda.synchronize()
+            got = idx.cpu().numpy()
+            want = target[:Mi].copy()
+            want[0] = min(int(target[0]), tie)
+            assert np.array_equal(got, want), (Mi, got, want)
+            # the reported value against the oracle at that column
+            Cc, Dc = oracle.gemm(A, qw, sc, Mi, N, K, cols=want)
+            v = val.cpu().numpy().astype(np.float64)
+            assert np.all(np.abs(v - np.diag(Cc)) <= TOL * np.diag(Dc)), (v, np.diag(Cc))
+
+
+def test_argmax_workspace_shared_with_split_k():
+    K, N = 1280, 528
+    A, qw, sc = synth.gen_problem(K, N, 44)
+    q, s, a = to_dev(qw, sc, A)
+    blob = w4.repack_weights(q, K, N)
+    C16, D16 = oracle.gemm(A, qw, sc, 16, N, K)
+    split = w4.make_plan(w4.PATH_MFMA, 2, 4, 4, w4.ASRC_RING)
+    ws = torch.zeros(w4.workspace_bytes(16, N, K, split), dtype=torch.uint8, device=DEV)
+    first = None
+    for rnd in range(3):
+        for M in (3, 16):
+            C = run_gemm(a, blob, s, N, M, plan=split, ws=ws)
+            assert max_err(C, C16[:M], D16[:M]) <= TOL
+            idx, val = w4.gemm_argmax(a[:M].contiguous(), blob, s, N, workspace=ws)
+            torch.cuda.synchronize()
+            argmax_check(idx, val, C16[:M], D16[:M], (rnd, M))
+            if M == 16:
+                if first is None:
+                    first = (idx.clone(), val.clone())
+                assert torch.equal(idx, first[0]) and torch.equal(val, first[1])
+    assert int(ws[:65536].view(torch.int32).abs().sum()) == 0
+    with pytest.raises(w4.W4A16Error):
+        w4.gemm_argmax(a[:2].contiguous(), blob, s, N, plan=split, workspace=ws)   # splits must be 1

@@ -67,11 +67,14 @@ def lib():
         L.w4a16_gemm.argtypes = [P, P, P, P, I, I, I, I, P, S, P]
         L.w4a16_gemm_plan.argtypes = [P, P, P, P, I, I, I, I, P, S, ctypes.POINTER(Plan), P]
         L.w4a16_gemm_silu_mul.argtypes = [P, P, P, P, I, I, I, I, P, S, P]
+        L.w4a16_gemm_argmax.argtypes = [P, P, P, P, P, I, I, I, I, P, S, P]
+        L.w4a16_gemm_argmax_plan.argtypes = [P, P, P, P, P, I, I, I, I, P, S, ctypes.POINTER(Plan), P]
         L.w4a16_gemm_silu_mul_plan.argtypes = [P, P, P, P, I, I, I, I, P, S, ctypes.POINTER(Plan), P]
         L.w4a16_dequant.argtypes = [P, P, P, I, I, P]
         L.w4a16_unpack.argtypes = [P, P, I, I, P]
         for f in ("w4a16_repack_weights", "w4a16_get_plan", "w4a16_gemm", "w4a16_gemm_plan",
-                  "w4a16_gemm_silu_mul", "w4a16_gemm_silu_mul_plan", "w4a16_dequant", "w4a16_unpack"):
+                  "w4a16_gemm_silu_mul", "w4a16_gemm_silu_mul_plan", "w4a16_gemm_argmax",
+                  "w4a16_gemm_argmax_plan", "w4a16_dequant", "w4a16_unpack"):
             getattr(L, f).restype = I
         _lib = L
     return _lib
@@ -205,6 +208,32 @@ def gemm_silu_mul(A: torch.Tensor, blob: torch.Tensor, scales: torch.Tensor, N: 
                                             _ptr(workspace), ws_bytes, ctypes.byref(plan), _stream(A))
     _check(st, "w4a16_gemm_silu_mul")
     return out
+
+
+ARGMAX_WORKSPACE_BYTES = 65536   # the workspace's counter region
+
+
+def gemm_argmax(A: torch.Tensor, blob: torch.Tensor, scales: torch.Tensor, N: int,
+                plan: Plan | None = None, workspace: torch.Tensor | None = None, group: int = GROUP):
+    """Per-row argmax of C = A . dequant(W) (lowest column among equal values).
+
+    Returns (idx int32 [M], val float32 [M]) device tensors.
+    """
+    M, K = A.shape
+    idx = torch.empty(M, dtype=torch.int32, device=A.device)
+    val = torch.empty(M, dtype=torch.float32, device=A.device)
+    if workspace is None:
+        workspace = _shared_workspace(A.device, ARGMAX_WORKSPACE_BYTES)
+    ws_bytes = workspace.numel() * workspace.element_size()
+    if plan is None:
+        st = lib().w4a16_gemm_argmax(_ptr(A), _ptr(blob), _ptr(scales), _ptr(idx), _ptr(val), M, N, K,
+                                     group, _ptr(workspace), ws_bytes, _stream(A))
+    else:
+        st = lib().w4a16_gemm_argmax_plan(_ptr(A), _ptr(blob), _ptr(scales), _ptr(idx), _ptr(val), M, N,
+                                          K, group, _ptr(workspace), ws_bytes, ctypes.byref(plan),
+                                          _stream(A))
+    _check(st, "w4a16_gemm_argmax")
+    return idx, val
 
 
 def dequant(blob: torch.Tensor, scales: torch.Tensor, K: int, N: int) -> torch.Tensor:

@@ -260,6 +260,10 @@ hipError_t launch(const void *fn, unsigned grid, unsigned block, size_t lds, hip
     return hipLaunchKernel(fn, dim3(grid), dim3(block), args, lds, stream);
 }
 
+static_assert(kArgmaxBinOffset + kArgmaxBins * 16 * 8 <= W4A16_ARGMAX_WORKSPACE_BYTES &&
+                  W4A16_ARGMAX_WORKSPACE_BYTES <= W4A16_SPLIT_COUNTER_BYTES,
+              "argmax counter and bins live in the workspace's counter region");
+
 // The gate/up epilogue needs strips of gate/up tile pairs: an even tile
 // count.  The automatic plan is moved to two tiles when it has one.
 void fuse_plan(int M, w4a16_plan_t *p) {
@@ -274,28 +278,37 @@ void fuse_plan(int M, w4a16_plan_t *p) {
     *p = q;
 }
 
-// fuse: 0 plain C[M][N]; 1 the gate/up epilogue, C is H[M][N/2]
+// fuse: 0 plain C[M][N]; 1 the gate/up epilogue, C is H[M][N/2]; 2 the row
+// argmax (C unused, results in idx / val)
 int run_gemm(const void *A, const void *wq, const void *scales, void *C, int M, int N, int K,
              int group, void *workspace, size_t workspace_bytes, const w4a16_plan_t *user,
-             void *stream, int fuse = 0) {
-    if (!A || !wq || !scales || !C) return W4A16_ERR_NULL;
+             void *stream, int fuse = 0, int *idx = nullptr, float *val = nullptr) {
+    if (!A || !wq || !scales) return W4A16_ERR_NULL;
+    if (fuse == 2 ? (!idx || !val) : !C) return W4A16_ERR_NULL;
     int st = check_shape(M, N, K);
     if (st != W4A16_OK) return st;
-    if (fuse && N % 32 != 0) return W4A16_ERR_SHAPE;
+    if (fuse == 1 && N % 32 != 0) return W4A16_ERR_SHAPE;
     if (group != W4A16_GROUP) return W4A16_ERR_GROUP;
-    if (!aligned16(A) || !aligned16(wq) || !aligned16(scales) || !aligned16(C))
+    if (!aligned16(A) || !aligned16(wq) || !aligned16(scales) || (fuse != 2 && !aligned16(C)))
         return W4A16_ERR_ALIGN;
+    if (fuse == 2 && (((uintptr_t)idx | (uintptr_t)val) & 3)) return W4A16_ERR_ALIGN;
     w4a16_plan_t p;
     if (user) {
         p = *user;
         st = validate_plan(p, M, N, K);
         if (st != W4A16_OK) return st;
-        if (fuse && p.tiles % 2 != 0) return W4A16_ERR_PLAN;
+        if (fuse == 1 && p.tiles % 2 != 0) return W4A16_ERR_PLAN;
+        if (fuse == 2 && p.splits != 1) return W4A16_ERR_PLAN;
     } else {
         auto_plan(M, N, K, &p);
-        if (fuse) fuse_plan(M, &p);
+        if (fuse == 1) fuse_plan(M, &p);
+        if (fuse == 2 && p.splits != 1) {
+            p.splits = 1;
+            if (validate_plan(p, M, N, K) != W4A16_OK) p.asrc = W4A16_ASRC_RING;
+            if (validate_plan(p, M, N, K) != W4A16_OK) p.asrc = W4A16_ASRC_GLOBAL;
+        }
     }
-    const size_t need = workspace_for(p, M, N);
+    const size_t need = fuse == 2 ? (size_t)W4A16_ARGMAX_WORKSPACE_BYTES : workspace_for(p, M, N);
     if (need > 0) {
         if (!workspace || workspace_bytes < need) return W4A16_ERR_WORKSPACE;
         if (!aligned16(workspace)) return W4A16_ERR_ALIGN;
@@ -338,7 +351,9 @@ int run_gemm(const void *A, const void *wq, const void *scales, void *C, int M, 
     a.nstrips = (a.NT + p.tiles - 1) / p.tiles;
     a.nunits = a.nstrips * a.S;
     a.fuse = fuse;
-    if (need > 0) {
+    a.amax_idx = idx;
+    a.amax_val = val;
+    if (need > 0) {   // split-K partials or argmax bins: the counter region first
         a.count = static_cast<uint32_t *>(workspace);
         a.part = reinterpret_cast<float *>(static_cast<char *>(workspace) + W4A16_SPLIT_COUNTER_BYTES);
     } else {
@@ -346,9 +361,16 @@ int run_gemm(const void *A, const void *wq, const void *scales, void *C, int M, 
         a.count = nullptr;
     }
     void *args[] = {&a};
-    const hipError_t e = launch(reinterpret_cast<const void *>(v->fn), (unsigned)a.nunits,
-                                64u * (unsigned)p.kwaves, (size_t)lds,
-                                static_cast<hipStream_t>(stream), args);
+    hipError_t e = launch(reinterpret_cast<const void *>(v->fn), (unsigned)a.nunits,
+                          64u * (unsigned)p.kwaves, (size_t)lds, static_cast<hipStream_t>(stream), args);
+    if (e == hipSuccess && fuse == 2) {
+        // fold the per-bin row maxima (stream order: after every atomic above)
+        unsigned long long *bins = reinterpret_cast<unsigned long long *>(
+            static_cast<char *>(workspace) + kArgmaxBinOffset);
+        hipLaunchKernelGGL(argmax_fold_kernel, dim3(1), dim3(kArgmaxBins * 16), 0,
+                           static_cast<hipStream_t>(stream), bins, M, idx, val);
+        e = hipGetLastError();
+    }
     return e == hipSuccess ? W4A16_OK : W4A16_ERR_LAUNCH;
 }
 
@@ -457,6 +479,20 @@ int w4a16_gemm_plan(const void *A, const void *wq_repacked, const void *scales, 
                     const w4a16_plan_t *plan, void *stream) {
     return run_gemm(A, wq_repacked, scales, C, M, N, K, group, workspace, workspace_bytes, plan,
                     stream);
+}
+
+int w4a16_gemm_argmax(const void *A, const void *wq_repacked, const void *scales, int *idx,
+                      float *val, int M, int N, int K, int group, void *workspace,
+                      size_t workspace_bytes, void *stream) {
+    return run_gemm(A, wq_repacked, scales, nullptr, M, N, K, group, workspace, workspace_bytes,
+                    nullptr, stream, 2, idx, val);
+}
+
+int w4a16_gemm_argmax_plan(const void *A, const void *wq_repacked, const void *scales, int *idx,
+                           float *val, int M, int N, int K, int group, void *workspace,
+                           size_t workspace_bytes, const w4a16_plan_t *plan, void *stream) {
+    return run_gemm(A, wq_repacked, scales, nullptr, M, N, K, group, workspace, workspace_bytes,
+                    plan, stream, 2, idx, val);
 }
 
 int w4a16_gemm_silu_mul(const void *A, const void *wq_repacked, const void *scales, void *H, int M,

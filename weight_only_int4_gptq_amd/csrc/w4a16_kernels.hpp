@@ -58,12 +58,22 @@ struct GemmArgs {
     int NT;                  // 16-column tiles = N / 16
     int nstrips;             // column strips = ceil(NT / tiles)
     int nunits;              // nstrips * S = grid size
-    int fuse;                // 1: the gate/up epilogue (see below), 0: plain C
+    int fuse;                // epilogue: 0 plain C, 1 gate/up activation, 2 row argmax
+    int *amax_idx;           // row argmax: column of each row's maximum [M]
+    float *amax_val;         // row argmax: its fp32 value [M]
 };
+
+// Row argmax: per-row maxima meet in kArgmaxBins 64-bit slots per row
+// (workgroup index modulo the bin count), kept in the workspace's counter
+// region at byte kArgmaxBinOffset; its counter is the region's first word.
+// Every call leaves the region zero, whichever kind of call it is.
+constexpr int kArgmaxBins = 64;
+constexpr int kArgmaxBinOffset = 256;
 
 // ---------------------------------------------------------------- LDS plan
 // Shared by host (sizing) and device (carving).  Offsets in bytes.
 struct LdsLayout {
+    int keys;   // row argmax: one 64-bit key per row [16]
     int a;      // staged A rows [M][Gwg*128 bf16 + pad]; ring: [KW][D][16 rows][256 B]
     int bias;   // GEMV: bias of each 32-row quarter [M][Gwg][4] fp32;
                 // MFMA with staged A: bias tile rows [Gwg][16] fp32
@@ -77,6 +87,8 @@ __host__ __device__ inline LdsLayout lds_layout(int path, int asrc, int M, int G
     const bool stage = (path == PATH_GEMV) || (asrc == ASRC_LDS);
     L.row = Gwg * kGroup * 2 + kRowPad;
     int off = 0;
+    L.keys = off;
+    off += 16 * 8;
     L.a = off;
     if (stage) off += M * L.row;
     else if (path == PATH_MFMA && asrc == ASRC_RING) off += KW * D * kRingSlotBytes;
@@ -157,6 +169,19 @@ __device__ __forceinline__ float bf16_bits_to_f32(uint32_t bits16) {
 __device__ __forceinline__ float pair_lo(uint32_t pair) { return __uint_as_float(pair << 16); }
 __device__ __forceinline__ float pair_hi(uint32_t pair) { return __uint_as_float(pair & 0xFFFF0000u); }
 
+// Order-preserving 64-bit key of (value, column): a larger value gives a
+// larger key, and for equal values the lower column does (-0 counts as +0).
+__device__ __forceinline__ unsigned long long argmax_key(float v, uint32_t col) {
+    uint32_t u = __float_as_uint(v == 0.0f ? 0.0f : v);
+    u = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+    return ((unsigned long long)u << 32) | (0xFFFFFFFFu - col);
+}
+__device__ __forceinline__ float argmax_key_value(unsigned long long k) {
+    uint32_t u = (uint32_t)(k >> 32);
+    u = (u & 0x80000000u) ? (u & 0x7FFFFFFFu) : ~u;
+    return __uint_as_float(u);
+}
+
 // fp32 -> bf16, round to nearest even (NaN stays a quiet NaN).
 __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
     uint32_t u = __float_as_uint(f);
@@ -228,6 +253,30 @@ __device__ __forceinline__ void lds_dma16(const void *gsrc, uint32_t lds_base) {
 
 __device__ __forceinline__ uint32_t lds_addr(const void *p) {
     return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void *)p;
+}
+
+// ---------------------------------------------------------------- row argmax fold
+// One workgroup of kArgmaxBins * 16 threads: thread (b, m) reads bin b of row
+// m and clears it; the rows' maxima meet in LDS; thread m < M writes the
+// column and value of row m.
+__global__ void __launch_bounds__(kArgmaxBins * 16) argmax_fold_kernel(unsigned long long *__restrict__ bins,
+                                                                       int M, int *__restrict__ idx,
+                                                                       float *__restrict__ val) {
+    __shared__ unsigned long long best[16];
+    const int m = threadIdx.x & 15, b = threadIdx.x >> 4;
+    if (threadIdx.x < 16) best[threadIdx.x] = 0ull;
+    __syncthreads();
+    if (m < M) {
+        const unsigned long long k = bins[b * 16 + m];
+        bins[b * 16 + m] = 0ull;
+        if (k) __hip_atomic_fetch_max(&best[m], k, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    }
+    __syncthreads();
+    if (threadIdx.x < (unsigned)M) {
+        const unsigned long long k = best[threadIdx.x];
+        idx[threadIdx.x] = (int)(0xFFFFFFFFu - (uint32_t)k);
+        val[threadIdx.x] = argmax_key_value(k);
+    }
 }
 
 // ---------------------------------------------------------------- repack
@@ -383,11 +432,11 @@ __global__ void __launch_bounds__(64 * KW) gemm_kernel(GemmArgs p) {
     // T/2 the up tiles of the same columns, NT/2 tiles further on.
     constexpr int kHalfT = T / 2;
     auto tile_of = [&](int t) {
-        if (p.fuse) return t < kHalfT ? strip * kHalfT + t : (p.NT >> 1) + strip * kHalfT + (t - kHalfT);
+        if (p.fuse == 1) return t < kHalfT ? strip * kHalfT + t : (p.NT >> 1) + strip * kHalfT + (t - kHalfT);
         return strip * T + t;
     };
     auto tile_ok = [&](int t) {
-        return p.fuse ? strip * kHalfT + (t < kHalfT ? t : t - kHalfT) < (p.NT >> 1) : strip * T + t < p.NT;
+        return p.fuse == 1 ? strip * kHalfT + (t < kHalfT ? t : t - kHalfT) < (p.NT >> 1) : strip * T + t < p.NT;
     };
 
     // wave-uniform bases (scalar) and per-lane byte offsets (vector, fixed)
@@ -704,7 +753,20 @@ __global__ void __launch_bounds__(64 * KW) gemm_kernel(GemmArgs p) {
         constexpr int kRows = (PATH == PATH_MFMA) ? kRowsV : MM;
         const bool holder = (PATH == PATH_MFMA) || h == 0;
         auto row_of = [&](int i) { return PATH == PATH_MFMA ? 4 * h + i : i; };
-        if (holder) {
+        if (p.fuse == 2) {
+            unsigned long long *keys = reinterpret_cast<unsigned long long *>(smem + L.keys);
+            if (threadIdx.x < 16) keys[threadIdx.x] = 0ull;
+            lds_barrier();
+            if (holder) {
+#pragma unroll
+                for (int t = 0; t < T; ++t)
+#pragma unroll
+                    for (int i = 0; i < kRows; ++i)
+                        if (row_of(i) < M && tile_ok(t))
+                            __hip_atomic_fetch_max(&keys[row_of(i)], argmax_key(row_val(t, i), (uint32_t)col_of(t, c)),
+                                                   __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+            }
+        } else if (holder) {
             if (p.S > 1 || !p.fuse) {
 #pragma unroll
                 for (int t = 0; t < T; ++t)
@@ -747,7 +809,18 @@ __global__ void __launch_bounds__(64 * KW) gemm_kernel(GemmArgs p) {
             for (int w = 1; w < KW; ++w) s += red[w * NV + e];
             return s;
         };
-        if (p.S > 1 || !p.fuse) {
+        if (p.fuse == 2) {
+            unsigned long long *keys = reinterpret_cast<unsigned long long *>(smem + L.keys);
+            if (threadIdx.x < 16) keys[threadIdx.x] = 0ull;
+            lds_barrier();
+#pragma unroll
+            for (int t = 0; t < T; ++t)
+                for (int mc = threadIdx.x; mc < M * 16; mc += 64 * KW) {
+                    if (!tile_ok(t)) continue;
+                    __hip_atomic_fetch_max(&keys[mc >> 4], argmax_key(reduced(t, mc), (uint32_t)col_of(t, mc & 15)),
+                                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+                }
+        } else if (p.S > 1 || !p.fuse) {
 #pragma unroll
             for (int t = 0; t < T; ++t)
                 for (int mc = threadIdx.x; mc < M * 16; mc += 64 * KW) {
@@ -764,6 +837,22 @@ __global__ void __launch_bounds__(64 * KW) gemm_kernel(GemmArgs p) {
                     emit_h(t, mc >> 4, mc & 15, reduced(t, mc), reduced(t + kHalfT, mc));
                 }
         }
+    }
+
+    if (p.fuse == 2) {
+        // Row argmax across workgroups (single split): this workgroup's row
+        // maxima go to its bin with device-scope 64-bit max atomics, issued
+        // and not waited for; the fold kernel that follows on the stream
+        // reads the bins.  Max is order-independent: the result does not
+        // depend on timing.
+        unsigned long long *keys = reinterpret_cast<unsigned long long *>(smem + L.keys);
+        unsigned long long *bins =
+            reinterpret_cast<unsigned long long *>(reinterpret_cast<uint8_t *>(p.count) + kArgmaxBinOffset);
+        lds_barrier();
+        if (threadIdx.x < (unsigned)M)
+            __hip_atomic_fetch_max(&bins[(blockIdx.x % kArgmaxBins) * 16 + threadIdx.x], keys[threadIdx.x],
+                                   __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        return;
     }
 
     if (p.S > 1) {

@@ -16,6 +16,7 @@ Prints ONE JSON line:
 --sweep prints one JSON line per (workload, M) instead (not the contract line);
 --stack times one decode step's full sequence of linear shapes.
 --ceiling measures a plain streaming read at the same byte counts.
+--tp-shards times one GPU's share of each linear under tensor parallelism.
 """
 from __future__ import annotations
 
@@ -266,6 +267,8 @@ def main():
     ap.add_argument("--stack", action="store_true", help="full decode-step sweep of linear shapes")
     ap.add_argument("--ceiling", action="store_true",
                     help="plain streaming-read bandwidth at the matmul byte counts (probe kernel)")
+    ap.add_argument("--tp-shards", action="store_true",
+                    help="one GPU's share of each decoder linear at TP = 2, 4, 8")
     ap.add_argument("--copy-calib", type=int, default=0, metavar="MIB",
                     help="after timing, copy MIB MiB a few times (reference for byte counters)")
     ap.add_argument("--summarize", nargs=3, metavar=("TRACE_DIR", "FETCH_DIR", "WRITE_DIR"),
@@ -294,6 +297,8 @@ def main():
         return stack(torch, w4, args)
     if args.ceiling:
         return ceiling(torch, w4, args)
+    if args.tp_shards:
+        return tp_shards(torch, w4, args)
 
     wl = synth.WORKLOADS[args.workload]
     M = args.m
@@ -437,6 +442,44 @@ def ceiling(torch, w4, args):
                           "launch": {"blocks": b, "threads": t, "unroll": u}, "buffer_sets": nbuf}), flush=True)
         del bufs
         torch.cuda.empty_cache()
+
+
+def tp_shards(torch, w4, args):
+    """One GPU's share of each decoder linear under tensor parallelism (TP = 2, 4, 8):
+    column shards (QKV; gate/up with its activation) and K shards with fp32
+    partial sums (attention output; down projection).  One JSON line per call."""
+    dev = torch.device("cuda:0")
+    shapes = [("qkv_cols", 5120, 8192, "cols"), ("o_rows", 6144, 5120, "rows"),
+              ("gate_up_cols_silu_mul", 5120, 34816, "cols_silu"), ("down_rows", 17408, 5120, "rows")]
+    for tp in (2, 4, 8):
+        for name, K, N, kind in shapes:
+            Ki, Ni = (K // tp, N) if kind == "rows" else (K, N // tp)
+            sets = sets_for(Ki, Ni, 1)
+            prob = Problem(torch, w4, Ki, Ni, Ki + Ni, "normal", sets)
+            f32_outs = [torch.empty((16, Ni), dtype=torch.float32, device=dev) for _ in range(sets)] \
+                if kind == "rows" else None
+            for M in (1, 8):
+                if kind == "rows":
+                    def call(i, M=M):
+                        j = i % sets
+                        w4.gemm_f32(prob.acts[j][:M], prob.blobs[j], prob.scales[j], Ni, out=f32_outs[j][:M])
+                    nb = synth.algorithmic_bytes_f32(M, Ni, Ki)
+                elif kind == "cols_silu":
+                    def call(i, M=M):
+                        j = i % sets
+                        w4.gemm_silu_mul(prob.acts[j][:M], prob.blobs[j], prob.scales[j], Ni, out=prob.houts[j][:M])
+                    nb = synth.algorithmic_bytes_silu_mul(M, Ni, Ki)
+                else:
+                    def call(i, M=M):
+                        prob.call(w4, M, i)
+                    nb = synth.algorithmic_bytes(M, Ni, Ki)
+                steps = max(20, min(args.steps, int(2e6 / nb * 100)))
+                ms = time_graph(torch, call, steps, min(args.warmup, 20))
+                print(json.dumps({"tp": tp, "call": name, "M": M, "K": Ki, "N": Ni,
+                                  "us_per_call": round(ms * 1e3, 3), "GBps": round(nb / (ms * 1e-3) / 1e9, 1),
+                                  "pct_peak": round(100 * nb / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 2)}), flush=True)
+            del prob, f32_outs
+            torch.cuda.empty_cache()
 
 
 def stack(torch, w4, args):

@@ -219,6 +219,25 @@ int w4a16_gemm_silu_mul_plan(const void *A, const void *wq_repacked, const void 
                              size_t workspace_bytes, const w4a16_plan_t *plan, void *stream);
 
 /*
+ * As w4a16_gemm, with C written as fp32 [M][N], not rounded: the partial sum
+ * of one K shard when a matmul is split by rows of W across GPUs (tensor
+ * parallelism, page "Qwen3.8 27B - NVFP4 for veloGB10", section "Running
+ * with veloGB10": two and four nodes).  A shard holds K_i rows of W (a
+ * multiple of 128: whole groups, with their scales) and the matching
+ * columns of A as its own [M][K_i] matrix; the shards' fp32 outputs are
+ * summed (an all-reduce) and rounded once.  Column shards need no mode of
+ * their own: they are matmuls of N_i columns.
+ *   C            device fp32 [M][N] (written), 16-byte aligned
+ */
+int w4a16_gemm_f32(const void *A, const void *wq_repacked, const void *scales, float *C, int M,
+                   int N, int K, int group, void *workspace, size_t workspace_bytes, void *stream);
+
+/* As w4a16_gemm_f32 with an explicit plan. */
+int w4a16_gemm_f32_plan(const void *A, const void *wq_repacked, const void *scales, float *C, int M,
+                        int N, int K, int group, void *workspace, size_t workspace_bytes,
+                        const w4a16_plan_t *plan, void *stream);
+
+/*
  * Output projection with the greedy pick in its epilogue: for each row m,
  *
  *     idx[m] = the column n of the largest C[m][n] = (A . dequant)[m][n]

@@ -119,6 +119,11 @@ def algorithmic_bytes_argmax(M: int, N: int, K: int) -> int:
     return K * N // 2 + (K // GROUP) * N * 2 + M * K * 2 + M * 8
 
 
+def algorithmic_bytes_f32(M: int, N: int, K: int) -> int:
+    """Bytes of a K shard's call: codes, scales, A, and fp32 partial sums C[M, N] written."""
+    return K * N // 2 + (K // GROUP) * N * 2 + M * K * 2 + M * N * 4
+
+
 def algorithmic_bytes(M: int, N: int, K: int) -> int:
     """Bytes one call must move at least: int4 codes, bf16 scales, bf16 A, bf16 C."""
     return K * N // 2 + (K // GROUP) * N * 2 + M * K * 2 + M * N * 2

@@ -505,3 +505,67 @@ def test_argmax_workspace_shared_with_split_k():
     assert int(ws[:65536].view(torch.int32).abs().sum()) == 0
     with pytest.raises(w4.W4A16Error):
         w4.gemm_argmax(a[:2].contiguous(), blob, s, N, plan=split, workspace=ws)   # splits must be 1
+
+
+# ------------------------------------------------------------- fp32 output, tensor-parallel shards
+
+@pytest.mark.parametrize("K,N,seed", [(512, 1024, 50), (1152, 592, 51)])
+def test_f32_output_parity(K, N, seed):
+    A, qw, sc = synth.gen_problem(K, N, seed)
+    q, s, a = to_dev(qw, sc, A)
+    blob = w4.repack_weights(q, K, N)
+    C16, D16 = oracle.gemm(A, qw, sc, 16, N, K)
+    worst = 0.0
+    for M in (1, 2, 4, 5, 8, 16):
+        cases = [None] + [p for p in ALL_PLANS if w4.plan_ok(M, N, K, p)][::2]
+        for p in cases:
+            C = w4.gemm_f32(a[:M].contiguous(), blob, s, N, plan=p)
+            torch.cuda.synchronize()
+            e = oracle.normalized_error(C.cpu().numpy().astype(np.float64), C16[:M], D16[:M])
+            worst = max(worst, float(e.max()))
+            assert e.max() <= TOL, (M, p, float(e.max()))
+            # the bf16 call rounds exactly these sums
+            if p is None:
+                Cb = run_gemm(a, blob, s, N, M)
+                assert torch.equal(Cb, C.to(torch.bfloat16))
+    note(f"  fp32 worst normalized error {worst:.3e}")
+
+
+@pytest.mark.parametrize("tp", [2, 4, 8])
+def test_tensor_parallel_row_shards_sum_to_the_full_matmul(tp):
+    # down projection geometry along K (17408 = 136 groups), narrow N: each
+    # shard holds K/tp rows of W (whole groups) and the matching columns of
+    # A; the fp32 shard outputs summed equal the full product within the bound
+    K, N = 17408, 512
+    A, qw, sc = synth.gen_problem(K, N, 52, act="silu_mul")
+    Cref, Dref = oracle.gemm(A, qw, sc, 16, N, K)
+    Ki = K // tp
+    total = None
+    for i in range(tp):
+        A_i = np.ascontiguousarray(A[:, i * Ki:(i + 1) * Ki])
+        qw_i = np.ascontiguousarray(qw[i * Ki // 8:(i + 1) * Ki // 8])
+        sc_i = np.ascontiguousarray(sc[i * Ki // 128:(i + 1) * Ki // 128])
+        q, s, a = to_dev(qw_i, sc_i, A_i)
+        blob = w4.repack_weights(q, Ki, N)
+        C_i = w4.gemm_f32(a, blob, s, N)
+        total = C_i if total is None else total + C_i
+    torch.cuda.synchronize()
+    e = oracle.normalized_error(total.cpu().numpy().astype(np.float64), Cref, Dref)
+    note(f"[tp rows] tp={tp} K_i={Ki} worst {e.max():.3e}")
+    assert e.max() <= TOL
+
+
+def test_tensor_parallel_column_shards():
+    # QKV geometry split four ways by columns: each shard is the matmul of
+    # its columns, equal to those columns of the full product
+    K, N, tp = 5120, 8192, 4
+    A, qw, sc = synth.gen_problem(K, N, 53)
+    q, s, a = to_dev(qw, sc, A)
+    full = run_gemm(a, w4.repack_weights(q, K, N), s, N, 4)
+    Ni = N // tp
+    for i in range(tp):
+        qw_i = np.ascontiguousarray(qw[:, i * Ni:(i + 1) * Ni])
+        sc_i = np.ascontiguousarray(sc[:, i * Ni:(i + 1) * Ni])
+        q_i, s_i, _ = to_dev(qw_i, sc_i)
+        C_i = run_gemm(a, w4.repack_weights(q_i, K, Ni), s_i, Ni, 4)
+        assert torch.equal(C_i, full[:, i * Ni:(i + 1) * Ni]), i

@@ -68,13 +68,16 @@ def lib():
         L.w4a16_gemm_plan.argtypes = [P, P, P, P, I, I, I, I, P, S, ctypes.POINTER(Plan), P]
         L.w4a16_gemm_silu_mul.argtypes = [P, P, P, P, I, I, I, I, P, S, P]
         L.w4a16_gemm_argmax.argtypes = [P, P, P, P, P, I, I, I, I, P, S, P]
+        L.w4a16_gemm_f32.argtypes = [P, P, P, P, I, I, I, I, P, S, P]
+        L.w4a16_gemm_f32_plan.argtypes = [P, P, P, P, I, I, I, I, P, S, ctypes.POINTER(Plan), P]
         L.w4a16_gemm_argmax_plan.argtypes = [P, P, P, P, P, I, I, I, I, P, S, ctypes.POINTER(Plan), P]
         L.w4a16_gemm_silu_mul_plan.argtypes = [P, P, P, P, I, I, I, I, P, S, ctypes.POINTER(Plan), P]
         L.w4a16_dequant.argtypes = [P, P, P, I, I, P]
         L.w4a16_unpack.argtypes = [P, P, I, I, P]
         for f in ("w4a16_repack_weights", "w4a16_get_plan", "w4a16_gemm", "w4a16_gemm_plan",
                   "w4a16_gemm_silu_mul", "w4a16_gemm_silu_mul_plan", "w4a16_gemm_argmax",
-                  "w4a16_gemm_argmax_plan", "w4a16_dequant", "w4a16_unpack"):
+                  "w4a16_gemm_argmax_plan", "w4a16_gemm_f32", "w4a16_gemm_f32_plan",
+                  "w4a16_dequant", "w4a16_unpack"):
             getattr(L, f).restype = I
         _lib = L
     return _lib
@@ -207,6 +210,28 @@ def gemm_silu_mul(A: torch.Tensor, blob: torch.Tensor, scales: torch.Tensor, N: 
         st = lib().w4a16_gemm_silu_mul_plan(_ptr(A), _ptr(blob), _ptr(scales), _ptr(out), M, N, K, group,
                                             _ptr(workspace), ws_bytes, ctypes.byref(plan), _stream(A))
     _check(st, "w4a16_gemm_silu_mul")
+    return out
+
+
+def gemm_f32(A: torch.Tensor, blob: torch.Tensor, scales: torch.Tensor, N: int,
+             out: torch.Tensor | None = None, plan: Plan | None = None,
+             workspace: torch.Tensor | None = None, group: int = GROUP):
+    """C[M, N] = A . dequant(blob, scales) as unrounded fp32 (a K shard's partial sum)."""
+    M, K = A.shape
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.float32, device=A.device)
+    if workspace is None:
+        need = workspace_bytes(M, N, K, plan)
+        if need:
+            workspace = _shared_workspace(A.device, need)
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    if plan is None:
+        st = lib().w4a16_gemm_f32(_ptr(A), _ptr(blob), _ptr(scales), _ptr(out), M, N, K, group,
+                                  _ptr(workspace), ws_bytes, _stream(A))
+    else:
+        st = lib().w4a16_gemm_f32_plan(_ptr(A), _ptr(blob), _ptr(scales), _ptr(out), M, N, K, group,
+                                       _ptr(workspace), ws_bytes, ctypes.byref(plan), _stream(A))
+    _check(st, "w4a16_gemm_f32")
     return out
 
 

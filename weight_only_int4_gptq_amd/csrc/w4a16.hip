@@ -152,39 +152,58 @@ int validate_plan(const w4a16_plan_t &p, int M, int N, int K) {
 // The row-count dispatcher.  Plan choice, from graph-replayed timings of
 // every compiled plan on MI355X (cold weights) over the decoder shapes
 // K x N = 5120 x 8192, 6144 x 5120, 5120 x 34816, 17408 x 5120 and
-// 5120 x 248320, M = 1..16:
-//  * M = 1: the GEMV kernel, two tiles per workgroup, four wavefronts along K
-//    (eight for long K), ring depth 4 (5 for wide N);
+// 5120 x 248320 and their tensor-parallel shards (N / 2, 4, 8 for the first
+// and third, K / 2, 4, 8 for the second and fourth), M = 1..16.
+// Widths: "narrow" up to 384 tiles of 16 columns, "mid" 513..2047, "wide"
+// from 2048, "very wide" from 8192; "long" K from 128 groups of 128.
+//  * M = 1: the GEMV kernel; narrow N with K of 32 groups or more: one tile
+//    per workgroup and eight wavefronts along K; mid: one tile, each
+//    wavefront's groups loaded in
+//    one go; otherwise two tiles, four wavefronts (eight for long K), ring
+//    depth 4 (5 for wide N);
 //  * M = 2..4: matrix cores with A staged in LDS (the bias formed in the
 //    loop); four tiles and depth 2 for wide N at M = 2 and for very wide N,
 //    else two tiles and depth 4; for long K eight wavefronts stage the whole
 //    K range of A (up to the full 160 KiB of LDS, one workgroup per CU);
 //  * M >= 5, matrix cores:
-//      - very wide N (>= 8192 tiles) from M = 8: one wavefront owns eight
-//        tiles (A from global memory), so each A fragment it loads serves
-//        eight times the weights;
-//      - wide N: four tiles, A per group from global memory below M = 12,
-//        through the per-wavefront LDS ring (contiguous DMA loads) above;
+//      - very wide N from M = 8: one wavefront owns eight tiles (A from
+//        global memory), so each A fragment it loads serves eight times the
+//        weights;
+//      - wide and mid N: four tiles, A per group from global memory below
+//        M = 12, through the per-wavefront LDS ring (contiguous DMA loads)
+//        from M = 12;
 //      - long K: A through the ring from M = 8; below, a quarter of K of A
 //        staged in LDS (split four ways);
-//      - otherwise all of A staged in LDS with eight wavefronts along K up
-//        to M = 12, the ring above.
-// "Wide" is N >= 32768 (2048 tiles), "long" K >= 16384 (128 groups).
+//      - narrow N up to 256 tiles: one tile, all of A staged in LDS, eight
+//        wavefronts along K;
+//      - otherwise all of A staged in LDS up to M = 12 (eight wavefronts
+//        along K from 40 groups, else four), the ring above.
 void auto_plan(int M, int N, int K, w4a16_plan_t *out) {
     const int NT = N / 16, G = K / W4A16_GROUP;
     const bool wide = NT >= 2048, deep = G >= 128;
+    const bool narrow = NT <= 384;             // few strips: one tile each, more waves along K
+    const bool mid = NT > 512 && NT < 2048;    // between the QKV and gate/up widths
     w4a16_plan_t p;
     p.kwaves = 4;
     p.splits = 1;
     p.asrc = W4A16_ASRC_LDS;
     if (M == 1) {
         p.path = W4A16_PATH_GEMV;
-        p.tiles = 2;
-        if (deep) p.kwaves = 8;
-        p.depth = (wide && !deep) ? 5 : 4;
+        if (narrow && G >= 32) {
+            p.tiles = 1;
+            p.kwaves = 8;
+            p.depth = 4;
+        } else if (mid && !deep) {             // one tile, each wavefront's groups in one go
+            p.tiles = 1;
+            p.depth = (G == 40) ? 10 : 8;
+        } else {
+            p.tiles = 2;
+            if (deep) p.kwaves = 8;
+            p.depth = (wide && !deep) ? 5 : 4;
+        }
     } else if (M <= 4) {
         p.path = W4A16_PATH_MFMA;
-        if (deep && !wide) {                 // the whole long K range of A in LDS
+        if (deep && !wide) {                   // the whole long K range of A in LDS
             p.tiles = 2;
             p.kwaves = 8;
             p.depth = 4;
@@ -197,12 +216,12 @@ void auto_plan(int M, int N, int K, w4a16_plan_t *out) {
         }
     } else {
         p.path = W4A16_PATH_MFMA;
-        if (NT >= 8192 && M >= 8) {          // very wide N: one wavefront per eight tiles
+        if (NT >= 8192 && M >= 8) {            // very wide N: one wavefront per eight tiles
             p.asrc = W4A16_ASRC_GLOBAL;
             p.tiles = 8;
             p.kwaves = 1;
             p.depth = 4;
-        } else if (wide) {
+        } else if (wide || mid) {
             p.asrc = M >= 12 ? W4A16_ASRC_RING : W4A16_ASRC_GLOBAL;
             p.tiles = 4;
             p.depth = 2;
@@ -211,16 +230,20 @@ void auto_plan(int M, int N, int K, w4a16_plan_t *out) {
             p.depth = 4;
             if (M >= 8) {
                 p.asrc = W4A16_ASRC_RING;
-            } else {                         // a quarter of K of A in LDS
+            } else {                           // a quarter of K of A in LDS
                 p.asrc = W4A16_ASRC_LDS;
                 p.splits = 4;
             }
+        } else if (narrow && NT <= 256) {      // one tile, all of A in LDS
+            p.tiles = 1;
+            p.kwaves = 8;
+            p.depth = 4;
         } else {
             p.tiles = 2;
             p.depth = 4;
-            if (M <= 12) {                   // all of A in LDS, eight wavefronts along K
+            if (M <= 12) {                     // all of A in LDS, more waves along long K
                 p.asrc = W4A16_ASRC_LDS;
-                p.kwaves = 8;
+                p.kwaves = G >= 40 ? 8 : 4;
             } else {
                 p.asrc = W4A16_ASRC_RING;
             }
@@ -230,9 +253,14 @@ void auto_plan(int M, int N, int K, w4a16_plan_t *out) {
     if (p.kwaves * p.splits > G) {
         p.splits = 1;
         if (p.kwaves > G) {
-            p.tiles = 1;
-            p.kwaves = 1;
-            p.depth = 8;
+            if (G >= 4) {
+                p.kwaves = 4;
+                p.depth = 0;
+            } else {
+                p.tiles = 1;
+                p.kwaves = 1;
+                p.depth = 8;
+            }
         }
     }
     if (p.path == W4A16_PATH_GEMV && plan_lds(p, M, G) > kLdsBudget) {
@@ -279,7 +307,7 @@ void fuse_plan(int M, w4a16_plan_t *p) {
 }
 
 // fuse: 0 plain C[M][N]; 1 the gate/up epilogue, C is H[M][N/2]; 2 the row
-// argmax (C unused, results in idx / val)
+// argmax (C unused, results in idx / val); 3 C as fp32 [M][N]
 int run_gemm(const void *A, const void *wq, const void *scales, void *C, int M, int N, int K,
              int group, void *workspace, size_t workspace_bytes, const w4a16_plan_t *user,
              void *stream, int fuse = 0, int *idx = nullptr, float *val = nullptr) {
@@ -479,6 +507,19 @@ int w4a16_gemm_plan(const void *A, const void *wq_repacked, const void *scales, 
                     const w4a16_plan_t *plan, void *stream) {
     return run_gemm(A, wq_repacked, scales, C, M, N, K, group, workspace, workspace_bytes, plan,
                     stream);
+}
+
+int w4a16_gemm_f32(const void *A, const void *wq_repacked, const void *scales, float *C, int M,
+                   int N, int K, int group, void *workspace, size_t workspace_bytes, void *stream) {
+    return run_gemm(A, wq_repacked, scales, C, M, N, K, group, workspace, workspace_bytes, nullptr,
+                    stream, 3);
+}
+
+int w4a16_gemm_f32_plan(const void *A, const void *wq_repacked, const void *scales, float *C, int M,
+                        int N, int K, int group, void *workspace, size_t workspace_bytes,
+                        const w4a16_plan_t *plan, void *stream) {
+    return run_gemm(A, wq_repacked, scales, C, M, N, K, group, workspace, workspace_bytes, plan,
+                    stream, 3);
 }
 
 int w4a16_gemm_argmax(const void *A, const void *wq_repacked, const void *scales, int *idx,

@@ -58,7 +58,8 @@ struct GemmArgs {
     int NT;                  // 16-column tiles = N / 16
     int nstrips;             // column strips = ceil(NT / tiles)
     int nunits;              // nstrips * S = grid size
-    int fuse;                // epilogue: 0 plain C, 1 gate/up activation, 2 row argmax
+    int fuse;                // epilogue: 0 plain C, 1 gate/up activation, 2 row argmax,
+                             // 3 C as fp32 (unrounded partial sums of a K shard)
     int *amax_idx;           // row argmax: column of each row's maximum [M]
     float *amax_val;         // row argmax: its fp32 value [M]
 };
@@ -735,7 +736,10 @@ __global__ void __launch_bounds__(64 * KW) gemm_kernel(GemmArgs p) {
     const int NV = T * M * 16;   // values (t, m, c) of this workgroup
     auto col_of = [&](int t, int cc) { return (size_t)tile_of(t) * 16 + cc; };
     auto emit_c = [&](int t, int m, int cc, float val) {      // plain, one split
-        p.C[(size_t)m * p.N + col_of(t, cc)] = f32_to_bf16_rne(val);
+        if (p.fuse == 3)
+            reinterpret_cast<float *>(p.C)[(size_t)m * p.N + col_of(t, cc)] = val;
+        else
+            p.C[(size_t)m * p.N + col_of(t, cc)] = f32_to_bf16_rne(val);
     };
     auto emit_h = [&](int t, int m, int cc, float g, float u) {   // gate/up, one split
         const float hv = g / (1.0f + expf(-g)) * u;
@@ -767,7 +771,7 @@ __global__ void __launch_bounds__(64 * KW) gemm_kernel(GemmArgs p) {
                                                    __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
             }
         } else if (holder) {
-            if (p.S > 1 || !p.fuse) {
+            if (p.S > 1 || p.fuse != 1) {
 #pragma unroll
                 for (int t = 0; t < T; ++t)
 #pragma unroll
@@ -820,7 +824,7 @@ __global__ void __launch_bounds__(64 * KW) gemm_kernel(GemmArgs p) {
                     __hip_atomic_fetch_max(&keys[mc >> 4], argmax_key(reduced(t, mc), (uint32_t)col_of(t, mc & 15)),
                                            __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
                 }
-        } else if (p.S > 1 || !p.fuse) {
+        } else if (p.S > 1 || p.fuse != 1) {
 #pragma unroll
             for (int t = 0; t < T; ++t)
                 for (int mc = threadIdx.x; mc < M * 16; mc += 64 * KW) {
@@ -877,7 +881,7 @@ __global__ void __launch_bounds__(64 * KW) gemm_kernel(GemmArgs p) {
                                            __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                 return s;
             };
-            if (!p.fuse) {
+            if (p.fuse != 1) {
 #pragma unroll
                 for (int t = 0; t < T; ++t)
                     for (int mc = threadIdx.x; mc < M * 16; mc += 64 * KW) {

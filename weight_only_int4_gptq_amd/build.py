@@ -13,11 +13,17 @@ import subprocess
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 LIB = os.path.join(PKG, "libw4a16.so")
-SOURCES = [os.path.join(PKG, "csrc", "w4a16.hip")]
+# compiled separately (in parallel) and linked into one library: the host
+# code, and the two instantiation sets of the matmul kernels
+SOURCES = [os.path.join(PKG, "csrc", f) for f in ("w4a16.hip", "variants_plain.hip", "variants_epi.hip")]
 PROBE_LIB = os.path.join(PKG, "libw4a16_probe.so")
 PROBE_SOURCES = [os.path.join(PKG, "csrc", "probe_stream.hip")]
-DEPENDS = SOURCES + [os.path.join(PKG, "csrc", "w4a16_kernels.hpp"),
+DEPENDS = SOURCES + [os.path.join(PKG, "csrc", "w4a16_kernels.hpp"), os.path.join(PKG, "csrc", "w4a16_variants.hpp"),
                      os.path.join(ROOT, "include", "w4a16.h")]
+FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++20", "-fPIC",
+         # packed fp32 VALU forms stay off: plain fp32 ops only
+         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+NOISE = "is not a recognized feature for this target"
 
 
 def hipcc() -> str:
@@ -27,20 +33,36 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found")
 
 
-def _compile(out: str, sources: list, verbose: bool) -> str:
-    tmp = out + ".tmp"
-    cmd = [hipcc(), "--offload-arch=gfx950", "-O3", "-std=c++20", "-fPIC", "-shared",
-           # packed fp32 VALU forms stay off: plain fp32 ops only
-           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-           "-I", os.path.join(ROOT, "include"), "-o", tmp] + sources
+def _run(cmd, what):
     res = subprocess.run(cmd, capture_output=True, text=True)
-    noise = "is not a recognized feature for this target"
-    err = "\n".join(l for l in (res.stderr or "").splitlines() if noise not in l)
+    err = "\n".join(l for l in (res.stderr or "").splitlines() if NOISE not in l)
     if res.returncode != 0:
-        raise RuntimeError(f"hipcc failed ({res.returncode}):\n{err}")
-    if verbose and err.strip():
-        print(err)
+        raise RuntimeError(f"hipcc failed on {what} ({res.returncode}):\n{err}")
+    return err
+
+
+def _compile(out: str, sources: list, verbose: bool) -> str:
+    """Compile each source to an object in parallel, then link the shared library."""
+    objs = [out + "." + os.path.basename(src) + ".o" for src in sources]
+    procs = []
+    for src, obj in zip(sources, objs):
+        cmd = [hipcc()] + FLAGS + ["-I", os.path.join(ROOT, "include"), "-c", "-o", obj, src]
+        procs.append((subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.PIPE, text=True), src))
+    errs = []
+    for proc, src in procs:
+        _, err = proc.communicate()
+        err = "\n".join(l for l in (err or "").splitlines() if NOISE not in l)
+        if proc.returncode != 0:
+            errs.append(f"hipcc failed on {os.path.basename(src)} ({proc.returncode}):\n{err}")
+        elif verbose and err.strip():
+            print(err)
+    if errs:
+        raise RuntimeError("\n".join(errs))
+    tmp = out + ".tmp"
+    _run([hipcc()] + FLAGS + ["-shared", "-o", tmp] + objs, "link")
     os.replace(tmp, out)
+    for obj in objs:
+        os.remove(obj)
     return out
 
 

@@ -14,6 +14,7 @@
 
 #include "w4a16.h"
 #include "w4a16_kernels.hpp"
+#include "w4a16_variants.hpp"
 
 namespace {
 
@@ -21,69 +22,32 @@ using namespace w4a16;
 
 constexpr int kLdsBudget = 64 * 1024;    // automatic GEMV plans: at least two workgroups per CU
 constexpr int kLdsMax = 160 * 1024;      // explicit plans: gfx950's LDS per workgroup
+constexpr int kMaxVariants = 1024;       // bound on the shape count (checked before use)
 
 // ---------------------------------------------------------------- kernel table
-
-using KernelFn = void (*)(GemmArgs);
-
-struct Variant {
-    int path, mm, tiles, kwaves, depth, asrc;   // mm: compile-time row count (0: run time)
-    KernelFn fn;
-};
-
-// (tiles, kwaves, depth) shapes instantiated for every path / row count
-#define W4A16_SHAPES(X, P, MM, AS) \
-    X(P, MM, 1, 1, 8, AS) X(P, MM, 1, 4, 8, AS) X(P, MM, 1, 8, 4, AS) X(P, MM, 1, 8, 8, AS) \
-    X(P, MM, 2, 4, 4, AS) X(P, MM, 2, 8, 4, AS) X(P, MM, 2, 4, 8, AS) X(P, MM, 4, 4, 2, AS) \
-    X(P, MM, 4, 4, 4, AS)
-#define W4A16_V(P, MM, T, KW, D, AS) {P, MM, T, KW, D, AS, gemm_kernel<P, MM, T, KW, D, AS>},
-
-// one-shot shapes (the ring covers a wavefront's whole K range) for one row
-// A streamed per group through a per-wavefront LDS ring (matrix-core path)
-#define W4A16_RINGS(X, P, MM, AS) \
-    X(P, MM, 1, 4, 4, AS) X(P, MM, 1, 8, 4, AS) X(P, MM, 2, 4, 2, AS) X(P, MM, 2, 4, 4, AS) \
-    X(P, MM, 4, 4, 2, AS) X(P, MM, 4, 2, 2, AS) X(P, MM, 4, 4, 4, AS) X(P, MM, 8, 1, 4, AS) \
-    X(P, MM, 8, 2, 2, AS) X(P, MM, 8, 4, 2, AS)
-
-// eight-tile strips: A read once per eight tiles (matrix-core paths)
-#define W4A16_WIDE(X, P, MM, AS) \
-    X(P, MM, 8, 4, 2, AS) X(P, MM, 8, 2, 2, AS) X(P, MM, 8, 2, 4, AS) X(P, MM, 8, 1, 4, AS)
-
-#define W4A16_ONESHOT(X, P, MM, AS) \
-    X(P, MM, 2, 4, 10, AS) X(P, MM, 2, 4, 5, AS) X(P, MM, 4, 4, 5, AS) X(P, MM, 4, 8, 5, AS) \
-    X(P, MM, 1, 4, 10, AS) X(P, MM, 2, 2, 10, AS) X(P, MM, 4, 2, 5, AS) X(P, MM, 1, 8, 17, AS) \
-    X(P, MM, 2, 8, 17, AS) X(P, MM, 2, 4, 17, AS) X(P, MM, 4, 4, 10, AS) X(P, MM, 2, 2, 17, AS)
-
-const Variant kVariants[] = {
-    W4A16_ONESHOT(W4A16_V, PATH_GEMV, 1, ASRC_LDS) W4A16_ONESHOT(W4A16_V, PATH_MFMA, 1, ASRC_LDS)
-    W4A16_ONESHOT(W4A16_V, PATH_MFMA, 1, ASRC_GLOBAL)
-    W4A16_SHAPES(W4A16_V, PATH_GEMV, 1, ASRC_LDS) W4A16_SHAPES(W4A16_V, PATH_GEMV, 2, ASRC_LDS)
-    W4A16_SHAPES(W4A16_V, PATH_GEMV, 3, ASRC_LDS) W4A16_SHAPES(W4A16_V, PATH_GEMV, 4, ASRC_LDS)
-    W4A16_RINGS(W4A16_V, PATH_MFMA, 0, ASRC_RING)
-    W4A16_WIDE(W4A16_V, PATH_MFMA, 0, ASRC_LDS) W4A16_WIDE(W4A16_V, PATH_MFMA, 0, ASRC_GLOBAL)
-    W4A16_WIDE(W4A16_V, PATH_MFMA, 2, ASRC_LDS) W4A16_WIDE(W4A16_V, PATH_MFMA, 3, ASRC_LDS)
-    W4A16_WIDE(W4A16_V, PATH_MFMA, 4, ASRC_LDS)
-    W4A16_SHAPES(W4A16_V, PATH_MFMA, 0, ASRC_LDS) W4A16_SHAPES(W4A16_V, PATH_MFMA, 0, ASRC_GLOBAL)
-    W4A16_SHAPES(W4A16_V, PATH_MFMA, 1, ASRC_LDS) W4A16_SHAPES(W4A16_V, PATH_MFMA, 1, ASRC_GLOBAL)
-    W4A16_SHAPES(W4A16_V, PATH_MFMA, 2, ASRC_LDS) W4A16_SHAPES(W4A16_V, PATH_MFMA, 2, ASRC_GLOBAL)
-    W4A16_SHAPES(W4A16_V, PATH_MFMA, 3, ASRC_LDS) W4A16_SHAPES(W4A16_V, PATH_MFMA, 3, ASRC_GLOBAL)
-    W4A16_SHAPES(W4A16_V, PATH_MFMA, 4, ASRC_LDS) W4A16_SHAPES(W4A16_V, PATH_MFMA, 4, ASRC_GLOBAL)
-};
+// Two instantiations of every kernel shape (w4a16_variants.hpp): plain
+// matmuls, and kernels that also carry the epilogue modes (gate/up
+// activation, row argmax, fp32 output), compiled in their own translation
+// units.  The plain ones have no mode code at all.
 
 int default_depth(int tiles) { return tiles == 1 ? 8 : (tiles == 2 ? 4 : 2); }
 
 // The kernel for a plan: GEMV kernels are compiled per row count (1..4);
 // MFMA kernels too for M <= 4 (LDS or global A), and take M at run time
 // above and with ring A.
-const Variant *find_variant(const w4a16_plan_t &p, int M) {
+// epi: a kernel that carries the epilogue modes (else a plain matmul)
+const Variant *find_variant(const w4a16_plan_t &p, int M, bool epi = false) {
     // ring A kernels take M at run time for every row count
     const int mm = (p.path == W4A16_PATH_GEMV || (M <= 4 && p.asrc != W4A16_ASRC_RING)) ? M : 0;
     const int asrc = (p.path == W4A16_PATH_GEMV) ? ASRC_LDS : p.asrc;
     const int depth = p.depth ? p.depth : default_depth(p.tiles);
-    for (const Variant &v : kVariants)
+    const Variant *table = epi ? kVariantsEpi : kVariantsPlain;
+    for (int i = 0; i < kNumVariants; ++i) {
+        const Variant &v = table[i];
         if (v.path == p.path && v.mm == mm && v.tiles == p.tiles && v.kwaves == p.kwaves &&
             v.depth == depth && v.asrc == asrc)
             return &v;
+    }
     return nullptr;
 }
 
@@ -345,22 +309,24 @@ int run_gemm(const void *A, const void *wq, const void *scales, void *C, int M, 
     st = check_device(&lds_max);
     if (st != W4A16_OK) return st;
 
-    const Variant *v = find_variant(p, M);
+    const Variant *v = find_variant(p, M, fuse != 0);
     if (!v) return W4A16_ERR_PLAN;
     const int lds = plan_lds(p, M, K / W4A16_GROUP);
     if (lds + 256 > lds_max) return W4A16_ERR_PLAN;   // 256: the kernel's static LDS
     if (lds > 65536) {
         // above 64 KiB the kernel must be allowed its dynamic LDS first (once)
-        static std::atomic<uint8_t> raised[sizeof(kVariants) / sizeof(kVariants[0])];
-        const size_t vi = (size_t)(v - kVariants);
-        if (!raised[vi].load(std::memory_order_relaxed)) {
+        static std::atomic<uint8_t> raised[2][kMaxVariants];
+        const bool epi = fuse != 0;
+        const size_t vi = (size_t)(v - (epi ? kVariantsEpi : kVariantsPlain));
+        if (vi >= (size_t)kMaxVariants) return W4A16_ERR_LAUNCH;
+        if (!raised[epi][vi].load(std::memory_order_relaxed)) {
             const void *fn = reinterpret_cast<const void *>(v->fn);
             hipFuncAttributes fa;
             if (hipFuncGetAttributes(&fa, fn) != hipSuccess ||
                 hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize,
                                     lds_max - (int)fa.sharedSizeBytes) != hipSuccess)
                 return W4A16_ERR_LAUNCH;
-            raised[vi].store(1, std::memory_order_relaxed);
+            raised[epi][vi].store(1, std::memory_order_relaxed);
         }
     }
     GemmArgs a;

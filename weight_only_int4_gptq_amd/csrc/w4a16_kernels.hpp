@@ -260,7 +260,7 @@ __device__ __forceinline__ uint32_t lds_addr(const void *p) {
 // One workgroup of kArgmaxBins * 16 threads: thread (b, m) reads bin b of row
 // m and clears it; the rows' maxima meet in LDS; thread m < M writes the
 // column and value of row m.
-__global__ void __launch_bounds__(kArgmaxBins * 16) argmax_fold_kernel(unsigned long long *__restrict__ bins,
+static __global__ void __launch_bounds__(kArgmaxBins * 16) argmax_fold_kernel(unsigned long long *__restrict__ bins,
                                                                        int M, int *__restrict__ idx,
                                                                        float *__restrict__ val) {
     __shared__ unsigned long long best[16];
@@ -293,7 +293,7 @@ __device__ __forceinline__ uint32_t gptq_word_to_tile_word(uint32_t x) {
     return out;
 }
 
-__global__ void __launch_bounds__(256) repack_kernel(const uint32_t *__restrict__ qweight,
+static __global__ void __launch_bounds__(256) repack_kernel(const uint32_t *__restrict__ qweight,
                                                      u32x4 *__restrict__ blob, int N, int G,
                                                      long long npieces) {
     const long long pc = (long long)blockIdx.x * 256 + threadIdx.x;
@@ -313,7 +313,7 @@ __global__ void __launch_bounds__(256) repack_kernel(const uint32_t *__restrict_
 }
 
 // Scales [G][N] -> [tile][group][16]: one thread per scale.
-__global__ void __launch_bounds__(256) repack_scales_kernel(const uint16_t *__restrict__ scales,
+static __global__ void __launch_bounds__(256) repack_scales_kernel(const uint16_t *__restrict__ scales,
                                                             uint16_t *__restrict__ out, int N, int G,
                                                             long long count) {
     const long long i = (long long)blockIdx.x * 256 + threadIdx.x;
@@ -396,7 +396,9 @@ __global__ void __launch_bounds__(256) export_kernel(const u32x4 *__restrict__ b
 // order; with S > 1 the workgroups of one strip meet in the workspace, where
 // the last one to arrive adds the S partials in a fixed order.  No float
 // atomics: the result does not depend on timing.
-template <int PATH, int MM, int T, int KW, int D, int ASRC>
+// EPI: the kernel carries the epilogue modes of GemmArgs::fuse; without it
+// the mode is 0 (plain C) and no other mode's code is compiled in.
+template <int PATH, int MM, int T, int KW, int D, int ASRC, bool EPI>
 __global__ void __launch_bounds__(64 * KW) gemm_kernel(GemmArgs p) {
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
     __shared__ int s_last;
@@ -432,12 +434,13 @@ __global__ void __launch_bounds__(64 * KW) gemm_kernel(GemmArgs p) {
     // (T even): the first T/2 slots hold gate tiles strip*T/2 + t, the last
     // T/2 the up tiles of the same columns, NT/2 tiles further on.
     constexpr int kHalfT = T / 2;
+    const int fuse = EPI ? p.fuse : 0;
     auto tile_of = [&](int t) {
-        if (p.fuse == 1) return t < kHalfT ? strip * kHalfT + t : (p.NT >> 1) + strip * kHalfT + (t - kHalfT);
+        if (fuse == 1) return t < kHalfT ? strip * kHalfT + t : (p.NT >> 1) + strip * kHalfT + (t - kHalfT);
         return strip * T + t;
     };
     auto tile_ok = [&](int t) {
-        return p.fuse == 1 ? strip * kHalfT + (t < kHalfT ? t : t - kHalfT) < (p.NT >> 1) : strip * T + t < p.NT;
+        return fuse == 1 ? strip * kHalfT + (t < kHalfT ? t : t - kHalfT) < (p.NT >> 1) : strip * T + t < p.NT;
     };
 
     // wave-uniform bases (scalar) and per-lane byte offsets (vector, fixed)
@@ -736,7 +739,7 @@ __global__ void __launch_bounds__(64 * KW) gemm_kernel(GemmArgs p) {
     const int NV = T * M * 16;   // values (t, m, c) of this workgroup
     auto col_of = [&](int t, int cc) { return (size_t)tile_of(t) * 16 + cc; };
     auto emit_c = [&](int t, int m, int cc, float val) {      // plain, one split
-        if (p.fuse == 3)
+        if (fuse == 3)
             reinterpret_cast<float *>(p.C)[(size_t)m * p.N + col_of(t, cc)] = val;
         else
             p.C[(size_t)m * p.N + col_of(t, cc)] = f32_to_bf16_rne(val);
@@ -757,7 +760,7 @@ __global__ void __launch_bounds__(64 * KW) gemm_kernel(GemmArgs p) {
         constexpr int kRows = (PATH == PATH_MFMA) ? kRowsV : MM;
         const bool holder = (PATH == PATH_MFMA) || h == 0;
         auto row_of = [&](int i) { return PATH == PATH_MFMA ? 4 * h + i : i; };
-        if (p.fuse == 2) {
+        if (fuse == 2) {
             unsigned long long *keys = reinterpret_cast<unsigned long long *>(smem + L.keys);
             if (threadIdx.x < 16) keys[threadIdx.x] = 0ull;
             lds_barrier();
@@ -771,7 +774,7 @@ __global__ void __launch_bounds__(64 * KW) gemm_kernel(GemmArgs p) {
                                                    __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
             }
         } else if (holder) {
-            if (p.S > 1 || p.fuse != 1) {
+            if (p.S > 1 || fuse != 1) {
 #pragma unroll
                 for (int t = 0; t < T; ++t)
 #pragma unroll
@@ -813,7 +816,7 @@ __global__ void __launch_bounds__(64 * KW) gemm_kernel(GemmArgs p) {
             for (int w = 1; w < KW; ++w) s += red[w * NV + e];
             return s;
         };
-        if (p.fuse == 2) {
+        if (fuse == 2) {
             unsigned long long *keys = reinterpret_cast<unsigned long long *>(smem + L.keys);
             if (threadIdx.x < 16) keys[threadIdx.x] = 0ull;
             lds_barrier();
@@ -824,7 +827,7 @@ __global__ void __launch_bounds__(64 * KW) gemm_kernel(GemmArgs p) {
                     __hip_atomic_fetch_max(&keys[mc >> 4], argmax_key(reduced(t, mc), (uint32_t)col_of(t, mc & 15)),
                                            __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
                 }
-        } else if (p.S > 1 || p.fuse != 1) {
+        } else if (p.S > 1 || fuse != 1) {
 #pragma unroll
             for (int t = 0; t < T; ++t)
                 for (int mc = threadIdx.x; mc < M * 16; mc += 64 * KW) {
@@ -843,7 +846,7 @@ __global__ void __launch_bounds__(64 * KW) gemm_kernel(GemmArgs p) {
         }
     }
 
-    if (p.fuse == 2) {
+    if (fuse == 2) {
         // Row argmax across workgroups (single split): this workgroup's row
         // maxima go to its bin with device-scope 64-bit max atomics, issued
         // and not waited for; the fold kernel that follows on the stream
@@ -881,7 +884,7 @@ __global__ void __launch_bounds__(64 * KW) gemm_kernel(GemmArgs p) {
                                            __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                 return s;
             };
-            if (p.fuse != 1) {
+            if (fuse != 1) {
 #pragma unroll
                 for (int t = 0; t < T; ++t)
                     for (int mc = threadIdx.x; mc < M * 16; mc += 64 * KW) {

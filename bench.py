@@ -41,7 +41,10 @@ PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 LLC_BYTES = 256 << 20          # MI355X Infinity Cache
 ROTATE_BYTES = 1 << 30         # rotate over >= 1 GiB of buffer sets
 KERNEL_SOURCES = ["weight_only_int4_gptq_amd/csrc/w4a16.hip",
-                  "weight_only_int4_gptq_amd/csrc/w4a16_kernels.hpp"]
+                  "weight_only_int4_gptq_amd/csrc/w4a16_kernels.hpp",
+                  "weight_only_int4_gptq_amd/csrc/w4a16_variants.hpp",
+                  "weight_only_int4_gptq_amd/csrc/variants_plain.hip",
+                  "weight_only_int4_gptq_amd/csrc/variants_epi.hip"]
 
 
 def log(*a):
@@ -110,6 +113,13 @@ def time_graph(torch, fn, steps, warmup):
     e1.record()
     torch.cuda.synchronize()
     return e0.elapsed_time(e1) / steps
+
+
+def graph_steps(args, nbytes):
+    """Calls per captured graph for the sweeps: at least 100, so that the fixed
+    cost of one replay is a small share of the per-call time, and at most
+    --steps, or about 4 GB of weight reads, whichever is fewer (but not below 100)."""
+    return max(100, min(args.steps, int(4e9 / nbytes)))
 
 
 def measure(torch, w4, prob, M, steps, warmup):
@@ -358,7 +368,7 @@ def sweep(torch, w4, args):
         sets = sets_for(wl.K, wl.N, 1)
         prob = Problem(torch, w4, wl.K, wl.N, wl.seed, wl.act, sets)
         for M in Ms:
-            steps = max(20, min(args.steps, int(2e6 / synth.algorithmic_bytes(M, wl.N, wl.K) * 100)))
+            steps = graph_steps(args, synth.algorithmic_bytes(M, wl.N, wl.K))
             r = measure(torch, w4, prob, M, steps, min(args.warmup, 20))
             rec = {"workload": wname, "M": M, "K": wl.K, "N": wl.N, "plan": w4.get_plan(M, wl.N, wl.K).as_dict(),
                    "us_per_call": round(r["us_per_call"], 3), "GBps": round(r["gbs"], 1),
@@ -372,7 +382,7 @@ def sweep(torch, w4, args):
                     j = i % prob.sets
                     w4.gemm_silu_mul(prob.acts[j][:M], prob.blobs[j], prob.scales[j], prob.N,
                                      out=prob.houts[j][:M])
-                steps = max(20, min(args.steps, int(2e6 / synth.algorithmic_bytes(M, wl.N, wl.K) * 100)))
+                steps = graph_steps(args, synth.algorithmic_bytes(M, wl.N, wl.K))
                 ms = time_graph(torch, fcall, steps, min(args.warmup, 20))
                 nb = synth.algorithmic_bytes_silu_mul(M, wl.N, wl.K)
                 print(json.dumps({"workload": "gate_up_silu_mul", "M": M, "K": wl.K, "N": wl.N,
@@ -385,7 +395,7 @@ def sweep(torch, w4, args):
                 def acall(i, M=M):
                     j = i % prob.sets
                     w4.gemm_argmax(prob.acts[j][:M], prob.blobs[j], prob.scales[j], prob.N)
-                steps = max(20, min(args.steps, int(2e6 / synth.algorithmic_bytes(M, wl.N, wl.K) * 100)))
+                steps = graph_steps(args, synth.algorithmic_bytes(M, wl.N, wl.K))
                 ms = time_graph(torch, acall, steps, min(args.warmup, 20))
                 nb = synth.algorithmic_bytes_argmax(M, wl.N, wl.K)
                 print(json.dumps({"workload": "lm_head_argmax", "M": M, "K": wl.K, "N": wl.N,
@@ -473,7 +483,7 @@ def tp_shards(torch, w4, args):
                     def call(i, M=M):
                         prob.call(w4, M, i)
                     nb = synth.algorithmic_bytes(M, Ni, Ki)
-                steps = max(20, min(args.steps, int(2e6 / nb * 100)))
+                steps = graph_steps(args, nb)
                 ms = time_graph(torch, call, steps, min(args.warmup, 20))
                 print(json.dumps({"tp": tp, "call": name, "M": M, "K": Ki, "N": Ni,
                                   "us_per_call": round(ms * 1e3, 3), "GBps": round(nb / (ms * 1e-3) / 1e9, 1),

@@ -17,6 +17,11 @@ Contents
     ``max |C_gpu - C_ref| / sum|a*w|`` per output.
   * ``bf16_bits_to_f64`` / ``f32_exact_to_bf16_bits``: exact bf16 reading,
     and round-to-nearest-even of fp32-representable values to bf16.
+  * ``silu``, ``gemm_silu_mul``, ``row_argmax``: the gate/up activation and
+    the greedy pick on top of ``gemm``.
+  * ``nvfp4_*``: the NVFP4 weight-only variant (E2M1 codes, one E4M3 scale
+    per 16 rows, an fp32 per-tensor factor), wrappers around ``nvfp4.c``;
+    ``nvfp4_exact_gemm`` in exact rationals for tiny shapes.
 
 What is computed follows the checkpoint contract on the page "Qwen3.8-27B on
 single DGX Spark ..." (section "Quality."): symmetric GPTQ, 4-bit, group 128,
@@ -35,17 +40,18 @@ import numpy as np
 
 GROUP = 128
 _HERE = os.path.dirname(os.path.abspath(__file__))
-_SRC = os.path.join(_HERE, "oracle.c")
+_SRCS = [os.path.join(_HERE, "oracle.c"), os.path.join(_HERE, "nvfp4.c")]
 _LIB_PATH = os.path.join(_HERE, "liboracle.so")
 _lib = None
 
 
 def build(force: bool = False) -> str:
-    """Compile oracle.c with gcc (portable x86-64, OpenMP) into liboracle.so."""
-    if force or not os.path.exists(_LIB_PATH):
+    """Compile oracle.c and nvfp4.c with gcc (portable x86-64, OpenMP) into liboracle.so."""
+    stale = os.path.exists(_LIB_PATH) and any(os.path.getmtime(s) > os.path.getmtime(_LIB_PATH) for s in _SRCS)
+    if force or stale or not os.path.exists(_LIB_PATH):
         tmp = _LIB_PATH + ".tmp"
         cmd = ["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-std=c99",
-               "-o", tmp, _SRC, "-lm"]
+               "-o", tmp, *_SRCS, "-lm"]
         subprocess.run(cmd, check=True)
         os.replace(tmp, _LIB_PATH)
     return _LIB_PATH
@@ -67,6 +73,17 @@ def _load():
         lib.oracle_bf16_to_f64.argtypes = [ctypes.c_uint16]
         lib.oracle_bf16_to_f64.restype = ctypes.c_double
         lib.oracle_max_threads.restype = ctypes.c_int
+        d = ctypes.c_double
+        lib.oracle_e2m1_to_f64.argtypes = [ctypes.c_uint]
+        lib.oracle_e2m1_to_f64.restype = d
+        lib.oracle_e4m3_to_f64.argtypes = [ctypes.c_uint]
+        lib.oracle_e4m3_to_f64.restype = d
+        lib.oracle_nvfp4_unpack.argtypes = [P, i, i, P]
+        lib.oracle_nvfp4_dequant.argtypes = [P, P, i, i, P]
+        lib.oracle_nvfp4_gemm.argtypes = [P, P, P, d, i, i, i, P, i, i, P, P]
+        lib.oracle_nvfp4_repack.argtypes = [P, i, i, P]
+        lib.oracle_nvfp4_unrepack.argtypes = [P, i, i, P]
+        lib.oracle_nvfp4_repack_scales.argtypes = [P, i, i, P]
         _lib = lib
     return _lib
 
@@ -317,4 +334,147 @@ def normalized_error(C_test: np.ndarray, C_ref: np.ndarray, D_ref: np.ndarray) -
     nz = D_ref > 0
     out[nz] = num[nz] / D_ref[nz]
     out[~nz] = np.where(C_test[~nz] == 0.0, 0.0, np.inf)
+    return out
+
+
+# ---------------------------------------------------------------------------
+# NVFP4 weight-only variant (nvfp4.c)
+# ---------------------------------------------------------------------------
+
+NVFP4_BLOCK = 16
+
+
+def _check_nvfp4(K: int, N: int, multiple: int = GROUP):
+    if K % multiple or K <= 0 or N <= 0:
+        raise ValueError(f"oracle: K must be a positive multiple of {multiple}, N positive")
+
+
+def e2m1_to_f64(codes) -> np.ndarray:
+    """Values of 4-bit E2M1 codes (sign, 2-bit exponent with bias 1, 1-bit mantissa)."""
+    c = np.asarray(codes, dtype=np.int64)
+    f = _load().oracle_e2m1_to_f64
+    return np.array([f(int(x) & 0xF) for x in c.ravel()], dtype=np.float64).reshape(c.shape)
+
+
+def e4m3_to_f64(bytes_) -> np.ndarray:
+    """Values of FP8 E4M3 bytes (bias 7, subnormals, S.1111.111 = NaN, no infinities)."""
+    b = np.asarray(bytes_, dtype=np.int64)
+    f = _load().oracle_e4m3_to_f64
+    return np.array([f(int(x) & 0xFF) for x in b.ravel()], dtype=np.float64).reshape(b.shape)
+
+
+def nvfp4_unpack(packed: np.ndarray, K: int, N: int) -> np.ndarray:
+    """Codes [K, N] in [0, 15] from packed uint8 [N, K/2] (low nibble = even k)."""
+    _check_nvfp4(K, N, 2)
+    pk = np.ascontiguousarray(packed, dtype=np.uint8).reshape(N, K // 2)
+    out = np.empty((K, N), dtype=np.uint8)
+    _load().oracle_nvfp4_unpack(_ptr(pk), K, N, _ptr(out))
+    return out
+
+
+def nvfp4_dequant(packed: np.ndarray, scales: np.ndarray, K: int, N: int) -> np.ndarray:
+    """W[k, n] = e2m1(code) * e4m3(scale[n, k // 16]) in fp64, without the per-tensor factor."""
+    _check_nvfp4(K, N, NVFP4_BLOCK)
+    pk = np.ascontiguousarray(packed, dtype=np.uint8).reshape(N, K // 2)
+    sc = np.ascontiguousarray(scales, dtype=np.uint8).reshape(N, K // NVFP4_BLOCK)
+    out = np.empty((K, N), dtype=np.float64)
+    _load().oracle_nvfp4_dequant(_ptr(pk), _ptr(sc), K, N, _ptr(out))
+    return out
+
+
+def nvfp4_gemm(A: np.ndarray, packed: np.ndarray, scales: np.ndarray, alpha: float, M: int, N: int,
+               K: int, cols=None, nthreads: int = 0):
+    """fp64 reference C[M, ncols] = alpha * A . W[:, cols] and D = |alpha| * sum |a*w|.
+
+    ``A`` is bf16 bits [M, K]; ``alpha`` is used at its exact value (pass an
+    fp32-representable number to match a caller that holds it in fp32).
+    """
+    _check_nvfp4(K, N, NVFP4_BLOCK)
+    if not 1 <= M <= 16:
+        raise ValueError("oracle.nvfp4_gemm: 1 <= M <= 16")
+    a = np.ascontiguousarray(np.ascontiguousarray(A, dtype=np.uint16).reshape(-1, K)[:M])
+    pk = np.ascontiguousarray(packed, dtype=np.uint8).reshape(N, K // 2)
+    sc = np.ascontiguousarray(scales, dtype=np.uint8).reshape(N, K // NVFP4_BLOCK)
+    if cols is None:
+        ncols, cptr = N, None
+    else:
+        c = np.ascontiguousarray(cols, dtype=np.int32)
+        if c.size and (c.min() < 0 or c.max() >= N):
+            raise ValueError("oracle.nvfp4_gemm: column index out of range")
+        ncols, cptr = int(c.size), _ptr(c)
+    C = np.empty((M, ncols), dtype=np.float64)
+    D = np.empty((M, ncols), dtype=np.float64)
+    _load().oracle_nvfp4_gemm(_ptr(a), _ptr(pk), _ptr(sc), float(alpha), M, N, K, cptr, ncols,
+                              int(nthreads), _ptr(C), _ptr(D))
+    return C, D
+
+
+def nvfp4_repack(packed: np.ndarray, K: int, N: int) -> np.ndarray:
+    """Tile-order blob (uint8, K*N/2 bytes) built from the written layout definition."""
+    _check_nvfp4(K, N)
+    if N % 16:
+        raise ValueError("oracle.nvfp4_repack: N must be a multiple of 16")
+    pk = np.ascontiguousarray(packed, dtype=np.uint8).reshape(N, K // 2)
+    out = np.empty(K * N // 2, dtype=np.uint8)
+    _load().oracle_nvfp4_repack(_ptr(pk), K, N, _ptr(out))
+    return out
+
+
+def nvfp4_unrepack(blob: np.ndarray, K: int, N: int) -> np.ndarray:
+    """Inverse of ``nvfp4_repack``: packed uint8 [N, K/2]."""
+    _check_nvfp4(K, N)
+    if N % 16:
+        raise ValueError("oracle.nvfp4_unrepack: N must be a multiple of 16")
+    b = np.ascontiguousarray(blob, dtype=np.uint8).reshape(-1)
+    out = np.empty((N, K // 2), dtype=np.uint8)
+    _load().oracle_nvfp4_unrepack(_ptr(b), K, N, _ptr(out))
+    return out
+
+
+def nvfp4_repack_scales(scales: np.ndarray, K: int, N: int) -> np.ndarray:
+    """Scales [N, K/16] -> [tile][superblock][16 columns][8 blocks] (uint8)."""
+    _check_nvfp4(K, N)
+    if N % 16:
+        raise ValueError("oracle.nvfp4_repack_scales: N must be a multiple of 16")
+    sc = np.ascontiguousarray(scales, dtype=np.uint8).reshape(N, K // NVFP4_BLOCK)
+    out = np.empty(K * N // NVFP4_BLOCK, dtype=np.uint8)
+    _load().oracle_nvfp4_repack_scales(_ptr(sc), K, N, _ptr(out))
+    return out
+
+
+def _e2m1_fraction(code: int) -> Fraction:
+    sign = -1 if code & 8 else 1
+    e, m = (code >> 1) & 3, code & 1
+    mag = Fraction(m, 2) if e == 0 else Fraction(2 + m, 2) * Fraction(2) ** (e - 1)
+    return sign * mag
+
+
+def _e4m3_fraction(byte: int) -> Fraction:
+    sign = -1 if byte & 0x80 else 1
+    e, m = (byte >> 3) & 15, byte & 7
+    if e == 15 and m == 7:
+        raise ValueError("E4M3 NaN has no rational value")
+    mag = Fraction(m, 8) * Fraction(1, 64) if e == 0 else Fraction(8 + m, 8) * Fraction(2) ** (e - 7)
+    return sign * mag
+
+
+def nvfp4_exact_gemm(A_bits, packed, scale_bytes, alpha: Fraction, M: int, N: int, K: int):
+    """Exact rational C for tiny shapes (Python integers and Fractions only).
+
+    Each element and scale is decoded from its bit fields by the format
+    definition, independently of nvfp4.c.
+    """
+    A_bits = np.asarray(A_bits, dtype=np.uint16).reshape(-1, K)
+    packed = np.asarray(packed, dtype=np.uint8).reshape(N, K // 2)
+    scale_bytes = np.asarray(scale_bytes, dtype=np.uint8).reshape(N, K // NVFP4_BLOCK)
+    out = [[Fraction(0)] * N for _ in range(M)]
+    for n in range(N):
+        for k in range(K):
+            byte = int(packed[n, k // 2])
+            code = byte & 0xF if k % 2 == 0 else byte >> 4
+            w = alpha * _e2m1_fraction(code) * _e4m3_fraction(int(scale_bytes[n, k // NVFP4_BLOCK]))
+            if w == 0:
+                continue
+            for m in range(M):
+                out[m][n] += _bf16_fraction(int(A_bits[m, k])) * w
     return out

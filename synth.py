@@ -19,6 +19,17 @@ section "Specifications": hidden 5120, 24 Q / 4 KV heads of head_dim 256,
 
 Draw order from ``numpy.random.default_rng(seed)``: words, then scales, then A
 (16 rows; an M-row call uses the first M rows).
+
+NVFP4 weight-only variant (same shapes, seeds offset by 10):
+
+* codes: uniform bytes, i.e. two independent uniform 4-bit E2M1 codes per
+  byte (all 16 codes, -0 included), packed uint8 [N, K/2];
+* block scales: E4M3 bytes with sign 0, exponent field uniform on [4, 10] and
+  mantissa uniform on [0, 7] (values 2^-3 .. 1.875 * 2^3: finite and
+  positive, as a block maximum over 6 is after a per-tensor factor), uint8
+  [N, K/16];
+* per-tensor factor: fp32(0.0037);
+* A as above; draw order codes, scales, A.
 """
 from __future__ import annotations
 
@@ -107,6 +118,39 @@ def gen_problem(K: int, N: int, seed: int, act: str = "normal", M: int = M_MAX):
 def gen_workload(name: str, M: int = M_MAX):
     w = WORKLOADS[name]
     return gen_problem(w.K, w.N, w.seed, w.act, M)
+
+
+NVFP4_BLOCK = 16
+NVFP4_SEED_OFFSET = 10
+NVFP4_ALPHA = float(np.float32(0.0037))
+
+
+def gen_nvfp4_weights(K: int, N: int, rng: np.random.Generator):
+    """(packed codes uint8 [N, K/2], E4M3 scale bytes uint8 [N, K/16])."""
+    if K % GROUP or N <= 0:
+        raise ValueError("K must be a multiple of 128")
+    packed = rng.integers(0, 256, size=(N, K // 2), dtype=np.uint8)
+    e = rng.integers(4, 11, size=(N, K // NVFP4_BLOCK), dtype=np.uint8)
+    m = rng.integers(0, 8, size=(N, K // NVFP4_BLOCK), dtype=np.uint8)
+    return packed, ((e << 3) | m).astype(np.uint8)
+
+
+def gen_nvfp4_problem(K: int, N: int, seed: int, act: str = "normal", M: int = M_MAX):
+    """(A, packed, scale bytes) for one seeded NVFP4 problem, drawn in the documented order."""
+    rng = np.random.default_rng(seed)
+    packed, scales = gen_nvfp4_weights(K, N, rng)
+    A = gen_activations(M, K, rng, act)
+    return A, packed, scales
+
+
+def gen_nvfp4_workload(name: str, M: int = M_MAX):
+    w = WORKLOADS[name]
+    return gen_nvfp4_problem(w.K, w.N, w.seed + NVFP4_SEED_OFFSET, w.act, M)
+
+
+def algorithmic_bytes_nvfp4(M: int, N: int, K: int) -> int:
+    """Bytes of one NVFP4 call: 4-bit codes, one E4M3 byte per 16 weights, bf16 A, bf16 C."""
+    return K * N // 2 + (K // NVFP4_BLOCK) * N + M * K * 2 + M * N * 2
 
 
 def algorithmic_bytes_silu_mul(M: int, N: int, K: int) -> int:

@@ -36,6 +36,7 @@ if ROOT not in sys.path:
 import synth  # noqa: E402
 
 METRIC = "achieved HBM GB/s (% of peak) for W4A16 matmul at M=1,4,8,16; µs/call"
+METRIC_NVFP4 = "achieved HBM GB/s (% of peak) for the NVFP4 weight-only (W4A16) matmul; µs/call"
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
 PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 LLC_BYTES = 256 << 20          # MI355X Infinity Cache
@@ -44,7 +45,11 @@ KERNEL_SOURCES = ["weight_only_int4_gptq_amd/csrc/w4a16.hip",
                   "weight_only_int4_gptq_amd/csrc/w4a16_kernels.hpp",
                   "weight_only_int4_gptq_amd/csrc/w4a16_variants.hpp",
                   "weight_only_int4_gptq_amd/csrc/variants_plain.hip",
-                  "weight_only_int4_gptq_amd/csrc/variants_epi.hip"]
+                  "weight_only_int4_gptq_amd/csrc/variants_epi.hip",
+                  "weight_only_int4_gptq_amd/csrc/variants_plain_rt.hip",
+                  "weight_only_int4_gptq_amd/csrc/variants_epi_rt.hip",
+                  "weight_only_int4_gptq_amd/build.py",
+                  "weight_only_int4_gptq_amd/csrc/variants_nvfp4.hip"]
 
 
 def log(*a):
@@ -81,9 +86,51 @@ class Problem:
         self.K, self.N, self.sets = K, N, sets
         torch.cuda.synchronize()
 
+    fmt = "gptq"
+
     def call(self, w4, M, i):
         j = i % self.sets
         w4.gemm(self.acts[j][:M], self.blobs[j], self.scales[j], self.N, out=self.outs[j][:M])
+
+    def bytes(self, M):
+        return synth.algorithmic_bytes(M, self.N, self.K)
+
+    def oracle_call(self, M, **kw):
+        import oracle
+        A, qw, sc = self.host
+        return oracle.gemm(A, qw, sc, M, self.N, self.K, **kw)
+
+
+class NvProblem:
+    """NVFP4 buffers for one (K, N) shape over `sets` distinct buffer sets (same interface as Problem)."""
+
+    fmt = "nvfp4"
+
+    def __init__(self, torch, w4, K, N, seed, act, sets, Mmax=16):
+        dev = torch.device("cuda:0")
+        A, packed, sc = synth.gen_nvfp4_problem(K, N, seed, act, Mmax)
+        self.host = (A, packed, sc)
+        blob, s = w4.nvfp4_repack(torch.from_numpy(packed).to(dev), torch.from_numpy(sc).to(dev), K, N)
+        a = torch.from_numpy(A.view(np.int16)).to(dev).view(torch.bfloat16)
+        self.blobs = [blob] + [blob.clone() for _ in range(sets - 1)]
+        self.scales = [s] + [s.clone() for _ in range(sets - 1)]
+        self.acts = [a] + [a.clone() for _ in range(sets - 1)]
+        self.outs = [torch.empty((Mmax, N), dtype=torch.bfloat16, device=dev) for _ in range(sets)]
+        self.K, self.N, self.sets = K, N, sets
+        torch.cuda.synchronize()
+
+    def call(self, w4, M, i):
+        j = i % self.sets
+        w4.nvfp4_gemm(self.acts[j][:M], self.blobs[j], self.scales[j], synth.NVFP4_ALPHA, self.N,
+                      out=self.outs[j][:M])
+
+    def bytes(self, M):
+        return synth.algorithmic_bytes_nvfp4(M, self.N, self.K)
+
+    def oracle_call(self, M, **kw):
+        import oracle
+        A, packed, sc = self.host
+        return oracle.nvfp4_gemm(A, packed, sc, synth.NVFP4_ALPHA, M, self.N, self.K, **kw)
 
 
 def sets_for(K, N, M):
@@ -124,7 +171,7 @@ def graph_steps(args, nbytes):
 
 def measure(torch, w4, prob, M, steps, warmup):
     ms_graph = time_graph(torch, lambda i: prob.call(w4, M, i), steps, warmup)
-    nbytes = synth.algorithmic_bytes(M, prob.N, prob.K)
+    nbytes = prob.bytes(M)
     flops = 2.0 * M * prob.N * prob.K
     return {
         "ms_per_step": ms_graph,
@@ -150,17 +197,16 @@ def copy_calibration(torch, mib, reps=4):
 def cpu_baseline(prob, M, seconds=10.0):
     import oracle
 
-    A, qw, sc = prob.host
     nthreads = oracle.max_threads()
-    oracle.gemm(A, qw, sc, M, prob.N, prob.K, cols=np.arange(64))    # load + warm
+    prob.oracle_call(M, cols=np.arange(64))    # load + warm
     reps, t0 = 0, time.perf_counter()
     while True:
-        oracle.gemm(A, qw, sc, M, prob.N, prob.K, nthreads=nthreads)
+        prob.oracle_call(M, nthreads=nthreads)
         reps += 1
         el = time.perf_counter() - t0
         if el >= seconds:
             break
-    nbytes = synth.algorithmic_bytes(M, prob.N, prob.K) * reps
+    nbytes = prob.bytes(M) * reps
     return {"value": round(nbytes / el / 1e9, 3), "unit": "GB/s", "cores": nthreads, "kind": "oracle",
             "sample": f"{reps} full calls of the same workload (M={M}, K={prob.K}, N={prob.N}), "
                       f"{el:.1f} s wall, fp64 C oracle with OpenMP over columns; "
@@ -197,7 +243,9 @@ def summarize_profiles(args):
     trace_dir, fetch_dir, write_dir = args.summarize
     wname, M, mib = args.workload, args.m, args.copy_calib
     wl = synth.WORKLOADS[wname]
-    tag = f"{wname}_m{M}"
+    nv = args.format == "nvfp4"
+    tag = f"{'nvfp4_' if nv else ''}{wname}_m{M}"
+    fmt_flag = " --format nvfp4" if nv else ""
     copy_kib = float(mib << 10)
 
     def counter(d):
@@ -213,9 +261,10 @@ def summarize_profiles(args):
     _, w_kib, nw, w_copy, ncw = counter(write_dir)
     f_fac, w_fac = copy_kib / f_copy, copy_kib / w_copy
     nbytes = round((f_kib * f_fac + w_kib * w_fac) * 1024)
-    algo = synth.algorithmic_bytes(M, wl.N, wl.K)
+    algo = (synth.algorithmic_bytes_nvfp4 if nv else synth.algorithmic_bytes)(M, wl.N, wl.K)
     cmd_f = (f"rocprofv3 --pmc FETCH_SIZE -d {fetch_dir} -o run --output-format csv -- "
-             f"python3 bench.py --workload {wname} --m {M} --steps 20 --warmup 5 --no-cpu --copy-calib {mib}")
+             f"python3 bench.py --workload {wname} --m {M}{fmt_flag} --steps 20 --warmup 5 --no-cpu "
+             f"--copy-calib {mib}")
     cmd_w = cmd_f.replace("FETCH_SIZE", "WRITE_SIZE").replace(fetch_dir, write_dir)
     path = os.path.join(ROOT, "profiles", "traffic.json")
     try:
@@ -234,7 +283,7 @@ def summarize_profiles(args):
 
     kshort = kname.split("(")[0].replace("void ", "").replace("w4a16::", "")
     with open(os.path.join(ROOT, "profiles", f"gemm_kernel_{tag}_hbm_bytes.md"), "w") as f:
-        f.write(f"# HBM bytes per launch: {kshort}, {wl.desc}, M={M}\n\n")
+        f.write(f"# HBM bytes per launch: {kshort}, {wl.desc}, M={M}{', NVFP4' if nv else ''}\n\n")
         f.write("Commands (repo root, TMPDIR=/tmp):\n\n")
         f.write(f"    {cmd_f}\n    {cmd_w}\n\n")
         f.write("| counter | matmul kernel, median KiB/dispatch | dispatches | "
@@ -249,9 +298,11 @@ def summarize_profiles(args):
     d = [int(r["End_Timestamp"]) - int(r["Start_Timestamp"]) for r in rows]
     stats = _csv_rows(os.path.join(trace_dir, "run_kernel_stats.csv"))
     with open(os.path.join(ROOT, "profiles", f"gemm_kernel_{tag}_kernel_trace.md"), "w") as f:
-        f.write(f"# Kernel trace: {wl.desc}, M={M} (the default bench run)\n\n")
+        what = f"NVFP4 weights, M={M}" if nv else f"M={M} (the default bench run)"
+        f.write(f"# Kernel trace: {wl.desc}, {what}\n\n")
+        extra = f" --workload {wname} --m {M}{fmt_flag}" if (nv or wname != "qkv" or M != 1) else ""
         f.write(f"Command (repo root, TMPDIR=/tmp):\n\n    rocprofv3 --kernel-trace --stats -d {trace_dir} "
-                f"-o run --output-format csv -- python3 bench.py\n\n")
+                f"-o run --output-format csv -- python3 bench.py{extra}\n\n")
         f.write("rocprofv3 --stats summary (run_kernel_stats.csv):\n\n| kernel | calls | average ns | min ns | max ns |\n|---|---|---|---|---|\n")
         for r in stats:
             f.write(f"| {r['Name'][:90]} | {r['Calls']} | {float(r['AverageNs']):.0f} | {r['MinNs']} | {r['MaxNs']} |\n")
@@ -271,6 +322,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--workload", default="qkv", choices=sorted(synth.WORKLOADS))
     ap.add_argument("--m", type=int, default=1)
+    ap.add_argument("--format", default="gptq", choices=("gptq", "nvfp4"),
+                    help="weight format of the measured call (gptq: the headline INT4 group-128 path)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--sweep", action="store_true", help="one JSON line per (workload, M)")
@@ -302,7 +355,7 @@ def main():
     name = torch.cuda.get_device_name(0)
 
     if args.sweep:
-        return sweep(torch, w4, args)
+        return nvfp4_sweep(torch, w4, args) if args.format == "nvfp4" else sweep(torch, w4, args)
     if args.stack:
         return stack(torch, w4, args)
     if args.ceiling:
@@ -313,10 +366,15 @@ def main():
     wl = synth.WORKLOADS[args.workload]
     M = args.m
     sets = sets_for(wl.K, wl.N, M)
-    log(f"bench: {wl.desc} M={M} on {name}; {sets} buffer sets")
-    prob = Problem(torch, w4, wl.K, wl.N, wl.seed, wl.act, sets)
+    nv = args.format == "nvfp4"
+    log(f"bench: {wl.desc} M={M} ({args.format}) on {name}; {sets} buffer sets")
+    if nv:
+        prob = NvProblem(torch, w4, wl.K, wl.N, wl.seed + synth.NVFP4_SEED_OFFSET, wl.act, sets)
+    else:
+        prob = Problem(torch, w4, wl.K, wl.N, wl.seed, wl.act, sets)
     r = measure(torch, w4, prob, M, args.steps, args.warmup)
-    plan = w4.get_plan(M, wl.N, wl.K).as_dict()
+    plan = (w4.nvfp4_get_plan if nv else w4.get_plan)(M, wl.N, wl.K).as_dict()
+    tag = f"{'nvfp4_' if nv else ''}{args.workload}_m{M}"
     log(f"bench: {r['us_per_call']:.3f} us/call {r['gbs']:.0f} GB/s; plan {plan}")
     if args.copy_calib:
         copy_calibration(torch, args.copy_calib)
@@ -324,9 +382,9 @@ def main():
     # one launch per step: the per-launch duration is the timed region / steps
     roof = {"bound": "hbm", "achieved": round(r["gbs"], 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
             "frac": round(r["gbs"] / PEAK_HBM_GBS, 4),
-            "traffic": traffic_record(f"{args.workload}_m{M}")}
+            "traffic": traffic_record(tag)}
     out = {
-        "metric": METRIC,
+        "metric": METRIC_NVFP4 if nv else METRIC,
         "value": round(r["gbs"], 1),
         "unit": "GB/s",
         "n_gpus": 1,
@@ -339,8 +397,9 @@ def main():
         "dtype": "bf16",
         "data": "synthetic",
         "config": {
-            "workload": f"{args.workload}: {wl.desc}, M={M}, group 128",
-            "M": M, "K": wl.K, "N": wl.N, "group": 128,
+            "workload": (f"{args.workload}: {wl.desc}, M={M}, NVFP4 weights (E2M1, E4M3 scale per 16)"
+                         if nv else f"{args.workload}: {wl.desc}, M={M}, group 128"),
+            "M": M, "K": wl.K, "N": wl.N, "group": 16 if nv else 128,
             "us_per_call": round(r["us_per_call"], 3),
             "pct_of_peak_hbm": round(100 * r["gbs"] / PEAK_HBM_GBS, 2),
             "algorithmic_bytes_per_call": r["bytes"],
@@ -359,6 +418,22 @@ def main():
     else:
         out["cpu_baseline"] = None
     print(json.dumps(out), flush=True)
+
+
+def nvfp4_sweep(torch, w4, args):
+    """NVFP4 weight-only calls: one JSON line per (workload, M)."""
+    for wname in ("qkv", "gate_up", "down", "lm_head"):
+        wl = synth.WORKLOADS[wname]
+        sets = sets_for(wl.K, wl.N, 1)
+        prob = NvProblem(torch, w4, wl.K, wl.N, wl.seed + synth.NVFP4_SEED_OFFSET, wl.act, sets)
+        for M in (1, 2, 4, 8, 16):
+            r = measure(torch, w4, prob, M, graph_steps(args, prob.bytes(M)), min(args.warmup, 20))
+            print(json.dumps({"format": "nvfp4", "workload": wname, "M": M, "K": wl.K, "N": wl.N,
+                              "plan": w4.nvfp4_get_plan(M, wl.N, wl.K).as_dict(),
+                              "us_per_call": round(r["us_per_call"], 3), "GBps": round(r["gbs"], 1),
+                              "pct_peak": round(100 * r["gbs"] / PEAK_HBM_GBS, 2), "sets": sets}), flush=True)
+        del prob
+        torch.cuda.empty_cache()
 
 
 def sweep(torch, w4, args):

@@ -67,6 +67,7 @@ extern "C" {
 #define W4A16_ERR_PLAN       -8   /* an explicit plan names a variant this build does not have */
 
 #define W4A16_GROUP 128
+#define W4A16_NVFP4_GROUP 16   /* rows per E4M3 block scale of the NVFP4 calls */
 #define W4A16_MAX_M 16
 
 /* Execution paths of the row-count dispatcher. */
@@ -284,6 +285,82 @@ int w4a16_dequant(const void *wq_repacked, const void *scales, float *W, int K, 
  * codes[k][n] = q in [0, 15], device uint8 [K][N] (written).
  */
 int w4a16_unpack(const void *wq_repacked, uint8_t *codes, int K, int N, void *stream);
+
+/*
+ * ---------------------------------------------------------------- NVFP4
+ * The same decode/verify matmul for NVFP4 weight-only checkpoints: the
+ * compressed-tensors "nvfp4-pack-quantized" format of the page "Qwen3.8 27B
+ * - NVFP4 for veloGB10" (section "Specifications"), with group size 16 (page
+ * "SuperQwen3.8-27b-abliterated-NVFP4-2xDGX", table "Release highlights"),
+ * run with BF16 activations as the page "Qwen3.8-27B on DGX Spark (GB10):
+ * vLLM 0.24 + NVFP4, the sm_121 kernel gotcha" describes (W4A16, sections
+ * "What Spark-native means" and "The right stack for Spark").  The pages do
+ * not define the encodings; these calls take the published ones:
+ *
+ *     C[m][n] = alpha * sum_k A[m][k] * e2m1(code(k, n)) * e4m3(scale(k/16, n))
+ *
+ *   packed   uint8 [N][K/2]: row n holds column n of W; byte j holds the
+ *            FP4 E2M1 code of row k = 2j in its low nibble and of k = 2j + 1
+ *            in its high nibble (bit 3 sign, bits 2..1 exponent with bias 1,
+ *            bit 0 mantissa).
+ *   scales   uint8 [N][K/16]: FP8 E4M3 (bias 7, OCP encoding) of rows
+ *            16kb .. 16kb + 15 of column n at (n, kb).
+ *   alpha    fp32 per-tensor factor applied to the fp32 sum (for a
+ *            checkpoint that stores a global scale g to divide by, 1/g).
+ *   blob     K*N/2 bytes: 16-byte pieces (t, g, h, c) at piece index
+ *            ((t*G + g)*4 + h)*16 + c (G = K/128); byte 2b + p of a piece
+ *            holds rows 128g + 16b + 4h + 2p (low nibble) and the next row
+ *            (high nibble) of column n = 16t + c.
+ *   repacked scales  K*N/16 bytes: the scale of block 8g + b of column
+ *            n = 16t + c at byte ((t*G + g)*16 + c)*8 + b.
+ * Valid shapes as for the GPTQ calls (K a multiple of 128, N of 16,
+ * 1 <= M <= 16); group must be W4A16_NVFP4_GROUP.  A block scale of NaN
+ * (S.1111.111) makes its outputs NaN.  Plain C output only.
+ */
+
+/* Bytes of the NVFP4 blob (= K*N/2) and of its repacked scales (= K*N/16); 0 for invalid shapes. */
+size_t w4a16_nvfp4_repacked_bytes(int K, int N);
+size_t w4a16_nvfp4_repacked_scale_bytes(int K, int N);
+
+/*
+ * One-time repacks into the layouts above (pure permutations of bytes).
+ *   packed / scales           device, as above (read only)
+ *   wq_repacked / scales_repacked  device, the sizes above (written)
+ */
+int w4a16_nvfp4_repack_weights(const void *packed, void *wq_repacked, int K, int N, void *stream);
+int w4a16_nvfp4_repack_scales(const void *scales, void *scales_repacked, int K, int N, void *stream);
+
+/* Planning for the NVFP4 calls: as w4a16_get_plan, w4a16_check_plan, w4a16_workspace_bytes. */
+int w4a16_nvfp4_get_plan(int M, int N, int K, w4a16_plan_t *plan);
+int w4a16_nvfp4_check_plan(int M, int N, int K, const w4a16_plan_t *plan);
+size_t w4a16_nvfp4_workspace_bytes(int M, int N, int K, const w4a16_plan_t *plan);
+
+/*
+ * C = alpha * A . dequant(blob, scales), dispatched by row count.
+ *   A            device bf16 [M][K]
+ *   wq_repacked, scales   device, from the NVFP4 repacks for this K, N
+ *   alpha        the per-tensor factor
+ *   C            device bf16 [M][N] (written), rounded to nearest even once
+ *   group        must be W4A16_NVFP4_GROUP
+ *   workspace    as for w4a16_gemm, at least w4a16_nvfp4_workspace_bytes(M, N, K, NULL)
+ * Every converted weight e2m1 * e4m3 is exact; each 16-row block's partial
+ * sum is scaled and accumulated in fp32.  Deterministic.
+ */
+int w4a16_nvfp4_gemm(const void *A, const void *wq_repacked, const void *scales, float alpha, void *C,
+                     int M, int N, int K, int group, void *workspace, size_t workspace_bytes,
+                     void *stream);
+
+/* As w4a16_nvfp4_gemm with an explicit plan (no ring A plans for NVFP4). */
+int w4a16_nvfp4_gemm_plan(const void *A, const void *wq_repacked, const void *scales, float alpha,
+                          void *C, int M, int N, int K, int group, void *workspace,
+                          size_t workspace_bytes, const w4a16_plan_t *plan, void *stream);
+
+/*
+ * Test export of the NVFP4 device dequantization: W[k][n] = e2m1 * e4m3 as
+ * fp32 (exact; without alpha), device fp32 [K][N] (written).
+ */
+int w4a16_nvfp4_dequant(const void *wq_repacked, const void *scales, float *W, int K, int N,
+                        void *stream);
 
 #ifdef __cplusplus
 }

@@ -24,7 +24,7 @@ NULL = ctypes.c_void_p(0)
 
 def declared_functions():
     text = open(HEADER).read()
-    return sorted(set(re.findall(r"\b(w4a16_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(w4a16_[a-z0-9_]+)\s*\(", text)))
 
 
 def test_library_exports_every_declared_symbol():
@@ -216,3 +216,40 @@ def test_argmax_without_device():
     if torch.cuda.is_available():
         pytest.skip("a GPU is present")
     assert _argmax() == -6          # N = 1008: a multiple of 16 is enough here
+
+
+def _nv(A=P, wq=P, s=P, C=P2, M=1, N=1024, K=512, group=16, ws=NULL, wsb=0, plan=None, alpha=1.0):
+    L = w4.lib()
+    if plan is None:
+        return L.w4a16_nvfp4_gemm(A, wq, s, alpha, C, M, N, K, group, ws, wsb, NULL)
+    return L.w4a16_nvfp4_gemm_plan(A, wq, s, alpha, C, M, N, K, group, ws, wsb, ctypes.byref(plan), NULL)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(A=NULL), -1), (dict(C=NULL), -1), (dict(s=NULL), -1), (dict(M=0), -2), (dict(M=17), -2),
+    (dict(K=520), -2), (dict(N=1000), -2), (dict(group=128), -3), (dict(C=ODD), -4),
+    (dict(plan=w4.make_plan(w4.PATH_MFMA, 4, 4, 1, w4.ASRC_RING)), -8),     # no ring A for NVFP4
+    (dict(plan=w4.make_plan(w4.PATH_GEMV, 1, 4), M=5), -8),
+])
+def test_nvfp4_argument_errors(kw, status):
+    assert _nv(**kw) == status
+
+
+def test_nvfp4_sizes_plans_and_no_device():
+    assert w4.nvfp4_repacked_bytes(5120, 8192) == 5120 * 8192 // 2
+    assert w4.nvfp4_repacked_scale_bytes(5120, 8192) == 5120 * 8192 // 16
+    assert w4.nvfp4_repacked_bytes(100, 16) == 0
+    L = w4.lib()
+    assert L.w4a16_nvfp4_repack_weights(NULL, P, 512, 1024, NULL) == -1
+    assert L.w4a16_nvfp4_repack_weights(P, P2, 512, 1000, NULL) == -2
+    assert L.w4a16_nvfp4_repack_scales(ODD, P2, 512, 1024, NULL) == -4
+    assert L.w4a16_nvfp4_dequant(P, NULL, P2, 512, 1024, NULL) == -1
+    for M in range(1, 17):
+        for (N, K) in ((8192, 5120), (34816, 5120), (5120, 17408), (248320, 5120), (1024, 512), (16, 128)):
+            p = w4.nvfp4_get_plan(M, N, K)
+            assert w4.nvfp4_plan_ok(M, N, K, p), (M, N, K, p)
+            assert p.asrc != w4.ASRC_RING
+    import torch
+    if not torch.cuda.is_available():
+        assert _nv() == -6
+        assert L.w4a16_nvfp4_repack_weights(P, P2, 512, 1024, NULL) == -6

@@ -20,6 +20,7 @@ OK = 0
 PATH_AUTO, PATH_GEMV, PATH_MFMA = 0, 1, 2
 ASRC_LDS, ASRC_GLOBAL, ASRC_RING = 0, 1, 2
 GROUP = 128
+NVFP4_GROUP = 16
 
 
 class W4A16Error(RuntimeError):
@@ -74,6 +75,24 @@ def lib():
         L.w4a16_gemm_silu_mul_plan.argtypes = [P, P, P, P, I, I, I, I, P, S, ctypes.POINTER(Plan), P]
         L.w4a16_dequant.argtypes = [P, P, P, I, I, P]
         L.w4a16_unpack.argtypes = [P, P, I, I, P]
+        F = ctypes.c_float
+        L.w4a16_nvfp4_repacked_bytes.argtypes = [I, I]
+        L.w4a16_nvfp4_repacked_bytes.restype = S
+        L.w4a16_nvfp4_repacked_scale_bytes.argtypes = [I, I]
+        L.w4a16_nvfp4_repacked_scale_bytes.restype = S
+        L.w4a16_nvfp4_repack_weights.argtypes = [P, P, I, I, P]
+        L.w4a16_nvfp4_repack_scales.argtypes = [P, P, I, I, P]
+        L.w4a16_nvfp4_get_plan.argtypes = [I, I, I, ctypes.POINTER(Plan)]
+        L.w4a16_nvfp4_check_plan.argtypes = [I, I, I, ctypes.POINTER(Plan)]
+        L.w4a16_nvfp4_workspace_bytes.argtypes = [I, I, I, ctypes.POINTER(Plan)]
+        L.w4a16_nvfp4_workspace_bytes.restype = S
+        L.w4a16_nvfp4_gemm.argtypes = [P, P, P, F, P, I, I, I, I, P, S, P]
+        L.w4a16_nvfp4_gemm_plan.argtypes = [P, P, P, F, P, I, I, I, I, P, S, ctypes.POINTER(Plan), P]
+        L.w4a16_nvfp4_dequant.argtypes = [P, P, P, I, I, P]
+        for f in ("w4a16_nvfp4_repack_weights", "w4a16_nvfp4_repack_scales", "w4a16_nvfp4_get_plan",
+                  "w4a16_nvfp4_check_plan", "w4a16_nvfp4_gemm", "w4a16_nvfp4_gemm_plan",
+                  "w4a16_nvfp4_dequant"):
+            getattr(L, f).restype = I
         for f in ("w4a16_repack_weights", "w4a16_get_plan", "w4a16_gemm", "w4a16_gemm_plan",
                   "w4a16_gemm_silu_mul", "w4a16_gemm_silu_mul_plan", "w4a16_gemm_argmax",
                   "w4a16_gemm_argmax_plan", "w4a16_gemm_f32", "w4a16_gemm_f32_plan",
@@ -274,3 +293,71 @@ def unpack(blob: torch.Tensor, K: int, N: int) -> torch.Tensor:
     codes = torch.empty((K, N), dtype=torch.uint8, device=blob.device)
     _check(lib().w4a16_unpack(_ptr(blob), _ptr(codes), K, N, _stream(blob)), "w4a16_unpack")
     return codes
+
+
+# ---------------------------------------------------------------- NVFP4
+
+def nvfp4_repacked_bytes(K: int, N: int) -> int:
+    return int(lib().w4a16_nvfp4_repacked_bytes(K, N))
+
+
+def nvfp4_repacked_scale_bytes(K: int, N: int) -> int:
+    return int(lib().w4a16_nvfp4_repacked_scale_bytes(K, N))
+
+
+def nvfp4_repack(packed: torch.Tensor, scales: torch.Tensor, K: int, N: int):
+    """One-time repacks of NVFP4 weights: packed E2M1 codes (uint8 device
+    tensor [N, K/2]) and E4M3 block scales (uint8 [N, K/16]) ->
+    (blob uint8 [K*N/2], repacked scales uint8 [K*N/16])."""
+    blob = torch.empty(max(nvfp4_repacked_bytes(K, N), 1), dtype=torch.uint8, device=packed.device)
+    sc = torch.empty(max(nvfp4_repacked_scale_bytes(K, N), 1), dtype=torch.uint8, device=packed.device)
+    _check(lib().w4a16_nvfp4_repack_weights(_ptr(packed), _ptr(blob), K, N, _stream(packed)),
+           "w4a16_nvfp4_repack_weights")
+    _check(lib().w4a16_nvfp4_repack_scales(_ptr(scales), _ptr(sc), K, N, _stream(scales)),
+           "w4a16_nvfp4_repack_scales")
+    return blob, sc
+
+
+def nvfp4_get_plan(M: int, N: int, K: int) -> Plan:
+    p = Plan()
+    _check(lib().w4a16_nvfp4_get_plan(M, N, K, ctypes.byref(p)), "w4a16_nvfp4_get_plan")
+    return p
+
+
+def nvfp4_plan_ok(M: int, N: int, K: int, plan: Plan) -> bool:
+    return lib().w4a16_nvfp4_check_plan(M, N, K, ctypes.byref(plan)) == OK
+
+
+def nvfp4_workspace_bytes(M: int, N: int, K: int, plan: Plan | None = None) -> int:
+    return int(lib().w4a16_nvfp4_workspace_bytes(M, N, K, ctypes.byref(plan) if plan else None))
+
+
+def nvfp4_gemm(A: torch.Tensor, blob: torch.Tensor, scales: torch.Tensor, alpha: float, N: int,
+               out: torch.Tensor | None = None, plan: Plan | None = None,
+               workspace: torch.Tensor | None = None, group: int = NVFP4_GROUP):
+    """C[M, N] = alpha * A . dequant(blob, scales) for NVFP4 weights (from ``nvfp4_repack``)."""
+    M, K = A.shape
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.bfloat16, device=A.device)
+    if workspace is None:
+        need = nvfp4_workspace_bytes(M, N, K, plan)
+        if need:
+            workspace = _shared_workspace(A.device, need)
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    if plan is None:
+        st = lib().w4a16_nvfp4_gemm(_ptr(A), _ptr(blob), _ptr(scales), float(alpha), _ptr(out), M, N, K,
+                                    group, _ptr(workspace), ws_bytes, _stream(A))
+    else:
+        st = lib().w4a16_nvfp4_gemm_plan(_ptr(A), _ptr(blob), _ptr(scales), float(alpha), _ptr(out), M, N,
+                                         K, group, _ptr(workspace), ws_bytes, ctypes.byref(plan),
+                                         _stream(A))
+    _check(st, "w4a16_nvfp4_gemm")
+    return out
+
+
+def nvfp4_dequant(blob: torch.Tensor, scales: torch.Tensor, K: int, N: int) -> torch.Tensor:
+    """Test export: fp32 W[K, N] = e2m1 * e4m3 from the device conversions (repacked inputs)."""
+    W = torch.empty((K, N), dtype=torch.float32, device=blob.device)
+    _check(lib().w4a16_nvfp4_dequant(_ptr(blob), _ptr(scales), _ptr(W), K, N, _stream(blob)),
+           "w4a16_nvfp4_dequant")
+    return W

@@ -14,8 +14,17 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 LIB = os.path.join(PKG, "libw4a16.so")
 # compiled separately (in parallel) and linked into one library: the host
-# code, and the two instantiation sets of the matmul kernels
-SOURCES = [os.path.join(PKG, "csrc", f) for f in ("w4a16.hip", "variants_plain.hip", "variants_epi.hip")]
+# code, the GPTQ matmul kernels (plain and with epilogue modes, each in
+# compile-time-row and run-time-row units) and the NVFP4 ones
+SOURCES = [os.path.join(PKG, "csrc", f) for f in ("w4a16.hip", "variants_plain.hip", "variants_plain_rt.hip",
+                                                   "variants_epi.hip", "variants_epi_rt.hip", "variants_nvfp4.hip")]
+# Matrix-core results in ordinary VGPRs rather than accumulation registers:
+# the kernels that read every product back with VALU instructions (the
+# NVFP4 block scales; the run-time-row shapes) otherwise copy each result out
+# of the accumulation registers first.  Measured per unit: the GEMV and
+# compile-time-row kernels are as fast or faster without it.
+SOURCE_FLAGS = {name: ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]
+                for name in ("variants_plain_rt.hip", "variants_epi_rt.hip", "variants_nvfp4.hip")}
 PROBE_LIB = os.path.join(PKG, "libw4a16_probe.so")
 PROBE_SOURCES = [os.path.join(PKG, "csrc", "probe_stream.hip")]
 DEPENDS = SOURCES + [os.path.join(PKG, "csrc", "w4a16_kernels.hpp"), os.path.join(PKG, "csrc", "w4a16_variants.hpp"),
@@ -46,7 +55,8 @@ def _compile(out: str, sources: list, verbose: bool) -> str:
     objs = [out + "." + os.path.basename(src) + ".o" for src in sources]
     procs = []
     for src, obj in zip(sources, objs):
-        cmd = [hipcc()] + FLAGS + ["-I", os.path.join(ROOT, "include"), "-c", "-o", obj, src]
+        cmd = ([hipcc()] + FLAGS + SOURCE_FLAGS.get(os.path.basename(src), []) +
+               ["-I", os.path.join(ROOT, "include"), "-c", "-o", obj, src])
         procs.append((subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.PIPE, text=True), src))
     errs = []
     for proc, src in procs:

@@ -1,5 +1,5 @@
 // Matmul kernels that carry the epilogue modes (gate/up activation, row
-// argmax, fp32 output), for every compiled shape.
+// argmax, fp32 output), compile-time row counts.
 #include <hip/hip_runtime.h>
 
 #include "w4a16_variants.hpp"
@@ -7,6 +7,7 @@
 namespace w4a16 {
 
 #define W4A16_V(P, MM, T, KW, D, AS) {P, MM, T, KW, D, AS, gemm_kernel<P, MM, T, KW, D, AS, true>},
-const Variant kVariantsEpi[] = {W4A16_VARIANT_LIST(W4A16_V)};
+const Variant kVariantsEpiCt[] = {W4A16_VARIANT_LIST_CT(W4A16_V)};
+const int kNumEpiCt = sizeof(kVariantsEpiCt) / sizeof(kVariantsEpiCt[0]);
 
 }  // namespace w4a16

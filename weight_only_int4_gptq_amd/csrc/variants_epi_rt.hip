@@ -1,0 +1,13 @@
+// Matmul kernels that carry the epilogue modes (gate/up activation, row
+// argmax, fp32 output) and take the row count at run time.
+#include <hip/hip_runtime.h>
+
+#include "w4a16_variants.hpp"
+
+namespace w4a16 {
+
+#define W4A16_V(P, MM, T, KW, D, AS) {P, MM, T, KW, D, AS, gemm_kernel<P, MM, T, KW, D, AS, true>},
+const Variant kVariantsEpiRt[] = {W4A16_VARIANT_LIST_RT(W4A16_V)};
+const int kNumEpiRt = sizeof(kVariantsEpiRt) / sizeof(kVariantsEpiRt[0]);
+
+}  // namespace w4a16

@@ -22,7 +22,7 @@ using namespace w4a16;
 
 constexpr int kLdsBudget = 64 * 1024;    // automatic GEMV plans: at least two workgroups per CU
 constexpr int kLdsMax = 160 * 1024;      // explicit plans: gfx950's LDS per workgroup
-constexpr int kMaxVariants = 1024;       // bound on the shape count (checked before use)
+constexpr int kMaxVariants = 2048;       // bound on the kernel count over all tables (checked before use)
 
 // ---------------------------------------------------------------- kernel table
 // Two instantiations of every kernel shape (w4a16_variants.hpp): plain
@@ -35,20 +35,47 @@ int default_depth(int tiles) { return tiles == 1 ? 8 : (tiles == 2 ? 4 : 2); }
 // The kernel for a plan: GEMV kernels are compiled per row count (1..4);
 // MFMA kernels too for M <= 4 (LDS or global A), and take M at run time
 // above and with ring A.
-// epi: a kernel that carries the epilogue modes (else a plain matmul)
-const Variant *find_variant(const w4a16_plan_t &p, int M, bool epi = false) {
+// epi: a kernel that carries the epilogue modes (else a plain matmul);
+// fmt: the weight format (NVFP4 kernels are plain matmuls only)
+const Variant *find_variant(const w4a16_plan_t &p, int M, bool epi = false, int fmt = FMT_GPTQ) {
     // ring A kernels take M at run time for every row count
     const int mm = (p.path == W4A16_PATH_GEMV || (M <= 4 && p.asrc != W4A16_ASRC_RING)) ? M : 0;
     const int asrc = (p.path == W4A16_PATH_GEMV) ? ASRC_LDS : p.asrc;
     const int depth = p.depth ? p.depth : default_depth(p.tiles);
-    const Variant *table = epi ? kVariantsEpi : kVariantsPlain;
-    for (int i = 0; i < kNumVariants; ++i) {
-        const Variant &v = table[i];
-        if (v.path == p.path && v.mm == mm && v.tiles == p.tiles && v.kwaves == p.kwaves &&
-            v.depth == depth && v.asrc == asrc)
-            return &v;
+    if (fmt == FMT_NVFP4 && epi) return nullptr;
+    VariantTable tabs[2];
+    int ntabs = 0;
+    if (fmt == FMT_NVFP4) {
+        tabs[ntabs++] = {kVariantsNv, kNumVariantsNv};
+    } else if (epi) {
+        tabs[ntabs++] = {kVariantsEpiCt, kNumEpiCt};
+        tabs[ntabs++] = {kVariantsEpiRt, kNumEpiRt};
+    } else {
+        tabs[ntabs++] = {kVariantsPlainCt, kNumPlainCt};
+        tabs[ntabs++] = {kVariantsPlainRt, kNumPlainRt};
     }
+    for (int ti = 0; ti < ntabs; ++ti)
+        for (int i = 0; i < tabs[ti].n; ++i) {
+            const Variant &v = tabs[ti].v[i];
+            if (v.path == p.path && v.mm == mm && v.tiles == p.tiles && v.kwaves == p.kwaves &&
+                v.depth == depth && v.asrc == asrc)
+                return &v;
+        }
     return nullptr;
+}
+
+// A dense index of a kernel over every table (for per-kernel host caches), or
+// -1 if it is in none.
+int variant_slot(const Variant *v) {
+    const VariantTable tabs[] = {{kVariantsPlainCt, kNumPlainCt}, {kVariantsPlainRt, kNumPlainRt},
+                                 {kVariantsEpiCt, kNumEpiCt},     {kVariantsEpiRt, kNumEpiRt},
+                                 {kVariantsNv, kNumVariantsNv}};
+    int base = 0;
+    for (const VariantTable &t : tabs) {
+        if (v >= t.v && v < t.v + t.n) return base + (int)(v - t.v);
+        base += t.n;
+    }
+    return -1;
 }
 
 // ---------------------------------------------------------------- checks
@@ -97,7 +124,7 @@ int plan_lds(const w4a16_plan_t &p, int M, int G) {
     return lds_layout(p.path, asrc, M, Gwg, p.tiles, p.kwaves, depth).total;
 }
 
-int validate_plan(const w4a16_plan_t &p, int M, int N, int K) {
+int validate_plan(const w4a16_plan_t &p, int M, int N, int K, int fmt = FMT_GPTQ) {
     const int G = K / W4A16_GROUP;
     if (p.path != W4A16_PATH_GEMV && p.path != W4A16_PATH_MFMA) return W4A16_ERR_PLAN;
     if (p.path == W4A16_PATH_GEMV && M > 4) return W4A16_ERR_PLAN;
@@ -105,7 +132,7 @@ int validate_plan(const w4a16_plan_t &p, int M, int N, int K) {
     if (p.asrc != W4A16_ASRC_LDS && p.asrc != W4A16_ASRC_GLOBAL && p.asrc != W4A16_ASRC_RING)
         return W4A16_ERR_PLAN;
     if (p.depth < 0) return W4A16_ERR_PLAN;
-    if (!find_variant(p, M)) return W4A16_ERR_PLAN;
+    if (!find_variant(p, M, false, fmt)) return W4A16_ERR_PLAN;
     if (plan_lds(p, M, G) + 256 > kLdsMax) return W4A16_ERR_PLAN;
     const long long nstrips = (N / 16 + p.tiles - 1) / p.tiles;
     if (nstrips * p.splits >= (1ll << 31)) return W4A16_ERR_PLAN;
@@ -242,6 +269,71 @@ void auto_plan(int M, int N, int K, w4a16_plan_t *out) {
     *out = p;
 }
 
+// NVFP4 plans, from graph-replayed timings of every compiled NVFP4 plan on
+// MI355X (cold weights) over the decoder shapes, M = 1..16.  The matrix-core
+// path pays one scale multiply per 16-row block and output, so it wins later
+// than for GPTQ on narrow N and favours split K for long K:
+//  * M = 1: long K: matrix cores, two tiles, eight wavefronts, A in LDS;
+//    below the gate/up width: GEMV, two tiles, eight wavefronts, depth 2;
+//    wide: GEMV, two tiles, four wavefronts, depth 5;
+//  * M = 2..4: very wide N: four tiles, depth 2; long K: two tiles, eight
+//    wavefronts; narrow N: one tile, eight wavefronts; else two tiles, four
+//    wavefronts; A in LDS throughout;
+//  * M >= 5: very wide N: eight tiles per wavefront from 12 rows, else four
+//    tiles, four wavefronts, A from global memory; wide N: the latter; long
+//    K: four tiles split four ways (A in LDS) up to 8 rows, two ways with A
+//    from global memory above; otherwise two tiles and eight wavefronts with
+//    A in LDS up to 8 rows, four tiles split two ways above.
+// The first of these that this build compiled and that fits is taken, else
+// the first compiled fallback.
+void auto_plan_nv(int M, int N, int K, w4a16_plan_t *out) {
+    const int NT = N / 16, G = K / W4A16_GROUP;
+    const bool wide = NT >= 2048, vwide = NT >= 8192, deep = G >= 128;
+    w4a16_plan_t p;
+    p.path = W4A16_PATH_MFMA;
+    p.tiles = 2;
+    p.kwaves = 4;
+    p.splits = 1;
+    p.asrc = W4A16_ASRC_LDS;
+    p.depth = 4;
+    auto set = [&](int path, int t, int kw, int s, int asrc, int d) {
+        p.path = path, p.tiles = t, p.kwaves = kw, p.splits = s, p.asrc = asrc, p.depth = d;
+    };
+    if (M == 1) {
+        if (deep) set(W4A16_PATH_MFMA, 2, 8, 1, W4A16_ASRC_LDS, 4);
+        else if (!wide) set(W4A16_PATH_GEMV, 2, 8, 1, W4A16_ASRC_LDS, 2);
+        else set(W4A16_PATH_GEMV, 2, 4, 1, W4A16_ASRC_LDS, 5);
+    } else if (M <= 4) {
+        if (vwide) set(W4A16_PATH_MFMA, 4, 4, 1, W4A16_ASRC_LDS, 2);
+        else if (deep) set(W4A16_PATH_MFMA, 2, 8, 1, W4A16_ASRC_LDS, 4);
+        else if (!wide) set(W4A16_PATH_MFMA, 1, 8, 1, W4A16_ASRC_LDS, 4);
+        else set(W4A16_PATH_MFMA, 2, 4, 1, W4A16_ASRC_LDS, 4);
+    } else {
+        if (vwide && M >= 12) set(W4A16_PATH_MFMA, 8, 1, 1, W4A16_ASRC_GLOBAL, 4);
+        else if (wide) set(W4A16_PATH_MFMA, 4, 4, 1, W4A16_ASRC_GLOBAL, 2);
+        else if (deep) set(W4A16_PATH_MFMA, 4, 4, M <= 8 ? 4 : 2, M <= 8 ? W4A16_ASRC_LDS : W4A16_ASRC_GLOBAL, 2);
+        else if (M <= 8) set(W4A16_PATH_MFMA, 2, 8, 1, W4A16_ASRC_LDS, 4);
+        else set(W4A16_PATH_MFMA, 4, 4, 2, W4A16_ASRC_LDS, 2);
+    }
+    // splits no larger than the groups allow (a power of two), and no more
+    // wavefronts along K than each split's groups
+    while (p.splits > 1 && p.splits * p.kwaves > G) p.splits >>= 1;
+    while (p.kwaves > 1 && p.kwaves > G) p.kwaves >>= 1;
+    w4a16_plan_t cand[7] = {p, p, p, p, p, p, p};
+    cand[1].asrc = W4A16_ASRC_GLOBAL;
+    cand[2].tiles = 2, cand[2].kwaves = 4, cand[2].depth = 4, cand[2].splits = 1;
+    cand[3] = cand[2], cand[3].asrc = W4A16_ASRC_GLOBAL;
+    cand[4] = cand[2], cand[4].path = M <= 4 ? W4A16_PATH_GEMV : W4A16_PATH_MFMA;
+    cand[5].tiles = 1, cand[5].kwaves = 1, cand[5].depth = 8, cand[5].splits = 1, cand[5].asrc = W4A16_ASRC_LDS;
+    cand[6] = cand[5], cand[6].path = W4A16_PATH_MFMA, cand[6].asrc = W4A16_ASRC_GLOBAL;
+    for (const w4a16_plan_t &c : cand)
+        if (validate_plan(c, M, N, K, FMT_NVFP4) == W4A16_OK) {
+            *out = c;
+            return;
+        }
+    *out = cand[6];
+}
+
 size_t workspace_for(const w4a16_plan_t &p, int M, int N) {
     if (p.splits <= 1) return 0;
     return (size_t)W4A16_SPLIT_COUNTER_BYTES + (size_t)p.splits * (size_t)M * (size_t)N * sizeof(float);
@@ -272,25 +364,31 @@ void fuse_plan(int M, w4a16_plan_t *p) {
 
 // fuse: 0 plain C[M][N]; 1 the gate/up epilogue, C is H[M][N/2]; 2 the row
 // argmax (C unused, results in idx / val); 3 C as fp32 [M][N]
+// fmt: FMT_GPTQ (group 128, bf16 scales) or FMT_NVFP4 (group 16, E4M3
+// scales, alpha the per-tensor factor; plain C only)
 int run_gemm(const void *A, const void *wq, const void *scales, void *C, int M, int N, int K,
              int group, void *workspace, size_t workspace_bytes, const w4a16_plan_t *user,
-             void *stream, int fuse = 0, int *idx = nullptr, float *val = nullptr) {
+             void *stream, int fuse = 0, int *idx = nullptr, float *val = nullptr,
+             int fmt = FMT_GPTQ, float alpha = 1.0f) {
     if (!A || !wq || !scales) return W4A16_ERR_NULL;
     if (fuse == 2 ? (!idx || !val) : !C) return W4A16_ERR_NULL;
     int st = check_shape(M, N, K);
     if (st != W4A16_OK) return st;
     if (fuse == 1 && N % 32 != 0) return W4A16_ERR_SHAPE;
-    if (group != W4A16_GROUP) return W4A16_ERR_GROUP;
+    if (group != (fmt == FMT_NVFP4 ? W4A16_NVFP4_GROUP : W4A16_GROUP)) return W4A16_ERR_GROUP;
+    if (fmt == FMT_NVFP4 && fuse != 0) return W4A16_ERR_PLAN;
     if (!aligned16(A) || !aligned16(wq) || !aligned16(scales) || (fuse != 2 && !aligned16(C)))
         return W4A16_ERR_ALIGN;
     if (fuse == 2 && (((uintptr_t)idx | (uintptr_t)val) & 3)) return W4A16_ERR_ALIGN;
     w4a16_plan_t p;
     if (user) {
         p = *user;
-        st = validate_plan(p, M, N, K);
+        st = validate_plan(p, M, N, K, fmt);
         if (st != W4A16_OK) return st;
         if (fuse == 1 && p.tiles % 2 != 0) return W4A16_ERR_PLAN;
         if (fuse == 2 && p.splits != 1) return W4A16_ERR_PLAN;
+    } else if (fmt == FMT_NVFP4) {
+        auto_plan_nv(M, N, K, &p);
     } else {
         auto_plan(M, N, K, &p);
         if (fuse == 1) fuse_plan(M, &p);
@@ -309,24 +407,23 @@ int run_gemm(const void *A, const void *wq, const void *scales, void *C, int M, 
     st = check_device(&lds_max);
     if (st != W4A16_OK) return st;
 
-    const Variant *v = find_variant(p, M, fuse != 0);
+    const Variant *v = find_variant(p, M, fuse != 0, fmt);
     if (!v) return W4A16_ERR_PLAN;
     const int lds = plan_lds(p, M, K / W4A16_GROUP);
     if (lds + 256 > lds_max) return W4A16_ERR_PLAN;   // 256: the kernel's static LDS
     if (lds > 65536) {
         // above 64 KiB the kernel must be allowed its dynamic LDS first (once)
-        static std::atomic<uint8_t> raised[2][kMaxVariants];
-        const bool epi = fuse != 0;
-        const size_t vi = (size_t)(v - (epi ? kVariantsEpi : kVariantsPlain));
-        if (vi >= (size_t)kMaxVariants) return W4A16_ERR_LAUNCH;
-        if (!raised[epi][vi].load(std::memory_order_relaxed)) {
+        static std::atomic<uint8_t> raised[kMaxVariants];
+        const int vi = variant_slot(v);
+        if (vi < 0 || vi >= kMaxVariants) return W4A16_ERR_LAUNCH;
+        if (!raised[vi].load(std::memory_order_relaxed)) {
             const void *fn = reinterpret_cast<const void *>(v->fn);
             hipFuncAttributes fa;
             if (hipFuncGetAttributes(&fa, fn) != hipSuccess ||
                 hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize,
                                     lds_max - (int)fa.sharedSizeBytes) != hipSuccess)
                 return W4A16_ERR_LAUNCH;
-            raised[epi][vi].store(1, std::memory_order_relaxed);
+            raised[vi].store(1, std::memory_order_relaxed);
         }
     }
     GemmArgs a;
@@ -347,6 +444,7 @@ int run_gemm(const void *A, const void *wq, const void *scales, void *C, int M, 
     a.fuse = fuse;
     a.amax_idx = idx;
     a.amax_val = val;
+    a.alpha = alpha;
     if (need > 0) {   // split-K partials or argmax bins: the counter region first
         a.count = static_cast<uint32_t *>(workspace);
         a.part = reinterpret_cast<float *>(static_cast<char *>(workspace) + W4A16_SPLIT_COUNTER_BYTES);
@@ -377,7 +475,7 @@ const char *w4a16_status_string(int status) {
         case W4A16_OK: return "ok";
         case W4A16_ERR_NULL: return "null pointer argument";
         case W4A16_ERR_SHAPE: return "invalid shape (need 1<=M<=16, K%128==0, N%16==0)";
-        case W4A16_ERR_GROUP: return "group size must be 128";
+        case W4A16_ERR_GROUP: return "group size must be 128 (GPTQ) or 16 (NVFP4)";
         case W4A16_ERR_ALIGN: return "device pointer not 16-byte aligned";
         case W4A16_ERR_WORKSPACE: return "workspace missing or too small";
         case W4A16_ERR_DEVICE: return "no gfx950 HIP device";
@@ -547,6 +645,117 @@ int w4a16_dequant(const void *wq_repacked, const void *scales, float *W, int K, 
 int w4a16_unpack(const void *wq_repacked, uint8_t *codes, int K, int N, void *stream) {
     if (!wq_repacked || !codes) return W4A16_ERR_NULL;
     return run_export(wq_repacked, nullptr, nullptr, codes, K, N, stream);
+}
+
+// ---------------------------------------------------------------- NVFP4
+
+size_t w4a16_nvfp4_repacked_bytes(int K, int N) {
+    if (check_weight_shape(K, N) != W4A16_OK) return 0;
+    return (size_t)K * (size_t)N / 2;
+}
+
+size_t w4a16_nvfp4_repacked_scale_bytes(int K, int N) {
+    if (check_weight_shape(K, N) != W4A16_OK) return 0;
+    return (size_t)(K / W4A16_NVFP4_GROUP) * (size_t)N;
+}
+
+int w4a16_nvfp4_repack_weights(const void *packed, void *wq_repacked, int K, int N, void *stream) {
+    if (!packed || !wq_repacked) return W4A16_ERR_NULL;
+    int st = check_weight_shape(K, N);
+    if (st != W4A16_OK) return st;
+    if (!aligned16(packed) || !aligned16(wq_repacked)) return W4A16_ERR_ALIGN;
+    st = check_device();
+    if (st != W4A16_OK) return st;
+    const long long npieces = (long long)K * N / 32;
+    const unsigned grid = (unsigned)((npieces + 255) / 256);
+    const uint8_t *in = static_cast<const uint8_t *>(packed);
+    u32x4 *b = static_cast<u32x4 *>(wq_repacked);
+    int k = K, g = K / W4A16_GROUP;
+    long long np = npieces;
+    void *args[] = {&in, &b, &k, &g, &np};
+    const hipError_t e = launch(reinterpret_cast<const void *>(nv_repack_kernel), grid, 256, 0,
+                                static_cast<hipStream_t>(stream), args);
+    return e == hipSuccess ? W4A16_OK : W4A16_ERR_LAUNCH;
+}
+
+int w4a16_nvfp4_repack_scales(const void *scales, void *scales_repacked, int K, int N, void *stream) {
+    if (!scales || !scales_repacked) return W4A16_ERR_NULL;
+    int st = check_weight_shape(K, N);
+    if (st != W4A16_OK) return st;
+    if (!aligned16(scales) || !aligned16(scales_repacked)) return W4A16_ERR_ALIGN;
+    st = check_device();
+    if (st != W4A16_OK) return st;
+    const long long count = (long long)(K / W4A16_NVFP4_GROUP) * N;
+    const unsigned grid = (unsigned)((count + 255) / 256);
+    const uint8_t *in = static_cast<const uint8_t *>(scales);
+    uint8_t *out = static_cast<uint8_t *>(scales_repacked);
+    int k = K, g = K / W4A16_GROUP;
+    long long cnt = count;
+    void *args[] = {&in, &out, &k, &g, &cnt};
+    const hipError_t e = launch(reinterpret_cast<const void *>(nv_repack_scales_kernel), grid, 256, 0,
+                                static_cast<hipStream_t>(stream), args);
+    return e == hipSuccess ? W4A16_OK : W4A16_ERR_LAUNCH;
+}
+
+int w4a16_nvfp4_get_plan(int M, int N, int K, w4a16_plan_t *plan) {
+    if (!plan) return W4A16_ERR_NULL;
+    const int st = check_shape(M, N, K);
+    if (st != W4A16_OK) return st;
+    auto_plan_nv(M, N, K, plan);
+    return W4A16_OK;
+}
+
+int w4a16_nvfp4_check_plan(int M, int N, int K, const w4a16_plan_t *plan) {
+    if (!plan) return W4A16_ERR_NULL;
+    const int st = check_shape(M, N, K);
+    if (st != W4A16_OK) return st;
+    return validate_plan(*plan, M, N, K, FMT_NVFP4);
+}
+
+size_t w4a16_nvfp4_workspace_bytes(int M, int N, int K, const w4a16_plan_t *plan) {
+    if (check_shape(M, N, K) != W4A16_OK) return 0;
+    w4a16_plan_t p;
+    if (plan) {
+        p = *plan;
+        if (validate_plan(p, M, N, K, FMT_NVFP4) != W4A16_OK) return 0;
+    } else {
+        auto_plan_nv(M, N, K, &p);
+    }
+    return workspace_for(p, M, N);
+}
+
+int w4a16_nvfp4_gemm(const void *A, const void *wq_repacked, const void *scales, float alpha, void *C,
+                     int M, int N, int K, int group, void *workspace, size_t workspace_bytes,
+                     void *stream) {
+    return run_gemm(A, wq_repacked, scales, C, M, N, K, group, workspace, workspace_bytes, nullptr,
+                    stream, 0, nullptr, nullptr, FMT_NVFP4, alpha);
+}
+
+int w4a16_nvfp4_gemm_plan(const void *A, const void *wq_repacked, const void *scales, float alpha,
+                          void *C, int M, int N, int K, int group, void *workspace,
+                          size_t workspace_bytes, const w4a16_plan_t *plan, void *stream) {
+    return run_gemm(A, wq_repacked, scales, C, M, N, K, group, workspace, workspace_bytes, plan,
+                    stream, 0, nullptr, nullptr, FMT_NVFP4, alpha);
+}
+
+int w4a16_nvfp4_dequant(const void *wq_repacked, const void *scales, float *W, int K, int N,
+                        void *stream) {
+    if (!wq_repacked || !scales || !W) return W4A16_ERR_NULL;
+    int st = check_weight_shape(K, N);
+    if (st != W4A16_OK) return st;
+    if (!aligned16(wq_repacked) || !aligned16(scales) || !aligned16(W)) return W4A16_ERR_ALIGN;
+    st = check_device();
+    if (st != W4A16_OK) return st;
+    const long long npieces = (long long)K * N / 32;
+    const unsigned grid = (unsigned)((npieces + 255) / 256);
+    const u32x4 *b = static_cast<const u32x4 *>(wq_repacked);
+    const uint8_t *sc = static_cast<const uint8_t *>(scales);
+    int n = N, g = K / W4A16_GROUP;
+    long long np = npieces;
+    void *args[] = {&b, &sc, &W, &n, &g, &np};
+    const hipError_t e = launch(reinterpret_cast<const void *>(nv_export_kernel), grid, 256, 0,
+                                static_cast<hipStream_t>(stream), args);
+    return e == hipSuccess ? W4A16_OK : W4A16_ERR_LAUNCH;
 }
 
 }  // extern "C"

@@ -19,6 +19,16 @@
 // codes are all 8 therefore contributes exactly zero, as it must.  The group
 // scale multiplies the group's partial sum, so no dequantized weight is ever
 // rounded.
+//
+// The same kernels also run the NVFP4 weight-only variant (FMT_NVFP4): 4-bit
+// E2M1 codes with one E4M3 scale per 16 consecutive rows of a column and one
+// fp32 factor per tensor (the nvfp4-pack-quantized checkpoints of the page
+// "Qwen3.8 27B - NVFP4 for veloGB10", section "Specifications"; group size 16
+// on the page "SuperQwen3.8-27b-abliterated-NVFP4-2xDGX", table "Release
+// highlights").  E2M1 -> bf16 is one hardware conversion per code pair, exact
+// and signed, so no bias is needed; the block scale multiplies the 16-row
+// block's partial sum (one 16x16x16 matrix-core product, or two dot2, per
+// block), and the per-tensor factor multiplies the final sum.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -41,14 +51,19 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
 
 enum { PATH_GEMV = 1, PATH_MFMA = 2 };
 enum { ASRC_LDS = 0, ASRC_GLOBAL = 1, ASRC_RING = 2 };
+enum { FMT_GPTQ = 0, FMT_NVFP4 = 1 };
+constexpr int kNvBlock = 16;                   // NVFP4 rows per block scale
 
 struct GemmArgs {
     const uint16_t *A;       // bf16 [M][K]
     const u32x4 *blob;       // repacked weights, 64 pieces of 16 B per (tile, group)
     const uint16_t *scales;  // repacked bf16 scales: [tile][group][16 columns]
+                             // (NVFP4: E4M3 bytes [tile][group][16 columns][8 blocks])
     uint16_t *C;             // bf16 [M][N]
     float *part;             // split-K partials [S][M][N] (S > 1 only)
     uint32_t *count;         // split-K arrival counters [nstrips] (S > 1 only)
@@ -62,6 +77,7 @@ struct GemmArgs {
                              // 3 C as fp32 (unrounded partial sums of a K shard)
     int *amax_idx;           // row argmax: column of each row's maximum [M]
     float *amax_val;         // row argmax: its fp32 value [M]
+    float alpha;             // NVFP4: per-tensor factor of the sum
 };
 
 // Row argmax: per-row maxima meet in kArgmaxBins 64-bit slots per row
@@ -208,6 +224,40 @@ __device__ __forceinline__ f32x4 mfma16x16x32(u32x4 a, u32x4 b, f32x4 c) {
 __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
     return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a),
                                            __builtin_bit_cast(bf16x2, b), c, false);
+}
+
+// ---------------------------------------------------------------- NVFP4 helpers
+// E2M1 code pair (byte SEL of w, low nibble first) -> bf16 pair, by the
+// gfx950 conversion instruction with scale 1.0.  Its scale operand only
+// contributes a power of two, so an E4M3 block scale (three mantissa bits)
+// cannot be folded in here; it multiplies the block's partial sum instead,
+// and every converted weight is exact.
+template <int SEL>
+__device__ __forceinline__ uint32_t e2m1x2_to_bf16x2(uint32_t w) {
+    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, 1.0f, SEL));
+}
+
+// Block B (0..7) of a lane's 16 repacked bytes: rows 4h .. 4h+3 of the
+// block as two bf16 pairs (byte 2B holds rows 4h, 4h+1; byte 2B+1 rows
+// 4h+2, 4h+3).
+template <int B>
+__device__ __forceinline__ u32x2 nv_block(const u32x4 &w) {
+    const uint32_t x = w[B >> 1];
+    return u32x2{e2m1x2_to_bf16x2<2 * (B & 1)>(x), e2m1x2_to_bf16x2<2 * (B & 1) + 1>(x)};
+}
+
+// E4M3 scale of block B from a lane's 8 scale bytes (gfx950 converts OCP E4M3).
+template <int B>
+__device__ __forceinline__ float nv_scale(const uint32_t *s) {
+    return __builtin_amdgcn_cvt_f32_fp8((int)s[B >> 2], B & 3);
+}
+
+// 16x16x16 bf16 product: lane l supplies A[l % 16][4 (l / 16) + i] and
+// B[4 (l / 16) + i][l % 16], i = 0..3, and receives rows 4 (l / 16) + v of
+// column l % 16.
+__device__ __forceinline__ f32x4 mfma16x16x16(u32x2 a, u32x2 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4, a),
+                                                     __builtin_bit_cast(s16x4, b), c, 0, 0, 0);
 }
 
 // Sum of a value over the 4 lanes l, l^16, l^32, l^48 (the four K quarters of
@@ -362,6 +412,73 @@ __global__ void __launch_bounds__(256) export_kernel(const u32x4 *__restrict__ b
     }
 }
 
+// ---------------------------------------------------------------- NVFP4 repack
+// One thread per 16-byte piece (t, g, h, c) of column n = 16 t + c: byte
+// 2 b + p is byte 64 g + 8 b + 2 h + p of column n's packed codes [N][K/2]
+// (rows 128 g + 16 b + 4 h + 2 p and the next one).
+static __global__ void __launch_bounds__(256) nv_repack_kernel(const uint8_t *__restrict__ packed,
+                                                        u32x4 *__restrict__ blob, int K, int G,
+                                                        long long npieces) {
+    const long long pc = (long long)blockIdx.x * 256 + threadIdx.x;
+    if (pc >= npieces) return;
+    const int c = (int)(pc & 15), h = (int)((pc >> 4) & 3);
+    const long long tg = pc >> 6;
+    const int g = (int)(tg % G);
+    const long long t = tg / G;
+    const uint8_t *src = packed + (t * 16 + c) * (long long)(K / 2) + 64 * g + 2 * h;
+    u32x4 out;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        const uint32_t lo = *reinterpret_cast<const uint16_t *>(src + 16 * r);
+        const uint32_t hi = *reinterpret_cast<const uint16_t *>(src + 16 * r + 8);
+        out[r] = lo | (hi << 16);
+    }
+    blob[pc] = out;
+}
+
+// NVFP4 scales [N][K/16] -> [tile][superblock][16 columns][8 blocks]: one
+// thread per byte.
+static __global__ void __launch_bounds__(256) nv_repack_scales_kernel(const uint8_t *__restrict__ scales,
+                                                               uint8_t *__restrict__ out, int K, int G,
+                                                               long long count) {
+    const long long i = (long long)blockIdx.x * 256 + threadIdx.x;
+    if (i >= count) return;
+    const int b = (int)(i & 7), c = (int)((i >> 3) & 15);
+    const long long tg = i >> 7;
+    const int g = (int)(tg % G);
+    const long long t = tg / G;
+    out[i] = scales[(t * 16 + c) * (long long)(K / kNvBlock) + 8 * g + b];
+}
+
+// Test export: fp32 W[k][n] = e2m1 * e4m3 through the GEMM kernels' own
+// conversions (exact: at most six significant bits).
+static __global__ void __launch_bounds__(256) nv_export_kernel(const u32x4 *__restrict__ blob,
+                                                        const uint8_t *__restrict__ scales,
+                                                        float *__restrict__ W, int N, int G,
+                                                        long long npieces) {
+    const long long pc = (long long)blockIdx.x * 256 + threadIdx.x;
+    if (pc >= npieces) return;
+    const int c = (int)(pc & 15), h = (int)((pc >> 4) & 3);
+    const long long tg = pc >> 6;
+    const int g = (int)(tg % G);
+    const long long n = (tg / G) * 16 + c;
+    const u32x4 w = blob[pc];
+    const u32x2 sraw = *reinterpret_cast<const u32x2 *>(scales + (tg * 16 + c) * 8);
+    const uint32_t s[2] = {sraw[0], sraw[1]};
+    [&]<int... B>(std::integer_sequence<int, B...>) {
+        (([&] {
+             const u32x2 v = nv_block<B>(w);
+             const float sc = nv_scale<B>(s);
+             const long long k = (long long)g * kGroup + B * kNvBlock + 4 * h;
+             W[k * N + n] = pair_lo(v[0]) * sc;
+             W[(k + 1) * N + n] = pair_hi(v[0]) * sc;
+             W[(k + 2) * N + n] = pair_lo(v[1]) * sc;
+             W[(k + 3) * N + n] = pair_hi(v[1]) * sc;
+         }()),
+         ...);
+    }(std::make_integer_sequence<int, 8>{});
+}
+
 // ---------------------------------------------------------------- GEMM
 //
 // Work decomposition.  A workgroup owns one column strip of T 16-column tiles
@@ -398,26 +515,32 @@ __global__ void __launch_bounds__(256) export_kernel(const u32x4 *__restrict__ b
 // atomics: the result does not depend on timing.
 // EPI: the kernel carries the epilogue modes of GemmArgs::fuse; without it
 // the mode is 0 (plain C) and no other mode's code is compiled in.
-template <int PATH, int MM, int T, int KW, int D, int ASRC, bool EPI>
+// FMT: the weight format.  NVFP4 pieces have the same geometry (one
+// 1 KiB piece set per 16 columns x 128 rows); lane l holds rows 4h .. 4h+3 of
+// each of the eight 16-row blocks, and 8 scale bytes per (tile, group).
+template <int PATH, int MM, int T, int KW, int D, int ASRC, bool EPI, int FMT = FMT_GPTQ>
 __global__ void __launch_bounds__(64 * KW) gemm_kernel(GemmArgs p) {
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
     __shared__ int s_last;
 
+    constexpr bool kNv = FMT == FMT_NVFP4;
     constexpr bool kGlobalA = (PATH == PATH_MFMA && ASRC == ASRC_GLOBAL);
     constexpr bool kRingA = (PATH == PATH_MFMA && ASRC == ASRC_RING);
     constexpr bool kStage = !kGlobalA && !kRingA;
-    constexpr int kLoadsPerGroup = 2 * T + (kGlobalA ? 4 : 0);   // loads the compiler sees
+    static_assert(!kNv || (!kRingA && !EPI), "NVFP4: plain epilogue, A staged or from global memory");
+    constexpr int kLoadsPerGroup = 2 * T + (kGlobalA ? (kNv ? 8 : 4) : 0);   // loads the compiler sees
     // Matrix-core bias: formed in the loop from the A fragments already
     // loaded (four more MFMAs per group, shared by the T tiles), except for
     // four-tile strips of one or two rows, where one pass over the staged A
     // before the loop measures faster.
-    constexpr bool kBiasInLoop = PATH == PATH_MFMA && !(kStage && MM >= 1 && MM <= 2 && T >= 4);
+    constexpr bool kBiasInLoop = !kNv && PATH == PATH_MFMA && !(kStage && MM >= 1 && MM <= 2 && T >= 4);
     // rows of the 4-row block held by lane group h that are ever stored
     constexpr int kRowsV = (MM >= 1 && MM <= 4) ? MM : 4;
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int M = (MM >= 1) ? MM : p.M;
+    constexpr int kScaleBytes = kNv ? 128 : 32;   // scale bytes per (tile, group)
     const int c = lane & 15, h = lane >> 4;
     const int arow_m = min(c, M - 1);   // MFMA A-operand row of this lane
 
@@ -450,13 +573,15 @@ __global__ void __launch_bounds__(64 * KW) gemm_kernel(GemmArgs p) {
     for (int t = 0; t < T; ++t) {
         const size_t tile = (size_t)min(tile_of(t), p.NT - 1);
         wbase[t] = reinterpret_cast<const uint8_t *>(p.blob) + tile * (size_t)p.G * 1024;
-        sbase[t] = reinterpret_cast<const uint8_t *>(p.scales) + tile * (size_t)p.G * 32;
+        sbase[t] = reinterpret_cast<const uint8_t *>(p.scales) + tile * (size_t)p.G * kScaleBytes;
     }
     const uint32_t w_lane = (uint32_t)lane * 16;             // this lane's 16 B of a 1 KiB piece
-    const uint32_t s_lane = (uint32_t)(c >> 1) * 4;          // dword holding this column's scale
-    const uint32_t s_sel = scale_selector(c);                  // this column's half of the dword
+    // GPTQ: the dword holding this column's bf16 scale, and its half;
+    // NVFP4: this column's 8 block-scale bytes
+    const uint32_t s_lane = kNv ? (uint32_t)c * 8 : (uint32_t)(c >> 1) * 4;
+    const uint32_t s_sel = scale_selector(c);
     const uint8_t *abase = reinterpret_cast<const uint8_t *>(p.A) +
-                           ((size_t)arow_m * p.K + (size_t)h * 32) * 2;   // MFMA A from global
+                           ((size_t)arow_m * p.K + (size_t)h * (kNv ? 4 : 32)) * 2;   // MFMA A from global
 
     // ---- 1. asynchronous LDS fill of this workgroup's K range of A
     if constexpr (kStage) {
@@ -477,8 +602,8 @@ __global__ void __launch_bounds__(64 * KW) gemm_kernel(GemmArgs p) {
 
     // ---- 2. weight ring, D groups deep, issued in slot order
     u32x4 wv[D][T];
-    uint32_t sv[D][T];
-    u32x4 av[kGlobalA ? D : 1][4];
+    uint32_t sv[D][T][kNv ? 2 : 1];
+    u32x4 av[kGlobalA ? D : 1][4];   // NVFP4: av[j][q] = the A fragments of blocks 2q, 2q+1
 
     // Ring A: the group's rows go to this wavefront's LDS slot as contiguous
     // 1 KiB DMA loads (four rows each; rows >= M repeat row M-1).  Inside a
@@ -502,11 +627,26 @@ __global__ void __launch_bounds__(64 * KW) gemm_kernel(GemmArgs p) {
         for (int t = 0; t < T; ++t) {
             wv[j][t] = __builtin_nontemporal_load(
                 reinterpret_cast<const u32x4 *>(wbase[t] + (size_t)g * 1024 + w_lane));
-            // the aligned dword that holds this lane's bf16 scale (a 16-bit
-            // load would be re-extended at the loop latch, which stalls the ring)
-            sv[j][t] = *reinterpret_cast<const uint32_t *>(sbase[t] + (size_t)g * 32 + s_lane);
+            if constexpr (kNv) {
+                const u32x2 x = *reinterpret_cast<const u32x2 *>(sbase[t] + (size_t)g * kScaleBytes + s_lane);
+                sv[j][t][0] = x[0];
+                sv[j][t][1] = x[1];
+            } else {
+                // the aligned dword that holds this lane's bf16 scale (a 16-bit
+                // load would be re-extended at the loop latch, which stalls the ring)
+                sv[j][t][0] = *reinterpret_cast<const uint32_t *>(sbase[t] + (size_t)g * kScaleBytes + s_lane);
+            }
         }
-        if constexpr (kGlobalA) {
+        if constexpr (kGlobalA && kNv) {
+            // rows 16b + 4h .. +3 of the group, b = 0..7: eight 8-byte pieces
+            const uint8_t *ap = abase + (size_t)g * kGroup * 2;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const u32x2 lo = *reinterpret_cast<const u32x2 *>(ap + (2 * q) * kNvBlock * 2);
+                const u32x2 hi = *reinterpret_cast<const u32x2 *>(ap + (2 * q + 1) * kNvBlock * 2);
+                av[j][q] = u32x4{lo[0], lo[1], hi[0], hi[1]};
+            }
+        } else if constexpr (kGlobalA) {
             // A rows >= M repeat row M-1: their results land in output rows
             // that are never written, and the loads stay branch free
             const u32x4 *ap = reinterpret_cast<const u32x4 *>(abase + (size_t)g * kGroup * 2);
@@ -535,7 +675,9 @@ __global__ void __launch_bounds__(64 * KW) gemm_kernel(GemmArgs p) {
             __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
         __builtin_amdgcn_s_barrier();
         float *bias = reinterpret_cast<float *>(smem + L.bias);
-        if constexpr (PATH == PATH_GEMV) {
+        if constexpr (kNv) {
+            // exact signed weights: no bias
+        } else if constexpr (PATH == PATH_GEMV) {
             // each 32-row quarter: the GEMV lane's dot2 chain with every code 8
             for (int m = 0; m < M; ++m)
             for (int rem = threadIdx.x; rem < Gwg * 4; rem += 64 * KW) {
@@ -596,7 +738,61 @@ __global__ void __launch_bounds__(64 * KW) gemm_kernel(GemmArgs p) {
     auto compute_group = [&](auto jc, int g, auto final_) {
         constexpr int j = decltype(jc)::value;
         const int gl = g - gw0;
-        if constexpr (PATH == PATH_MFMA) {
+        if constexpr (kNv) {
+            // Eight 16-row blocks per group; each block's partial sum is
+            // scaled by its E4M3 scale and added, so converted weights stay
+            // exact and no bias arises.
+            if constexpr (PATH == PATH_MFMA) {
+                // A fragments: row arow_m, rows 16b + 4h .. +3 of the group
+                u32x2 a[8];
+                if constexpr (kStage) {
+                    const uint8_t *arow = smem + L.a + arow_m * L.row + (gl * kGroup + 4 * h) * 2;
+#pragma unroll
+                    for (int b = 0; b < 8; ++b) a[b] = *reinterpret_cast<const u32x2 *>(arow + b * kNvBlock * 2);
+                } else {
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        a[2 * q] = u32x2{av[j][q][0], av[j][q][1]};
+                        a[2 * q + 1] = u32x2{av[j][q][2], av[j][q][3]};
+                    }
+                }
+#pragma unroll
+                for (int t = 0; t < T; ++t) {
+                    [&]<int... B>(std::integer_sequence<int, B...>) {
+                        (([&] {
+                             const f32x4 P = mfma16x16x16(a[B], nv_block<B>(wv[j][t]), f32x4{0.0f, 0.0f, 0.0f, 0.0f});
+                             const float sc = nv_scale<B>(sv[j][t]);
+#pragma unroll
+                             for (int v = 0; v < kRowsV; ++v) acc[t][v] = __builtin_fmaf(sc, P[v], acc[t][v]);
+                         }()),
+                         ...);
+                    }(std::make_integer_sequence<int, 8>{});
+                }
+            } else {
+                // GEMV: per block, two dot2 per row on the lane's four rows,
+                // then the scale
+                [&]<int... B>(std::integer_sequence<int, B...>) {
+                    (([&] {
+                         u32x2 ar[MM];
+#pragma unroll
+                         for (int m = 0; m < MM; ++m)
+                             ar[m] = *reinterpret_cast<const u32x2 *>(smem + L.a + m * L.row +
+                                                                     (gl * kGroup + B * kNvBlock + 4 * h) * 2);
+#pragma unroll
+                         for (int t = 0; t < T; ++t) {
+                             const u32x2 w = nv_block<B>(wv[j][t]);
+                             const float sc = nv_scale<B>(sv[j][t]);
+#pragma unroll
+                             for (int m = 0; m < MM; ++m) {
+                                 const float part = dot2_bf16(w[1], ar[m][1], dot2_bf16(w[0], ar[m][0], 0.0f));
+                                 acc[t][m] = __builtin_fmaf(sc, part, acc[t][m]);
+                             }
+                         }
+                     }()),
+                     ...);
+                }(std::make_integer_sequence<int, 8>{});
+            }
+        } else if constexpr (PATH == PATH_MFMA) {
             u32x4 a[4];
             f32x4 Q;
             if constexpr (kStage) {
@@ -642,7 +838,7 @@ __global__ void __launch_bounds__(64 * KW) gemm_kernel(GemmArgs p) {
                     P = mfma16x16x32(a[2 * rp], u32x4{b0[0], b0[1], b0[2], b0[3]}, P);
                     P = mfma16x16x32(a[2 * rp + 1], u32x4{b1[0], b1[1], b1[2], b1[3]}, P);
                 }
-                const float s = scale_from(sv[j][t], s_sel);
+                const float s = scale_from(sv[j][t][0], s_sel);
 #pragma unroll
                 for (int v = 0; v < kRowsV; ++v) acc[t][v] = __builtin_fmaf(s, P[v] - Q[v], acc[t][v]);
             }
@@ -681,7 +877,7 @@ __global__ void __launch_bounds__(64 * KW) gemm_kernel(GemmArgs p) {
             }
 #pragma unroll
             for (int t = 0; t < T; ++t) {
-                const float s = scale_from(sv[j][t], s_sel);
+                const float s = scale_from(sv[j][t][0], s_sel);
 #pragma unroll
                 for (int m = 0; m < MM; ++m) {
                     const float corr = reinterpret_cast<const float *>(smem + L.bias)[(m * Gwg + gl) * 4 + h];
@@ -739,6 +935,7 @@ __global__ void __launch_bounds__(64 * KW) gemm_kernel(GemmArgs p) {
     const int NV = T * M * 16;   // values (t, m, c) of this workgroup
     auto col_of = [&](int t, int cc) { return (size_t)tile_of(t) * 16 + cc; };
     auto emit_c = [&](int t, int m, int cc, float val) {      // plain, one split
+        if constexpr (kNv) val *= p.alpha;
         if (fuse == 3)
             reinterpret_cast<float *>(p.C)[(size_t)m * p.N + col_of(t, cc)] = val;
         else

@@ -36,25 +36,55 @@ struct Variant {
     X(P, MM, 1, 4, 10, AS) X(P, MM, 2, 2, 10, AS) X(P, MM, 4, 2, 5, AS) X(P, MM, 1, 8, 17, AS) \
     X(P, MM, 2, 8, 17, AS) X(P, MM, 2, 4, 17, AS) X(P, MM, 4, 4, 10, AS) X(P, MM, 2, 2, 17, AS)
 
-#define W4A16_VARIANT_LIST(X)                                                                       \
+// Kernels with compile-time rows (GEMV, and matrix-core kernels for one to
+// four rows) and kernels that take the row count at run time (matrix cores,
+// five rows and more, and ring A): two instantiation units each, compiled
+// with different register choices for the matrix-core results (see build.py).
+#define W4A16_VARIANT_LIST_CT(X)                                                                    \
     W4A16_ONESHOT(X, PATH_GEMV, 1, ASRC_LDS) W4A16_ONESHOT(X, PATH_MFMA, 1, ASRC_LDS)               \
     W4A16_ONESHOT(X, PATH_MFMA, 1, ASRC_GLOBAL)                                                     \
     W4A16_SHAPES(X, PATH_GEMV, 1, ASRC_LDS) W4A16_SHAPES(X, PATH_GEMV, 2, ASRC_LDS)                 \
     W4A16_SHAPES(X, PATH_GEMV, 3, ASRC_LDS) W4A16_SHAPES(X, PATH_GEMV, 4, ASRC_LDS)                 \
-    W4A16_RINGS(X, PATH_MFMA, 0, ASRC_RING)                                                         \
-    W4A16_WIDE(X, PATH_MFMA, 0, ASRC_LDS) W4A16_WIDE(X, PATH_MFMA, 0, ASRC_GLOBAL)                  \
     W4A16_WIDE(X, PATH_MFMA, 2, ASRC_LDS) W4A16_WIDE(X, PATH_MFMA, 3, ASRC_LDS)                     \
     W4A16_WIDE(X, PATH_MFMA, 4, ASRC_LDS)                                                           \
-    W4A16_SHAPES(X, PATH_MFMA, 0, ASRC_LDS) W4A16_SHAPES(X, PATH_MFMA, 0, ASRC_GLOBAL)              \
     W4A16_SHAPES(X, PATH_MFMA, 1, ASRC_LDS) W4A16_SHAPES(X, PATH_MFMA, 1, ASRC_GLOBAL)              \
     W4A16_SHAPES(X, PATH_MFMA, 2, ASRC_LDS) W4A16_SHAPES(X, PATH_MFMA, 2, ASRC_GLOBAL)              \
     W4A16_SHAPES(X, PATH_MFMA, 3, ASRC_LDS) W4A16_SHAPES(X, PATH_MFMA, 3, ASRC_GLOBAL)              \
     W4A16_SHAPES(X, PATH_MFMA, 4, ASRC_LDS) W4A16_SHAPES(X, PATH_MFMA, 4, ASRC_GLOBAL)
+#define W4A16_VARIANT_LIST_RT(X)                                                                    \
+    W4A16_RINGS(X, PATH_MFMA, 0, ASRC_RING)                                                         \
+    W4A16_WIDE(X, PATH_MFMA, 0, ASRC_LDS) W4A16_WIDE(X, PATH_MFMA, 0, ASRC_GLOBAL)                  \
+    W4A16_SHAPES(X, PATH_MFMA, 0, ASRC_LDS) W4A16_SHAPES(X, PATH_MFMA, 0, ASRC_GLOBAL)
 
-// kVariantsPlain: plain matmuls; kVariantsEpi: the same shapes with the
-// epilogue modes.  Both tables list the shapes in W4A16_VARIANT_LIST order.
-extern const Variant kVariantsPlain[];
-extern const Variant kVariantsEpi[];
-extern const int kNumVariants;
+// Kernel tables, one per instantiation unit: plain matmuls and kernels that
+// also carry the epilogue modes, each split into compile-time-row (Ct) and
+// run-time-row (Rt) shapes.
+struct VariantTable {
+    const Variant *v;
+    int n;
+};
+extern const Variant kVariantsPlainCt[], kVariantsPlainRt[], kVariantsEpiCt[], kVariantsEpiRt[];
+extern const int kNumPlainCt, kNumPlainRt, kNumEpiCt, kNumEpiRt;
+
+// NVFP4 weight-only kernels (plain epilogue; A staged in LDS or read from
+// global memory): the GEMV path for one to four rows, the matrix-core path
+// for every row count.
+#define W4A16_NV_GEMV(X, MM) \
+    X(PATH_GEMV, MM, 1, 1, 8, ASRC_LDS) X(PATH_GEMV, MM, 1, 8, 4, ASRC_LDS) X(PATH_GEMV, MM, 2, 4, 4, ASRC_LDS) \
+    X(PATH_GEMV, MM, 2, 8, 4, ASRC_LDS) X(PATH_GEMV, MM, 1, 4, 8, ASRC_LDS) X(PATH_GEMV, MM, 4, 4, 2, ASRC_LDS)
+#define W4A16_NV_MFMA(X, MM, AS) \
+    X(PATH_MFMA, MM, 1, 1, 8, AS) X(PATH_MFMA, MM, 1, 8, 4, AS) X(PATH_MFMA, MM, 2, 4, 4, AS) \
+    X(PATH_MFMA, MM, 2, 8, 4, AS) X(PATH_MFMA, MM, 4, 4, 2, AS) X(PATH_MFMA, MM, 1, 4, 8, AS)
+#define W4A16_NV_VARIANT_LIST(X)                                                                  \
+    W4A16_NV_GEMV(X, 1) W4A16_NV_GEMV(X, 2) W4A16_NV_GEMV(X, 3) W4A16_NV_GEMV(X, 4)               \
+    X(PATH_GEMV, 1, 2, 4, 5, ASRC_LDS) X(PATH_GEMV, 1, 1, 4, 10, ASRC_LDS)                         \
+    X(PATH_GEMV, 1, 2, 8, 2, ASRC_LDS) X(PATH_GEMV, 1, 2, 2, 8, ASRC_LDS)                           \
+    W4A16_NV_MFMA(X, 0, ASRC_LDS) W4A16_NV_MFMA(X, 0, ASRC_GLOBAL)                                 \
+    X(PATH_MFMA, 0, 8, 1, 4, ASRC_GLOBAL) X(PATH_MFMA, 0, 8, 2, 2, ASRC_GLOBAL)                    \
+    W4A16_NV_MFMA(X, 1, ASRC_LDS) W4A16_NV_MFMA(X, 2, ASRC_LDS) W4A16_NV_MFMA(X, 3, ASRC_LDS)     \
+    W4A16_NV_MFMA(X, 4, ASRC_LDS) W4A16_NV_MFMA(X, 2, ASRC_GLOBAL) W4A16_NV_MFMA(X, 4, ASRC_GLOBAL)
+
+extern const Variant kVariantsNv[];
+extern const int kNumVariantsNv;
 
 }  // namespace w4a16

@@ -147,11 +147,12 @@ int validate_plan(const w4a16_plan_t &p, int M, int N, int K, int fmt = FMT_GPTQ
 // and third, K / 2, 4, 8 for the second and fourth), M = 1..16.
 // Widths: "narrow" up to 384 tiles of 16 columns, "mid" 513..2047, "wide"
 // from 2048, "very wide" from 8192; "long" K from 128 groups of 128.
-//  * M = 1: the GEMV kernel; narrow N with K of 32 groups or more: one tile
-//    per workgroup and eight wavefronts along K; mid: one tile, each
-//    wavefront's groups loaded in
-//    one go; otherwise two tiles, four wavefronts (eight for long K), ring
-//    depth 4 (5 for wide N);
+//  * M = 1: the GEMV kernel; wide N: two tiles, four wavefronts, depth 5
+//    (eight wavefronts, depth 4 for long K); from 1024 tiles: one tile, four
+//    wavefronts, each wavefront's groups loaded in one go; narrower N, eight
+//    wavefronts along K: from 64 groups two tiles and depth 3, up to 256
+//    tiles with 32 groups or more one tile and depth 4, from 16 groups one
+//    tile and depth 2, else two tiles and depth 2;
 //  * M = 2..4: matrix cores with A staged in LDS (the bias formed in the
 //    loop); four tiles and depth 2 for wide N at M = 2 and for very wide N,
 //    else two tiles and depth 4; for long K eight wavefronts stage the whole
@@ -179,18 +180,30 @@ void auto_plan(int M, int N, int K, w4a16_plan_t *out) {
     p.splits = 1;
     p.asrc = W4A16_ASRC_LDS;
     if (M == 1) {
+        // eight wavefronts with shallow rings below the gate/up width: two
+        // wavefronts per SIMD, one's dequantization overlaps the other's wait
         p.path = W4A16_PATH_GEMV;
-        if (narrow && G >= 32) {
+        p.kwaves = 8;
+        if (wide) {
+            p.tiles = 2;
+            p.kwaves = deep ? 8 : 4;
+            p.depth = deep ? 4 : 5;
+        } else if (NT >= 1024) {               // one tile, each wavefront's groups in one go
             p.tiles = 1;
-            p.kwaves = 8;
-            p.depth = 4;
-        } else if (mid && !deep) {             // one tile, each wavefront's groups in one go
-            p.tiles = 1;
+            p.kwaves = 4;
             p.depth = (G == 40) ? 10 : 8;
+        } else if (G >= 64) {
+            p.tiles = 2;
+            p.depth = 3;
+        } else if (NT <= 256 && G >= 32) {
+            p.tiles = 1;
+            p.depth = 4;
+        } else if (G >= 16) {
+            p.tiles = 1;
+            p.depth = 2;
         } else {
             p.tiles = 2;
-            if (deep) p.kwaves = 8;
-            p.depth = (wide && !deep) ? 5 : 4;
+            p.depth = 2;
         }
     } else if (M <= 4) {
         p.path = W4A16_PATH_MFMA;

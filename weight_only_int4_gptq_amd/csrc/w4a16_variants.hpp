@@ -40,7 +40,13 @@ struct Variant {
 // four rows) and kernels that take the row count at run time (matrix cores,
 // five rows and more, and ring A): two instantiation units each, compiled
 // with different register choices for the matrix-core results (see build.py).
+// more wavefronts per SIMD for one row: shallow rings, eight or sixteen along K
+#define W4A16_MANYWAVE(X, P, MM, AS) \
+    X(P, MM, 2, 8, 2, AS) X(P, MM, 2, 8, 3, AS) X(P, MM, 4, 8, 2, AS) X(P, MM, 2, 16, 2, AS) \
+    X(P, MM, 1, 16, 2, AS) X(P, MM, 4, 4, 3, AS) X(P, MM, 2, 8, 5, AS) X(P, MM, 1, 8, 2, AS)
+
 #define W4A16_VARIANT_LIST_CT(X)                                                                    \
+    W4A16_MANYWAVE(X, PATH_GEMV, 1, ASRC_LDS)                                                       \
     W4A16_ONESHOT(X, PATH_GEMV, 1, ASRC_LDS) W4A16_ONESHOT(X, PATH_MFMA, 1, ASRC_LDS)               \
     W4A16_ONESHOT(X, PATH_MFMA, 1, ASRC_GLOBAL)                                                     \
     W4A16_SHAPES(X, PATH_GEMV, 1, ASRC_LDS) W4A16_SHAPES(X, PATH_GEMV, 2, ASRC_LDS)                 \

@@ -42,8 +42,10 @@
  *     no unsupported case falls back silently to another path.
  *   - Device pointers must be 16-byte aligned.  Output buffers must not
  *     overlap any input (not checked).
- *   - Valid shapes: 1 <= M <= 16, K a positive multiple of 128, N a positive
- *     multiple of 16, K*N/2 < 2^40.  group must be 128.
+ *   - Valid shapes: 1 <= M <= 16, K a positive multiple of 128 up to
+ *     W4A16_MAX_K (2^24; the kernels address a tile's weights and the rows of
+ *     A through 32-bit buffer offsets), N a positive multiple of 16,
+ *     K*N/2 < 2^40.  group must be 128.
  */
 #ifndef W4A16_H
 #define W4A16_H
@@ -69,6 +71,7 @@ extern "C" {
 #define W4A16_GROUP 128
 #define W4A16_NVFP4_GROUP 16   /* rows per E4M3 block scale of the NVFP4 calls */
 #define W4A16_MAX_M 16
+#define W4A16_MAX_K (1 << 24)
 
 /* Execution paths of the row-count dispatcher. */
 #define W4A16_PATH_AUTO 0

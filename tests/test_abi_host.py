@@ -58,6 +58,7 @@ def _gemm(A=P, wq=P, s=P, C=P2, M=1, N=1024, K=512, group=128, ws=NULL, wsb=0, p
 @pytest.mark.parametrize("kw,status", [
     (dict(A=NULL), -1), (dict(wq=NULL), -1), (dict(s=NULL), -1), (dict(C=NULL), -1),
     (dict(M=0), -2), (dict(M=17), -2), (dict(K=500), -2), (dict(K=0), -2), (dict(N=1000), -2),
+    (dict(K=(1 << 24) + 128), -2),
     (dict(N=-16), -2), (dict(group=64), -3), (dict(A=ODD), -4), (dict(C=ODD), -4),
     (dict(s=ODD), -4), (dict(wq=ODD), -4),
 ])

@@ -84,7 +84,7 @@ bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 
 int check_shape(int M, int N, int K) {
     if (M < 1 || M > W4A16_MAX_M) return W4A16_ERR_SHAPE;
-    if (K <= 0 || (K % W4A16_GROUP) != 0) return W4A16_ERR_SHAPE;
+    if (K <= 0 || (K % W4A16_GROUP) != 0 || K > W4A16_MAX_K) return W4A16_ERR_SHAPE;
     if (N <= 0 || (N % 16) != 0) return W4A16_ERR_SHAPE;
     if ((unsigned long long)K * (unsigned long long)N / 2ull >= (1ull << 40)) return W4A16_ERR_SHAPE;
     return W4A16_OK;
@@ -487,7 +487,7 @@ const char *w4a16_status_string(int status) {
     switch (status) {
         case W4A16_OK: return "ok";
         case W4A16_ERR_NULL: return "null pointer argument";
-        case W4A16_ERR_SHAPE: return "invalid shape (need 1<=M<=16, K%128==0, N%16==0)";
+        case W4A16_ERR_SHAPE: return "invalid shape (need 1<=M<=16, K%128==0, K<=2^24, N%16==0)";
         case W4A16_ERR_GROUP: return "group size must be 128 (GPTQ) or 16 (NVFP4)";
         case W4A16_ERR_ALIGN: return "device pointer not 16-byte aligned";
         case W4A16_ERR_WORKSPACE: return "workspace missing or too small";

@@ -302,6 +302,14 @@ __device__ __forceinline__ void lds_dma16(const void *gsrc, uint32_t lds_base) {
 }
 #pragma clang diagnostic pop
 
+// Buffer resource of `bytes` bytes at `base` (gfx9 raw buffer: stride 0,
+// dword 3 = 0x00020000).  Loads through it take a per-lane offset (VGPR)
+// plus a wave-uniform offset (SGPR); offsets past `bytes` read zero.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void *base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes, 0x00020000);
+}
+constexpr int kCachePolicyNt = 2;   // non-temporal: streamed weights
+
 __device__ __forceinline__ uint32_t lds_addr(const void *p) {
     return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void *)p;
 }
@@ -566,22 +574,31 @@ __global__ void __launch_bounds__(64 * KW) gemm_kernel(GemmArgs p) {
         return fuse == 1 ? strip * kHalfT + (t < kHalfT ? t : t - kHalfT) < (p.NT >> 1) : strip * T + t < p.NT;
     };
 
-    // wave-uniform bases (scalar) and per-lane byte offsets (vector, fixed)
-    const uint8_t *wbase[T];
-    const uint8_t *sbase[T];
+    // Buffer resources (scalar): each tile's weights and scales, and A.
+    // Every load is resource + fixed per-lane offset + the group's
+    // wave-uniform offset, so the stream costs no vector address arithmetic.
+    __amdgpu_buffer_rsrc_t wres[T], sres[T];
 #pragma unroll
     for (int t = 0; t < T; ++t) {
         const size_t tile = (size_t)min(tile_of(t), p.NT - 1);
-        wbase[t] = reinterpret_cast<const uint8_t *>(p.blob) + tile * (size_t)p.G * 1024;
-        sbase[t] = reinterpret_cast<const uint8_t *>(p.scales) + tile * (size_t)p.G * kScaleBytes;
+        wres[t] = buffer_rsrc(reinterpret_cast<const uint8_t *>(p.blob) + tile * (size_t)p.G * 1024,
+                              (uint32_t)p.G * 1024u);
+        sres[t] = buffer_rsrc(reinterpret_cast<const uint8_t *>(p.scales) + tile * (size_t)p.G * kScaleBytes,
+                              (uint32_t)p.G * (uint32_t)kScaleBytes);
     }
     const uint32_t w_lane = (uint32_t)lane * 16;             // this lane's 16 B of a 1 KiB piece
     // GPTQ: the dword holding this column's bf16 scale, and its half;
     // NVFP4: this column's 8 block-scale bytes
     const uint32_t s_lane = kNv ? (uint32_t)c * 8 : (uint32_t)(c >> 1) * 4;
     const uint32_t s_sel = scale_selector(c);
+    // MFMA A from global memory: row arow_m, this lane group's rows of a
+    // group.  GPTQ reads its four 16-byte pieces through a pointer, NVFP4
+    // its eight 8-byte pieces through a buffer resource (each measured the
+    // faster for its format).
     const uint8_t *abase = reinterpret_cast<const uint8_t *>(p.A) +
-                           ((size_t)arow_m * p.K + (size_t)h * (kNv ? 4 : 32)) * 2;   // MFMA A from global
+                           ((size_t)arow_m * p.K + (size_t)h * (kNv ? 4 : 32)) * 2;
+    const __amdgpu_buffer_rsrc_t ares = buffer_rsrc(p.A, (uint32_t)M * (uint32_t)p.K * 2u);
+    const uint32_t a_lane = ((uint32_t)arow_m * (uint32_t)p.K + (uint32_t)h * (kNv ? 4u : 32u)) * 2u;
 
     // ---- 1. asynchronous LDS fill of this workgroup's K range of A
     if constexpr (kStage) {
@@ -625,25 +642,27 @@ __global__ void __launch_bounds__(64 * KW) gemm_kernel(GemmArgs p) {
         }
 #pragma unroll
         for (int t = 0; t < T; ++t) {
-            wv[j][t] = __builtin_nontemporal_load(
-                reinterpret_cast<const u32x4 *>(wbase[t] + (size_t)g * 1024 + w_lane));
+            wv[j][t] = __builtin_bit_cast(
+                u32x4, __builtin_amdgcn_raw_buffer_load_b128(wres[t], w_lane, g * 1024, kCachePolicyNt));
             if constexpr (kNv) {
-                const u32x2 x = *reinterpret_cast<const u32x2 *>(sbase[t] + (size_t)g * kScaleBytes + s_lane);
+                const u32x2 x = __builtin_bit_cast(
+                    u32x2, __builtin_amdgcn_raw_buffer_load_b64(sres[t], s_lane, g * kScaleBytes, 0));
                 sv[j][t][0] = x[0];
                 sv[j][t][1] = x[1];
             } else {
                 // the aligned dword that holds this lane's bf16 scale (a 16-bit
                 // load would be re-extended at the loop latch, which stalls the ring)
-                sv[j][t][0] = *reinterpret_cast<const uint32_t *>(sbase[t] + (size_t)g * kScaleBytes + s_lane);
+                sv[j][t][0] = __builtin_amdgcn_raw_buffer_load_b32(sres[t], s_lane, g * kScaleBytes, 0);
             }
         }
         if constexpr (kGlobalA && kNv) {
             // rows 16b + 4h .. +3 of the group, b = 0..7: eight 8-byte pieces
-            const uint8_t *ap = abase + (size_t)g * kGroup * 2;
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
-                const u32x2 lo = *reinterpret_cast<const u32x2 *>(ap + (2 * q) * kNvBlock * 2);
-                const u32x2 hi = *reinterpret_cast<const u32x2 *>(ap + (2 * q + 1) * kNvBlock * 2);
+                const u32x2 lo = __builtin_bit_cast(
+                    u32x2, __builtin_amdgcn_raw_buffer_load_b64(ares, a_lane + (2 * q) * kNvBlock * 2, g * kGroup * 2, 0));
+                const u32x2 hi = __builtin_bit_cast(
+                    u32x2, __builtin_amdgcn_raw_buffer_load_b64(ares, a_lane + (2 * q + 1) * kNvBlock * 2, g * kGroup * 2, 0));
                 av[j][q] = u32x4{lo[0], lo[1], hi[0], hi[1]};
             }
         } else if constexpr (kGlobalA) {

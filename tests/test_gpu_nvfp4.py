@@ -58,7 +58,7 @@ for path in (w4.PATH_GEMV, w4.PATH_MFMA):
     for t in (1, 2, 4, 8):
         for kw in (1, 2, 4, 8):
             for asrc in ((w4.ASRC_LDS,) if path == w4.PATH_GEMV else (w4.ASRC_LDS, w4.ASRC_GLOBAL)):
-                for depth in (0, 2, 4, 5, 8, 10):
+                for depth in (0, 2, 3, 4, 5, 8, 10):
                     ALL_PLANS.append(w4.make_plan(path, t, kw, 1, asrc, depth))
 
 

@@ -292,7 +292,7 @@ void auto_plan(int M, int N, int K, w4a16_plan_t *out) {
 //  * M = 2..4: very wide N: four tiles, depth 2; long K: two tiles, eight
 //    wavefronts; narrow N: one tile, eight wavefronts; else two tiles, four
 //    wavefronts; A in LDS throughout;
-//  * M >= 5: very wide N: eight tiles per wavefront from 12 rows, else four
+//  * M >= 5: very wide N: eight tiles per wavefront (depth 3) from 14 rows, else four
 //    tiles, four wavefronts, A from global memory; wide N: the latter; long
 //    K: four tiles split four ways (A in LDS) up to 8 rows, two ways with A
 //    from global memory above; otherwise two tiles and eight wavefronts with
@@ -322,7 +322,7 @@ void auto_plan_nv(int M, int N, int K, w4a16_plan_t *out) {
         else if (!wide) set(W4A16_PATH_MFMA, 1, 8, 1, W4A16_ASRC_LDS, 4);
         else set(W4A16_PATH_MFMA, 2, 4, 1, W4A16_ASRC_LDS, 4);
     } else {
-        if (vwide && M >= 12) set(W4A16_PATH_MFMA, 8, 1, 1, W4A16_ASRC_GLOBAL, 4);
+        if (vwide && M >= 14) set(W4A16_PATH_MFMA, 8, 1, 1, W4A16_ASRC_GLOBAL, 3);
         else if (wide) set(W4A16_PATH_MFMA, 4, 4, 1, W4A16_ASRC_GLOBAL, 2);
         else if (deep) set(W4A16_PATH_MFMA, 4, 4, M <= 8 ? 4 : 2, M <= 8 ? W4A16_ASRC_LDS : W4A16_ASRC_GLOBAL, 2);
         else if (M <= 8) set(W4A16_PATH_MFMA, 2, 8, 1, W4A16_ASRC_LDS, 4);

@@ -87,6 +87,7 @@ extern const int kNumPlainCt, kNumPlainRt, kNumEpiCt, kNumEpiRt;
     X(PATH_GEMV, 1, 2, 8, 2, ASRC_LDS) X(PATH_GEMV, 1, 2, 2, 8, ASRC_LDS)                           \
     W4A16_NV_MFMA(X, 0, ASRC_LDS) W4A16_NV_MFMA(X, 0, ASRC_GLOBAL)                                 \
     X(PATH_MFMA, 0, 8, 1, 4, ASRC_GLOBAL) X(PATH_MFMA, 0, 8, 2, 2, ASRC_GLOBAL)                    \
+    X(PATH_MFMA, 0, 8, 1, 2, ASRC_GLOBAL) X(PATH_MFMA, 0, 8, 1, 3, ASRC_GLOBAL)                    \
     W4A16_NV_MFMA(X, 1, ASRC_LDS) W4A16_NV_MFMA(X, 2, ASRC_LDS) W4A16_NV_MFMA(X, 3, ASRC_LDS)     \
     W4A16_NV_MFMA(X, 4, ASRC_LDS) W4A16_NV_MFMA(X, 2, ASRC_GLOBAL) W4A16_NV_MFMA(X, 4, ASRC_GLOBAL)
 

@@ -300,6 +300,14 @@ __device__ __forceinline__ void lds_dma16(const void *gsrc, uint32_t lds_base) {
                  : "v"(gsrc), "s"(lds_base)
                  : "memory", "m0");
 }
+// The same with a wave-uniform 64-bit base (SGPRs) and a 32-bit per-lane
+// byte offset: no vector address arithmetic when only the base moves.
+__device__ __forceinline__ void lds_dma16_sbase(uint32_t voff, const void *sbase, uint32_t lds_base) {
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+                 :
+                 : "v"(voff), "s"(sbase), "s"(lds_base)
+                 : "memory", "m0");
+}
 #pragma clang diagnostic pop
 
 // Buffer resource of `bytes` bytes at `base` (gfx9 raw buffer: stride 0,
@@ -628,17 +636,23 @@ __global__ void __launch_bounds__(64 * KW) gemm_kernel(GemmArgs p) {
     // matrix-core reads below (16 rows, one piece each) hit distinct banks.
     const int nd = (M + 3) >> 2;                             // DMA loads per group
     auto ring_slot = [&](int j) { return L.a + (wave * D + j) * kRingSlotBytes; };
+    // this lane's byte offset inside a group of A for DMA load i (rows
+    // 4i + h, swizzled piece c), fixed for the whole loop
+    uint32_t ring_off[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int row = min(4 * i + h, M - 1);
+        ring_off[i] = (uint32_t)row * (uint32_t)p.K * 2u + (uint32_t)((c ^ (row & 15)) << 4);
+    }
 
     auto load_group = [&](auto jc, int g) {
         constexpr int j = decltype(jc)::value;
         if constexpr (kRingA) {
             const uint32_t dst0 = __builtin_amdgcn_readfirstlane(lds_addr(smem + ring_slot(j)));
-            for (int i = 0; i < nd; ++i) {
-                const int row = min(4 * i + h, M - 1);
-                const uint8_t *src = reinterpret_cast<const uint8_t *>(p.A) +
-                                     ((size_t)row * p.K + (size_t)g * kGroup) * 2 + ((c ^ (row & 15)) << 4);
-                lds_dma16(src, dst0 + (i << 10));
-            }
+            const uint8_t *gbase = reinterpret_cast<const uint8_t *>(p.A) + (size_t)g * kGroup * 2;
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                if (i < nd) lds_dma16_sbase(ring_off[i], gbase, dst0 + (i << 10));
         }
 #pragma unroll
         for (int t = 0; t < T; ++t) {

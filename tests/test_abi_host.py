@@ -122,15 +122,20 @@ def test_row_count_dispatch():
         p = w4.get_plan(M, 34816, 5120)
         assert p.path == (w4.PATH_GEMV if M == 1 else w4.PATH_MFMA), (M, p)
         assert p.splits == 1
-        # wide N: A staged in LDS up to four rows, then read per group: from
-        # global memory, and through the LDS ring from 12 rows
+        # wide N: A through the LDS ring from two rows, two tiles up to 8
+        # rows, four above
         if M >= 2:
-            want = w4.ASRC_LDS if M <= 4 else (w4.ASRC_GLOBAL if M < 12 else w4.ASRC_RING)
-            assert p.asrc == want, (M, p)
-    # narrow N: all of A in LDS up to 12 rows, the ring above
-    assert w4.get_plan(8, 8192, 5120).asrc == w4.ASRC_LDS
-    assert w4.get_plan(12, 8192, 5120).kwaves == 8
+            assert p.asrc == w4.ASRC_RING, (M, p)
+            assert p.tiles == (2 if M <= 8 else 4), (M, p)
+    # QKV width: all of A in LDS up to 7 rows, the ring above
+    assert w4.get_plan(4, 8192, 5120).asrc == w4.ASRC_LDS
+    assert w4.get_plan(7, 8192, 5120).asrc == w4.ASRC_LDS
+    assert w4.get_plan(8, 8192, 5120).asrc == w4.ASRC_RING
     assert w4.get_plan(16, 8192, 5120).asrc == w4.ASRC_RING
+    # very wide N: LDS A at 3-4 rows, the ring elsewhere, eight tiles above 8 rows
+    assert w4.get_plan(4, 248320, 5120).asrc == w4.ASRC_LDS
+    assert w4.get_plan(2, 248320, 5120).asrc == w4.ASRC_RING
+    assert w4.get_plan(8, 248320, 5120).tiles == 4
     # long K with few column strips: split K (two rows and more)
     assert w4.get_plan(1, 5120, 17408).splits == 1
     assert w4.get_plan(4, 5120, 17408).splits == 1           # whole K of A in LDS

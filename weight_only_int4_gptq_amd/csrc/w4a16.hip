@@ -153,26 +153,27 @@ int validate_plan(const w4a16_plan_t &p, int M, int N, int K, int fmt = FMT_GPTQ
 //    wavefronts along K: from 64 groups two tiles and depth 3, up to 256
 //    tiles with 32 groups or more one tile and depth 4, from 16 groups one
 //    tile and depth 2, else two tiles and depth 2;
-//  * M = 2..4: matrix cores with A staged in LDS (the bias formed in the
-//    loop); four tiles and depth 2 for wide N at M = 2 and for very wide N,
-//    else two tiles and depth 4; for long K eight wavefronts stage the whole
-//    K range of A (up to the full 160 KiB of LDS, one workgroup per CU);
+//  * M = 2..4: matrix cores; long K: A staged in LDS, two tiles, eight
+//    wavefronts (the whole K range of A, up to the full 160 KiB of LDS, one
+//    workgroup per CU); very wide N: four tiles, depth 2, A in LDS (through
+//    the ring with two wavefronts at M = 2); wide and mid N: A through the
+//    per-wavefront LDS ring (contiguous DMA loads), two tiles, depth 2;
+//    otherwise A in LDS, two tiles, depth 4;
 //  * M >= 5, matrix cores:
-//      - very wide N from M = 8: one wavefront owns eight tiles (A from
-//        global memory), so each A fragment it loads serves eight times the
-//        weights;
-//      - wide and mid N: four tiles, A per group from global memory below
-//        M = 12, through the per-wavefront LDS ring (contiguous DMA loads)
-//        from M = 12;
+//      - very wide N: A through the ring, four tiles and two wavefronts up
+//        to 8 rows, eight tiles and four wavefronts above;
+//      - wide and mid N: A through the ring, depth 2, two tiles up to 8
+//        rows, four above;
 //      - long K: A through the ring from M = 8; below, a quarter of K of A
 //        staged in LDS (split four ways);
 //      - narrow N up to 256 tiles: one tile, all of A staged in LDS, eight
 //        wavefronts along K;
-//      - otherwise all of A staged in LDS up to M = 12 (eight wavefronts
-//        along K from 40 groups, else four), the ring above.
+//      - otherwise two tiles: all of A in LDS up to 7 rows and from 64
+//        groups (depth 4, eight wavefronts from 64 groups), A through the
+//        ring otherwise (depth 2).
 void auto_plan(int M, int N, int K, w4a16_plan_t *out) {
     const int NT = N / 16, G = K / W4A16_GROUP;
-    const bool wide = NT >= 2048, deep = G >= 128;
+    const bool wide = NT >= 2048, vwide = NT >= 8192, deep = G >= 128;
     const bool narrow = NT <= 384;             // few strips: one tile each, more waves along K
     const bool mid = NT > 512 && NT < 2048;    // between the QKV and gate/up widths
     w4a16_plan_t p;
@@ -211,8 +212,16 @@ void auto_plan(int M, int N, int K, w4a16_plan_t *out) {
             p.tiles = 2;
             p.kwaves = 8;
             p.depth = 4;
-        } else if (wide && (M == 2 || NT >= 8192)) {
+        } else if (vwide) {
             p.tiles = 4;
+            p.depth = 2;
+            if (M == 2) {                      // A through the ring, two wavefronts
+                p.asrc = W4A16_ASRC_RING;
+                p.kwaves = 2;
+            }
+        } else if (wide || mid) {              // A through the ring, shallow
+            p.asrc = W4A16_ASRC_RING;
+            p.tiles = 2;
             p.depth = 2;
         } else {
             p.tiles = 2;
@@ -220,14 +229,14 @@ void auto_plan(int M, int N, int K, w4a16_plan_t *out) {
         }
     } else {
         p.path = W4A16_PATH_MFMA;
-        if (NT >= 8192 && M >= 8) {            // very wide N: one wavefront per eight tiles
-            p.asrc = W4A16_ASRC_GLOBAL;
-            p.tiles = 8;
-            p.kwaves = 1;
-            p.depth = 4;
-        } else if (wide || mid) {
-            p.asrc = M >= 12 ? W4A16_ASRC_RING : W4A16_ASRC_GLOBAL;
-            p.tiles = 4;
+        if (vwide) {                           // A through the ring: 4 tiles x 2 waves, 8 x 4 above 8 rows
+            p.asrc = W4A16_ASRC_RING;
+            p.tiles = M <= 8 ? 4 : 8;
+            p.kwaves = M <= 8 ? 2 : 4;
+            p.depth = 2;
+        } else if (wide || mid) {              // A through the ring: two tiles up to 8 rows, four above
+            p.asrc = W4A16_ASRC_RING;
+            p.tiles = M <= 8 ? 2 : 4;
             p.depth = 2;
         } else if (deep) {
             p.tiles = 2;
@@ -242,15 +251,14 @@ void auto_plan(int M, int N, int K, w4a16_plan_t *out) {
             p.tiles = 1;
             p.kwaves = 8;
             p.depth = 4;
-        } else {
+        } else if (M <= 7 || G >= 64) {       // all of A in LDS (eight wavefronts from 64 groups)
             p.tiles = 2;
             p.depth = 4;
-            if (M <= 12) {                     // all of A in LDS, more waves along long K
-                p.asrc = W4A16_ASRC_LDS;
-                p.kwaves = G >= 40 ? 8 : 4;
-            } else {
-                p.asrc = W4A16_ASRC_RING;
-            }
+            if (G >= 64) p.kwaves = 8;
+        } else {                               // A through the ring, shallow
+            p.asrc = W4A16_ASRC_RING;
+            p.tiles = 2;
+            p.depth = 2;
         }
     }
     // short K: no more wavefronts along K than groups per workgroup
@@ -276,6 +284,7 @@ void auto_plan(int M, int N, int K, w4a16_plan_t *out) {
     if (p.path == W4A16_PATH_MFMA && p.asrc == W4A16_ASRC_LDS && plan_lds(p, M, G) + 256 > kLdsMax) {
         p.asrc = M >= 5 ? W4A16_ASRC_RING : W4A16_ASRC_GLOBAL;
         p.splits = 1;
+        if (p.asrc == W4A16_ASRC_RING && !find_variant(p, M)) p.kwaves = 4;   // the ring's shapes
     }
     // ring A has fewer compiled shapes (none for the short-K fallback)
     if (p.asrc == W4A16_ASRC_RING && !find_variant(p, M)) p.asrc = W4A16_ASRC_GLOBAL;
@@ -366,12 +375,10 @@ static_assert(kArgmaxBinOffset + kArgmaxBins * 16 * 8 <= W4A16_ARGMAX_WORKSPACE_
 void fuse_plan(int M, w4a16_plan_t *p) {
     if (p->tiles % 2 == 0) return;
     w4a16_plan_t q = *p;
-    q.tiles = 2;
-    q.depth = 0;
-    if (!find_variant(q, M)) {
-        q.kwaves = 4;
-        if (!find_variant(q, M)) q.asrc = W4A16_ASRC_GLOBAL;
-    }
+    q.tiles = 2;                               // same wavefronts and ring depth if compiled
+    if (!find_variant(q, M, true)) q.depth = 0;
+    if (!find_variant(q, M, true)) q.kwaves = 4;
+    if (!find_variant(q, M, true)) q.asrc = W4A16_ASRC_GLOBAL;
     *p = q;
 }
 

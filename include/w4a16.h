@@ -353,7 +353,7 @@ int w4a16_nvfp4_gemm(const void *A, const void *wq_repacked, const void *scales,
                      int M, int N, int K, int group, void *workspace, size_t workspace_bytes,
                      void *stream);
 
-/* As w4a16_nvfp4_gemm with an explicit plan (no ring A plans for NVFP4). */
+/* As w4a16_nvfp4_gemm with an explicit plan. */
 int w4a16_nvfp4_gemm_plan(const void *A, const void *wq_repacked, const void *scales, float alpha,
                           void *C, int M, int N, int K, int group, void *workspace,
                           size_t workspace_bytes, const w4a16_plan_t *plan, void *stream);

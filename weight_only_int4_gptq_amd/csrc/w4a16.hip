@@ -301,11 +301,11 @@ void auto_plan(int M, int N, int K, w4a16_plan_t *out) {
 //  * M = 2..4: very wide N: four tiles, depth 2; long K: two tiles, eight
 //    wavefronts; narrow N: one tile, eight wavefronts; else two tiles, four
 //    wavefronts; A in LDS throughout;
-//  * M >= 5: very wide N: eight tiles per wavefront (depth 3) from 14 rows, else four
-//    tiles, four wavefronts, A from global memory; wide N: the latter; long
-//    K: four tiles split four ways (A in LDS) up to 8 rows, two ways with A
-//    from global memory above; otherwise two tiles and eight wavefronts with
-//    A in LDS up to 8 rows, four tiles split two ways above.
+//  * M >= 5: A through the LDS ring, two tiles, four wavefronts, depth 2:
+//    very wide N above 8 rows (up to 8: four tiles, A from global memory);
+//    wide N; long K from 8 rows, split two ways (below: four tiles split
+//    four ways, A in LDS); otherwise from 8 rows (below: two tiles, eight
+//    wavefronts, A in LDS).
 // The first of these that this build compiled and that fits is taken, else
 // the first compiled fallback.
 void auto_plan_nv(int M, int N, int K, w4a16_plan_t *out) {
@@ -331,11 +331,20 @@ void auto_plan_nv(int M, int N, int K, w4a16_plan_t *out) {
         else if (!wide) set(W4A16_PATH_MFMA, 1, 8, 1, W4A16_ASRC_LDS, 4);
         else set(W4A16_PATH_MFMA, 2, 4, 1, W4A16_ASRC_LDS, 4);
     } else {
-        if (vwide && M >= 14) set(W4A16_PATH_MFMA, 8, 1, 1, W4A16_ASRC_GLOBAL, 3);
-        else if (wide) set(W4A16_PATH_MFMA, 4, 4, 1, W4A16_ASRC_GLOBAL, 2);
-        else if (deep) set(W4A16_PATH_MFMA, 4, 4, M <= 8 ? 4 : 2, M <= 8 ? W4A16_ASRC_LDS : W4A16_ASRC_GLOBAL, 2);
-        else if (M <= 8) set(W4A16_PATH_MFMA, 2, 8, 1, W4A16_ASRC_LDS, 4);
-        else set(W4A16_PATH_MFMA, 4, 4, 2, W4A16_ASRC_LDS, 2);
+        // A through the LDS ring (two tiles, depth 2) wherever it measured best
+        if (vwide) {
+            if (M <= 8) set(W4A16_PATH_MFMA, 4, 4, 1, W4A16_ASRC_GLOBAL, 2);
+            else set(W4A16_PATH_MFMA, 2, 4, 1, W4A16_ASRC_RING, 2);
+        } else if (wide) {
+            set(W4A16_PATH_MFMA, 2, 4, 1, W4A16_ASRC_RING, 2);
+        } else if (deep) {
+            if (M <= 7) set(W4A16_PATH_MFMA, 4, 4, 4, W4A16_ASRC_LDS, 2);
+            else set(W4A16_PATH_MFMA, 2, 4, 2, W4A16_ASRC_RING, 2);
+        } else if (M <= 7) {
+            set(W4A16_PATH_MFMA, 2, 8, 1, W4A16_ASRC_LDS, 4);
+        } else {
+            set(W4A16_PATH_MFMA, 2, 4, 1, W4A16_ASRC_RING, 2);
+        }
     }
     // splits no larger than the groups allow (a power of two), and no more
     // wavefronts along K than each split's groups

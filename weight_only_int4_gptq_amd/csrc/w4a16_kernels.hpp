@@ -543,7 +543,7 @@ __global__ void __launch_bounds__(64 * KW) gemm_kernel(GemmArgs p) {
     constexpr bool kGlobalA = (PATH == PATH_MFMA && ASRC == ASRC_GLOBAL);
     constexpr bool kRingA = (PATH == PATH_MFMA && ASRC == ASRC_RING);
     constexpr bool kStage = !kGlobalA && !kRingA;
-    static_assert(!kNv || (!kRingA && !EPI), "NVFP4: plain epilogue, A staged or from global memory");
+    static_assert(!kNv || !EPI, "NVFP4: plain epilogue");
     constexpr int kLoadsPerGroup = 2 * T + (kGlobalA ? (kNv ? 8 : 4) : 0);   // loads the compiler sees
     // Matrix-core bias: formed in the loop from the A fragments already
     // loaded (four more MFMAs per group, shared by the T tiles), except for
@@ -782,6 +782,16 @@ __global__ void __launch_bounds__(64 * KW) gemm_kernel(GemmArgs p) {
                     const uint8_t *arow = smem + L.a + arow_m * L.row + (gl * kGroup + 4 * h) * 2;
 #pragma unroll
                     for (int b = 0; b < 8; ++b) a[b] = *reinterpret_cast<const u32x2 *>(arow + b * kNvBlock * 2);
+                } else if constexpr (kRingA) {
+                    // as for GPTQ: wait for this slot's DMA loads explicitly;
+                    // rows 16b + 4h .. +3 are bytes 32b + 8h of row c, in
+                    // logical piece 2b + h/2, stored at piece (2b + h/2) ^ c
+                    constexpr int later = decltype(final_)::value ? D - 1 - j : D - 1;
+                    __builtin_amdgcn_s_waitcnt(waitcnt_vm(2 * T + later * (2 * T + 1)));
+                    const uint8_t *slot = smem + ring_slot(j) + c * (kGroup * 2) + ((h & 1) << 3);
+#pragma unroll
+                    for (int b = 0; b < 8; ++b)
+                        a[b] = *reinterpret_cast<const u32x2 *>(slot + (((2 * b + (h >> 1)) ^ c) << 4));
                 } else {
 #pragma unroll
                     for (int q = 0; q < 4; ++q) {

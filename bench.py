@@ -341,8 +341,9 @@ def main():
         return summarize_profiles(args)
 
     if args.gpus != 1:
-        print(f"bench.py: this build measures one GPU; --gpus {args.gpus} is not supported "
-              f"(the matmul shards by columns without communication, see DESIGN.md)", file=sys.stderr)
+        print(f"bench.py: measures one GPU; --gpus {args.gpus} is not supported "
+              f"(the matmul shards by columns without communication; one GPU's share is "
+              f"measured by --tp-shards)", file=sys.stderr)
         sys.exit(2)
 
     import torch

@@ -66,7 +66,7 @@ extern "C" {
 #define W4A16_ERR_WORKSPACE  -5   /* the plan needs a workspace that is missing or too small */
 #define W4A16_ERR_DEVICE     -6   /* no HIP device, or the current device is not gfx950 */
 #define W4A16_ERR_LAUNCH     -7   /* the HIP runtime rejected a launch */
-#define W4A16_ERR_PLAN       -8   /* an explicit plan names a variant this build does not have */
+#define W4A16_ERR_PLAN       -8   /* an explicit plan names a kernel shape the library does not have */
 
 #define W4A16_GROUP 128
 #define W4A16_NVFP4_GROUP 16   /* rows per E4M3 block scale of the NVFP4 calls */
@@ -139,7 +139,7 @@ int w4a16_repack_scales(const void *scales, void *scales_repacked, int K, int N,
 int w4a16_get_plan(int M, int N, int K, w4a16_plan_t *plan);
 
 /*
- * W4A16_OK if this build can run `plan` for (M, N, K) (a kernel exists and
+ * W4A16_OK if the library can run `plan` for (M, N, K) (a kernel exists and
  * its LDS fits), W4A16_ERR_PLAN if not, W4A16_ERR_SHAPE for invalid shapes.
  * Host-only, no device work.
  */
@@ -183,7 +183,7 @@ int w4a16_gemm(const void *A, const void *wq_repacked, const void *scales, void 
 
 /*
  * As w4a16_gemm, with an explicit plan (plan == NULL: same as w4a16_gemm).
- * Returns W4A16_ERR_PLAN when this build has no kernel for the plan.
+ * Returns W4A16_ERR_PLAN when the library has no kernel for the plan.
  */
 int w4a16_gemm_plan(const void *A, const void *wq_repacked, const void *scales, void *C,
                     int M, int N, int K, int group, void *workspace, size_t workspace_bytes,

@@ -13,7 +13,7 @@
  *   (page "Qwen3.8-27B on DGX Spark (GB10): vLLM 0.24 + NVFP4, the sm_121
  *   kernel gotcha", sections "What Spark-native means" and "The right stack
  *   for Spark").  They define neither the element nor the scale encoding;
- *   the readings taken (listed in the design doc) are the published formats
+ *   the readings taken are the published formats
  *   NVFP4 is built from:
  *     - element: FP4 E2M1 (OCP Microscaling Formats v1.0): bit 3 sign,
  *       bits 2..1 exponent with bias 1, bit 0 mantissa; exponent 0 is

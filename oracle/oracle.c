@@ -13,7 +13,7 @@
  *   judged against exact dequantization of its checkpoint, so the oracle is
  *   exactly that: dequantize exactly, then multiply in fp64.
  *
- *   Readings taken where the pages are silent (each listed in the design doc):
+ *   Readings taken where the pages are silent:
  *     - qweight is uint32 [K/8][N], N contiguous; nibble j of word (kb, n)
  *       (bits 4j..4j+3, low nibble first) holds the code of k = 8*kb + j.
  *     - "symmetric, no zero points" on a 4-bit code q in [0,15] means the

@@ -55,7 +55,7 @@ def max_err(C, Cref, Dref):
 
 # ------------------------------------------------------------- plans to force
 # every (path, tiles, kwaves, A source, ring depth) combination a build might
-# hold; plan_ok keeps the ones this build compiled (depth 0 = its default)
+# hold; plan_ok keeps the ones the library has kernels for (depth 0 = its default)
 ALL_PLANS = []
 for path in (w4.PATH_GEMV, w4.PATH_MFMA):
     for t in (1, 2, 4):
@@ -67,7 +67,7 @@ for path in (w4.PATH_GEMV, w4.PATH_MFMA):
 
 
 def plans_for(M, N, K):
-    """Every single-split plan this build can run for (M, N, K)."""
+    """Every single-split plan the library has a kernel for at (M, N, K)."""
     return [p for p in ALL_PLANS if w4.plan_ok(M, N, K, p)]
 
 

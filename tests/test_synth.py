@@ -44,3 +44,24 @@ def test_algorithmic_bytes():
     # K*N/2 + (K/128)*N*2 + M*K*2 + M*N*2
     assert synth.algorithmic_bytes(1, 8192, 5120) == 20971520 + 655360 + 10240 + 16384
     assert synth.algorithmic_bytes(16, 248320, 5120) == 635699200 + 19865600 + 163840 + 7946240
+
+
+def test_nvfp4_inputs_documented_ranges_and_order():
+    K, N = 512, 64
+    A, packed, scales = synth.gen_nvfp4_problem(K, N, 5)
+    assert packed.shape == (N, K // 2) and packed.dtype == np.uint8
+    assert scales.shape == (N, K // 16) and scales.dtype == np.uint8
+    # every code value appears (uniform bytes hold two uniform nibbles)
+    assert set(np.unique(packed & 0xF)) == set(range(16))
+    assert set(np.unique(packed >> 4)) == set(range(16))
+    # E4M3 scales: sign 0, exponent field 4..10, any mantissa; never NaN
+    e = (scales >> 3) & 0xF
+    assert np.all(scales < 0x80) and e.min() >= 4 and e.max() <= 10
+    assert not np.any((scales & 0x7F) == 0x7F)
+    # draw order: codes, scales, then A from the same generator
+    rng = np.random.default_rng(5)
+    p2, s2 = synth.gen_nvfp4_weights(K, N, rng)
+    A2 = synth.gen_activations(16, K, rng)
+    assert np.array_equal(p2, packed) and np.array_equal(s2, scales) and np.array_equal(A2, A)
+    assert synth.NVFP4_ALPHA == float(np.float32(0.0037))
+    assert synth.algorithmic_bytes_nvfp4(1, 8192, 5120) == 5120 * 8192 // 2 + 320 * 8192 + 5120 * 2 + 8192 * 2

@@ -48,7 +48,7 @@ def lib():
     global _lib
     if _lib is None:
         if not os.path.exists(LIB_PATH):
-            raise RuntimeError(f"{LIB_PATH} is not built; run __graft_entry__.build()")
+            raise RuntimeError(f"{LIB_PATH} is not built; run python weight_only_int4_gptq_amd/build.py")
         L = ctypes.CDLL(LIB_PATH)
         P, I, S = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
         L.w4a16_status_string.argtypes = [I]
@@ -159,7 +159,7 @@ def make_plan(path: int, tiles: int, kwaves: int, splits: int = 1, asrc: int = A
 
 
 def plan_ok(M: int, N: int, K: int, plan: Plan) -> bool:
-    """True if this build can run `plan` for (M, N, K)."""
+    """True if the library has a kernel for `plan` at (M, N, K) and its LDS fits."""
     return lib().w4a16_check_plan(M, N, K, ctypes.byref(plan)) == OK
 
 

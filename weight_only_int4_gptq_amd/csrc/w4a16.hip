@@ -306,7 +306,7 @@ void auto_plan(int M, int N, int K, w4a16_plan_t *out) {
 //    wide N; long K from 8 rows, split two ways (below: four tiles split
 //    four ways, A in LDS); otherwise from 8 rows (below: two tiles, eight
 //    wavefronts, A in LDS).
-// The first of these that this build compiled and that fits is taken, else
+// The first of these that the library has a kernel for and that fits is taken, else
 // the first compiled fallback.
 void auto_plan_nv(int M, int N, int K, w4a16_plan_t *out) {
     const int NT = N / 16, G = K / W4A16_GROUP;
@@ -509,7 +509,7 @@ const char *w4a16_status_string(int status) {
         case W4A16_ERR_WORKSPACE: return "workspace missing or too small";
         case W4A16_ERR_DEVICE: return "no gfx950 HIP device";
         case W4A16_ERR_LAUNCH: return "kernel launch failed";
-        case W4A16_ERR_PLAN: return "plan not available in this build";
+        case W4A16_ERR_PLAN: return "no compiled kernel for this plan";
         default: return "unknown status";
     }
 }

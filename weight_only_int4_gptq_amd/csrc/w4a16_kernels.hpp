@@ -246,10 +246,16 @@ __device__ __forceinline__ u32x2 nv_block(const u32x4 &w) {
     return u32x2{e2m1x2_to_bf16x2<2 * (B & 1)>(x), e2m1x2_to_bf16x2<2 * (B & 1) + 1>(x)};
 }
 
-// E4M3 scale of block B from a lane's 8 scale bytes (gfx950 converts OCP E4M3).
-template <int B>
-__device__ __forceinline__ float nv_scale(const uint32_t *s) {
-    return __builtin_amdgcn_cvt_f32_fp8((int)s[B >> 2], B & 3);
+// The eight E4M3 block scales of a lane's 8 scale bytes (gfx950 converts
+// OCP E4M3), two per instruction: out[b] is byte b.
+__device__ __forceinline__ void nv_scales(const uint32_t *s, float (&out)[8]) {
+    typedef float f32x2 __attribute__((ext_vector_type(2)));
+    const f32x2 v0 = __builtin_amdgcn_cvt_pk_f32_fp8((int)s[0], false);
+    const f32x2 v1 = __builtin_amdgcn_cvt_pk_f32_fp8((int)s[0], true);
+    const f32x2 v2 = __builtin_amdgcn_cvt_pk_f32_fp8((int)s[1], false);
+    const f32x2 v3 = __builtin_amdgcn_cvt_pk_f32_fp8((int)s[1], true);
+    out[0] = v0[0], out[1] = v0[1], out[2] = v1[0], out[3] = v1[1];
+    out[4] = v2[0], out[5] = v2[1], out[6] = v3[0], out[7] = v3[1];
 }
 
 // 16x16x16 bf16 product: lane l supplies A[l % 16][4 (l / 16) + i] and
@@ -481,10 +487,12 @@ static __global__ void __launch_bounds__(256) nv_export_kernel(const u32x4 *__re
     const u32x4 w = blob[pc];
     const u32x2 sraw = *reinterpret_cast<const u32x2 *>(scales + (tg * 16 + c) * 8);
     const uint32_t s[2] = {sraw[0], sraw[1]};
+    float scl[8];
+    nv_scales(s, scl);
     [&]<int... B>(std::integer_sequence<int, B...>) {
         (([&] {
              const u32x2 v = nv_block<B>(w);
-             const float sc = nv_scale<B>(s);
+             const float sc = scl[B];
              const long long k = (long long)g * kGroup + B * kNvBlock + 4 * h;
              W[k * N + n] = pair_lo(v[0]) * sc;
              W[(k + 1) * N + n] = pair_hi(v[0]) * sc;
@@ -801,10 +809,12 @@ __global__ void __launch_bounds__(64 * KW) gemm_kernel(GemmArgs p) {
                 }
 #pragma unroll
                 for (int t = 0; t < T; ++t) {
+                    float scl[8];
+                    nv_scales(sv[j][t], scl);
                     [&]<int... B>(std::integer_sequence<int, B...>) {
                         (([&] {
                              const f32x4 P = mfma16x16x16(a[B], nv_block<B>(wv[j][t]), f32x4{0.0f, 0.0f, 0.0f, 0.0f});
-                             const float sc = nv_scale<B>(sv[j][t]);
+                             const float sc = scl[B];
 #pragma unroll
                              for (int v = 0; v < kRowsV; ++v) acc[t][v] = __builtin_fmaf(sc, P[v], acc[t][v]);
                          }()),
@@ -814,6 +824,9 @@ __global__ void __launch_bounds__(64 * KW) gemm_kernel(GemmArgs p) {
             } else {
                 // GEMV: per block, two dot2 per row on the lane's four rows,
                 // then the scale
+                float scl[T][8];
+#pragma unroll
+                for (int t = 0; t < T; ++t) nv_scales(sv[j][t], scl[t]);
                 [&]<int... B>(std::integer_sequence<int, B...>) {
                     (([&] {
                          u32x2 ar[MM];
@@ -824,7 +837,7 @@ __global__ void __launch_bounds__(64 * KW) gemm_kernel(GemmArgs p) {
 #pragma unroll
                          for (int t = 0; t < T; ++t) {
                              const u32x2 w = nv_block<B>(wv[j][t]);
-                             const float sc = nv_scale<B>(sv[j][t]);
+                             const float sc = scl[t][B];
 #pragma unroll
                              for (int m = 0; m < MM; ++m) {
                                  const float part = dot2_bf16(w[1], ar[m][1], dot2_bf16(w[0], ar[m][0], 0.0f));

@@ -90,7 +90,6 @@ extern const int kNumPlainCt, kNumPlainRt, kNumEpiCt, kNumEpiRt;
     X(PATH_MFMA, 0, 8, 1, 2, ASRC_GLOBAL) X(PATH_MFMA, 0, 8, 1, 3, ASRC_GLOBAL)                    \
     X(PATH_MFMA, 0, 2, 4, 2, ASRC_RING) X(PATH_MFMA, 0, 2, 4, 4, ASRC_RING)                        \
     X(PATH_MFMA, 0, 4, 4, 2, ASRC_RING) X(PATH_MFMA, 0, 4, 2, 2, ASRC_RING)                        \
-    X(PATH_MFMA, 0, 8, 4, 2, ASRC_RING) X(PATH_MFMA, 0, 8, 2, 2, ASRC_RING)                        \
     W4A16_NV_MFMA(X, 1, ASRC_LDS) W4A16_NV_MFMA(X, 2, ASRC_LDS) W4A16_NV_MFMA(X, 3, ASRC_LDS)     \
     W4A16_NV_MFMA(X, 4, ASRC_LDS) W4A16_NV_MFMA(X, 2, ASRC_GLOBAL) W4A16_NV_MFMA(X, 4, ASRC_GLOBAL)
 

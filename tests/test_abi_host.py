@@ -149,10 +149,11 @@ def test_row_count_dispatch():
     # tiny K: no more K waves than K groups
     assert w4.get_plan(1, 1024, 512).kwaves <= 4
     assert w4.get_plan(1, 1024, 256).kwaves == 1
-    for M in (1, 2, 5, 16):
-        for K in (128, 256, 512, 5120, 17408):
+    for M in range(1, 17):
+        for K in (128, 256, 512, 5120, 17408, 1 << 20, 1 << 24):
             for N in (16, 1024, 8192, 34816):
                 assert w4.plan_ok(M, N, K, w4.get_plan(M, N, K)), (M, N, K)
+                assert w4.nvfp4_plan_ok(M, N, K, w4.nvfp4_get_plan(M, N, K)), (M, N, K)
     p = w4.Plan()
     assert w4.lib().w4a16_get_plan(0, 1024, 512, ctypes.byref(p)) == -2
 

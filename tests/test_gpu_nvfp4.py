@@ -259,3 +259,15 @@ def test_nvfp4_workload_parity_lm_head_sampled():
         e = float(oracle.normalized_error(got, Cref[:M], Dref[:M]).max())
         note(f"  lm_head M={M} plan={w4.nvfp4_get_plan(M, N, K)} max normalized error {e:.3e}")
         assert e <= TOL
+
+
+def test_nvfp4_maximum_k():
+    # K = 2^24, the largest valid K: A streams (global memory or the ring)
+    K, N = 1 << 24, 16
+    A, packed, scales = synth.gen_nvfp4_problem(K, N, 52, M=5)
+    blob, sc, a = to_dev(packed, scales, A)
+    Cref, Dref = oracle.nvfp4_gemm(A, packed, scales, ALPHA, 5, N, K)
+    for M in (1, 2, 5):
+        note(f"[nvfp4 max K] M={M} plan={w4.nvfp4_get_plan(M, N, K)}")
+        C = run(a, blob, sc, N, M)
+        assert max_err(C, Cref[:M], Dref[:M]) <= TOL, M

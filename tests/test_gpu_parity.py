@@ -569,3 +569,20 @@ def test_tensor_parallel_column_shards():
         q_i, s_i, _ = to_dev(qw_i, sc_i)
         C_i = run_gemm(a, w4.repack_weights(q_i, K, Ni), s_i, Ni, 4)
         assert torch.equal(C_i, full[:, i * Ni:(i + 1) * Ni]), i
+
+
+# ------------------------------------------------------------- maximum K
+
+def test_gemm_maximum_k():
+    # K = 2^24, the largest valid K (131072 groups): A is too long to stage in
+    # LDS, so the planner streams it; one 16-column tile
+    K, N = 1 << 24, 16
+    A, qw, sc = synth.gen_problem(K, N, 51, M=8)
+    q, s, a = to_dev(qw, sc, A)
+    blob = w4.repack_weights(q, K, N)
+    Cref, Dref = oracle.gemm(A, qw, sc, 8, N, K)
+    for M in (1, 3, 8):
+        note(f"[max K] M={M} plan={w4.get_plan(M, N, K)}")
+        C = run_gemm(a, blob, s, N, M)
+        e = max_err(C, Cref[:M], Dref[:M])
+        assert e <= TOL, (M, e)

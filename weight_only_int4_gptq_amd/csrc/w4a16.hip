@@ -350,19 +350,25 @@ void auto_plan_nv(int M, int N, int K, w4a16_plan_t *out) {
     // wavefronts along K than each split's groups
     while (p.splits > 1 && p.splits * p.kwaves > G) p.splits >>= 1;
     while (p.kwaves > 1 && p.kwaves > G) p.kwaves >>= 1;
-    w4a16_plan_t cand[7] = {p, p, p, p, p, p, p};
+    // fallbacks: A from global memory; the LDS ring (its kernels take any
+    // row count, so they also cover K ranges of A too long to stage); the
+    // common shapes; the short-K shapes
+    w4a16_plan_t cand[9] = {p, p, p, p, p, p, p, p, p};
     cand[1].asrc = W4A16_ASRC_GLOBAL;
-    cand[2].tiles = 2, cand[2].kwaves = 4, cand[2].depth = 4, cand[2].splits = 1;
-    cand[3] = cand[2], cand[3].asrc = W4A16_ASRC_GLOBAL;
-    cand[4] = cand[2], cand[4].path = M <= 4 ? W4A16_PATH_GEMV : W4A16_PATH_MFMA;
-    cand[5].tiles = 1, cand[5].kwaves = 1, cand[5].depth = 8, cand[5].splits = 1, cand[5].asrc = W4A16_ASRC_LDS;
-    cand[6] = cand[5], cand[6].path = W4A16_PATH_MFMA, cand[6].asrc = W4A16_ASRC_GLOBAL;
+    cand[2].path = W4A16_PATH_MFMA, cand[2].asrc = W4A16_ASRC_RING, cand[2].tiles = 2, cand[2].kwaves = 4;
+    cand[2].depth = 2;
+    cand[3] = cand[2], cand[3].splits = 1;
+    cand[4].tiles = 2, cand[4].kwaves = 4, cand[4].depth = 4, cand[4].splits = 1;
+    cand[5] = cand[4], cand[5].asrc = W4A16_ASRC_GLOBAL;
+    cand[6] = cand[4], cand[6].path = M <= 4 ? W4A16_PATH_GEMV : W4A16_PATH_MFMA;
+    cand[7].tiles = 1, cand[7].kwaves = 1, cand[7].depth = 8, cand[7].splits = 1, cand[7].asrc = W4A16_ASRC_LDS;
+    cand[8] = cand[7], cand[8].path = W4A16_PATH_MFMA, cand[8].asrc = W4A16_ASRC_GLOBAL;
     for (const w4a16_plan_t &c : cand)
         if (validate_plan(c, M, N, K, FMT_NVFP4) == W4A16_OK) {
             *out = c;
             return;
         }
-    *out = cand[6];
+    *out = cand[3];
 }
 
 size_t workspace_for(const w4a16_plan_t &p, int M, int N) {

@@ -49,7 +49,8 @@ KERNEL_SOURCES = ["weight_only_int4_gptq_amd/csrc/w4a16.hip",
                   "weight_only_int4_gptq_amd/csrc/variants_plain_rt.hip",
                   "weight_only_int4_gptq_amd/csrc/variants_epi_rt.hip",
                   "weight_only_int4_gptq_amd/build.py",
-                  "weight_only_int4_gptq_amd/csrc/variants_nvfp4.hip"]
+                  "weight_only_int4_gptq_amd/csrc/variants_nvfp4.hip",
+                  "weight_only_int4_gptq_amd/csrc/variants_nvfp4_epi.hip"]
 
 
 def log(*a):

@@ -318,7 +318,7 @@ int w4a16_unpack(const void *wq_repacked, uint8_t *codes, int K, int N, void *st
  *            n = 16t + c at byte ((t*G + g)*16 + c)*8 + b.
  * Valid shapes as for the GPTQ calls (K a multiple of 128, N of 16,
  * 1 <= M <= 16); group must be W4A16_NVFP4_GROUP.  A block scale of NaN
- * (S.1111.111) makes its outputs NaN.  Plain C output only.
+ * (S.1111.111) makes its outputs NaN.
  */
 
 /* Bytes of the NVFP4 blob (= K*N/2) and of its repacked scales (= K*N/16); 0 for invalid shapes. */
@@ -357,6 +357,38 @@ int w4a16_nvfp4_gemm(const void *A, const void *wq_repacked, const void *scales,
 int w4a16_nvfp4_gemm_plan(const void *A, const void *wq_repacked, const void *scales, float alpha,
                           void *C, int M, int N, int K, int group, void *workspace,
                           size_t workspace_bytes, const w4a16_plan_t *plan, void *stream);
+
+/*
+ * The epilogue modes of the GPTQ calls for NVFP4 weights: the same contracts
+ * as w4a16_gemm_silu_mul, w4a16_gemm_argmax and w4a16_gemm_f32 (and their
+ * _plan forms), with C = alpha * A . dequant(blob, scales).  alpha multiplies
+ * each fp32 sum before the epilogue: before SiLU(gate) * up, before the
+ * argmax comparison (a negative alpha picks the smallest sum), and in the
+ * fp32 output.  group must be W4A16_NVFP4_GROUP.  A checkpoint quantized to
+ * NVFP4 for all its GEMMs (page "Qwen3.8 27B - NVFP4 for veloGB10", section
+ * "Specifications": recipe "all") runs its gate/up, output projection and
+ * tensor-parallel shards through these.
+ */
+int w4a16_nvfp4_gemm_silu_mul(const void *A, const void *wq_repacked, const void *scales, float alpha,
+                              void *H, int M, int N, int K, int group, void *workspace,
+                              size_t workspace_bytes, void *stream);
+int w4a16_nvfp4_gemm_silu_mul_plan(const void *A, const void *wq_repacked, const void *scales,
+                                   float alpha, void *H, int M, int N, int K, int group,
+                                   void *workspace, size_t workspace_bytes, const w4a16_plan_t *plan,
+                                   void *stream);
+int w4a16_nvfp4_gemm_argmax(const void *A, const void *wq_repacked, const void *scales, float alpha,
+                            int *idx, float *val, int M, int N, int K, int group, void *workspace,
+                            size_t workspace_bytes, void *stream);
+int w4a16_nvfp4_gemm_argmax_plan(const void *A, const void *wq_repacked, const void *scales,
+                                 float alpha, int *idx, float *val, int M, int N, int K, int group,
+                                 void *workspace, size_t workspace_bytes, const w4a16_plan_t *plan,
+                                 void *stream);
+int w4a16_nvfp4_gemm_f32(const void *A, const void *wq_repacked, const void *scales, float alpha,
+                         float *C, int M, int N, int K, int group, void *workspace,
+                         size_t workspace_bytes, void *stream);
+int w4a16_nvfp4_gemm_f32_plan(const void *A, const void *wq_repacked, const void *scales, float alpha,
+                              float *C, int M, int N, int K, int group, void *workspace,
+                              size_t workspace_bytes, const w4a16_plan_t *plan, void *stream);
 
 /*
  * Test export of the NVFP4 device dequantization: W[k][n] = e2m1 * e4m3 as

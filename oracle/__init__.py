@@ -299,16 +299,25 @@ def gemm_silu_mul(A: np.ndarray, qweight: np.ndarray, scales: np.ndarray, M: int
     their own sum |a*w| (D_g, D_u): the GEMM's normalized error bound
     carried through the activation.
     """
+    j, cols = _gate_up_columns(N, js, "gemm_silu_mul")
+    C, D = gemm(A, qweight, scales, M, N, K, cols=cols, nthreads=nthreads)
+    return _silu_mul(C, D, j.size)
+
+
+def _gate_up_columns(N: int, js, who: str):
     if N % 32:
-        raise ValueError("oracle.gemm_silu_mul: N must be a multiple of 32")
+        raise ValueError(f"oracle.{who}: N must be a multiple of 32")
     half = N // 2
     j = np.arange(half, dtype=np.int64) if js is None else np.asarray(js, dtype=np.int64)
     if j.size and (j.min() < 0 or j.max() >= half):
-        raise ValueError("oracle.gemm_silu_mul: column index out of range")
-    cols = np.concatenate([j, j + half])
-    C, D = gemm(A, qweight, scales, M, N, K, cols=cols, nthreads=nthreads)
-    g, u = C[:, :j.size], C[:, j.size:]
-    dg, du = D[:, :j.size], D[:, j.size:]
+        raise ValueError(f"oracle.{who}: column index out of range")
+    return j, np.concatenate([j, j + half])
+
+
+def _silu_mul(C, D, nj: int):
+    """(H, E) from the gate sums C[:, :nj] and up sums C[:, nj:] and their D."""
+    g, u = C[:, :nj], C[:, nj:]
+    dg, du = D[:, :nj], D[:, nj:]
     H = silu(g) * u
     E = np.abs(silu_derivative(g)) * np.abs(u) * dg + np.abs(silu(g)) * du
     return H, E
@@ -407,6 +416,20 @@ def nvfp4_gemm(A: np.ndarray, packed: np.ndarray, scales: np.ndarray, alpha: flo
     _load().oracle_nvfp4_gemm(_ptr(a), _ptr(pk), _ptr(sc), float(alpha), M, N, K, cptr, ncols,
                               int(nthreads), _ptr(C), _ptr(D))
     return C, D
+
+
+def nvfp4_gemm_silu_mul(A: np.ndarray, packed: np.ndarray, scales: np.ndarray, alpha: float, M: int,
+                        N: int, K: int, js=None, nthreads: int = 0):
+    """fp64 reference of the gate/up activation on NVFP4 weights:
+
+        H[m, j] = silu(C[m, j]) * C[m, j + N/2],   C = alpha * A . dequant(W)  (as ``nvfp4_gemm``)
+
+    The same reading of the gate/up layout and the same first-order bound E
+    as ``gemm_silu_mul``, with D = |alpha| sum |a*w|.  Returns (H, E).
+    """
+    j, cols = _gate_up_columns(N, js, "nvfp4_gemm_silu_mul")
+    C, D = nvfp4_gemm(A, packed, scales, alpha, M, N, K, cols=cols, nthreads=nthreads)
+    return _silu_mul(C, D, j.size)
 
 
 def nvfp4_repack(packed: np.ndarray, K: int, N: int) -> np.ndarray:

@@ -259,3 +259,54 @@ def test_nvfp4_sizes_plans_and_no_device():
     if not torch.cuda.is_available():
         assert _nv() == -6
         assert L.w4a16_nvfp4_repack_weights(P, P2, 512, 1024, NULL) == -6
+
+
+def _nv_epi(kind, A=P, wq=P, s=P, out=P2, val=P2, M=1, N=1024, K=512, group=16, ws=P, wsb=1 << 24,
+            plan=None, alpha=0.5):
+    L = w4.lib()
+    name = {"silu": "w4a16_nvfp4_gemm_silu_mul", "argmax": "w4a16_nvfp4_gemm_argmax",
+            "f32": "w4a16_nvfp4_gemm_f32"}[kind]
+    head = (A, wq, s, alpha, out, val) if kind == "argmax" else (A, wq, s, alpha, out)
+    tail = (M, N, K, group, ws, wsb)
+    if plan is None:
+        return getattr(L, name)(*head, *tail, NULL)
+    return getattr(L, name + "_plan")(*head, *tail, ctypes.byref(plan), NULL)
+
+
+@pytest.mark.parametrize("kind,kw,status", [
+    ("silu", dict(A=NULL), -1), ("silu", dict(out=NULL), -1), ("silu", dict(s=NULL), -1),
+    ("silu", dict(N=1008), -2), ("silu", dict(group=128), -3), ("silu", dict(out=ODD), -4),
+    ("silu", dict(plan=w4.make_plan(w4.PATH_MFMA, 1, 4)), -8),
+    ("argmax", dict(out=NULL), -1), ("argmax", dict(val=NULL), -1), ("argmax", dict(M=17), -2),
+    ("argmax", dict(group=128), -3), ("argmax", dict(out=ctypes.c_void_p(0x20002)), -4),
+    ("argmax", dict(wsb=65535), -5), ("argmax", dict(ws=NULL), -5),
+    ("argmax", dict(plan=w4.make_plan(w4.PATH_MFMA, 1, 4, 2)), -8),
+    ("f32", dict(out=NULL), -1), ("f32", dict(K=520), -2), ("f32", dict(group=128), -3),
+    ("f32", dict(plan=w4.make_plan(w4.PATH_MFMA, 1, 1, 1, w4.ASRC_RING)), -8),
+])
+def test_nvfp4_epilogue_argument_errors(kind, kw, status):
+    assert _nv_epi(kind, **kw) == status
+
+
+@pytest.mark.parametrize("kind", ["silu", "argmax", "f32"])
+def test_epilogue_auto_plans_have_a_kernel(kind):
+    # without a device a call that passed every host check (the automatic
+    # plan and its compiled kernel included) returns "no device": so no
+    # automatic plan of any mode, format or row count lacks a kernel
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present")
+    L = w4.lib()
+    shapes = ((8192, 5120), (34816, 5120), (5120, 17408), (248320, 5120), (1024, 512), (64, 128),
+              (2048, 1 << 24))
+    for M in range(1, 17):
+        for N, K in shapes:
+            assert _nv_epi(kind, M=M, N=N, K=K, wsb=1 << 40) == -6, (kind, M, N, K)
+            g = dict(M=M, N=N, K=K, group=128, ws=P, wsb=1 << 40)
+            if kind == "silu":
+                st = L.w4a16_gemm_silu_mul(P, P, P, P2, M, N, K, 128, P, 1 << 40, NULL)
+            elif kind == "argmax":
+                st = L.w4a16_gemm_argmax(P, P, P, P2, P2, M, N, K, 128, P, 1 << 40, NULL)
+            else:
+                st = L.w4a16_gemm_f32(P, P, P, P2, M, N, K, 128, P, 1 << 40, NULL)
+            assert st == -6, (kind, g)

@@ -208,3 +208,50 @@ def test_nvfp4_dequant_products_are_fp32_exact():
     scales[(scales & 0x7F) == 0x7F] = 0x01
     W = oracle.nvfp4_dequant(packed, scales, K, N)
     assert np.array_equal(W.astype(np.float32).astype(np.float64), W)
+
+
+def test_nvfp4_gemm_silu_mul_halves_alpha_and_zero_gate():
+    # one-hot A on row k, scales 1.0 (0x38): C[0, n] = alpha * e2m1(code(k, n)), so
+    # H[0, j] = silu(alpha g_j) * alpha u_j with g, u read from the table
+    K, N, k = 256, 64, 77
+    rng = np.random.default_rng(11)
+    packed = rng.integers(0, 256, size=(N, K // 2), dtype=np.uint8)
+    scales = np.full((N, K // 16), 0x38, dtype=np.uint8)
+    A = np.zeros((1, K), dtype=np.uint16)
+    A[0, k] = 0x3F80
+    codes = packed[:, k // 2] >> 4 if k % 2 else packed[:, k // 2] & 0xF
+    for alpha in (1.0, 0.5, -2.0):
+        H, E = oracle.nvfp4_gemm_silu_mul(A, packed, scales, alpha, 1, N, K)
+        for j in range(N // 2):
+            g = alpha * E2M1[int(codes[j])]
+            u = alpha * E2M1[int(codes[j + N // 2])]
+            want = g / (1.0 + math.exp(-g)) * u
+            assert abs(H[0, j] - want) <= 1e-12 * max(1.0, abs(want)), (alpha, j, H[0, j], want)
+        assert np.all(E >= 0)
+    # gate codes 0 (+0) and 8 (-0) give exact zeros whatever the up half holds
+    p0 = packed.copy()
+    p0[: N // 2] = np.where(rng.integers(0, 2, size=p0[: N // 2].shape) > 0, 0x00, 0x88).astype(np.uint8)
+    A2 = synth.gen_activations(3, K, rng)
+    H0, _ = oracle.nvfp4_gemm_silu_mul(A2, p0, scales, 0.25, 3, N, K)
+    assert np.all(H0 == 0.0)
+    # column subsets equal the full result
+    H, E = oracle.nvfp4_gemm_silu_mul(A2, packed, scales, 0.25, 3, N, K)
+    js = np.array([31, 0, 9])
+    Hs, Es = oracle.nvfp4_gemm_silu_mul(A2, packed, scales, 0.25, 3, N, K, js=js)
+    assert np.array_equal(Hs, H[:, js]) and np.array_equal(Es, E[:, js])
+
+
+def test_nvfp4_row_argmax_follows_the_sign_of_alpha():
+    # one-hot A picks row k of W: the argmax of alpha * W[k] is the column of
+    # the largest entry for alpha > 0 and of the smallest for alpha < 0
+    K, N, k = 128, 48, 40
+    rng = np.random.default_rng(12)
+    packed = rng.integers(0, 256, size=(N, K // 2), dtype=np.uint8)
+    scales = rng.integers(0x30, 0x50, size=(N, K // 16), dtype=np.uint8)
+    A = np.zeros((1, K), dtype=np.uint16)
+    A[0, k] = 0x3F80
+    W = oracle.nvfp4_dequant(packed, scales, K, N)
+    Cp, _ = oracle.nvfp4_gemm(A, packed, scales, 0.5, 1, N, K)
+    Cn, _ = oracle.nvfp4_gemm(A, packed, scales, -0.5, 1, N, K)
+    assert oracle.row_argmax(Cp)[0] == int(np.argmax(W[k]))
+    assert oracle.row_argmax(Cn)[0] == int(np.argmin(W[k]))

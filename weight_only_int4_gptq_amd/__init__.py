@@ -89,9 +89,18 @@ def lib():
         L.w4a16_nvfp4_gemm.argtypes = [P, P, P, F, P, I, I, I, I, P, S, P]
         L.w4a16_nvfp4_gemm_plan.argtypes = [P, P, P, F, P, I, I, I, I, P, S, ctypes.POINTER(Plan), P]
         L.w4a16_nvfp4_dequant.argtypes = [P, P, P, I, I, P]
+        PL = ctypes.POINTER(Plan)
+        L.w4a16_nvfp4_gemm_silu_mul.argtypes = [P, P, P, F, P, I, I, I, I, P, S, P]
+        L.w4a16_nvfp4_gemm_silu_mul_plan.argtypes = [P, P, P, F, P, I, I, I, I, P, S, PL, P]
+        L.w4a16_nvfp4_gemm_argmax.argtypes = [P, P, P, F, P, P, I, I, I, I, P, S, P]
+        L.w4a16_nvfp4_gemm_argmax_plan.argtypes = [P, P, P, F, P, P, I, I, I, I, P, S, PL, P]
+        L.w4a16_nvfp4_gemm_f32.argtypes = [P, P, P, F, P, I, I, I, I, P, S, P]
+        L.w4a16_nvfp4_gemm_f32_plan.argtypes = [P, P, P, F, P, I, I, I, I, P, S, PL, P]
         for f in ("w4a16_nvfp4_repack_weights", "w4a16_nvfp4_repack_scales", "w4a16_nvfp4_get_plan",
                   "w4a16_nvfp4_check_plan", "w4a16_nvfp4_gemm", "w4a16_nvfp4_gemm_plan",
-                  "w4a16_nvfp4_dequant"):
+                  "w4a16_nvfp4_dequant", "w4a16_nvfp4_gemm_silu_mul", "w4a16_nvfp4_gemm_silu_mul_plan",
+                  "w4a16_nvfp4_gemm_argmax", "w4a16_nvfp4_gemm_argmax_plan", "w4a16_nvfp4_gemm_f32",
+                  "w4a16_nvfp4_gemm_f32_plan"):
             getattr(L, f).restype = I
         for f in ("w4a16_repack_weights", "w4a16_get_plan", "w4a16_gemm", "w4a16_gemm_plan",
                   "w4a16_gemm_silu_mul", "w4a16_gemm_silu_mul_plan", "w4a16_gemm_argmax",
@@ -352,6 +361,72 @@ def nvfp4_gemm(A: torch.Tensor, blob: torch.Tensor, scales: torch.Tensor, alpha:
                                          K, group, _ptr(workspace), ws_bytes, ctypes.byref(plan),
                                          _stream(A))
     _check(st, "w4a16_nvfp4_gemm")
+    return out
+
+
+def _nv_ws(A, N, K, plan, workspace, minimum=0):
+    M = A.shape[0]
+    if workspace is None:
+        need = max(nvfp4_workspace_bytes(M, N, K, plan), minimum)
+        if need:
+            workspace = _shared_workspace(A.device, need)
+    return workspace, (workspace.numel() * workspace.element_size() if workspace is not None else 0)
+
+
+def nvfp4_gemm_silu_mul(A: torch.Tensor, blob: torch.Tensor, scales: torch.Tensor, alpha: float, N: int,
+                        out: torch.Tensor | None = None, plan: Plan | None = None,
+                        workspace: torch.Tensor | None = None, group: int = NVFP4_GROUP):
+    """H[M, N/2] = silu(C[:, :N/2]) * C[:, N/2:], C = alpha * A . dequant(NVFP4 gate/up weight [K, N])."""
+    M, K = A.shape
+    if out is None:
+        out = torch.empty((M, N // 2), dtype=torch.bfloat16, device=A.device)
+    ws, wsb = _nv_ws(A, N, K, plan, workspace)
+    if plan is None:
+        st = lib().w4a16_nvfp4_gemm_silu_mul(_ptr(A), _ptr(blob), _ptr(scales), float(alpha), _ptr(out), M, N, K,
+                                             group, _ptr(ws), wsb, _stream(A))
+    else:
+        st = lib().w4a16_nvfp4_gemm_silu_mul_plan(_ptr(A), _ptr(blob), _ptr(scales), float(alpha), _ptr(out), M,
+                                                  N, K, group, _ptr(ws), wsb, ctypes.byref(plan), _stream(A))
+    _check(st, "w4a16_nvfp4_gemm_silu_mul")
+    return out
+
+
+def nvfp4_gemm_argmax(A: torch.Tensor, blob: torch.Tensor, scales: torch.Tensor, alpha: float, N: int,
+                      plan: Plan | None = None, workspace: torch.Tensor | None = None,
+                      group: int = NVFP4_GROUP):
+    """Per-row argmax of C = alpha * A . dequant(NVFP4 W): (idx int32 [M], val float32 [M])."""
+    M, K = A.shape
+    idx = torch.empty(M, dtype=torch.int32, device=A.device)
+    val = torch.empty(M, dtype=torch.float32, device=A.device)
+    if workspace is None:
+        workspace = _shared_workspace(A.device, ARGMAX_WORKSPACE_BYTES)
+    wsb = workspace.numel() * workspace.element_size()
+    if plan is None:
+        st = lib().w4a16_nvfp4_gemm_argmax(_ptr(A), _ptr(blob), _ptr(scales), float(alpha), _ptr(idx), _ptr(val),
+                                           M, N, K, group, _ptr(workspace), wsb, _stream(A))
+    else:
+        st = lib().w4a16_nvfp4_gemm_argmax_plan(_ptr(A), _ptr(blob), _ptr(scales), float(alpha), _ptr(idx),
+                                                _ptr(val), M, N, K, group, _ptr(workspace), wsb,
+                                                ctypes.byref(plan), _stream(A))
+    _check(st, "w4a16_nvfp4_gemm_argmax")
+    return idx, val
+
+
+def nvfp4_gemm_f32(A: torch.Tensor, blob: torch.Tensor, scales: torch.Tensor, alpha: float, N: int,
+                   out: torch.Tensor | None = None, plan: Plan | None = None,
+                   workspace: torch.Tensor | None = None, group: int = NVFP4_GROUP):
+    """C = alpha * A . dequant(NVFP4 W) as unrounded fp32 (a K shard's partial sum)."""
+    M, K = A.shape
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.float32, device=A.device)
+    ws, wsb = _nv_ws(A, N, K, plan, workspace)
+    if plan is None:
+        st = lib().w4a16_nvfp4_gemm_f32(_ptr(A), _ptr(blob), _ptr(scales), float(alpha), _ptr(out), M, N, K,
+                                        group, _ptr(ws), wsb, _stream(A))
+    else:
+        st = lib().w4a16_nvfp4_gemm_f32_plan(_ptr(A), _ptr(blob), _ptr(scales), float(alpha), _ptr(out), M, N,
+                                             K, group, _ptr(ws), wsb, ctypes.byref(plan), _stream(A))
+    _check(st, "w4a16_nvfp4_gemm_f32")
     return out
 
 

@@ -17,14 +17,16 @@ LIB = os.path.join(PKG, "libw4a16.so")
 # code, the GPTQ matmul kernels (plain and with epilogue modes, each in
 # compile-time-row and run-time-row units) and the NVFP4 ones
 SOURCES = [os.path.join(PKG, "csrc", f) for f in ("w4a16.hip", "variants_plain.hip", "variants_plain_rt.hip",
-                                                   "variants_epi.hip", "variants_epi_rt.hip", "variants_nvfp4.hip")]
+                                                   "variants_epi.hip", "variants_epi_rt.hip", "variants_nvfp4.hip",
+                                                   "variants_nvfp4_epi.hip")]
 # Matrix-core results in ordinary VGPRs rather than accumulation registers:
 # the kernels that read every product back with VALU instructions (the
 # NVFP4 block scales; the run-time-row shapes) otherwise copy each result out
 # of the accumulation registers first.  Measured per unit: the GEMV and
 # compile-time-row kernels are as fast or faster without it.
 SOURCE_FLAGS = {name: ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]
-                for name in ("variants_plain_rt.hip", "variants_epi_rt.hip", "variants_nvfp4.hip")}
+                for name in ("variants_plain_rt.hip", "variants_epi_rt.hip", "variants_nvfp4.hip",
+                             "variants_nvfp4_epi.hip")}
 PROBE_LIB = os.path.join(PKG, "libw4a16_probe.so")
 PROBE_SOURCES = [os.path.join(PKG, "csrc", "probe_stream.hip")]
 DEPENDS = SOURCES + [os.path.join(PKG, "csrc", "w4a16_kernels.hpp"), os.path.join(PKG, "csrc", "w4a16_variants.hpp"),

@@ -36,17 +36,16 @@ int default_depth(int tiles) { return tiles == 1 ? 8 : (tiles == 2 ? 4 : 2); }
 // MFMA kernels too for M <= 4 (LDS or global A), and take M at run time
 // above and with ring A.
 // epi: a kernel that carries the epilogue modes (else a plain matmul);
-// fmt: the weight format (NVFP4 kernels are plain matmuls only)
+// fmt: the weight format
 const Variant *find_variant(const w4a16_plan_t &p, int M, bool epi = false, int fmt = FMT_GPTQ) {
     // ring A kernels take M at run time for every row count
     const int mm = (p.path == W4A16_PATH_GEMV || (M <= 4 && p.asrc != W4A16_ASRC_RING)) ? M : 0;
     const int asrc = (p.path == W4A16_PATH_GEMV) ? ASRC_LDS : p.asrc;
     const int depth = p.depth ? p.depth : default_depth(p.tiles);
-    if (fmt == FMT_NVFP4 && epi) return nullptr;
     VariantTable tabs[2];
     int ntabs = 0;
     if (fmt == FMT_NVFP4) {
-        tabs[ntabs++] = {kVariantsNv, kNumVariantsNv};
+        tabs[ntabs++] = epi ? VariantTable{kVariantsNvEpi, kNumVariantsNvEpi} : VariantTable{kVariantsNv, kNumVariantsNv};
     } else if (epi) {
         tabs[ntabs++] = {kVariantsEpiCt, kNumEpiCt};
         tabs[ntabs++] = {kVariantsEpiRt, kNumEpiRt};
@@ -69,7 +68,7 @@ const Variant *find_variant(const w4a16_plan_t &p, int M, bool epi = false, int 
 int variant_slot(const Variant *v) {
     const VariantTable tabs[] = {{kVariantsPlainCt, kNumPlainCt}, {kVariantsPlainRt, kNumPlainRt},
                                  {kVariantsEpiCt, kNumEpiCt},     {kVariantsEpiRt, kNumEpiRt},
-                                 {kVariantsNv, kNumVariantsNv}};
+                                 {kVariantsNv, kNumVariantsNv},   {kVariantsNvEpi, kNumVariantsNvEpi}};
     int base = 0;
     for (const VariantTable &t : tabs) {
         if (v >= t.v && v < t.v + t.n) return base + (int)(v - t.v);
@@ -387,13 +386,14 @@ static_assert(kArgmaxBinOffset + kArgmaxBins * 16 * 8 <= W4A16_ARGMAX_WORKSPACE_
 
 // The gate/up epilogue needs strips of gate/up tile pairs: an even tile
 // count.  The automatic plan is moved to two tiles when it has one.
-void fuse_plan(int M, w4a16_plan_t *p) {
+void fuse_plan(int M, w4a16_plan_t *p, int fmt = FMT_GPTQ) {
     if (p->tiles % 2 == 0) return;
     w4a16_plan_t q = *p;
     q.tiles = 2;                               // same wavefronts and ring depth if compiled
-    if (!find_variant(q, M, true)) q.depth = 0;
-    if (!find_variant(q, M, true)) q.kwaves = 4;
-    if (!find_variant(q, M, true)) q.asrc = W4A16_ASRC_GLOBAL;
+    if (!find_variant(q, M, true, fmt)) q.depth = 0;
+    if (!find_variant(q, M, true, fmt)) q.kwaves = 4;
+    if (!find_variant(q, M, true, fmt)) q.asrc = W4A16_ASRC_GLOBAL;
+    if (!find_variant(q, M, true, fmt)) q.asrc = W4A16_ASRC_RING, q.depth = 2;
     *p = q;
 }
 
@@ -411,7 +411,6 @@ int run_gemm(const void *A, const void *wq, const void *scales, void *C, int M, 
     if (st != W4A16_OK) return st;
     if (fuse == 1 && N % 32 != 0) return W4A16_ERR_SHAPE;
     if (group != (fmt == FMT_NVFP4 ? W4A16_NVFP4_GROUP : W4A16_GROUP)) return W4A16_ERR_GROUP;
-    if (fmt == FMT_NVFP4 && fuse != 0) return W4A16_ERR_PLAN;
     if (!aligned16(A) || !aligned16(wq) || !aligned16(scales) || (fuse != 2 && !aligned16(C)))
         return W4A16_ERR_ALIGN;
     if (fuse == 2 && (((uintptr_t)idx | (uintptr_t)val) & 3)) return W4A16_ERR_ALIGN;
@@ -422,15 +421,15 @@ int run_gemm(const void *A, const void *wq, const void *scales, void *C, int M, 
         if (st != W4A16_OK) return st;
         if (fuse == 1 && p.tiles % 2 != 0) return W4A16_ERR_PLAN;
         if (fuse == 2 && p.splits != 1) return W4A16_ERR_PLAN;
-    } else if (fmt == FMT_NVFP4) {
-        auto_plan_nv(M, N, K, &p);
+        if (fuse != 0 && !find_variant(p, M, true, fmt)) return W4A16_ERR_PLAN;
     } else {
-        auto_plan(M, N, K, &p);
-        if (fuse == 1) fuse_plan(M, &p);
+        if (fmt == FMT_NVFP4) auto_plan_nv(M, N, K, &p);
+        else auto_plan(M, N, K, &p);
+        if (fuse == 1) fuse_plan(M, &p, fmt);
         if (fuse == 2 && p.splits != 1) {
             p.splits = 1;
-            if (validate_plan(p, M, N, K) != W4A16_OK) p.asrc = W4A16_ASRC_RING;
-            if (validate_plan(p, M, N, K) != W4A16_OK) p.asrc = W4A16_ASRC_GLOBAL;
+            if (validate_plan(p, M, N, K, fmt) != W4A16_OK) p.asrc = W4A16_ASRC_RING;
+            if (validate_plan(p, M, N, K, fmt) != W4A16_OK) p.asrc = W4A16_ASRC_GLOBAL;
         }
     }
     const size_t need = fuse == 2 ? (size_t)W4A16_ARGMAX_WORKSPACE_BYTES : workspace_for(p, M, N);
@@ -438,12 +437,12 @@ int run_gemm(const void *A, const void *wq, const void *scales, void *C, int M, 
         if (!workspace || workspace_bytes < need) return W4A16_ERR_WORKSPACE;
         if (!aligned16(workspace)) return W4A16_ERR_ALIGN;
     }
+    const Variant *v = find_variant(p, M, fuse != 0, fmt);
+    if (!v) return W4A16_ERR_PLAN;
     int lds_max = 0;
     st = check_device(&lds_max);
     if (st != W4A16_OK) return st;
 
-    const Variant *v = find_variant(p, M, fuse != 0, fmt);
-    if (!v) return W4A16_ERR_PLAN;
     const int lds = plan_lds(p, M, K / W4A16_GROUP);
     if (lds + 256 > lds_max) return W4A16_ERR_PLAN;   // 256: the kernel's static LDS
     if (lds > 65536) {
@@ -771,6 +770,50 @@ int w4a16_nvfp4_gemm_plan(const void *A, const void *wq_repacked, const void *sc
                           size_t workspace_bytes, const w4a16_plan_t *plan, void *stream) {
     return run_gemm(A, wq_repacked, scales, C, M, N, K, group, workspace, workspace_bytes, plan,
                     stream, 0, nullptr, nullptr, FMT_NVFP4, alpha);
+}
+
+int w4a16_nvfp4_gemm_silu_mul(const void *A, const void *wq_repacked, const void *scales, float alpha,
+                              void *H, int M, int N, int K, int group, void *workspace,
+                              size_t workspace_bytes, void *stream) {
+    return run_gemm(A, wq_repacked, scales, H, M, N, K, group, workspace, workspace_bytes, nullptr,
+                    stream, 1, nullptr, nullptr, FMT_NVFP4, alpha);
+}
+
+int w4a16_nvfp4_gemm_silu_mul_plan(const void *A, const void *wq_repacked, const void *scales,
+                                   float alpha, void *H, int M, int N, int K, int group,
+                                   void *workspace, size_t workspace_bytes, const w4a16_plan_t *plan,
+                                   void *stream) {
+    return run_gemm(A, wq_repacked, scales, H, M, N, K, group, workspace, workspace_bytes, plan,
+                    stream, 1, nullptr, nullptr, FMT_NVFP4, alpha);
+}
+
+int w4a16_nvfp4_gemm_argmax(const void *A, const void *wq_repacked, const void *scales, float alpha,
+                            int *idx, float *val, int M, int N, int K, int group, void *workspace,
+                            size_t workspace_bytes, void *stream) {
+    return run_gemm(A, wq_repacked, scales, nullptr, M, N, K, group, workspace, workspace_bytes,
+                    nullptr, stream, 2, idx, val, FMT_NVFP4, alpha);
+}
+
+int w4a16_nvfp4_gemm_argmax_plan(const void *A, const void *wq_repacked, const void *scales,
+                                 float alpha, int *idx, float *val, int M, int N, int K, int group,
+                                 void *workspace, size_t workspace_bytes, const w4a16_plan_t *plan,
+                                 void *stream) {
+    return run_gemm(A, wq_repacked, scales, nullptr, M, N, K, group, workspace, workspace_bytes,
+                    plan, stream, 2, idx, val, FMT_NVFP4, alpha);
+}
+
+int w4a16_nvfp4_gemm_f32(const void *A, const void *wq_repacked, const void *scales, float alpha,
+                         float *C, int M, int N, int K, int group, void *workspace,
+                         size_t workspace_bytes, void *stream) {
+    return run_gemm(A, wq_repacked, scales, C, M, N, K, group, workspace, workspace_bytes, nullptr,
+                    stream, 3, nullptr, nullptr, FMT_NVFP4, alpha);
+}
+
+int w4a16_nvfp4_gemm_f32_plan(const void *A, const void *wq_repacked, const void *scales, float alpha,
+                              float *C, int M, int N, int K, int group, void *workspace,
+                              size_t workspace_bytes, const w4a16_plan_t *plan, void *stream) {
+    return run_gemm(A, wq_repacked, scales, C, M, N, K, group, workspace, workspace_bytes, plan,
+                    stream, 3, nullptr, nullptr, FMT_NVFP4, alpha);
 }
 
 int w4a16_nvfp4_dequant(const void *wq_repacked, const void *scales, float *W, int K, int N,

@@ -551,7 +551,6 @@ __global__ void __launch_bounds__(64 * KW) gemm_kernel(GemmArgs p) {
     constexpr bool kGlobalA = (PATH == PATH_MFMA && ASRC == ASRC_GLOBAL);
     constexpr bool kRingA = (PATH == PATH_MFMA && ASRC == ASRC_RING);
     constexpr bool kStage = !kGlobalA && !kRingA;
-    static_assert(!kNv || !EPI, "NVFP4: plain epilogue");
     constexpr int kLoadsPerGroup = 2 * T + (kGlobalA ? (kNv ? 8 : 4) : 0);   // loads the compiler sees
     // Matrix-core bias: formed in the loop from the A fragments already
     // loaded (four more MFMAs per group, shared by the T tiles), except for
@@ -990,14 +989,22 @@ __global__ void __launch_bounds__(64 * KW) gemm_kernel(GemmArgs p) {
     // rounding at the end; H has N/2 columns.
     const int NV = T * M * 16;   // values (t, m, c) of this workgroup
     auto col_of = [&](int t, int cc) { return (size_t)tile_of(t) * 16 + cc; };
+    // NVFP4: the per-tensor factor multiplies every finished sum before its
+    // epilogue (rounding, activation, argmax key)
+    auto fin = [&](float v) {
+        if constexpr (kNv) return v * p.alpha;
+        else return v;
+    };
     auto emit_c = [&](int t, int m, int cc, float val) {      // plain, one split
-        if constexpr (kNv) val *= p.alpha;
+        val = fin(val);
         if (fuse == 3)
             reinterpret_cast<float *>(p.C)[(size_t)m * p.N + col_of(t, cc)] = val;
         else
             p.C[(size_t)m * p.N + col_of(t, cc)] = f32_to_bf16_rne(val);
     };
     auto emit_h = [&](int t, int m, int cc, float g, float u) {   // gate/up, one split
+        g = fin(g);
+        u = fin(u);
         const float hv = g / (1.0f + expf(-g)) * u;
         p.C[(size_t)m * (p.N >> 1) + col_of(t, cc)] = f32_to_bf16_rne(hv);
     };
@@ -1023,7 +1030,7 @@ __global__ void __launch_bounds__(64 * KW) gemm_kernel(GemmArgs p) {
 #pragma unroll
                     for (int i = 0; i < kRows; ++i)
                         if (row_of(i) < M && tile_ok(t))
-                            __hip_atomic_fetch_max(&keys[row_of(i)], argmax_key(row_val(t, i), (uint32_t)col_of(t, c)),
+                            __hip_atomic_fetch_max(&keys[row_of(i)], argmax_key(fin(row_val(t, i)), (uint32_t)col_of(t, c)),
                                                    __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
             }
         } else if (holder) {
@@ -1077,7 +1084,7 @@ __global__ void __launch_bounds__(64 * KW) gemm_kernel(GemmArgs p) {
             for (int t = 0; t < T; ++t)
                 for (int mc = threadIdx.x; mc < M * 16; mc += 64 * KW) {
                     if (!tile_ok(t)) continue;
-                    __hip_atomic_fetch_max(&keys[mc >> 4], argmax_key(reduced(t, mc), (uint32_t)col_of(t, mc & 15)),
+                    __hip_atomic_fetch_max(&keys[mc >> 4], argmax_key(fin(reduced(t, mc)), (uint32_t)col_of(t, mc & 15)),
                                            __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
                 }
         } else if (p.S > 1 || fuse != 1) {

@@ -93,7 +93,7 @@ extern const int kNumPlainCt, kNumPlainRt, kNumEpiCt, kNumEpiRt;
     W4A16_NV_MFMA(X, 1, ASRC_LDS) W4A16_NV_MFMA(X, 2, ASRC_LDS) W4A16_NV_MFMA(X, 3, ASRC_LDS)     \
     W4A16_NV_MFMA(X, 4, ASRC_LDS) W4A16_NV_MFMA(X, 2, ASRC_GLOBAL) W4A16_NV_MFMA(X, 4, ASRC_GLOBAL)
 
-extern const Variant kVariantsNv[];
-extern const int kNumVariantsNv;
+extern const Variant kVariantsNv[], kVariantsNvEpi[];   // plain, and with the epilogue modes
+extern const int kNumVariantsNv, kNumVariantsNvEpi;
 
 }  // namespace w4a16

@@ -82,6 +82,8 @@ extern "C" {
 #define W4A16_ASRC_LDS    0  /* staged once per workgroup in LDS */
 #define W4A16_ASRC_GLOBAL 1  /* read per group from global memory (L1/L2) */
 #define W4A16_ASRC_RING   2  /* per group through a per-wavefront LDS ring (DMA) */
+#define W4A16_ASRC_SPLITN 3  /* staged once per workgroup in LDS; the wavefronts split
+                                the columns instead of K (kwaves x tiles tiles share it) */
 
 /*
  * A launch plan.  w4a16_gemm chooses one from (M, N, K); w4a16_gemm_plan
@@ -89,11 +91,12 @@ extern "C" {
  *   path    W4A16_PATH_GEMV or W4A16_PATH_MFMA
  *   tiles   16-column tiles per wavefront (1, 2 or 4)
  *   kwaves  wavefronts of one workgroup that split the workgroup's K range
+ *           (with W4A16_ASRC_SPLITN: that split its columns, tiles each)
  *   splits  workgroups that split K for the same columns: 1 (none), 2, 4, 8, ...
  *           (a power of two); more than one needs a workspace (see
  *           w4a16_workspace_bytes)
- *   asrc    W4A16_ASRC_LDS, W4A16_ASRC_GLOBAL or W4A16_ASRC_RING (the last
- *           two on the MFMA path only)
+ *   asrc    W4A16_ASRC_LDS, W4A16_ASRC_GLOBAL, W4A16_ASRC_RING or
+ *           W4A16_ASRC_SPLITN (the last three on the MFMA path only)
  *   depth   K groups each wavefront keeps in flight (0 = the default for
  *           `tiles`: 8, 4, 2 for 1, 2, 4 tiles)
  */

@@ -122,20 +122,29 @@ def test_row_count_dispatch():
         p = w4.get_plan(M, 34816, 5120)
         assert p.path == (w4.PATH_GEMV if M == 1 else w4.PATH_MFMA), (M, p)
         assert p.splits == 1
-        # wide N: A through the LDS ring from two rows, two tiles up to 8
-        # rows, four above
-        if M >= 2:
-            assert p.asrc == w4.ASRC_RING, (M, p)
-            assert p.tiles == (2 if M <= 8 else 4), (M, p)
+        # wide N: A through the LDS ring from two to 8 rows, two tiles;
+        # above, four wavefronts split the columns (one tile each) around a
+        # shared ring
+        if 2 <= M <= 8:
+            assert p.asrc == w4.ASRC_RING and p.tiles == 2, (M, p)
+        elif M >= 9:
+            assert p.asrc == w4.ASRC_SPLITN and (p.tiles, p.kwaves, p.depth) == (1, 4, 4), (M, p)
     # QKV width: all of A in LDS up to 7 rows, the ring above
     assert w4.get_plan(4, 8192, 5120).asrc == w4.ASRC_LDS
     assert w4.get_plan(7, 8192, 5120).asrc == w4.ASRC_LDS
     assert w4.get_plan(8, 8192, 5120).asrc == w4.ASRC_RING
     assert w4.get_plan(16, 8192, 5120).asrc == w4.ASRC_RING
-    # very wide N: LDS A at 3-4 rows, the ring elsewhere, eight tiles above 8 rows
+    # very wide N: LDS A at 3-4 rows, the ring at 2, split-N from 5 rows
+    # (two tiles per wavefront up to 8 rows, four above)
     assert w4.get_plan(4, 248320, 5120).asrc == w4.ASRC_LDS
     assert w4.get_plan(2, 248320, 5120).asrc == w4.ASRC_RING
-    assert w4.get_plan(8, 248320, 5120).tiles == 4
+    assert w4.get_plan(8, 248320, 5120).asrc == w4.ASRC_SPLITN
+    assert w4.get_plan(8, 248320, 5120).tiles == 2
+    assert w4.get_plan(16, 248320, 5120).tiles == 4
+    # the same for NVFP4 weights from 5 rows; wide N from 9 rows
+    assert w4.nvfp4_get_plan(5, 248320, 5120).asrc == w4.ASRC_SPLITN
+    assert w4.nvfp4_get_plan(9, 34816, 5120).asrc == w4.ASRC_SPLITN
+    assert w4.nvfp4_get_plan(8, 34816, 5120).asrc == w4.ASRC_RING
     # long K with few column strips: split K (two rows and more)
     assert w4.get_plan(1, 5120, 17408).splits == 1
     assert w4.get_plan(4, 5120, 17408).splits == 1           # whole K of A in LDS
@@ -145,13 +154,12 @@ def test_row_count_dispatch():
     assert w4.get_plan(16, 5120, 17408).asrc == w4.ASRC_RING
     assert w4.get_plan(1, 5120, 17408).kwaves == 8
     assert w4.get_plan(1, 248320, 5120).tiles == 2
-    assert w4.get_plan(16, 248320, 5120).tiles == 8
     # tiny K: no more K waves than K groups
     assert w4.get_plan(1, 1024, 512).kwaves <= 4
     assert w4.get_plan(1, 1024, 256).kwaves == 1
     for M in range(1, 17):
         for K in (128, 256, 512, 5120, 17408, 1 << 20, 1 << 24):
-            for N in (16, 1024, 8192, 34816):
+            for N in (16, 1024, 8192, 34816) + ((131072,) if K <= 5120 else ()):
                 assert w4.plan_ok(M, N, K, w4.get_plan(M, N, K)), (M, N, K)
                 assert w4.nvfp4_plan_ok(M, N, K, w4.nvfp4_get_plan(M, N, K)), (M, N, K)
     p = w4.Plan()

@@ -57,7 +57,7 @@ ALL_PLANS = []
 for path in (w4.PATH_GEMV, w4.PATH_MFMA):
     for t in (1, 2, 4, 8):
         for kw in (1, 2, 4, 8):
-            for asrc in ((w4.ASRC_LDS,) if path == w4.PATH_GEMV else (w4.ASRC_LDS, w4.ASRC_GLOBAL, w4.ASRC_RING)):
+            for asrc in ((w4.ASRC_LDS,) if path == w4.PATH_GEMV else (w4.ASRC_LDS, w4.ASRC_GLOBAL, w4.ASRC_RING, w4.ASRC_SPLITN)):
                 for depth in (0, 2, 3, 4, 5, 8, 10):
                     ALL_PLANS.append(w4.make_plan(path, t, kw, 1, asrc, depth))
 
@@ -143,7 +143,7 @@ def test_nvfp4_split_k_parity_and_reuse(splits):
     blob, sc, a = to_dev(packed, scales, A)
     Cref, Dref = oracle.nvfp4_gemm(A, packed, scales, ALPHA, 16, N, K)
     for M in (1, 3, 4, 8, 16):
-        for path, asrc in ((w4.PATH_GEMV, 0), (w4.PATH_MFMA, 0), (w4.PATH_MFMA, 1), (w4.PATH_MFMA, 2)):
+        for path, asrc in ((w4.PATH_GEMV, 0), (w4.PATH_MFMA, 0), (w4.PATH_MFMA, 1), (w4.PATH_MFMA, 2), (w4.PATH_MFMA, 3)):
             if path == w4.PATH_GEMV and M > 4:
                 continue
             for t, kw in ((1, 8), (2, 4)):

@@ -61,7 +61,7 @@ for path in (w4.PATH_GEMV, w4.PATH_MFMA):
     for t in (1, 2, 4):
         for kw in (1, 2, 4, 5, 8, 10, 16):
             for asrc in ((w4.ASRC_LDS,) if path == w4.PATH_GEMV
-                         else (w4.ASRC_LDS, w4.ASRC_GLOBAL, w4.ASRC_RING)):
+                         else (w4.ASRC_LDS, w4.ASRC_GLOBAL, w4.ASRC_RING, w4.ASRC_SPLITN)):
                 for depth in (0, 2, 3, 4, 5, 8, 10, 17):
                     ALL_PLANS.append(w4.make_plan(path, t, kw, 1, asrc, depth))
 
@@ -154,7 +154,7 @@ def test_gemm_split_k_parity_and_reuse(splits):
     blob = w4.repack_weights(q, K, N)
     Cref, Dref = oracle.gemm(A, qw, sc, 16, N, K)
     for M in (1, 3, 4, 8, 16):
-        for path, asrc in ((w4.PATH_GEMV, 0), (w4.PATH_MFMA, 0), (w4.PATH_MFMA, 1), (w4.PATH_MFMA, 2)):
+        for path, asrc in ((w4.PATH_GEMV, 0), (w4.PATH_MFMA, 0), (w4.PATH_MFMA, 1), (w4.PATH_MFMA, 2), (w4.PATH_MFMA, 3)):
             if path == w4.PATH_GEMV and M > 4:
                 continue
             for t, kw in ((1, 4), (2, 8)):
@@ -185,7 +185,7 @@ def test_split_k_workspace_shared_across_shapes():
         cases.append((K, N, a, blob, s, Cref, Dref))
     plans = [w4.make_plan(w4.PATH_MFMA, 2, 4, 4, w4.ASRC_LDS), w4.make_plan(w4.PATH_MFMA, 4, 4, 2, w4.ASRC_GLOBAL),
              w4.make_plan(w4.PATH_GEMV, 1, 4, 8), w4.make_plan(w4.PATH_MFMA, 1, 8, 2, w4.ASRC_GLOBAL),
-             w4.make_plan(w4.PATH_MFMA, 4, 4, 2, w4.ASRC_RING)]
+             w4.make_plan(w4.PATH_MFMA, 4, 4, 2, w4.ASRC_RING), w4.make_plan(w4.PATH_MFMA, 2, 4, 4, w4.ASRC_SPLITN)]
     need = max(w4.workspace_bytes(16, N, K, p) for (K, N, *_) in cases for p in plans)
     ws = torch.zeros(need, dtype=torch.uint8, device=DEV)
     for rnd in range(2):
@@ -361,7 +361,7 @@ def test_silu_mul_split_k(splits):
     blob = w4.repack_weights(q, K, N)
     Href, E = oracle.gemm_silu_mul(A, qw, sc, 16, N, K)
     for M in (1, 4, 9, 16):
-        for path, asrc in ((w4.PATH_GEMV, 0), (w4.PATH_MFMA, 0), (w4.PATH_MFMA, 1), (w4.PATH_MFMA, 2)):
+        for path, asrc in ((w4.PATH_GEMV, 0), (w4.PATH_MFMA, 0), (w4.PATH_MFMA, 1), (w4.PATH_MFMA, 2), (w4.PATH_MFMA, 3)):
             if path == w4.PATH_GEMV and M > 4:
                 continue
             p = w4.make_plan(path, 2, 4, splits, asrc)

@@ -18,7 +18,7 @@ LIB_PATH = os.path.join(_HERE, "libw4a16.so")
 
 OK = 0
 PATH_AUTO, PATH_GEMV, PATH_MFMA = 0, 1, 2
-ASRC_LDS, ASRC_GLOBAL, ASRC_RING = 0, 1, 2
+ASRC_LDS, ASRC_GLOBAL, ASRC_RING, ASRC_SPLITN = 0, 1, 2, 3
 GROUP = 128
 NVFP4_GROUP = 16
 

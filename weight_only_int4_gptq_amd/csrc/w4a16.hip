@@ -38,8 +38,11 @@ int default_depth(int tiles) { return tiles == 1 ? 8 : (tiles == 2 ? 4 : 2); }
 // epi: a kernel that carries the epilogue modes (else a plain matmul);
 // fmt: the weight format
 const Variant *find_variant(const w4a16_plan_t &p, int M, bool epi = false, int fmt = FMT_GPTQ) {
-    // ring A kernels take M at run time for every row count
-    const int mm = (p.path == W4A16_PATH_GEMV || (M <= 4 && p.asrc != W4A16_ASRC_RING)) ? M : 0;
+    // ring and split-N kernels take M at run time for every row count
+    const int mm = (p.path == W4A16_PATH_GEMV ||
+                    (M <= 4 && p.asrc != W4A16_ASRC_RING && p.asrc != W4A16_ASRC_SPLITN))
+                       ? M
+                       : 0;
     const int asrc = (p.path == W4A16_PATH_GEMV) ? ASRC_LDS : p.asrc;
     const int depth = p.depth ? p.depth : default_depth(p.tiles);
     VariantTable tabs[2];
@@ -123,17 +126,24 @@ int plan_lds(const w4a16_plan_t &p, int M, int G) {
     return lds_layout(p.path, asrc, M, Gwg, p.tiles, p.kwaves, depth).total;
 }
 
+// 16-column tiles of one workgroup's strip
+long long strip_tiles(const w4a16_plan_t &p) {
+    const bool splitn = p.path == W4A16_PATH_MFMA && p.asrc == W4A16_ASRC_SPLITN;
+    return (long long)p.tiles * (splitn ? p.kwaves : 1);
+}
+
 int validate_plan(const w4a16_plan_t &p, int M, int N, int K, int fmt = FMT_GPTQ) {
     const int G = K / W4A16_GROUP;
     if (p.path != W4A16_PATH_GEMV && p.path != W4A16_PATH_MFMA) return W4A16_ERR_PLAN;
     if (p.path == W4A16_PATH_GEMV && M > 4) return W4A16_ERR_PLAN;
     if (p.splits < 1 || p.splits > G || (p.splits & (p.splits - 1)) != 0) return W4A16_ERR_PLAN;
-    if (p.asrc != W4A16_ASRC_LDS && p.asrc != W4A16_ASRC_GLOBAL && p.asrc != W4A16_ASRC_RING)
+    if (p.asrc != W4A16_ASRC_LDS && p.asrc != W4A16_ASRC_GLOBAL && p.asrc != W4A16_ASRC_RING &&
+        p.asrc != W4A16_ASRC_SPLITN)
         return W4A16_ERR_PLAN;
     if (p.depth < 0) return W4A16_ERR_PLAN;
     if (!find_variant(p, M, false, fmt)) return W4A16_ERR_PLAN;
     if (plan_lds(p, M, G) + 256 > kLdsMax) return W4A16_ERR_PLAN;
-    const long long nstrips = (N / 16 + p.tiles - 1) / p.tiles;
+    const long long nstrips = (N / 16 + strip_tiles(p) - 1) / strip_tiles(p);
     if (nstrips * p.splits >= (1ll << 31)) return W4A16_ERR_PLAN;
     if (p.splits > 1 && nstrips > W4A16_SPLIT_COUNTER_BYTES / 4) return W4A16_ERR_PLAN;
     return W4A16_OK;
@@ -159,10 +169,11 @@ int validate_plan(const w4a16_plan_t &p, int M, int N, int K, int fmt = FMT_GPTQ
 //    per-wavefront LDS ring (contiguous DMA loads), two tiles, depth 2;
 //    otherwise A in LDS, two tiles, depth 4;
 //  * M >= 5, matrix cores:
-//      - very wide N: A through the ring, four tiles and two wavefronts up
-//        to 8 rows, eight tiles and four wavefronts above;
-//      - wide and mid N: A through the ring, depth 2, two tiles up to 8
-//        rows, four above;
+//      - very wide N: four wavefronts split the columns (two tiles each up
+//        to 8 rows, four above) around one shared ring of A, depth 2;
+//      - wide N from 9 rows: the same with one tile each, depth 4;
+//      - wide (up to 8 rows) and mid N: A through the ring, depth 2, two
+//        tiles up to 8 rows, four above;
 //      - long K: A through the ring from M = 8; below, a quarter of K of A
 //        staged in LDS (split four ways);
 //      - narrow N up to 256 tiles: one tile, all of A staged in LDS, eight
@@ -228,11 +239,14 @@ void auto_plan(int M, int N, int K, w4a16_plan_t *out) {
         }
     } else {
         p.path = W4A16_PATH_MFMA;
-        if (vwide) {                           // A through the ring: 4 tiles x 2 waves, 8 x 4 above 8 rows
-            p.asrc = W4A16_ASRC_RING;
-            p.tiles = M <= 8 ? 4 : 8;
-            p.kwaves = M <= 8 ? 2 : 4;
+        if (vwide) {                           // four wavefronts split 8 (16 above 8 rows) tiles, shared A
+            p.asrc = W4A16_ASRC_SPLITN;
+            p.tiles = M <= 8 ? 2 : 4;
             p.depth = 2;
+        } else if (wide && M >= 9) {           // four wavefronts split 4 tiles, shared A, depth 4
+            p.asrc = W4A16_ASRC_SPLITN;
+            p.tiles = 1;
+            p.depth = 4;
         } else if (wide || mid) {              // A through the ring: two tiles up to 8 rows, four above
             p.asrc = W4A16_ASRC_RING;
             p.tiles = M <= 8 ? 2 : 4;
@@ -261,7 +275,8 @@ void auto_plan(int M, int N, int K, w4a16_plan_t *out) {
         }
     }
     // short K: no more wavefronts along K than groups per workgroup
-    if (p.kwaves * p.splits > G) {
+    // (split-N wavefronts split the columns)
+    if (p.asrc != W4A16_ASRC_SPLITN && p.kwaves * p.splits > G) {
         p.splits = 1;
         if (p.kwaves > G) {
             if (G >= 4) {
@@ -300,11 +315,13 @@ void auto_plan(int M, int N, int K, w4a16_plan_t *out) {
 //  * M = 2..4: very wide N: four tiles, depth 2; long K: two tiles, eight
 //    wavefronts; narrow N: one tile, eight wavefronts; else two tiles, four
 //    wavefronts; A in LDS throughout;
-//  * M >= 5: A through the LDS ring, two tiles, four wavefronts, depth 2:
-//    very wide N above 8 rows (up to 8: four tiles, A from global memory);
-//    wide N; long K from 8 rows, split two ways (below: four tiles split
-//    four ways, A in LDS); otherwise from 8 rows (below: two tiles, eight
-//    wavefronts, A in LDS).
+//  * M >= 5: very wide N: four wavefronts split the columns (two tiles
+//    each) around one shared ring of A, depth 2; wide N from 9 rows: the
+//    same with one tile each, depth 4.  Otherwise A through the LDS ring,
+//    two tiles, four wavefronts, depth 2: wide N up to 8 rows; long K
+//    from 8 rows, split two ways (below: four tiles split four ways, A in
+//    LDS); otherwise from 8 rows (below: two tiles, eight wavefronts, A in
+//    LDS).
 // The first of these that the library has a kernel for and that fits is taken, else
 // the first compiled fallback.
 void auto_plan_nv(int M, int N, int K, w4a16_plan_t *out) {
@@ -330,12 +347,14 @@ void auto_plan_nv(int M, int N, int K, w4a16_plan_t *out) {
         else if (!wide) set(W4A16_PATH_MFMA, 1, 8, 1, W4A16_ASRC_LDS, 4);
         else set(W4A16_PATH_MFMA, 2, 4, 1, W4A16_ASRC_LDS, 4);
     } else {
-        // A through the LDS ring (two tiles, depth 2) wherever it measured best
+        // A through the LDS ring (two tiles, depth 2) wherever it measured
+        // best; four wavefronts splitting the columns around one shared ring
+        // for the widest N (and wide N from 9 rows)
         if (vwide) {
-            if (M <= 8) set(W4A16_PATH_MFMA, 4, 4, 1, W4A16_ASRC_GLOBAL, 2);
-            else set(W4A16_PATH_MFMA, 2, 4, 1, W4A16_ASRC_RING, 2);
+            set(W4A16_PATH_MFMA, 2, 4, 1, W4A16_ASRC_SPLITN, 2);
         } else if (wide) {
-            set(W4A16_PATH_MFMA, 2, 4, 1, W4A16_ASRC_RING, 2);
+            if (M >= 9) set(W4A16_PATH_MFMA, 1, 4, 1, W4A16_ASRC_SPLITN, 4);
+            else set(W4A16_PATH_MFMA, 2, 4, 1, W4A16_ASRC_RING, 2);
         } else if (deep) {
             if (M <= 7) set(W4A16_PATH_MFMA, 4, 4, 4, W4A16_ASRC_LDS, 2);
             else set(W4A16_PATH_MFMA, 2, 4, 2, W4A16_ASRC_RING, 2);
@@ -348,7 +367,7 @@ void auto_plan_nv(int M, int N, int K, w4a16_plan_t *out) {
     // splits no larger than the groups allow (a power of two), and no more
     // wavefronts along K than each split's groups
     while (p.splits > 1 && p.splits * p.kwaves > G) p.splits >>= 1;
-    while (p.kwaves > 1 && p.kwaves > G) p.kwaves >>= 1;
+    while (p.asrc != W4A16_ASRC_SPLITN && p.kwaves > 1 && p.kwaves > G) p.kwaves >>= 1;
     // fallbacks: A from global memory; the LDS ring (its kernels take any
     // row count, so they also cover K ranges of A too long to stage); the
     // common shapes; the short-K shapes
@@ -389,6 +408,12 @@ static_assert(kArgmaxBinOffset + kArgmaxBins * 16 * 8 <= W4A16_ARGMAX_WORKSPACE_
 void fuse_plan(int M, w4a16_plan_t *p, int fmt = FMT_GPTQ) {
     if (p->tiles % 2 == 0) return;
     w4a16_plan_t q = *p;
+    if (q.asrc == W4A16_ASRC_SPLITN) {         // one-tile split-N: the ring plan of the same width
+        q.asrc = W4A16_ASRC_RING;
+        q.tiles = (fmt == FMT_GPTQ && M >= 9) ? 4 : 2;
+        q.kwaves = 4;
+        q.depth = 2;
+    }
     q.tiles = 2;                               // same wavefronts and ring depth if compiled
     if (!find_variant(q, M, true, fmt)) q.depth = 0;
     if (!find_variant(q, M, true, fmt)) q.kwaves = 4;
@@ -400,7 +425,7 @@ void fuse_plan(int M, w4a16_plan_t *p, int fmt = FMT_GPTQ) {
 // fuse: 0 plain C[M][N]; 1 the gate/up epilogue, C is H[M][N/2]; 2 the row
 // argmax (C unused, results in idx / val); 3 C as fp32 [M][N]
 // fmt: FMT_GPTQ (group 128, bf16 scales) or FMT_NVFP4 (group 16, E4M3
-// scales, alpha the per-tensor factor; plain C only)
+// scales, alpha the per-tensor factor)
 int run_gemm(const void *A, const void *wq, const void *scales, void *C, int M, int N, int K,
              int group, void *workspace, size_t workspace_bytes, const w4a16_plan_t *user,
              void *stream, int fuse = 0, int *idx = nullptr, float *val = nullptr,
@@ -473,7 +498,7 @@ int run_gemm(const void *A, const void *wq, const void *scales, void *C, int M, 
     a.Slog2 = 0;
     while ((1 << a.Slog2) < a.S) ++a.Slog2;
     a.NT = N / 16;
-    a.nstrips = (a.NT + p.tiles - 1) / p.tiles;
+    a.nstrips = (int)((a.NT + strip_tiles(p) - 1) / strip_tiles(p));
     a.nunits = a.nstrips * a.S;
     a.fuse = fuse;
     a.amax_idx = idx;

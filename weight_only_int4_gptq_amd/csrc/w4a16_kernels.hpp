@@ -55,7 +55,11 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 
 enum { PATH_GEMV = 1, PATH_MFMA = 2 };
-enum { ASRC_LDS = 0, ASRC_GLOBAL = 1, ASRC_RING = 2 };
+// ASRC_SPLITN: the four wavefronts of a workgroup split the strip's columns
+// (T tiles each) instead of its K range, and A goes per group through one
+// LDS ring shared by them: each group of A is fetched once for 4 * T tiles
+// (matrix-core path)
+enum { ASRC_LDS = 0, ASRC_GLOBAL = 1, ASRC_RING = 2, ASRC_SPLITN = 3 };
 enum { FMT_GPTQ = 0, FMT_NVFP4 = 1 };
 constexpr int kNvBlock = 16;                   // NVFP4 rows per block scale
 
@@ -109,11 +113,12 @@ __host__ __device__ inline LdsLayout lds_layout(int path, int asrc, int M, int G
     L.a = off;
     if (stage) off += M * L.row;
     else if (path == PATH_MFMA && asrc == ASRC_RING) off += KW * D * kRingSlotBytes;
+    else if (path == PATH_MFMA && asrc == ASRC_SPLITN) off += (D + 1) * kRingSlotBytes;
     L.bias = off;
     if (path == PATH_GEMV) off += M * Gwg * 4 * 4;
     else if (stage) off += Gwg * 16 * 4;
     L.red = off;
-    if (KW > 1) off += KW * T * M * 16 * 4;
+    if (KW > 1 && asrc != ASRC_SPLITN) off += KW * T * M * 16 * 4;
     L.total = off;
     return L;
 }
@@ -288,6 +293,15 @@ constexpr int kWaitLgkm0 = 15 | (7 << 4) | (0 << 8) | (3 << 14);
 __device__ __forceinline__ void lds_barrier() {
     __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
     __builtin_amdgcn_s_barrier();
+}
+
+// Workgroup barrier that also orders LDS accesses for the compiler: no LDS
+// read after it is moved above it, none before it below it.  At workgroup
+// scope the fences wait for no global memory operation.
+__device__ __forceinline__ void wg_barrier() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
 }
 
 // 16 bytes per lane from global memory straight into LDS: lane l's bytes land
@@ -550,7 +564,12 @@ __global__ void __launch_bounds__(64 * KW) gemm_kernel(GemmArgs p) {
     constexpr bool kNv = FMT == FMT_NVFP4;
     constexpr bool kGlobalA = (PATH == PATH_MFMA && ASRC == ASRC_GLOBAL);
     constexpr bool kRingA = (PATH == PATH_MFMA && ASRC == ASRC_RING);
-    constexpr bool kStage = !kGlobalA && !kRingA;
+    constexpr bool kSplitN = (PATH == PATH_MFMA && ASRC == ASRC_SPLITN);
+    constexpr bool kStage = !kGlobalA && !kRingA && !kSplitN;
+    static_assert(!kSplitN || KW == 4, "split-N: four wavefronts, one DMA load of A each per group");
+    // wavefronts whose partial sums meet in LDS (split-N wavefronts each
+    // hold whole sums of their own tiles)
+    constexpr int KWR = kSplitN ? 1 : KW;
     constexpr int kLoadsPerGroup = 2 * T + (kGlobalA ? (kNv ? 8 : 4) : 0);   // loads the compiler sees
     // Matrix-core bias: formed in the loop from the A fragments already
     // loaded (four more MFMAs per group, shared by the T tiles), except for
@@ -571,7 +590,8 @@ __global__ void __launch_bounds__(64 * KW) gemm_kernel(GemmArgs p) {
     const int strip = u >> p.Slog2, z = u & (p.S - 1);
     const int gw0 = (p.G * z) >> p.Slog2, gw1 = (p.G * (z + 1)) >> p.Slog2;
     const int Gwg = gw1 - gw0;
-    const int gk0 = gw0 + (Gwg * wave) / KW, gk1 = gw0 + (Gwg * (wave + 1)) / KW;
+    const int gk0 = kSplitN ? gw0 : gw0 + (Gwg * wave) / KW;
+    const int gk1 = kSplitN ? gw1 : gw0 + (Gwg * (wave + 1)) / KW;
     const int ng = gk1 - gk0;
     const LdsLayout L = lds_layout(PATH, ASRC, M, Gwg, T, KW, D);
     const DequantConsts kc = dequant_consts();
@@ -579,14 +599,16 @@ __global__ void __launch_bounds__(64 * KW) gemm_kernel(GemmArgs p) {
     // Tiles of this strip.  Plain: T consecutive tiles.  Gate/up epilogue
     // (T even): the first T/2 slots hold gate tiles strip*T/2 + t, the last
     // T/2 the up tiles of the same columns, NT/2 tiles further on.
+    // Split-N: wavefront w of strip s takes the tiles of sub-strip s*KW + w.
     constexpr int kHalfT = T / 2;
     const int fuse = EPI ? p.fuse : 0;
+    const int vs = kSplitN ? strip * KW + wave : strip;
     auto tile_of = [&](int t) {
-        if (fuse == 1) return t < kHalfT ? strip * kHalfT + t : (p.NT >> 1) + strip * kHalfT + (t - kHalfT);
-        return strip * T + t;
+        if (fuse == 1) return t < kHalfT ? vs * kHalfT + t : (p.NT >> 1) + vs * kHalfT + (t - kHalfT);
+        return vs * T + t;
     };
     auto tile_ok = [&](int t) {
-        return fuse == 1 ? strip * kHalfT + (t < kHalfT ? t : t - kHalfT) < (p.NT >> 1) : strip * T + t < p.NT;
+        return fuse == 1 ? vs * kHalfT + (t < kHalfT ? t : t - kHalfT) < (p.NT >> 1) : vs * T + t < p.NT;
     };
 
     // Buffer resources (scalar): each tile's weights and scales, and A.
@@ -651,6 +673,16 @@ __global__ void __launch_bounds__(64 * KW) gemm_kernel(GemmArgs p) {
         const int row = min(4 * i + h, M - 1);
         ring_off[i] = (uint32_t)row * (uint32_t)p.K * 2u + (uint32_t)((c ^ (row & 15)) << 4);
     }
+    // Split-N: one ring of D + 1 slots for the workgroup; group g (the i-th
+    // of the range) in slot i % (D + 1).  Wavefront w loads rows 4w .. 4w+3
+    // of every group (rows >= M repeat row M-1), so each wavefront issues
+    // exactly one DMA load per group and the wait counts stay static.  The
+    // refill issued after computing group i goes to the slot of group i - 1,
+    // which every wavefront has finished reading once it passed group i's
+    // barrier; hence the one spare slot.
+    auto shared_slot = [&](int g) { return L.a + ((g - gk0) % (D + 1)) * kRingSlotBytes; };
+    const int sh_row = min(4 * wave + h, M - 1);
+    const uint32_t sh_off = (uint32_t)sh_row * (uint32_t)p.K * 2u + (uint32_t)((c ^ (sh_row & 15)) << 4);
 
     auto load_group = [&](auto jc, int g) {
         constexpr int j = decltype(jc)::value;
@@ -660,6 +692,10 @@ __global__ void __launch_bounds__(64 * KW) gemm_kernel(GemmArgs p) {
 #pragma unroll
             for (int i = 0; i < 4; ++i)
                 if (i < nd) lds_dma16_sbase(ring_off[i], gbase, dst0 + (i << 10));
+        } else if constexpr (kSplitN) {
+            const uint32_t dst = __builtin_amdgcn_readfirstlane(lds_addr(smem + shared_slot(g))) + (wave << 10);
+            const uint8_t *gbase = reinterpret_cast<const uint8_t *>(p.A) + (size_t)g * kGroup * 2;
+            lds_dma16_sbase(sh_off, gbase, dst);
         }
 #pragma unroll
         for (int t = 0; t < T; ++t) {
@@ -789,13 +825,15 @@ __global__ void __launch_bounds__(64 * KW) gemm_kernel(GemmArgs p) {
                     const uint8_t *arow = smem + L.a + arow_m * L.row + (gl * kGroup + 4 * h) * 2;
 #pragma unroll
                     for (int b = 0; b < 8; ++b) a[b] = *reinterpret_cast<const u32x2 *>(arow + b * kNvBlock * 2);
-                } else if constexpr (kRingA) {
+                } else if constexpr (kRingA || kSplitN) {
                     // as for GPTQ: wait for this slot's DMA loads explicitly;
                     // rows 16b + 4h .. +3 are bytes 32b + 8h of row c, in
                     // logical piece 2b + h/2, stored at piece (2b + h/2) ^ c
                     constexpr int later = decltype(final_)::value ? D - 1 - j : D - 1;
                     __builtin_amdgcn_s_waitcnt(waitcnt_vm(2 * T + later * (2 * T + 1)));
-                    const uint8_t *slot = smem + ring_slot(j) + c * (kGroup * 2) + ((h & 1) << 3);
+                    if constexpr (kSplitN) wg_barrier();   // every wavefront's rows have landed
+                    const uint8_t *slot = smem + (kSplitN ? shared_slot(g) : ring_slot(j)) + c * (kGroup * 2) +
+                                          ((h & 1) << 3);
 #pragma unroll
                     for (int b = 0; b < 8; ++b)
                         a[b] = *reinterpret_cast<const u32x2 *>(slot + (((2 * b + (h >> 1)) ^ c) << 4));
@@ -863,13 +901,14 @@ __global__ void __launch_bounds__(64 * KW) gemm_kernel(GemmArgs p) {
                     Q = reinterpret_cast<const f32x4 *>(smem + L.bias)[gl * 4 + h];
                 }
             } else {
-                if constexpr (kRingA) {
+                if constexpr (kRingA || kSplitN) {
                     // the compiler does not see the DMA loads: wait for this
                     // slot's explicitly (every load issued after them counted
                     // as if each later group had one DMA load: never fewer)
                     constexpr int later = decltype(final_)::value ? D - 1 - j : D - 1;
                     __builtin_amdgcn_s_waitcnt(waitcnt_vm(2 * T + later * (2 * T + 1)));
-                    const uint8_t *slot = smem + ring_slot(j) + c * (kGroup * 2);
+                    if constexpr (kSplitN) wg_barrier();   // every wavefront's rows have landed
+                    const uint8_t *slot = smem + (kSplitN ? shared_slot(g) : ring_slot(j)) + c * (kGroup * 2);
 #pragma unroll
                     for (int r = 0; r < 4; ++r)
                         a[r] = *reinterpret_cast<const u32x4 *>(slot + (((h * 4 + r) ^ c) << 4));
@@ -1014,7 +1053,7 @@ __global__ void __launch_bounds__(64 * KW) gemm_kernel(GemmArgs p) {
                            __HIP_MEMORY_SCOPE_AGENT);
     };
 
-    if constexpr (KW == 1) {
+    if constexpr (KWR == 1) {
         // lane (c, h) holds rows 4h + v (MFMA) or, in lanes h == 0, all rows (GEMV)
         auto row_val = [&](int t, int i) { return acc[t][i]; };
         constexpr int kRows = (PATH == PATH_MFMA) ? kRowsV : MM;
@@ -1144,17 +1183,20 @@ __global__ void __launch_bounds__(64 * KW) gemm_kernel(GemmArgs p) {
                                            __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                 return s;
             };
+            // split-N: each wavefront adds its own tiles
+            const int mc0 = kSplitN ? lane : (int)threadIdx.x;
+            constexpr int kMcStep = kSplitN ? 64 : 64 * KW;
             if (fuse != 1) {
 #pragma unroll
                 for (int t = 0; t < T; ++t)
-                    for (int mc = threadIdx.x; mc < M * 16; mc += 64 * KW) {
+                    for (int mc = mc0; mc < M * 16; mc += kMcStep) {
                         if (!tile_ok(t)) continue;
                         emit_c(t, mc >> 4, mc & 15, summed(t, mc >> 4, mc & 15));
                     }
             } else {
 #pragma unroll
                 for (int t = 0; t < kHalfT; ++t)
-                    for (int mc = threadIdx.x; mc < M * 16; mc += 64 * KW) {
+                    for (int mc = mc0; mc < M * 16; mc += kMcStep) {
                         if (!tile_ok(t)) continue;
                         const int m = mc >> 4, cc = mc & 15;
                         emit_h(t, m, cc, summed(t, m, cc), summed(t + kHalfT, m, cc));

@@ -57,8 +57,13 @@ struct Variant {
     W4A16_SHAPES(X, PATH_MFMA, 2, ASRC_LDS) W4A16_SHAPES(X, PATH_MFMA, 2, ASRC_GLOBAL)              \
     W4A16_SHAPES(X, PATH_MFMA, 3, ASRC_LDS) W4A16_SHAPES(X, PATH_MFMA, 3, ASRC_GLOBAL)              \
     W4A16_SHAPES(X, PATH_MFMA, 4, ASRC_LDS) W4A16_SHAPES(X, PATH_MFMA, 4, ASRC_GLOBAL)
+// four wavefronts splitting the columns around one shared ring of A
+#define W4A16_SPLITN(X, P, MM, AS) \
+    X(P, MM, 1, 4, 2, AS) X(P, MM, 1, 4, 4, AS) X(P, MM, 2, 4, 2, AS) X(P, MM, 2, 4, 3, AS) \
+    X(P, MM, 2, 4, 4, AS) X(P, MM, 4, 4, 2, AS)
+
 #define W4A16_VARIANT_LIST_RT(X)                                                                    \
-    W4A16_RINGS(X, PATH_MFMA, 0, ASRC_RING)                                                         \
+    W4A16_RINGS(X, PATH_MFMA, 0, ASRC_RING) W4A16_SPLITN(X, PATH_MFMA, 0, ASRC_SPLITN)             \
     W4A16_WIDE(X, PATH_MFMA, 0, ASRC_LDS) W4A16_WIDE(X, PATH_MFMA, 0, ASRC_GLOBAL)                  \
     W4A16_SHAPES(X, PATH_MFMA, 0, ASRC_LDS) W4A16_SHAPES(X, PATH_MFMA, 0, ASRC_GLOBAL)
 
@@ -72,9 +77,9 @@ struct VariantTable {
 extern const Variant kVariantsPlainCt[], kVariantsPlainRt[], kVariantsEpiCt[], kVariantsEpiRt[];
 extern const int kNumPlainCt, kNumPlainRt, kNumEpiCt, kNumEpiRt;
 
-// NVFP4 weight-only kernels (plain epilogue; A staged in LDS, read from
-// global memory or through the LDS ring): the GEMV path for one to four
-// rows, the matrix-core path for every row count.
+// NVFP4 weight-only kernels (one table plain, one with the epilogue modes;
+// A staged in LDS, read from global memory or through the LDS ring): the
+// GEMV path for one to four rows, the matrix-core path for every row count.
 #define W4A16_NV_GEMV(X, MM) \
     X(PATH_GEMV, MM, 1, 1, 8, ASRC_LDS) X(PATH_GEMV, MM, 1, 8, 4, ASRC_LDS) X(PATH_GEMV, MM, 2, 4, 4, ASRC_LDS) \
     X(PATH_GEMV, MM, 2, 8, 4, ASRC_LDS) X(PATH_GEMV, MM, 1, 4, 8, ASRC_LDS) X(PATH_GEMV, MM, 4, 4, 2, ASRC_LDS)
@@ -90,6 +95,8 @@ extern const int kNumPlainCt, kNumPlainRt, kNumEpiCt, kNumEpiRt;
     X(PATH_MFMA, 0, 8, 1, 2, ASRC_GLOBAL) X(PATH_MFMA, 0, 8, 1, 3, ASRC_GLOBAL)                    \
     X(PATH_MFMA, 0, 2, 4, 2, ASRC_RING) X(PATH_MFMA, 0, 2, 4, 4, ASRC_RING)                        \
     X(PATH_MFMA, 0, 4, 4, 2, ASRC_RING) X(PATH_MFMA, 0, 4, 2, 2, ASRC_RING)                        \
+    X(PATH_MFMA, 0, 2, 4, 2, ASRC_SPLITN) X(PATH_MFMA, 0, 2, 4, 4, ASRC_SPLITN)                    \
+    X(PATH_MFMA, 0, 1, 4, 4, ASRC_SPLITN) X(PATH_MFMA, 0, 4, 4, 2, ASRC_SPLITN)                    \
     W4A16_NV_MFMA(X, 1, ASRC_LDS) W4A16_NV_MFMA(X, 2, ASRC_LDS) W4A16_NV_MFMA(X, 3, ASRC_LDS)     \
     W4A16_NV_MFMA(X, 4, ASRC_LDS) W4A16_NV_MFMA(X, 2, ASRC_GLOBAL) W4A16_NV_MFMA(X, 4, ASRC_GLOBAL)
 

@@ -309,9 +309,9 @@ void auto_plan(int M, int N, int K, w4a16_plan_t *out) {
 // MI355X (cold weights) over the decoder shapes, M = 1..16.  The matrix-core
 // path pays one scale multiply per 16-row block and output, so it wins later
 // than for GPTQ on narrow N and favours split K for long K:
-//  * M = 1: long K: matrix cores, two tiles, eight wavefronts, A in LDS;
-//    below the gate/up width: GEMV, two tiles, eight wavefronts, depth 2;
-//    wide: GEMV, two tiles, four wavefronts, depth 5;
+//  * M = 1, GEMV: wide: two tiles, four wavefronts, depth 5; long K: two
+//    tiles, eight wavefronts, depth 3; otherwise one tile, eight
+//    wavefronts, depth 2 (QKV and every tensor-parallel shard);
 //  * M = 2..4: very wide N: four tiles, depth 2; long K: two tiles, eight
 //    wavefronts; narrow N: one tile, eight wavefronts; else two tiles, four
 //    wavefronts; A in LDS throughout;
@@ -338,9 +338,9 @@ void auto_plan_nv(int M, int N, int K, w4a16_plan_t *out) {
         p.path = path, p.tiles = t, p.kwaves = kw, p.splits = s, p.asrc = asrc, p.depth = d;
     };
     if (M == 1) {
-        if (deep) set(W4A16_PATH_MFMA, 2, 8, 1, W4A16_ASRC_LDS, 4);
-        else if (!wide) set(W4A16_PATH_GEMV, 2, 8, 1, W4A16_ASRC_LDS, 2);
-        else set(W4A16_PATH_GEMV, 2, 4, 1, W4A16_ASRC_LDS, 5);
+        if (wide) set(W4A16_PATH_GEMV, 2, 4, 1, W4A16_ASRC_LDS, 5);
+        else if (deep) set(W4A16_PATH_GEMV, 2, 8, 1, W4A16_ASRC_LDS, 3);
+        else set(W4A16_PATH_GEMV, 1, 8, 1, W4A16_ASRC_LDS, 2);
     } else if (M <= 4) {
         if (vwide) set(W4A16_PATH_MFMA, 4, 4, 1, W4A16_ASRC_LDS, 2);
         else if (deep) set(W4A16_PATH_MFMA, 2, 8, 1, W4A16_ASRC_LDS, 4);
@@ -366,8 +366,10 @@ void auto_plan_nv(int M, int N, int K, w4a16_plan_t *out) {
     }
     // splits no larger than the groups allow (a power of two), and no more
     // wavefronts along K than each split's groups
+    // (one row: up to two wavefronts per group, the idle ones finish at once)
+    const int kwmax = (M == 1) ? 2 * G : G;
     while (p.splits > 1 && p.splits * p.kwaves > G) p.splits >>= 1;
-    while (p.asrc != W4A16_ASRC_SPLITN && p.kwaves > 1 && p.kwaves > G) p.kwaves >>= 1;
+    while (p.asrc != W4A16_ASRC_SPLITN && p.kwaves > 1 && p.kwaves > kwmax) p.kwaves >>= 1;
     // fallbacks: A from global memory; the LDS ring (its kernels take any
     // row count, so they also cover K ranges of A too long to stage); the
     // common shapes; the short-K shapes

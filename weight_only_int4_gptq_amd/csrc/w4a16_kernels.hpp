@@ -521,7 +521,8 @@ static __global__ void __launch_bounds__(256) nv_export_kernel(const u32x4 *__re
 //
 // Work decomposition.  A workgroup owns one column strip of T 16-column tiles
 // and one of S contiguous ranges of K groups; its KW wavefronts split that
-// range further.  Every wavefront streams, for each of its groups, T pieces
+// range further.  (Split-N, ASRC_SPLITN: the strip has KW * T tiles, and
+// each wavefront takes T of them over the whole range.)  Every wavefront streams, for each of its groups, T pieces
 // of 1 KiB (one 16-byte load per lane, the whole 1 KiB contiguous) plus the
 // 16 scales of each tile, through a D-deep register ring, so D*T KiB per
 // wavefront are in flight from the start.  All addresses are a wave-uniform
@@ -548,7 +549,7 @@ static __global__ void __launch_bounds__(256) nv_export_kernel(const u32x4 *__re
 // (MFMA only) takes M at run time, up to 16.
 //
 // The partial sums of the KW wavefronts meet in LDS and are added in a fixed
-// order; with S > 1 the workgroups of one strip meet in the workspace, where
+// order (split-N wavefronts hold whole sums of their own tiles); with S > 1 the workgroups of one strip meet in the workspace, where
 // the last one to arrive adds the S partials in a fixed order.  No float
 // atomics: the result does not depend on timing.
 // EPI: the kernel carries the epilogue modes of GemmArgs::fuse; without it

@@ -90,6 +90,8 @@ extern const int kNumPlainCt, kNumPlainRt, kNumEpiCt, kNumEpiRt;
     W4A16_NV_GEMV(X, 1) W4A16_NV_GEMV(X, 2) W4A16_NV_GEMV(X, 3) W4A16_NV_GEMV(X, 4)               \
     X(PATH_GEMV, 1, 2, 4, 5, ASRC_LDS) X(PATH_GEMV, 1, 1, 4, 10, ASRC_LDS)                         \
     X(PATH_GEMV, 1, 2, 8, 2, ASRC_LDS) X(PATH_GEMV, 1, 2, 2, 8, ASRC_LDS)                           \
+    X(PATH_GEMV, 1, 1, 8, 2, ASRC_LDS) X(PATH_GEMV, 1, 1, 8, 3, ASRC_LDS)                           \
+    X(PATH_GEMV, 1, 1, 16, 2, ASRC_LDS) X(PATH_GEMV, 1, 2, 8, 3, ASRC_LDS)                          \
     W4A16_NV_MFMA(X, 0, ASRC_LDS) W4A16_NV_MFMA(X, 0, ASRC_GLOBAL)                                 \
     X(PATH_MFMA, 0, 8, 1, 4, ASRC_GLOBAL) X(PATH_MFMA, 0, 8, 2, 2, ASRC_GLOBAL)                    \
     X(PATH_MFMA, 0, 8, 1, 2, ASRC_GLOBAL) X(PATH_MFMA, 0, 8, 1, 3, ASRC_GLOBAL)                    \

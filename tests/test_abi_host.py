@@ -318,3 +318,21 @@ def test_epilogue_auto_plans_have_a_kernel(kind):
             else:
                 st = L.w4a16_gemm_f32(P, P, P, P2, M, N, K, 128, P, 1 << 40, NULL)
             assert st == -6, (kind, g)
+
+
+def test_split_n_plans():
+    # four wavefronts split the columns: compiled for kwaves = 4 only, any row
+    # count (run-time M), both formats; the strip is kwaves x tiles tiles
+    N, K = 8192, 5120
+    for M in (1, 4, 5, 16):
+        for t, d in ((1, 2), (1, 4), (2, 2), (2, 3), (2, 4), (4, 2)):
+            assert w4.plan_ok(M, N, K, w4.make_plan(w4.PATH_MFMA, t, 4, 1, w4.ASRC_SPLITN, d)), (M, t, d)
+        assert not w4.plan_ok(M, N, K, w4.make_plan(w4.PATH_MFMA, 2, 8, 1, w4.ASRC_SPLITN, 2))
+        assert not w4.plan_ok(M, N, K, w4.make_plan(w4.PATH_MFMA, 2, 2, 1, w4.ASRC_SPLITN, 4))
+        for t, d in ((2, 2), (2, 4), (1, 4), (4, 2)):
+            assert w4.nvfp4_plan_ok(M, N, K, w4.make_plan(w4.PATH_MFMA, t, 4, 1, w4.ASRC_SPLITN, d)), (M, t, d)
+    # split-K partials as for any plan: [S][M][N] fp32 after the counter region
+    p = w4.make_plan(w4.PATH_MFMA, 2, 4, 4, w4.ASRC_SPLITN, 2)
+    assert w4.workspace_bytes(16, N, K, p) == 65536 + 4 * 16 * N * 4
+    # strips of 4 x 2 tiles: 8192 / 16 / 8 = 64 strips x 4 splits
+    assert w4.plan_ok(16, N, K, p)

@@ -167,7 +167,8 @@ int validate_plan(const w4a16_plan_t &p, int M, int N, int K, int fmt = FMT_GPTQ
 //    workgroup per CU); very wide N: four tiles, depth 2, A in LDS (through
 //    the ring with two wavefronts at M = 2); wide and mid N: A through the
 //    per-wavefront LDS ring (contiguous DMA loads), two tiles, depth 2;
-//    otherwise A in LDS, two tiles, depth 4;
+//    narrow N from 16 groups: A in LDS, one tile, eight wavefronts, depth 4
+//    (the tensor-parallel shards); otherwise A in LDS, two tiles, depth 4;
 //  * M >= 5, matrix cores:
 //      - very wide N: four wavefronts split the columns (two tiles each up
 //        to 8 rows, four above) around one shared ring of A, depth 2;
@@ -233,6 +234,10 @@ void auto_plan(int M, int N, int K, w4a16_plan_t *out) {
             p.asrc = W4A16_ASRC_RING;
             p.tiles = 2;
             p.depth = 2;
+        } else if (narrow && G >= 16) {        // one tile, eight wavefronts (two per SIMD)
+            p.tiles = 1;
+            p.kwaves = 8;
+            p.depth = 4;
         } else {
             p.tiles = 2;
             p.depth = 4;

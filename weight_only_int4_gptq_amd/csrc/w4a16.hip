@@ -167,8 +167,9 @@ int validate_plan(const w4a16_plan_t &p, int M, int N, int K, int fmt = FMT_GPTQ
 //    workgroup per CU); very wide N: four tiles, depth 2, A in LDS (through
 //    the ring with two wavefronts at M = 2); wide and mid N: A through the
 //    per-wavefront LDS ring (contiguous DMA loads), two tiles, depth 2;
-//    narrow N from 16 groups: A in LDS, one tile, eight wavefronts, depth 4
-//    (the tensor-parallel shards); otherwise A in LDS, two tiles, depth 4;
+//    narrow N from 16 groups: A in LDS, eight wavefronts, depth 4, one
+//    tile (two from 64 groups) (the tensor-parallel shards); otherwise A in
+//    LDS, two tiles, depth 4;
 //  * M >= 5, matrix cores:
 //      - very wide N: four wavefronts split the columns (two tiles each up
 //        to 8 rows, four above) around one shared ring of A, depth 2;
@@ -181,7 +182,9 @@ int validate_plan(const w4a16_plan_t &p, int M, int N, int K, int fmt = FMT_GPTQ
 //        wavefronts along K;
 //      - otherwise two tiles: all of A in LDS up to 7 rows and from 64
 //        groups (depth 4, eight wavefronts from 64 groups), A through the
-//        ring otherwise (depth 2).
+//        ring otherwise (depth 2; depth 4 for narrow N from 32 groups).
+//  Staged A that does not fit in LDS goes through the ring with four
+//  wavefronts.
 void auto_plan(int M, int N, int K, w4a16_plan_t *out) {
     const int NT = N / 16, G = K / W4A16_GROUP;
     const bool wide = NT >= 2048, vwide = NT >= 8192, deep = G >= 128;
@@ -234,8 +237,8 @@ void auto_plan(int M, int N, int K, w4a16_plan_t *out) {
             p.asrc = W4A16_ASRC_RING;
             p.tiles = 2;
             p.depth = 2;
-        } else if (narrow && G >= 16) {        // one tile, eight wavefronts (two per SIMD)
-            p.tiles = 1;
+        } else if (narrow && G >= 16) {        // eight wavefronts (two per SIMD): one tile, two from 64 groups
+            p.tiles = G >= 64 ? 2 : 1;
             p.kwaves = 8;
             p.depth = 4;
         } else {
@@ -273,10 +276,10 @@ void auto_plan(int M, int N, int K, w4a16_plan_t *out) {
             p.tiles = 2;
             p.depth = 4;
             if (G >= 64) p.kwaves = 8;
-        } else {                               // A through the ring, shallow
+        } else {                               // A through the ring (depth 4 for narrow N from 32 groups)
             p.asrc = W4A16_ASRC_RING;
             p.tiles = 2;
-            p.depth = 2;
+            p.depth = (narrow && G >= 32) ? 4 : 2;
         }
     }
     // short K: no more wavefronts along K than groups per workgroup
@@ -303,7 +306,7 @@ void auto_plan(int M, int N, int K, w4a16_plan_t *out) {
     if (p.path == W4A16_PATH_MFMA && p.asrc == W4A16_ASRC_LDS && plan_lds(p, M, G) + 256 > kLdsMax) {
         p.asrc = M >= 5 ? W4A16_ASRC_RING : W4A16_ASRC_GLOBAL;
         p.splits = 1;
-        if (p.asrc == W4A16_ASRC_RING && !find_variant(p, M)) p.kwaves = 4;   // the ring's shapes
+        if (p.asrc == W4A16_ASRC_RING) p.kwaves = 4;   // the ring measures best with four
     }
     // ring A has fewer compiled shapes (none for the short-K fallback)
     if (p.asrc == W4A16_ASRC_RING && !find_variant(p, M)) p.asrc = W4A16_ASRC_GLOBAL;

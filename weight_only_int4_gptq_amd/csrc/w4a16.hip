@@ -328,13 +328,15 @@ void auto_plan(int M, int N, int K, w4a16_plan_t *out) {
 //    same with one tile each, depth 4.  Otherwise A through the LDS ring,
 //    two tiles, four wavefronts, depth 2: wide N up to 8 rows; long K
 //    from 8 rows, split two ways (below: four tiles split four ways, A in
-//    LDS); otherwise from 8 rows (below: two tiles, eight wavefronts, A in
-//    LDS).
+//    LDS); narrow N (the tensor-parallel shards) up to 8 rows: A in LDS,
+//    eight wavefronts, depth 4, one tile (two from 64 groups); otherwise
+//    from 8 rows, depth 4 for narrow N from 64 groups (below: two tiles,
+//    eight wavefronts, A in LDS).
 // The first of these that the library has a kernel for and that fits is taken, else
 // the first compiled fallback.
 void auto_plan_nv(int M, int N, int K, w4a16_plan_t *out) {
     const int NT = N / 16, G = K / W4A16_GROUP;
-    const bool wide = NT >= 2048, vwide = NT >= 8192, deep = G >= 128;
+    const bool wide = NT >= 2048, vwide = NT >= 8192, deep = G >= 128, narrow = NT <= 384;
     w4a16_plan_t p;
     p.path = W4A16_PATH_MFMA;
     p.tiles = 2;
@@ -366,10 +368,12 @@ void auto_plan_nv(int M, int N, int K, w4a16_plan_t *out) {
         } else if (deep) {
             if (M <= 7) set(W4A16_PATH_MFMA, 4, 4, 4, W4A16_ASRC_LDS, 2);
             else set(W4A16_PATH_MFMA, 2, 4, 2, W4A16_ASRC_RING, 2);
+        } else if (narrow && M <= 8) {         // one tile (two from 64 groups), eight wavefronts
+            set(W4A16_PATH_MFMA, G >= 64 ? 2 : 1, 8, 1, W4A16_ASRC_LDS, 4);
         } else if (M <= 7) {
             set(W4A16_PATH_MFMA, 2, 8, 1, W4A16_ASRC_LDS, 4);
         } else {
-            set(W4A16_PATH_MFMA, 2, 4, 1, W4A16_ASRC_RING, 2);
+            set(W4A16_PATH_MFMA, 2, 4, 1, W4A16_ASRC_RING, (narrow && G >= 64) ? 4 : 2);
         }
     }
     // splits no larger than the groups allow (a power of two), and no more

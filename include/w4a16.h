@@ -17,10 +17,10 @@
  *   qweight  uint32 [K/8][N], N contiguous.  Nibble j of word (kb, n), i.e.
  *            bits 4j..4j+3 (low nibble first), is the code q in [0, 15] of
  *            row k = 8*kb + j.  The weight is w = (q - 8) * s.
- *   scales   bf16 [K/128][N], N contiguous: s for (group floor(k/128), column n).
- *            The GEMM reads them repacked (w4a16_repack_scales): the scale of
- *            (g, n) at index (t*G + g)*16 + c with t = n/16, c = n%16, so one
- *            tile's scales follow each other in the order the kernel reads them.
+ *   scales   bf16 [K/128][N], N contiguous: s for (group floor(k/128), column n),
+ *            exactly as the checkpoint stores them.  The GEMM reads them in
+ *            place (tile t's 16 scales of group g are the 32 bytes at
+ *            g*2N + 32t); they are never repacked.
  *   A        bf16 [M][K], K contiguous (row stride K).
  *   C        bf16 [M][N], N contiguous (row stride N); fp32 accumulation,
  *            rounded to nearest even once at the end.
@@ -45,7 +45,8 @@
  *   - Valid shapes: 1 <= M <= 16, K a positive multiple of 128 up to
  *     W4A16_MAX_K (2^24; the kernels address a tile's weights and the rows of
  *     A through 32-bit buffer offsets), N a positive multiple of 16,
- *     K*N/2 < 2^40.  group must be 128.
+ *     K*N/2 < 2^40, (K/128)*N*2 < 2^31 (the scales are addressed with 32-bit
+ *     byte offsets).  group must be 128.
  */
 #ifndef W4A16_H
 #define W4A16_H
@@ -94,7 +95,7 @@ extern "C" {
  *           (with W4A16_ASRC_SPLITN: that split its columns, tiles each)
  *   splits  workgroups that split K for the same columns: 1 (none), 2, 4, 8, ...
  *           (a power of two); more than one needs a workspace (see
- *           w4a16_workspace_bytes)
+ *           w4a16_workspace_bytes_plan)
  *   asrc    W4A16_ASRC_LDS, W4A16_ASRC_GLOBAL, W4A16_ASRC_RING or
  *           W4A16_ASRC_SPLITN (the last three on the MFMA path only)
  *   depth   K groups each wavefront keeps in flight (0 = the default for
@@ -116,24 +117,20 @@ const char *w4a16_status_string(int status);
 size_t w4a16_repacked_bytes(int K, int N);
 
 /*
- * One-time repack of GPTQ words into the blob layout described above.
+ * One-time repack of GPTQ words into the blob layout described above, the
+ * only preparation a checkpoint needs: its scales are used as they are.
+ * The input is the checkpoint format of the page "Qwen3.8-27B on single DGX
+ * Spark ..." (section "Quality.": symmetric GPTQ, 4-bit, group 128, no
+ * act-order, no zero points); the blob order is this library's own, chosen
+ * so that one wavefront loads one 16-column x 128-row piece with a single
+ * 16-byte load per lane.
  *   qweight      device, uint32 [K/8][N] as in the header comment (read only)
  *   wq_repacked  device, w4a16_repacked_bytes(K, N) bytes (written)
  * A pure permutation of nibbles: every code is moved, none is changed.
- * Returns W4A16_OK or an error status.
+ * Returns W4A16_OK, or W4A16_ERR_NULL / _SHAPE / _ALIGN / _DEVICE / _LAUNCH
+ * (nothing is enqueued on an error).
  */
 int w4a16_repack_weights(const void *qweight, void *wq_repacked, int K, int N, void *stream);
-
-/* Bytes of the repacked scales (= (K/128)*N*2), 0 for invalid shapes. */
-size_t w4a16_repacked_scale_bytes(int K, int N);
-
-/*
- * One-time repack of the bf16 scales [K/128][N] into the tile order above.
- *   scales           device, bf16 [K/128][N] (read only)
- *   scales_repacked  device, w4a16_repacked_scale_bytes(K, N) bytes (written)
- * A pure permutation.  Returns W4A16_OK or an error status.
- */
-int w4a16_repack_scales(const void *scales, void *scales_repacked, int K, int N, void *stream);
 
 /*
  * The plan w4a16_gemm uses for (M, N, K): fills *plan and returns W4A16_OK,
@@ -159,25 +156,42 @@ int w4a16_check_plan(int M, int N, int K, const w4a16_plan_t *plan);
 #define W4A16_SPLIT_COUNTER_BYTES 65536
 
 /*
- * Workspace bytes a plan needs: W4A16_SPLIT_COUNTER_BYTES plus
- * 4 * splits * M * N, or 0 when splits == 1.  plan == NULL means the plan
- * w4a16_gemm would choose.  Returns 0 for invalid arguments.
+ * Workspace bytes that serve every call at (M, N, K) with its automatic plan
+ * (w4a16_gemm, w4a16_gemm_f32, w4a16_gemm_silu_mul, w4a16_gemm_argmax): at
+ * least W4A16_SPLIT_COUNTER_BYTES, plus the split-K partials
+ * 4 * splits * M * N when a plan splits K.  0 for invalid shapes.
  * A workspace must be zero-filled before its first use.  Every call leaves
  * the counter region zero again and writes partials only after it, so one
  * workspace serves calls of any shape and plan issued one after another
  * (stream order); calls that share a workspace must not run concurrently.
+ * Calls whose plan needs no workspace accept NULL.
  */
-size_t w4a16_workspace_bytes(int M, int N, int K, const w4a16_plan_t *plan);
+size_t w4a16_workspace_bytes(int M, int N, int K);
 
 /*
- * C = A . dequant(blob, scales), dispatched by row count.
+ * Workspace bytes one plan needs: W4A16_SPLIT_COUNTER_BYTES plus
+ * 4 * splits * M * N, or 0 when splits == 1.  plan == NULL means the plan
+ * w4a16_gemm would choose.  Returns 0 for invalid arguments.
+ */
+size_t w4a16_workspace_bytes_plan(int M, int N, int K, const w4a16_plan_t *plan);
+
+/*
+ * C = A . dequant(blob, scales), dispatched by row count: the backbone and
+ * output-projection matmul of the page "Qwen3.8-27B on single DGX Spark ..."
+ * (section "How.": kernels dispatched by row count; M = 1 is a decode step,
+ * M > 1 the rows a speculative verify adds, page "One Config Line Made My 27B
+ * Model 2.7x Faster", section "The fix: use the MTP head you already
+ * downloaded"), on weights of the checkpoint contract (same first page,
+ * section "Quality.").
  *   A            device bf16 [M][K]
  *   wq_repacked  device blob from w4a16_repack_weights for this K, N
- *   scales       device, repacked scales from w4a16_repack_scales
+ *   scales       device bf16 [K/128][N], the checkpoint's scales
  *   C            device bf16 [M][N] (written)
  *   group        must be 128
- *   workspace    device, at least w4a16_workspace_bytes(M, N, K, NULL) bytes,
- *                zero-filled before first use; may be NULL when that is 0
+ *   workspace    device, at least w4a16_workspace_bytes(M, N, K) bytes,
+ *                zero-filled before first use; may be NULL when the plan
+ *                needs none (w4a16_workspace_bytes_plan(M, N, K, NULL) == 0)
+ * Returns W4A16_OK or a negative status (nothing is enqueued on an error).
  * Deterministic: the same arguments give bitwise the same C.
  */
 int w4a16_gemm(const void *A, const void *wq_repacked, const void *scales, void *C,
@@ -209,7 +223,7 @@ int w4a16_gemm_plan(const void *A, const void *wq_repacked, const void *scales, 
  *   H            device bf16 [M][N/2] (written)
  *   N            the fused width, a multiple of 32
  *   other arguments as w4a16_gemm (blob and scales of the [K][N] fused
- *   weight; workspace at least w4a16_workspace_bytes(M, N, K, NULL)).
+ *   weight; workspace at least w4a16_workspace_bytes(M, N, K)).
  * The plan w4a16_gemm would choose is used with an even tile count (gate
  * and up tiles of the same columns in one workgroup).
  */
@@ -280,17 +294,19 @@ int w4a16_gemm_argmax_plan(const void *A, const void *wq_repacked, const void *s
 
 /*
  * Test export of the device dequantization used by both GEMM paths:
- * W[k][n] = (q - 8) * s as fp32 (exact), device fp32 [K][N] (written);
- * `scales` are the repacked scales.
+ * W[k][n] = (q - 8) * s as fp32 (exact: at most 11 significant bits),
+ * device fp32 [K][N] (written); `scales` are the checkpoint's [K/128][N].
+ * The dequantization whose exactness the page "Qwen3.8-27B on single DGX
+ * Spark ..." (section "Quality.") gates the runtime against.
  */
-int w4a16_dequant(const void *wq_repacked, const void *scales, float *W, int K, int N,
-                  void *stream);
+int w4a16_dequant_debug(const void *wq_repacked, const void *scales, float *W, int K, int N,
+                        void *stream);
 
 /*
  * Test export of the device unpacking used by both GEMM paths:
  * codes[k][n] = q in [0, 15], device uint8 [K][N] (written).
  */
-int w4a16_unpack(const void *wq_repacked, uint8_t *codes, int K, int N, void *stream);
+int w4a16_unpack_debug(const void *wq_repacked, uint8_t *codes, int K, int N, void *stream);
 
 /*
  * ---------------------------------------------------------------- NVFP4
@@ -336,10 +352,12 @@ size_t w4a16_nvfp4_repacked_scale_bytes(int K, int N);
 int w4a16_nvfp4_repack_weights(const void *packed, void *wq_repacked, int K, int N, void *stream);
 int w4a16_nvfp4_repack_scales(const void *scales, void *scales_repacked, int K, int N, void *stream);
 
-/* Planning for the NVFP4 calls: as w4a16_get_plan, w4a16_check_plan, w4a16_workspace_bytes. */
+/* Planning for the NVFP4 calls: as w4a16_get_plan, w4a16_check_plan,
+ * w4a16_workspace_bytes and w4a16_workspace_bytes_plan. */
 int w4a16_nvfp4_get_plan(int M, int N, int K, w4a16_plan_t *plan);
 int w4a16_nvfp4_check_plan(int M, int N, int K, const w4a16_plan_t *plan);
-size_t w4a16_nvfp4_workspace_bytes(int M, int N, int K, const w4a16_plan_t *plan);
+size_t w4a16_nvfp4_workspace_bytes(int M, int N, int K);
+size_t w4a16_nvfp4_workspace_bytes_plan(int M, int N, int K, const w4a16_plan_t *plan);
 
 /*
  * C = alpha * A . dequant(blob, scales), dispatched by row count.
@@ -348,7 +366,7 @@ size_t w4a16_nvfp4_workspace_bytes(int M, int N, int K, const w4a16_plan_t *plan
  *   alpha        the per-tensor factor
  *   C            device bf16 [M][N] (written), rounded to nearest even once
  *   group        must be W4A16_NVFP4_GROUP
- *   workspace    as for w4a16_gemm, at least w4a16_nvfp4_workspace_bytes(M, N, K, NULL)
+ *   workspace    as for w4a16_gemm, at least w4a16_nvfp4_workspace_bytes(M, N, K)
  * Every converted weight e2m1 * e4m3 is exact; each 16-row block's partial
  * sum is scaled and accumulated in fp32.  Deterministic.
  */

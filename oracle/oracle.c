@@ -172,17 +172,3 @@ void oracle_unrepack(const uint32_t *blob, int K, int N, uint32_t *qweight) {
         }
 }
 
-/*
- * Repacked scales, written from their layout definition: the bf16 scale of
- * (group g, column n) moves to index (t * G + g) * 16 + c with t = n / 16,
- * c = n % 16, so the 16 scales of one (tile, group) are adjacent and the
- * groups of one tile follow each other.  A pure permutation of 16-bit values.
- */
-void oracle_repack_scales(const uint16_t *scales, int K, int N, uint16_t *out) {
-    int G = K / GROUP;
-    for (int g = 0; g < G; ++g)
-        for (int n = 0; n < N; ++n) {
-            size_t idx = ((size_t)(n / 16) * G + g) * 16 + (size_t)(n % 16);
-            out[idx] = scales[(size_t)g * N + n];
-        }
-}

@@ -72,6 +72,8 @@ WORKLOADS = {
                         desc="Fused gate/up MLP: K=5120, N=34816 (2x17408)"),
     "down": Workload("down", 17408, 5120, (1, 4, 8, 16), 3, act="silu_mul",
                      desc="Down projection: K=17408, N=5120, A = SiLU(x)*y"),
+    "attn_out": Workload("attn_out", 6144, 5120, (1, 2, 4, 8, 16), 5,
+                         desc="Attention output projection: K=6144 (24 heads x 256), N=5120"),
     "lm_head": Workload("lm_head", 5120, 248320, (1, 8, 16), 4,
                         desc="Output head: K=5120, N=248320"),
 }

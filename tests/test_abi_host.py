@@ -87,8 +87,15 @@ def test_split_plan_needs_workspace():
     assert need == 65536 + 2 * 8 * 1024 * 4
     assert _gemm(M=8, plan=p) == -5
     assert _gemm(M=8, plan=p, ws=P, wsb=need - 1) == -5
-    assert w4.workspace_bytes(8, 1024, 512) == 0       # short K: the automatic plan does not split
-    assert w4.workspace_bytes(6, 5120, 17408) > 0      # long K, few strips: it does
+    L = w4.lib()
+    # short K: the automatic plan does not split (no workspace), but the
+    # any-call query still covers the argmax call's counter region
+    assert L.w4a16_workspace_bytes_plan(8, 1024, 512, None) == 0
+    assert w4.workspace_bytes(8, 1024, 512) == 65536
+    for (M, N, K) in ((1, 5120, 17408), (6, 5120, 17408), (16, 8192, 5120), (9, 34816, 5120)):
+        auto = L.w4a16_workspace_bytes_plan(M, N, K, None)
+        assert w4.workspace_bytes(M, N, K) >= max(auto, 65536), (M, N, K)
+    assert L.w4a16_workspace_bytes(0, 1024, 512) == 0
 
 
 def test_no_device_is_an_error_not_a_crash():
@@ -98,7 +105,7 @@ def test_no_device_is_an_error_not_a_crash():
         pytest.skip("a GPU is present")
     assert _gemm() == -6
     assert w4.lib().w4a16_repack_weights(P, P2, 512, 1024, NULL) == -6
-    assert w4.lib().w4a16_dequant(P, P, P2, 512, 1024, NULL) == -6
+    assert w4.lib().w4a16_dequant_debug(P, P, P2, 512, 1024, NULL) == -6
 
 
 def test_repack_and_export_argument_errors():
@@ -107,13 +114,32 @@ def test_repack_and_export_argument_errors():
     assert L.w4a16_repack_weights(P, P2, 500, 1024, NULL) == -2
     assert L.w4a16_repack_weights(P, P2, 512, 1000, NULL) == -2
     assert L.w4a16_repack_weights(ODD, P2, 512, 1024, NULL) == -4
-    assert L.w4a16_dequant(P, NULL, P2, 512, 1024, NULL) == -1
-    assert L.w4a16_unpack(P, NULL, 512, 1024, NULL) == -1
-    assert L.w4a16_unpack(P, P2, 512, 1000, NULL) == -2
-    assert L.w4a16_repack_scales(NULL, P, 512, 1024, NULL) == -1
-    assert L.w4a16_repack_scales(P, P2, 512, 1000, NULL) == -2
-    assert L.w4a16_repack_scales(ODD, P2, 512, 1024, NULL) == -4
-    assert L.w4a16_repacked_scale_bytes(512, 1024) == 4 * 1024 * 2
+    assert L.w4a16_dequant_debug(P, NULL, P2, 512, 1024, NULL) == -1
+    assert L.w4a16_dequant_debug(P, ODD, P2, 512, 1024, NULL) == -4
+    assert L.w4a16_unpack_debug(P, NULL, 512, 1024, NULL) == -1
+    assert L.w4a16_unpack_debug(P, P2, 512, 1000, NULL) == -2
+
+
+def test_boundary_names_of_the_contract():
+    # the calls the contract fixes: a one-time weight repack and the matmul on
+    # the checkpoint's [K/128, N] scales, plus sizes, the workspace query, the
+    # dequant debug export and the status text
+    text = open(HEADER).read()
+    for sig in (r"size_t\s+w4a16_repacked_bytes\(int K, int N\)",
+                r"int\s+w4a16_repack_weights\(const void \*qweight, void \*wq_repacked, int K, int N, void \*stream\)",
+                r"size_t\s+w4a16_workspace_bytes\(int M, int N, int K\)",
+                r"int\s+w4a16_gemm\(const void \*A, const void \*wq_repacked, const void \*scales, void \*C,\s+"
+                r"int M, int N, int K, int group, void \*workspace, size_t workspace_bytes,\s+void \*stream\)",
+                r"int\s+w4a16_dequant_debug\(const void \*wq_repacked, const void \*scales, float \*W, int K, int N,",
+                r"const char \*w4a16_status_string\(int status\)"):
+        assert re.search(sig, text), sig
+    L = w4.lib()
+    for name in ("w4a16_repacked_bytes", "w4a16_repack_weights", "w4a16_workspace_bytes", "w4a16_gemm",
+                 "w4a16_dequant_debug", "w4a16_status_string"):
+        assert hasattr(L, name), name
+    # scales are consumed as the checkpoint stores them: no scale repack exists
+    assert "w4a16_repack_scales(" not in text
+    assert not hasattr(L, "w4a16_repack_scales")
 
 
 def test_row_count_dispatch():
@@ -160,6 +186,9 @@ def test_row_count_dispatch():
     for M in range(1, 17):
         for K in (128, 256, 512, 5120, 17408, 1 << 20, 1 << 24):
             for N in (16, 1024, 8192, 34816) + ((131072,) if K <= 5120 else ()):
+                if (K // 128) * N * 2 >= 1 << 31:       # scales beyond 32-bit byte offsets
+                    assert w4.lib().w4a16_get_plan(M, N, K, ctypes.byref(w4.Plan())) == -2
+                    continue
                 assert w4.plan_ok(M, N, K, w4.get_plan(M, N, K)), (M, N, K)
                 assert w4.nvfp4_plan_ok(M, N, K, w4.nvfp4_get_plan(M, N, K)), (M, N, K)
     p = w4.Plan()

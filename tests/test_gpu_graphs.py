@@ -21,7 +21,7 @@ DEV = "cuda:0"
 def _gptq(K, N, seed):
     A, qw, sc = synth.gen_problem(K, N, seed)
     q = torch.from_numpy(qw.view(np.int32)).to(DEV)
-    s = w4.repack_scales(torch.from_numpy(sc.view(np.int16)).to(DEV), K, N)
+    s = torch.from_numpy(sc.view(np.int16)).to(DEV).view(torch.bfloat16)   # the checkpoint's scales
     blob = w4.repack_weights(q, K, N)
     a = torch.from_numpy(A.view(np.int16)).to(DEV).view(torch.bfloat16)
     return a, blob, s

@@ -52,13 +52,39 @@ def _run(cmd, what):
     return err
 
 
-def _compile(out: str, sources: list, verbose: bool) -> str:
-    """Compile each source to an object in parallel, then link the shared library."""
+CACHE = os.path.join(ROOT, "_build")
+
+
+def _key(src: str, cmd: list) -> str:
+    """Hash of a translation unit's text, every header it may include and its command."""
+    import hashlib
+    h = hashlib.sha256(" ".join(cmd[1:]).encode())
+    for path in [src] + [d for d in DEPENDS if not d.endswith(".hip")]:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:20]
+
+
+def _compile(out: str, sources: list, verbose: bool, reuse: bool = False) -> str:
+    """Compile each source to an object in parallel, then link the shared library.
+
+    reuse=True keeps objects in _build/ keyed by a hash of their inputs and
+    recompiles only the units whose inputs changed (development builds).
+    """
     objs = [out + "." + os.path.basename(src) + ".o" for src in sources]
     procs = []
     for src, obj in zip(sources, objs):
         cmd = ([hipcc()] + FLAGS + SOURCE_FLAGS.get(os.path.basename(src), []) +
                ["-I", os.path.join(ROOT, "include"), "-c", "-o", obj, src])
+        if reuse:
+            os.makedirs(CACHE, exist_ok=True)
+            cached = os.path.join(CACHE, os.path.basename(src) + "." + _key(src, cmd) + ".o")
+            if os.path.exists(cached):
+                shutil.copyfile(cached, obj)
+                continue
+            cmd[cmd.index("-o") + 1] = cached
+            import shlex
+            cmd = ["bash", "-c", shlex.join(cmd) + " && cp " + shlex.quote(cached) + " " + shlex.quote(obj)]
         procs.append((subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.PIPE, text=True), src))
     errs = []
     for proc, src in procs:
@@ -78,15 +104,17 @@ def _compile(out: str, sources: list, verbose: bool) -> str:
     return out
 
 
-def build(force: bool = True, verbose: bool = False) -> str:
+def build(force: bool = True, verbose: bool = False, reuse: bool = False) -> str:
     """Compile libw4a16.so and libw4a16_probe.so for gfx950 (always, unless
-    force=False and they exist).  Returns the path of libw4a16.so."""
+    force=False and they exist; reuse=True recompiles only changed units).
+    Returns the path of libw4a16.so."""
     if force or not os.path.exists(PROBE_LIB):
-        _compile(PROBE_LIB, PROBE_SOURCES, verbose)
+        _compile(PROBE_LIB, PROBE_SOURCES, verbose, reuse)
     if not force and os.path.exists(LIB):
         return LIB
-    return _compile(LIB, SOURCES, verbose)
+    return _compile(LIB, SOURCES, verbose, reuse)
 
 
 if __name__ == "__main__":
-    print(build(verbose=True))
+    import sys
+    print(build(verbose=True, reuse="--reuse" in sys.argv))

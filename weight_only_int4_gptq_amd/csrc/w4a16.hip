@@ -89,6 +89,8 @@ int check_shape(int M, int N, int K) {
     if (K <= 0 || (K % W4A16_GROUP) != 0 || K > W4A16_MAX_K) return W4A16_ERR_SHAPE;
     if (N <= 0 || (N % 16) != 0) return W4A16_ERR_SHAPE;
     if ((unsigned long long)K * (unsigned long long)N / 2ull >= (1ull << 40)) return W4A16_ERR_SHAPE;
+    // the scales [K/128][N] are addressed with 32-bit byte offsets
+    if ((unsigned long long)(K / W4A16_GROUP) * (unsigned long long)N * 2ull >= (1ull << 31)) return W4A16_ERR_SHAPE;
     return W4A16_OK;
 }
 
@@ -427,13 +429,31 @@ void fuse_plan(int M, w4a16_plan_t *p, int fmt = FMT_GPTQ) {
         q.tiles = (fmt == FMT_GPTQ && M >= 9) ? 4 : 2;
         q.kwaves = 4;
         q.depth = 2;
+    } else {
+        q.tiles = 2;                           // same wavefronts and ring depth if compiled
     }
-    q.tiles = 2;                               // same wavefronts and ring depth if compiled
     if (!find_variant(q, M, true, fmt)) q.depth = 0;
     if (!find_variant(q, M, true, fmt)) q.kwaves = 4;
     if (!find_variant(q, M, true, fmt)) q.asrc = W4A16_ASRC_GLOBAL;
     if (!find_variant(q, M, true, fmt)) q.asrc = W4A16_ASRC_RING, q.depth = 2;
     *p = q;
+}
+
+// Workspace bytes that serve every call kind at (M, N, K) with its automatic
+// plan: the plain and fp32-output calls, the gate/up call (N a multiple of
+// 32) and the argmax call (the counter region alone).
+size_t workspace_any_call(int M, int N, int K, int fmt) {
+    if (check_shape(M, N, K) != W4A16_OK) return 0;
+    w4a16_plan_t p;
+    if (fmt == FMT_NVFP4) auto_plan_nv(M, N, K, &p);
+    else auto_plan(M, N, K, &p);
+    size_t need = workspace_for(p, M, N);
+    if (N % 32 == 0) {
+        fuse_plan(M, &p, fmt);
+        const size_t f = workspace_for(p, M, N);
+        if (f > need) need = f;
+    }
+    return need > (size_t)W4A16_ARGMAX_WORKSPACE_BYTES ? need : (size_t)W4A16_ARGMAX_WORKSPACE_BYTES;
 }
 
 // fuse: 0 plain C[M][N]; 1 the gate/up epilogue, C is H[M][N/2]; 2 the row
@@ -547,7 +567,7 @@ const char *w4a16_status_string(int status) {
     switch (status) {
         case W4A16_OK: return "ok";
         case W4A16_ERR_NULL: return "null pointer argument";
-        case W4A16_ERR_SHAPE: return "invalid shape (need 1<=M<=16, K%128==0, K<=2^24, N%16==0)";
+        case W4A16_ERR_SHAPE: return "invalid shape (need 1<=M<=16, K%128==0, K<=2^24, N%16==0, (K/128)*N*2 < 2^31)";
         case W4A16_ERR_GROUP: return "group size must be 128 (GPTQ) or 16 (NVFP4)";
         case W4A16_ERR_ALIGN: return "device pointer not 16-byte aligned";
         case W4A16_ERR_WORKSPACE: return "workspace missing or too small";
@@ -582,30 +602,6 @@ int w4a16_repack_weights(const void *qweight, void *wq_repacked, int K, int N, v
     return e == hipSuccess ? W4A16_OK : W4A16_ERR_LAUNCH;
 }
 
-size_t w4a16_repacked_scale_bytes(int K, int N) {
-    if (check_weight_shape(K, N) != W4A16_OK) return 0;
-    return (size_t)(K / W4A16_GROUP) * (size_t)N * 2;
-}
-
-int w4a16_repack_scales(const void *scales, void *scales_repacked, int K, int N, void *stream) {
-    if (!scales || !scales_repacked) return W4A16_ERR_NULL;
-    int st = check_weight_shape(K, N);
-    if (st != W4A16_OK) return st;
-    if (!aligned16(scales) || !aligned16(scales_repacked)) return W4A16_ERR_ALIGN;
-    st = check_device();
-    if (st != W4A16_OK) return st;
-    const long long count = (long long)(K / W4A16_GROUP) * N;
-    const unsigned grid = (unsigned)((count + 255) / 256);
-    const uint16_t *in = static_cast<const uint16_t *>(scales);
-    uint16_t *out = static_cast<uint16_t *>(scales_repacked);
-    int n = N, g = K / W4A16_GROUP;
-    long long cnt = count;
-    void *args[] = {&in, &out, &n, &g, &cnt};
-    const hipError_t e = launch(reinterpret_cast<const void *>(repack_scales_kernel), grid, 256, 0,
-                                static_cast<hipStream_t>(stream), args);
-    return e == hipSuccess ? W4A16_OK : W4A16_ERR_LAUNCH;
-}
-
 int w4a16_get_plan(int M, int N, int K, w4a16_plan_t *plan) {
     if (!plan) return W4A16_ERR_NULL;
     const int st = check_shape(M, N, K);
@@ -621,7 +617,7 @@ int w4a16_check_plan(int M, int N, int K, const w4a16_plan_t *plan) {
     return validate_plan(*plan, M, N, K);
 }
 
-size_t w4a16_workspace_bytes(int M, int N, int K, const w4a16_plan_t *plan) {
+size_t w4a16_workspace_bytes_plan(int M, int N, int K, const w4a16_plan_t *plan) {
     if (check_shape(M, N, K) != W4A16_OK) return 0;
     w4a16_plan_t p;
     if (plan) {
@@ -631,6 +627,10 @@ size_t w4a16_workspace_bytes(int M, int N, int K, const w4a16_plan_t *plan) {
         auto_plan(M, N, K, &p);
     }
     return workspace_for(p, M, N);
+}
+
+size_t w4a16_workspace_bytes(int M, int N, int K) {
+    return workspace_any_call(M, N, K, FMT_GPTQ);
 }
 
 int w4a16_gemm(const void *A, const void *wq_repacked, const void *scales, void *C, int M, int N,
@@ -709,13 +709,13 @@ static int run_export(const void *wq, const void *scales, float *W, uint8_t *cod
     return e == hipSuccess ? W4A16_OK : W4A16_ERR_LAUNCH;
 }
 
-int w4a16_dequant(const void *wq_repacked, const void *scales, float *W, int K, int N,
-                  void *stream) {
+int w4a16_dequant_debug(const void *wq_repacked, const void *scales, float *W, int K, int N,
+                        void *stream) {
     if (!wq_repacked || !scales || !W) return W4A16_ERR_NULL;
     return run_export(wq_repacked, scales, W, nullptr, K, N, stream);
 }
 
-int w4a16_unpack(const void *wq_repacked, uint8_t *codes, int K, int N, void *stream) {
+int w4a16_unpack_debug(const void *wq_repacked, uint8_t *codes, int K, int N, void *stream) {
     if (!wq_repacked || !codes) return W4A16_ERR_NULL;
     return run_export(wq_repacked, nullptr, nullptr, codes, K, N, stream);
 }
@@ -785,7 +785,7 @@ int w4a16_nvfp4_check_plan(int M, int N, int K, const w4a16_plan_t *plan) {
     return validate_plan(*plan, M, N, K, FMT_NVFP4);
 }
 
-size_t w4a16_nvfp4_workspace_bytes(int M, int N, int K, const w4a16_plan_t *plan) {
+size_t w4a16_nvfp4_workspace_bytes_plan(int M, int N, int K, const w4a16_plan_t *plan) {
     if (check_shape(M, N, K) != W4A16_OK) return 0;
     w4a16_plan_t p;
     if (plan) {
@@ -795,6 +795,10 @@ size_t w4a16_nvfp4_workspace_bytes(int M, int N, int K, const w4a16_plan_t *plan
         auto_plan_nv(M, N, K, &p);
     }
     return workspace_for(p, M, N);
+}
+
+size_t w4a16_nvfp4_workspace_bytes(int M, int N, int K) {
+    return workspace_any_call(M, N, K, FMT_NVFP4);
 }
 
 int w4a16_nvfp4_gemm(const void *A, const void *wq_repacked, const void *scales, float alpha, void *C,

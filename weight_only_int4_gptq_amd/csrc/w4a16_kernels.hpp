@@ -66,7 +66,7 @@ constexpr int kNvBlock = 16;                   // NVFP4 rows per block scale
 struct GemmArgs {
     const uint16_t *A;       // bf16 [M][K]
     const u32x4 *blob;       // repacked weights, 64 pieces of 16 B per (tile, group)
-    const uint16_t *scales;  // repacked bf16 scales: [tile][group][16 columns]
+    const uint16_t *scales;  // bf16 scales as in the checkpoint: [K/128][N]
                              // (NVFP4: E4M3 bytes [tile][group][16 columns][8 blocks])
     uint16_t *C;             // bf16 [M][N]
     float *part;             // split-K partials [S][M][N] (S > 1 only)
@@ -398,20 +398,8 @@ static __global__ void __launch_bounds__(256) repack_kernel(const uint32_t *__re
     blob[pc] = out;
 }
 
-// Scales [G][N] -> [tile][group][16]: one thread per scale.
-static __global__ void __launch_bounds__(256) repack_scales_kernel(const uint16_t *__restrict__ scales,
-                                                            uint16_t *__restrict__ out, int N, int G,
-                                                            long long count) {
-    const long long i = (long long)blockIdx.x * 256 + threadIdx.x;
-    if (i >= count) return;
-    const int c = (int)(i & 15);
-    const long long tg = i >> 4;
-    const int g = (int)(tg % G);
-    const long long t = tg / G;
-    out[i] = scales[(long long)g * N + t * 16 + c];
-}
-
-// Test exports: the same words_to_bf16x8 and scale layout the GEMM kernels use.
+// Test exports: the same words_to_bf16x8 the GEMM kernels use, and the
+// checkpoint's scales [K/128][N].
 template <bool CODES>
 __global__ void __launch_bounds__(256) export_kernel(const u32x4 *__restrict__ blob,
                                                      const uint16_t *__restrict__ scales,
@@ -426,7 +414,7 @@ __global__ void __launch_bounds__(256) export_kernel(const u32x4 *__restrict__ b
     const long long n = t * 16 + c;
     const u32x4 w = blob[pc];
     const DequantConsts kc = dequant_consts();
-    const float s = CODES ? 0.0f : bf16_bits_to_f32(scales[tg * 16 + c]);
+    const float s = CODES ? 0.0f : bf16_bits_to_f32(scales[(long long)g * N + n]);
     uint32_t bw[4][4];
     words_to_bf16x8<true>(w[0], w[1], kc, bw[0], bw[1]);
     words_to_bf16x8<true>(w[2], w[3], kc, bw[2], bw[3]);
@@ -616,13 +604,21 @@ __global__ void __launch_bounds__(64 * KW) gemm_kernel(GemmArgs p) {
     // Every load is resource + fixed per-lane offset + the group's
     // wave-uniform offset, so the stream costs no vector address arithmetic.
     __amdgpu_buffer_rsrc_t wres[T], sres[T];
+    const uint32_t s_gstride = kNv ? (uint32_t)kScaleBytes : (uint32_t)p.N * 2u;   // scale bytes between groups
 #pragma unroll
     for (int t = 0; t < T; ++t) {
         const size_t tile = (size_t)min(tile_of(t), p.NT - 1);
         wres[t] = buffer_rsrc(reinterpret_cast<const uint8_t *>(p.blob) + tile * (size_t)p.G * 1024,
                               (uint32_t)p.G * 1024u);
-        sres[t] = buffer_rsrc(reinterpret_cast<const uint8_t *>(p.scales) + tile * (size_t)p.G * kScaleBytes,
-                              (uint32_t)p.G * (uint32_t)kScaleBytes);
+        // GPTQ: the checkpoint's scales [G][N]: tile t's 16 scales of group g
+        // are the 32 bytes at g*2N + 32t.  NVFP4: repacked, one tile's
+        // groups after each other.
+        if constexpr (kNv)
+            sres[t] = buffer_rsrc(reinterpret_cast<const uint8_t *>(p.scales) + tile * (size_t)p.G * kScaleBytes,
+                                  (uint32_t)p.G * (uint32_t)kScaleBytes);
+        else
+            sres[t] = buffer_rsrc(reinterpret_cast<const uint8_t *>(p.scales) + tile * (size_t)kScaleBytes,
+                                  (uint32_t)(p.G - 1) * s_gstride + (uint32_t)kScaleBytes);
     }
     const uint32_t w_lane = (uint32_t)lane * 16;             // this lane's 16 B of a 1 KiB piece
     // GPTQ: the dword holding this column's bf16 scale, and its half;
@@ -704,13 +700,13 @@ __global__ void __launch_bounds__(64 * KW) gemm_kernel(GemmArgs p) {
                 u32x4, __builtin_amdgcn_raw_buffer_load_b128(wres[t], w_lane, g * 1024, kCachePolicyNt));
             if constexpr (kNv) {
                 const u32x2 x = __builtin_bit_cast(
-                    u32x2, __builtin_amdgcn_raw_buffer_load_b64(sres[t], s_lane, g * kScaleBytes, 0));
+                    u32x2, __builtin_amdgcn_raw_buffer_load_b64(sres[t], s_lane, g * s_gstride, 0));
                 sv[j][t][0] = x[0];
                 sv[j][t][1] = x[1];
             } else {
                 // the aligned dword that holds this lane's bf16 scale (a 16-bit
                 // load would be re-extended at the loop latch, which stalls the ring)
-                sv[j][t][0] = __builtin_amdgcn_raw_buffer_load_b32(sres[t], s_lane, g * kScaleBytes, 0);
+                sv[j][t][0] = __builtin_amdgcn_raw_buffer_load_b32(sres[t], s_lane, g * s_gstride, 0);
             }
         }
         if constexpr (kGlobalA && kNv) {

@@ -100,6 +100,12 @@ extern "C" {
  *           W4A16_ASRC_SPLITN (the last three on the MFMA path only)
  *   depth   K groups each wavefront keeps in flight (0 = the default for
  *           `tiles`: 8, 4, 2 for 1, 2, 4 tiles)
+ *   whole   with splits > 1: the number of leading column strips that one
+ *           workgroup computes whole; only the strips after them are split
+ *           `splits` ways (0: every strip is split).  A narrow matrix whose
+ *           strips outnumber the CUs by a remainder gives each CU one whole
+ *           strip and one piece of the remainder this way.  Ignored when
+ *           splits == 1.
  */
 typedef struct {
     int path;
@@ -108,6 +114,7 @@ typedef struct {
     int splits;
     int asrc;
     int depth;
+    int whole;
 } w4a16_plan_t;
 
 /* Human-readable name of a status code (static storage, never NULL). */

@@ -81,6 +81,18 @@ def test_gemm_plan_errors():
         assert _gemm(M=8, plan=p) == -8, p
 
 
+def test_remainder_split_plans_are_checked():
+    N, K = 1024, 1280                                # 64 one-tile strips, 10 groups
+    ok = w4.make_plan(w4.PATH_GEMV, 1, 4, 2, w4.ASRC_LDS, 0, 40)
+    assert w4.plan_ok(1, N, K, ok)
+    assert w4.plan_ok(1, N, K, w4.make_plan(w4.PATH_GEMV, 1, 4, 2, w4.ASRC_LDS, 0, 64))   # nothing left to split
+    assert not w4.plan_ok(1, N, K, w4.make_plan(w4.PATH_GEMV, 1, 4, 2, w4.ASRC_LDS, 0, 65))
+    assert not w4.plan_ok(1, N, K, w4.make_plan(w4.PATH_GEMV, 1, 4, 2, w4.ASRC_LDS, 0, -1))
+    # the workspace of a remainder split is that of the plain split
+    plain = w4.make_plan(w4.PATH_GEMV, 1, 4, 2, w4.ASRC_LDS)
+    assert w4.workspace_bytes(1, N, K, ok) == w4.workspace_bytes(1, N, K, plain) == 65536 + 2 * N * 4
+
+
 def test_split_plan_needs_workspace():
     p = w4.make_plan(w4.PATH_MFMA, 1, 4, splits=2)
     need = w4.workspace_bytes(8, 1024, 512, p)
@@ -172,13 +184,23 @@ def test_row_count_dispatch():
     assert w4.nvfp4_get_plan(9, 34816, 5120).asrc == w4.ASRC_SPLITN
     assert w4.nvfp4_get_plan(8, 34816, 5120).asrc == w4.ASRC_RING
     # long K with few column strips: split K (two rows and more)
-    assert w4.get_plan(1, 5120, 17408).splits == 1
-    assert w4.get_plan(4, 5120, 17408).splits == 1           # whole K of A in LDS
-    assert w4.get_plan(4, 5120, 17408).kwaves == 8
-    assert w4.get_plan(6, 5120, 17408).splits == 4
+    # the down projection (320 tiles, 136 groups) up to 8 rows: 256 whole
+    # one-tile strips and 64 strips in four K pieces, eight wavefronts
+    assert w4.get_plan(2, 5120, 17408).splits == 1           # the whole K of A in LDS
+    for M in (1, 4, 6, 8):
+        p = w4.get_plan(M, 5120, 17408)
+        assert (p.tiles, p.kwaves, p.splits, p.whole) == (1, 8, 4, 256), (M, p)
+        assert p.path == (w4.PATH_GEMV if M == 1 else w4.PATH_MFMA), (M, p)
+        assert M == 1 or p.asrc == w4.ASRC_RING, (M, p)
     assert w4.get_plan(16, 5120, 17408).splits == 1           # ring A
     assert w4.get_plan(16, 5120, 17408).asrc == w4.ASRC_RING
-    assert w4.get_plan(1, 5120, 17408).kwaves == 8
+    # the attention output (6144 x 5120) from two rows: ring A, two tiles, eight wavefronts
+    for M in range(2, 17):
+        p = w4.get_plan(M, 5120, 6144)
+        assert (p.path, p.asrc, p.tiles, p.kwaves, p.depth, p.splits) == (w4.PATH_MFMA, w4.ASRC_RING, 2, 8, 2, 1), (M, p)
+    # a K shard of it (68 groups) and the attention output (48 groups) are not split
+    assert w4.get_plan(1, 5120, 8704).splits == 1
+    assert w4.get_plan(1, 5120, 6144).splits == 1
     assert w4.get_plan(1, 248320, 5120).tiles == 2
     # tiny K: no more K waves than K groups
     assert w4.get_plan(1, 1024, 512).kwaves <= 4

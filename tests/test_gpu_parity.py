@@ -56,7 +56,7 @@ def max_err(C, Cref, Dref):
 # hold; plan_ok keeps the ones the library has kernels for (depth 0 = its default)
 ALL_PLANS = []
 for path in (w4.PATH_GEMV, w4.PATH_MFMA):
-    for t in (1, 2, 4):
+    for t in (1, 2, 4, 8):
         for kw in (1, 2, 4, 5, 8, 10, 16):
             for asrc in ((w4.ASRC_LDS,) if path == w4.PATH_GEMV
                          else (w4.ASRC_LDS, w4.ASRC_GLOBAL, w4.ASRC_RING, w4.ASRC_SPLITN)):
@@ -169,6 +169,40 @@ def test_gemm_split_k_parity_and_reuse(splits):
                 assert int(ws[:65536].view(torch.int32).abs().sum()) == 0
 
 
+@pytest.mark.parametrize("K,N,seed", [(1280, 528, 23), (17408, 48, 24), (2048, 1040, 25)])
+def test_gemm_remainder_split_parity(K, N, seed):
+    # the leading strips whole, the rest split along K: every path and A
+    # source, split counts 2 and 4, nothing / one / half / all but one /
+    # every strip whole; repeated calls are bitwise equal and leave the
+    # counters zero
+    A, qw, sc = synth.gen_problem(K, N, seed)
+    q, s, a = to_dev(qw, sc, A)
+    blob = w4.repack_weights(q, K, N)
+    Cref, Dref = oracle.gemm(A, qw, sc, 16, N, K)
+    shapes = [(w4.PATH_GEMV, 1, 8, 2, w4.ASRC_LDS), (w4.PATH_GEMV, 2, 4, 3, w4.ASRC_LDS),
+              (w4.PATH_MFMA, 1, 8, 2, w4.ASRC_RING), (w4.PATH_MFMA, 2, 4, 4, w4.ASRC_LDS),
+              (w4.PATH_MFMA, 2, 4, 4, w4.ASRC_GLOBAL), (w4.PATH_MFMA, 2, 4, 2, w4.ASRC_RING)]
+    ws = torch.zeros(65536 + 4 * 16 * N * 4, dtype=torch.uint8, device=DEV)
+    ran = 0
+    for M in (1, 3, 4, 8, 13, 16):
+        for (path, t, kw, d, asrc) in shapes:
+            nstrips = -(-(N // 16) // t)
+            for S in (2, 4):
+                for whole in sorted({0, 1, nstrips // 2, nstrips - 1, nstrips}):
+                    p = w4.make_plan(path, t, kw, S, asrc, d, whole)
+                    if not w4.plan_ok(M, N, K, p):
+                        continue
+                    C1 = run_gemm(a, blob, s, N, M, plan=p, ws=ws)
+                    C2 = run_gemm(a, blob, s, N, M, plan=p, ws=ws)
+                    e = max_err(C1, Cref[:M], Dref[:M])
+                    assert e <= TOL, (M, p, e)
+                    assert torch.equal(C1.view(torch.int16), C2.view(torch.int16)), (M, p)
+                    ran += 1
+    note(f"[remainder split] K={K} N={N}: {ran} plans")
+    assert ran > 50
+    assert int(ws[:65536].view(torch.int32).abs().sum()) == 0
+
+
 def test_split_k_workspace_shared_across_shapes():
     # one zero-filled workspace serves split calls of different M, N, splits
     # and tiles in stream order: each call's partials stay clear of the
@@ -182,7 +216,8 @@ def test_split_k_workspace_shared_across_shapes():
         cases.append((K, N, a, blob, s, Cref, Dref))
     plans = [w4.make_plan(w4.PATH_MFMA, 2, 4, 4, w4.ASRC_LDS), w4.make_plan(w4.PATH_MFMA, 4, 4, 2, w4.ASRC_GLOBAL),
              w4.make_plan(w4.PATH_GEMV, 1, 4, 8), w4.make_plan(w4.PATH_MFMA, 1, 8, 2, w4.ASRC_GLOBAL),
-             w4.make_plan(w4.PATH_MFMA, 4, 4, 2, w4.ASRC_RING), w4.make_plan(w4.PATH_MFMA, 2, 4, 4, w4.ASRC_SPLITN)]
+             w4.make_plan(w4.PATH_MFMA, 4, 4, 2, w4.ASRC_RING), w4.make_plan(w4.PATH_MFMA, 2, 4, 4, w4.ASRC_SPLITN),
+             w4.make_plan(w4.PATH_GEMV, 1, 8, 4, w4.ASRC_LDS, 2, 2), w4.make_plan(w4.PATH_MFMA, 1, 8, 2, w4.ASRC_RING, 2, 1)]
     need = max(w4.workspace_bytes(16, N, K, p) for (K, N, *_) in cases for p in plans)
     ws = torch.zeros(need, dtype=torch.uint8, device=DEV)
     for rnd in range(2):

@@ -31,7 +31,8 @@ class W4A16Error(RuntimeError):
 
 class Plan(ctypes.Structure):
     _fields_ = [("path", ctypes.c_int), ("tiles", ctypes.c_int), ("kwaves", ctypes.c_int),
-                ("splits", ctypes.c_int), ("asrc", ctypes.c_int), ("depth", ctypes.c_int)]
+                ("splits", ctypes.c_int), ("asrc", ctypes.c_int), ("depth", ctypes.c_int),
+                ("whole", ctypes.c_int)]
 
     def as_dict(self):
         return {f: getattr(self, f) for f, _ in self._fields_}
@@ -241,8 +242,8 @@ def get_plan(M: int, N: int, K: int) -> Plan:
 
 
 def make_plan(path: int, tiles: int, kwaves: int, splits: int = 1, asrc: int = ASRC_LDS,
-              depth: int = 0) -> Plan:
-    return Plan(path, tiles, kwaves, splits, asrc, depth)
+              depth: int = 0, whole: int = 0) -> Plan:
+    return Plan(path, tiles, kwaves, splits, asrc, depth, whole)
 
 
 def plan_ok(M: int, N: int, K: int, plan: Plan) -> bool:

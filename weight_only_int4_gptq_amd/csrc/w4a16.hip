@@ -23,6 +23,7 @@ using namespace w4a16;
 constexpr int kLdsBudget = 64 * 1024;    // automatic GEMV plans: at least two workgroups per CU
 constexpr int kLdsMax = 160 * 1024;      // explicit plans: gfx950's LDS per workgroup
 constexpr int kMaxVariants = 2048;       // bound on the kernel count over all tables (checked before use)
+constexpr int kPlanCUs = 256;            // CUs the plans are balanced for (MI355X)
 
 // ---------------------------------------------------------------- kernel table
 // Two instantiations of every kernel shape (w4a16_variants.hpp): plain
@@ -121,8 +122,13 @@ int check_device(int *lds_max = nullptr) {
 
 // ---------------------------------------------------------------- planning
 
+// K groups of the widest workgroup K range of a plan
+int plan_gwg(const w4a16_plan_t &p, int G) {
+    return (p.splits > 1 && p.whole == 0) ? (G + p.splits - 1) / p.splits : G;
+}
+
 int plan_lds(const w4a16_plan_t &p, int M, int G) {
-    const int Gwg = (G + p.splits - 1) / p.splits;
+    const int Gwg = plan_gwg(p, G);
     const int asrc = (p.path == W4A16_PATH_GEMV) ? ASRC_LDS : p.asrc;
     const int depth = p.depth ? p.depth : default_depth(p.tiles);
     return lds_layout(p.path, asrc, M, Gwg, p.tiles, p.kwaves, depth).total;
@@ -147,6 +153,7 @@ int validate_plan(const w4a16_plan_t &p, int M, int N, int K, int fmt = FMT_GPTQ
     if (plan_lds(p, M, G) + 256 > kLdsMax) return W4A16_ERR_PLAN;
     const long long nstrips = (N / 16 + strip_tiles(p) - 1) / strip_tiles(p);
     if (nstrips * p.splits >= (1ll << 31)) return W4A16_ERR_PLAN;
+    if (p.whole < 0 || (p.splits > 1 && p.whole > nstrips)) return W4A16_ERR_PLAN;
     if (p.splits > 1 && nstrips > W4A16_SPLIT_COUNTER_BYTES / 4) return W4A16_ERR_PLAN;
     return W4A16_OK;
 }
@@ -192,7 +199,7 @@ void auto_plan(int M, int N, int K, w4a16_plan_t *out) {
     const bool wide = NT >= 2048, vwide = NT >= 8192, deep = G >= 128;
     const bool narrow = NT <= 384;             // few strips: one tile each, more waves along K
     const bool mid = NT > 512 && NT < 2048;    // between the QKV and gate/up widths
-    w4a16_plan_t p;
+    w4a16_plan_t p{};
     p.kwaves = 4;
     p.splits = 1;
     p.asrc = W4A16_ASRC_LDS;
@@ -215,6 +222,9 @@ void auto_plan(int M, int N, int K, w4a16_plan_t *out) {
         } else if (NT <= 256 && G >= 32) {
             p.tiles = 1;
             p.depth = 4;
+        } else if (NT > 256 && G >= 32) {     // attention in and out: two tiles, shallow
+            p.tiles = 2;
+            p.depth = 2;
         } else if (G >= 16) {
             p.tiles = 1;
             p.depth = 2;
@@ -284,6 +294,37 @@ void auto_plan(int M, int N, int K, w4a16_plan_t *out) {
             p.depth = (narrow && G >= 32) ? 4 : 2;
         }
     }
+    // Narrow N above one strip per CU with 32 to 127 groups (the attention
+    // output projection, 6144 x 5120) from two rows: A through the ring,
+    // two tiles, eight wavefronts (two per SIMD), shallow rings.
+    if (M >= 2 && narrow && NT > kPlanCUs && G >= 32 && !deep) {
+        p.path = W4A16_PATH_MFMA;
+        p.asrc = W4A16_ASRC_RING;
+        p.tiles = 2;
+        p.kwaves = 8;
+        p.depth = 2;
+        p.splits = 1;
+    }
+    // Narrow N with long K, up to 8 rows: one tile per strip, eight
+    // wavefronts along K, and the strips beyond one per CU split into K
+    // pieces, so that every CU gets one whole strip and one piece
+    // (17408 x 5120: 256 whole strips and 64 strips in four pieces).  The
+    // pieces' hand-off finishes long before the whole strips do.  (Two
+    // rows keep the whole K range of A in LDS, which measures faster.)
+    if (narrow && deep && M <= 8 && M != 2 && NT > kPlanCUs && NT % kPlanCUs != 0) {
+        const int R = NT % kPlanCUs;
+        int S = 1;
+        while (S * 2 * R <= kPlanCUs && S * 2 <= G / 16) S *= 2;
+        if (S >= 2) {
+            p.path = (M == 1) ? W4A16_PATH_GEMV : W4A16_PATH_MFMA;
+            p.asrc = (M == 1) ? W4A16_ASRC_LDS : W4A16_ASRC_RING;
+            p.tiles = 1;
+            p.kwaves = 8;
+            p.depth = 2;
+            p.splits = S;
+            p.whole = NT - R;
+        }
+    }
     // short K: no more wavefronts along K than groups per workgroup
     // (split-N wavefronts split the columns)
     if (p.asrc != W4A16_ASRC_SPLITN && p.kwaves * p.splits > G) {
@@ -339,7 +380,7 @@ void auto_plan(int M, int N, int K, w4a16_plan_t *out) {
 void auto_plan_nv(int M, int N, int K, w4a16_plan_t *out) {
     const int NT = N / 16, G = K / W4A16_GROUP;
     const bool wide = NT >= 2048, vwide = NT >= 8192, deep = G >= 128, narrow = NT <= 384;
-    w4a16_plan_t p;
+    w4a16_plan_t p{};
     p.path = W4A16_PATH_MFMA;
     p.tiles = 2;
     p.kwaves = 4;
@@ -424,6 +465,10 @@ static_assert(kArgmaxBinOffset + kArgmaxBins * 16 * 8 <= W4A16_ARGMAX_WORKSPACE_
 void fuse_plan(int M, w4a16_plan_t *p, int fmt = FMT_GPTQ) {
     if (p->tiles % 2 == 0) return;
     w4a16_plan_t q = *p;
+    if (q.whole > 0) {                         // the strip count changes with the tile count
+        q.splits = 1;
+        q.whole = 0;
+    }
     if (q.asrc == W4A16_ASRC_SPLITN) {         // one-tile split-N: the ring plan of the same width
         q.asrc = W4A16_ASRC_RING;
         q.tiles = (fmt == FMT_GPTQ && M >= 9) ? 4 : 2;
@@ -444,7 +489,7 @@ void fuse_plan(int M, w4a16_plan_t *p, int fmt = FMT_GPTQ) {
 // 32) and the argmax call (the counter region alone).
 size_t workspace_any_call(int M, int N, int K, int fmt) {
     if (check_shape(M, N, K) != W4A16_OK) return 0;
-    w4a16_plan_t p;
+    w4a16_plan_t p{};
     if (fmt == FMT_NVFP4) auto_plan_nv(M, N, K, &p);
     else auto_plan(M, N, K, &p);
     size_t need = workspace_for(p, M, N);
@@ -473,7 +518,7 @@ int run_gemm(const void *A, const void *wq, const void *scales, void *C, int M, 
     if (!aligned16(A) || !aligned16(wq) || !aligned16(scales) || (fuse != 2 && !aligned16(C)))
         return W4A16_ERR_ALIGN;
     if (fuse == 2 && (((uintptr_t)idx | (uintptr_t)val) & 3)) return W4A16_ERR_ALIGN;
-    w4a16_plan_t p;
+    w4a16_plan_t p{};
     if (user) {
         p = *user;
         st = validate_plan(p, M, N, K, fmt);
@@ -533,7 +578,8 @@ int run_gemm(const void *A, const void *wq, const void *scales, void *C, int M, 
     while ((1 << a.Slog2) < a.S) ++a.Slog2;
     a.NT = N / 16;
     a.nstrips = (int)((a.NT + strip_tiles(p) - 1) / strip_tiles(p));
-    a.nunits = a.nstrips * a.S;
+    a.nwhole = a.S > 1 ? p.whole : 0;
+    a.nunits = a.nwhole + (a.nstrips - a.nwhole) * a.S;
     a.fuse = fuse;
     a.amax_idx = idx;
     a.amax_val = val;
@@ -619,7 +665,7 @@ int w4a16_check_plan(int M, int N, int K, const w4a16_plan_t *plan) {
 
 size_t w4a16_workspace_bytes_plan(int M, int N, int K, const w4a16_plan_t *plan) {
     if (check_shape(M, N, K) != W4A16_OK) return 0;
-    w4a16_plan_t p;
+    w4a16_plan_t p{};
     if (plan) {
         p = *plan;
         if (validate_plan(p, M, N, K) != W4A16_OK) return 0;
@@ -787,7 +833,7 @@ int w4a16_nvfp4_check_plan(int M, int N, int K, const w4a16_plan_t *plan) {
 
 size_t w4a16_nvfp4_workspace_bytes_plan(int M, int N, int K, const w4a16_plan_t *plan) {
     if (check_shape(M, N, K) != W4A16_OK) return 0;
-    w4a16_plan_t p;
+    w4a16_plan_t p{};
     if (plan) {
         p = *plan;
         if (validate_plan(p, M, N, K, FMT_NVFP4) != W4A16_OK) return 0;

@@ -72,11 +72,13 @@ struct GemmArgs {
     float *part;             // split-K partials [S][M][N] (S > 1 only)
     uint32_t *count;         // split-K arrival counters [nstrips] (S > 1 only)
     int M, N, K, G;          // G = K / 128
-    int S;                   // workgroups along K per column strip (a power of two)
+    int S;                   // workgroups along K per split column strip (a power of two)
     int Slog2;               // log2(S)
     int NT;                  // 16-column tiles = N / 16
     int nstrips;             // column strips = ceil(NT / tiles)
-    int nunits;              // nstrips * S = grid size
+    int nwhole;              // strips 0 .. nwhole-1 are computed whole by one workgroup each;
+                             // the others are split S ways along K
+    int nunits;              // nwhole + (nstrips - nwhole) * S = grid size
     int fuse;                // epilogue: 0 plain C, 1 gate/up activation, 2 row argmax,
                              // 3 C as fp32 (unrounded partial sums of a K shard)
     int *amax_idx;           // row argmax: column of each row's maximum [M]
@@ -575,9 +577,20 @@ __global__ void __launch_bounds__(64 * KW) gemm_kernel(GemmArgs p) {
     const int c = lane & 15, h = lane >> 4;
     const int arow_m = min(c, M - 1);   // MFMA A-operand row of this lane
 
-    const int u = xcd_unit(blockIdx.x, p.nunits);
-    const int strip = u >> p.Slog2, z = u & (p.S - 1);
-    const int gw0 = (p.G * z) >> p.Slog2, gw1 = (p.G * (z + 1)) >> p.Slog2;
+    // Work unit of this workgroup.  Units below nwhole are whole strips; the
+    // others are the S pieces (contiguous K ranges) of the remaining strips.
+    // With whole strips the units keep launch order, so the hardware's
+    // round-robin placement gives each CU one whole strip and one piece of
+    // the remainder; with every strip split, each XCD gets one contiguous
+    // range of units, so the pieces of a strip meet in one L2.
+    const int u = p.nwhole > 0 ? (int)blockIdx.x : xcd_unit(blockIdx.x, p.nunits);
+    const bool whole = u < p.nwhole;
+    const bool split = !whole && p.S > 1;                     // this workgroup writes a partial sum
+    const int ur = u - p.nwhole;
+    const int strip = whole ? u : p.nwhole + (ur >> p.Slog2);
+    const int z = whole ? 0 : (ur & (p.S - 1));
+    const int slog2 = whole ? 0 : p.Slog2;
+    const int gw0 = (p.G * z) >> slog2, gw1 = (p.G * (z + 1)) >> slog2;
     const int Gwg = gw1 - gw0;
     const int gk0 = kSplitN ? gw0 : gw0 + (Gwg * wave) / KW;
     const int gk1 = kSplitN ? gw1 : gw0 + (Gwg * (wave + 1)) / KW;
@@ -634,18 +647,21 @@ __global__ void __launch_bounds__(64 * KW) gemm_kernel(GemmArgs p) {
     const __amdgpu_buffer_rsrc_t ares = buffer_rsrc(p.A, (uint32_t)M * (uint32_t)p.K * 2u);
     const uint32_t a_lane = ((uint32_t)arow_m * (uint32_t)p.K + (uint32_t)h * (kNv ? 4u : 32u)) * 2u;
 
-    // ---- 1. asynchronous LDS fill of this workgroup's K range of A
+    // ---- 1. asynchronous LDS fill of this wavefront's own K range of A
+    // (all M rows), at its place in the workgroup's staged rows.  Each
+    // wavefront reads only the A it fills itself, so no workgroup barrier
+    // stands between the fill and the first group.
     if constexpr (kStage) {
-        const int rowbytes = Gwg * kGroup * 2;
-        const int chunks_per_row = (rowbytes + 1023) >> 10;
+        const int start = (gk0 - gw0) * kGroup * 2;          // byte offset of the range in a row
+        const int bytes = ng * kGroup * 2;
         for (int m = 0; m < M; ++m)
-            for (int q = wave; q < chunks_per_row; q += KW) {
+            for (int q = 0; (q << 10) < bytes; ++q) {
                 const int off = (q << 10) + lane * 16;
                 const uint32_t dst =
-                    __builtin_amdgcn_readfirstlane(lds_addr(smem + L.a + m * L.row + (q << 10)));
-                if (off < rowbytes) {
+                    __builtin_amdgcn_readfirstlane(lds_addr(smem + L.a + m * L.row + start + (q << 10)));
+                if (off < bytes) {
                     const uint8_t *src = reinterpret_cast<const uint8_t *>(p.A + (size_t)m * p.K +
-                                                                           (size_t)gw0 * kGroup) + off;
+                                                                           (size_t)gk0 * kGroup) + off;
                     lds_dma16(src, dst);
                 }
             }
@@ -738,22 +754,22 @@ __global__ void __launch_bounds__(64 * KW) gemm_kernel(GemmArgs p) {
         }(std::make_integer_sequence<int, D>{});
     }
 
-    // ---- 3. A is in LDS once every wavefront's fill has landed; then the
-    //         bias of every group, formed once per workgroup
+    // ---- 3. this wavefront's A is in LDS once its own fill has landed; then
+    //         the bias of each of its groups, formed by the wavefront itself
     if constexpr (kStage) {
         // this wavefront's fill is older than its ring loads (ng == 0: no ring)
         if (ng > 0)
             __builtin_amdgcn_s_waitcnt(waitcnt_vm(D * kLoadsPerGroup));
         else
             __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
-        __builtin_amdgcn_s_barrier();
         float *bias = reinterpret_cast<float *>(smem + L.bias);
+        const int gl0 = gk0 - gw0, gl1 = gk1 - gw0;          // own groups, relative to the range
         if constexpr (kNv) {
             // exact signed weights: no bias
         } else if constexpr (PATH == PATH_GEMV) {
             // each 32-row quarter: the GEMV lane's dot2 chain with every code 8
             for (int m = 0; m < M; ++m)
-            for (int rem = threadIdx.x; rem < Gwg * 4; rem += 64 * KW) {
+            for (int rem = gl0 * 4 + lane; rem < gl1 * 4; rem += 64) {
                 const int b = m * Gwg * 4 + rem;
                 const u32x4 *src = reinterpret_cast<const u32x4 *>(smem + L.a + m * L.row + rem * 64);
                 float s = 0.0f;
@@ -774,11 +790,11 @@ __global__ void __launch_bounds__(64 * KW) gemm_kernel(GemmArgs p) {
             // skips the store.
             const u32x4 bconst = {kBiasPair, kBiasPair, kBiasPair, kBiasPair};
             constexpr int kB = 4;
-            for (int gb = wave; gb < Gwg; gb += kB * KW) {
+            for (int gb = gl0; gb < gl1; gb += kB) {
                 u32x4 a[kB][4];
 #pragma unroll
                 for (int i = 0; i < kB; ++i) {
-                    const int gl = min(gb + i * KW, Gwg - 1);
+                    const int gl = min(gb + i, gl1 - 1);
                     const uint8_t *arow = smem + L.a + arow_m * L.row + (gl * kGroup + h * 32) * 2;
 #pragma unroll
                     for (int r = 0; r < 4; ++r) a[i][r] = reinterpret_cast<const u32x4 *>(arow)[r];
@@ -792,12 +808,16 @@ __global__ void __launch_bounds__(64 * KW) gemm_kernel(GemmArgs p) {
                     for (int i = 0; i < kB; ++i) Q[i] = mfma16x16x32(a[i][r], bconst, Q[i]);
 #pragma unroll
                 for (int i = 0; i < kB; ++i) {
-                    const int gl = gb + i * KW;
-                    if (c == 0 && gl < Gwg) reinterpret_cast<f32x4 *>(bias)[gl * 4 + h] = Q[i];
+                    const int gl = gb + i;
+                    if (c == 0 && gl < gl1) reinterpret_cast<f32x4 *>(bias)[gl * 4 + h] = Q[i];
                 }
             }
         }
-        lds_barrier();
+        // the wavefront's own LDS writes precede its reads (LDS operations of
+        // one wavefront complete in order); keep the compiler from moving
+        // the reads above the writes
+        __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+        asm volatile("" ::: "memory");
     }
 
     // ---- 4. main loop over this wavefront's groups
@@ -1070,13 +1090,13 @@ __global__ void __launch_bounds__(64 * KW) gemm_kernel(GemmArgs p) {
                                                    __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
             }
         } else if (holder) {
-            if (p.S > 1 || fuse != 1) {
+            if (split || fuse != 1) {
 #pragma unroll
                 for (int t = 0; t < T; ++t)
 #pragma unroll
                     for (int i = 0; i < kRows; ++i)
                         if (row_of(i) < M && tile_ok(t)) {
-                            if (p.S > 1) emit_part(t, row_of(i), c, row_val(t, i));
+                            if (split) emit_part(t, row_of(i), c, row_val(t, i));
                             else emit_c(t, row_of(i), c, row_val(t, i));
                         }
             } else {
@@ -1123,13 +1143,13 @@ __global__ void __launch_bounds__(64 * KW) gemm_kernel(GemmArgs p) {
                     __hip_atomic_fetch_max(&keys[mc >> 4], argmax_key(fin(reduced(t, mc)), (uint32_t)col_of(t, mc & 15)),
                                            __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
                 }
-        } else if (p.S > 1 || fuse != 1) {
+        } else if (split || fuse != 1) {
 #pragma unroll
             for (int t = 0; t < T; ++t)
                 for (int mc = threadIdx.x; mc < M * 16; mc += 64 * KW) {
                     if (!tile_ok(t)) continue;
                     const float s = reduced(t, mc);
-                    if (p.S > 1) emit_part(t, mc >> 4, mc & 15, s);
+                    if (split) emit_part(t, mc >> 4, mc & 15, s);
                     else emit_c(t, mc >> 4, mc & 15, s);
                 }
         } else {
@@ -1158,7 +1178,7 @@ __global__ void __launch_bounds__(64 * KW) gemm_kernel(GemmArgs p) {
         return;
     }
 
-    if (p.S > 1) {
+    if (split) {
         // Hand-off between the S workgroups of a strip without flushing any
         // L2: partials go out with device-coherent stores, every thread waits
         // for its own stores to complete, then one counter increment per

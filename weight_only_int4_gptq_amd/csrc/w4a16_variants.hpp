@@ -24,7 +24,7 @@ struct Variant {
 #define W4A16_RINGS(X, P, MM, AS) \
     X(P, MM, 1, 4, 4, AS) X(P, MM, 1, 8, 4, AS) X(P, MM, 2, 4, 2, AS) X(P, MM, 2, 4, 4, AS) \
     X(P, MM, 4, 4, 2, AS) X(P, MM, 4, 2, 2, AS) X(P, MM, 4, 4, 4, AS) X(P, MM, 8, 1, 4, AS) \
-    X(P, MM, 8, 2, 2, AS) X(P, MM, 8, 4, 2, AS)
+    X(P, MM, 8, 2, 2, AS) X(P, MM, 8, 4, 2, AS) X(P, MM, 1, 8, 2, AS) X(P, MM, 2, 8, 2, AS)
 
 // eight-tile strips: A read once per eight tiles (matrix-core paths)
 #define W4A16_WIDE(X, P, MM, AS) \

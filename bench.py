@@ -1,18 +1,22 @@
 """Benchmark of the W4A16 decode/verify matmul on one MI355X.
 
-Default run: the QKV-shaped decode call (M=1, K=5120, N=8192, group 128,
-synthetic inputs with the distributions of the 27B workloads), repeated
---steps times inside one HIP graph replay.  The weight blob, scales,
-activations and outputs rotate over enough distinct buffer sets (>= 1 GiB in
-total) that no call finds its weights in the 256 MiB last-level cache: every
-call streams its weights from HBM.
+Default run: the down projection of the 27B decoder (K=17408, N=5120, group
+128, A drawn as SiLU(x)*y) at the metric's row counts M = 1, 4, 8, 16, each
+timed as `--steps` calls inside one HIP graph replay.  The weight blob,
+scales, activations and outputs rotate over distinct buffer sets (>= 1 GiB in
+total) so that no call finds its weights in the 256 MiB last-level cache:
+every call streams its weights from HBM.  One step is one call at each M.
 
 Prints ONE JSON line:
-  value        algorithmic bytes per call / (graph replay time / steps), GB/s
-  roofline     the same per-launch duration (timed region / steps, one kernel
-               launch per step) against MI355X's 8 TB/s
-  cpu_baseline the fp64 CPU oracle on the same workload (rank 0 only)
+  value        algorithmic bytes of one step / its summed call times, GB/s
+  config       per-M us/call, GB/s, % of 8 TB/s, plan; MFMA utilisation at
+               M=16; extras: the other decoder shapes (QKV, attention out,
+               gate/up, lm_head) and the 257-call decode step at M=1 and 8
+  roofline     the same rates against MI355X's 8 TB/s, per M and for the step;
+               traffic = HBM bytes per launch from the rocprofv3 counters
+  cpu_baseline the fp64 CPU oracle on the same workload (M=1)
 
+--workload W --m M times one call shape (the profiled runs use these);
 --sweep prints one JSON line per (workload, M) instead (not the contract line);
 --stack times one decode step's full sequence of linear shapes.
 --ceiling measures a plain streaming read at the same byte counts.
@@ -38,6 +42,9 @@ import synth  # noqa: E402
 METRIC = "achieved HBM GB/s (% of peak) for W4A16 matmul at M=1,4,8,16; µs/call"
 METRIC_NVFP4 = "achieved HBM GB/s (% of peak) for the NVFP4 weight-only (W4A16) matmul; µs/call"
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
+# row counts of the headline line per workload: the metric's set (M = 1, 4, 8, 16)
+HEADLINE_MS = {"down": (1, 4, 8, 16), "qkv": (1, 4, 8, 16), "attn_out": (1, 4, 8, 16), "gate_up": (1, 4, 8, 16),
+               "lm_head": (1, 8, 16), "tiny": (1,)}
 PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 LLC_BYTES = 256 << 20          # MI355X Infinity Cache
 ROTATE_BYTES = 1 << 30         # rotate over >= 1 GiB of buffer sets
@@ -140,8 +147,14 @@ def sets_for(K, N, M):
     return max(1, -(-ROTATE_BYTES // per)) if per < 4 * LLC_BYTES else 1
 
 
-def time_graph(torch, fn, steps, warmup):
-    """Warm up eagerly, capture `steps` calls in one graph, replay and time it (ms/step)."""
+def time_graph(torch, fn, steps, warmup, sets=0):
+    """Warm up eagerly, capture `steps` calls in one graph, replay and time it (ms/step).
+
+    fn(i) makes call i (on buffer set i % sets when the caller rotates).  With
+    fewer steps than sets, calls on the remaining sets run eagerly between the
+    warm and the timed replay, so that every timed call's buffers were last
+    touched (sets - 1) calls earlier, whatever `steps` is.
+    """
     for i in range(warmup):
         fn(i)
     torch.cuda.synchronize()
@@ -154,6 +167,8 @@ def time_graph(torch, fn, steps, warmup):
                 fn(i)
     torch.cuda.synchronize()
     g.replay()                      # warm replay
+    for i in range(steps, sets):    # the other buffer sets, untimed
+        fn(i)
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
@@ -172,7 +187,7 @@ def graph_steps(args, nbytes):
 
 
 def measure(torch, w4, prob, M, steps, warmup):
-    ms_graph = time_graph(torch, lambda i: prob.call(w4, M, i), steps, warmup)
+    ms_graph = time_graph(torch, lambda i: prob.call(w4, M, i), steps, warmup, prob.sets)
     nbytes = prob.bytes(M)
     flops = 2.0 * M * prob.N * prob.K
     return {
@@ -299,22 +314,37 @@ def summarize_profiles(args):
     rows = [r for r in _csv_rows(os.path.join(trace_dir, "run_kernel_trace.csv")) if "gemm_kernel" in r["Kernel_Name"]]
     d = [int(r["End_Timestamp"]) - int(r["Start_Timestamp"]) for r in rows]
     stats = _csv_rows(os.path.join(trace_dir, "run_kernel_stats.csv"))
+    sets = sets_for(wl.K, wl.N, 1)
+    flush = max(0, sets - args.steps)            # untimed calls on the other buffer sets
+    w = args.warmup
+    a = w + args.steps                           # warm replay [w, a)
+    b = a + flush                                # the other sets [a, b), eager
+    e = b + args.steps                           # timed replay [b, e)
+    timed = st.mean(d[b:e]) if len(d) >= e else None
     with open(os.path.join(ROOT, "profiles", f"gemm_kernel_{tag}_kernel_trace.md"), "w") as f:
-        what = f"NVFP4 weights, M={M}" if nv else f"M={M} (the default bench run)"
+        what = f"NVFP4 weights, M={M}" if nv else f"M={M}"
         f.write(f"# Kernel trace: {wl.desc}, {what}\n\n")
-        extra = f" --workload {wname} --m {M}{fmt_flag}" if (nv or wname != "qkv" or M != 1) else ""
         f.write(f"Command (repo root, TMPDIR=/tmp):\n\n    rocprofv3 --kernel-trace --stats -d {trace_dir} "
-                f"-o run --output-format csv -- python3 bench.py{extra}\n\n")
+                f"-o run --output-format csv -- python3 bench.py --workload {wname} --m {M}{fmt_flag} "
+                f"--steps {args.steps} --warmup {args.warmup} --no-cpu\n\n")
         f.write("rocprofv3 --stats summary (run_kernel_stats.csv):\n\n| kernel | calls | average ns | min ns | max ns |\n|---|---|---|---|---|\n")
         for r in stats:
             f.write(f"| {r['Name'][:90]} | {r['Calls']} | {float(r['AverageNs']):.0f} | {r['MinNs']} | {r['MaxNs']} |\n")
-        if len(d) >= args.warmup + 2 * args.steps:
-            w, a, b = args.warmup, args.warmup + args.steps, args.warmup + 2 * args.steps
+        if timed is not None:
             f.write(f"\nMatmul kernel by phase: {w} eager warm-up launches average {st.mean(d[:w]):.0f} ns; "
                     f"warm graph replay average {st.mean(d[w:a]):.0f} ns; timed graph replay average "
-                    f"{st.mean(d[a:b]):.0f} ns over {args.steps} launches.\n")
+                    f"{timed:.0f} ns over {args.steps} launches ({timed and synth_bytes(nv, M, wl) / timed:.1f} GB/s, "
+                    f"{100 * synth_bytes(nv, M, wl) / timed / PEAK_HBM_GBS:.2f}% of 8 TB/s).\n")
         f.write(f"Kernel source hash: {kernel_source_hash()}\n")
+    rec[tag]["trace_timed_avg_ns"] = round(timed) if timed is not None else None
+    with open(path, "w") as f:
+        json.dump(rec, f, indent=1, sort_keys=True)
+        f.write("\n")
     print(json.dumps(rec[tag]))
+
+
+def synth_bytes(nv, M, wl):
+    return (synth.algorithmic_bytes_nvfp4 if nv else synth.algorithmic_bytes)(M, wl.N, wl.K)
 
 
 def main():
@@ -322,8 +352,11 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=400)
     ap.add_argument("--warmup", type=int, default=50)
-    ap.add_argument("--workload", default="qkv", choices=sorted(synth.WORKLOADS))
-    ap.add_argument("--m", type=int, default=1)
+    ap.add_argument("--workload", default="down", choices=sorted(synth.WORKLOADS))
+    ap.add_argument("--m", type=int, default=0,
+                    help="one row count (default: the metric's set for the workload, M = 1, 4, 8, 16 for down)")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="skip the further keys (other decoder shapes, the full decode step)")
     ap.add_argument("--format", default="gptq", choices=("gptq", "nvfp4"),
                     help="weight format of the measured call (gptq: the headline INT4 group-128 path)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
@@ -367,60 +400,102 @@ def main():
         return tp_shards(torch, w4, args)
 
     wl = synth.WORKLOADS[args.workload]
-    M = args.m
-    sets = sets_for(wl.K, wl.N, M)
     nv = args.format == "nvfp4"
-    log(f"bench: {wl.desc} M={M} ({args.format}) on {name}; {sets} buffer sets")
+    Ms = [args.m] if args.m else list(HEADLINE_MS.get(args.workload, (1,)))
+    sets = sets_for(wl.K, wl.N, 1)
+    log(f"bench: {wl.desc} M={Ms} ({args.format}) on {name}; {sets} buffer sets")
     if nv:
         prob = NvProblem(torch, w4, wl.K, wl.N, wl.seed + synth.NVFP4_SEED_OFFSET, wl.act, sets)
     else:
         prob = Problem(torch, w4, wl.K, wl.N, wl.seed, wl.act, sets)
-    r = measure(torch, w4, prob, M, args.steps, args.warmup)
-    plan = (w4.nvfp4_get_plan if nv else w4.get_plan)(M, wl.N, wl.K).as_dict()
-    tag = f"{'nvfp4_' if nv else ''}{args.workload}_m{M}"
-    log(f"bench: {r['us_per_call']:.3f} us/call {r['gbs']:.0f} GB/s; plan {plan}")
+    per_m, total_bytes, total_ms = [], 0, 0.0
+    for M in Ms:
+        r = measure(torch, w4, prob, M, args.steps, args.warmup)
+        plan = (w4.nvfp4_get_plan if nv else w4.get_plan)(M, wl.N, wl.K).as_dict()
+        tag = f"{'nvfp4_' if nv else ''}{args.workload}_m{M}"
+        log(f"bench: M={M} {r['us_per_call']:.3f} us/call {r['gbs']:.0f} GB/s; plan {plan}")
+        entry = {"M": M, "us_per_call": round(r["us_per_call"], 3), "GBps": round(r["gbs"], 1),
+                 "pct_of_peak_hbm": round(100 * r["gbs"] / PEAK_HBM_GBS, 2),
+                 "frac": round(r["gbs"] / PEAK_HBM_GBS, 4), "algorithmic_bytes": r["bytes"],
+                 "traffic": traffic_record(tag), "plan": plan}
+        if M == 16:
+            entry["mfma_util"] = round(r["tflops"] / PEAK_BF16_TFLOPS, 4)
+        per_m.append(entry)
+        total_bytes += r["bytes"]
+        total_ms += r["ms_per_step"]
     if args.copy_calib:
         copy_calibration(torch, args.copy_calib)
 
-    # one launch per step: the per-launch duration is the timed region / steps
-    roof = {"bound": "hbm", "achieved": round(r["gbs"], 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-            "frac": round(r["gbs"] / PEAK_HBM_GBS, 4),
-            "traffic": traffic_record(tag)}
+    # one step = one call at each of the M values, one kernel launch each; the
+    # headline rate is the bytes of the step over its summed call times
+    gbs = total_bytes / (total_ms * 1e-3) / 1e9
+    traffics = [e["traffic"] for e in per_m]
+    roof = {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+            "frac": round(gbs / PEAK_HBM_GBS, 4),
+            "traffic": (sum(traffics) if all(t is not None for t in traffics) else None),
+            "algorithmic_bytes": total_bytes,
+            "per_m": [{"M": e["M"], "achieved": e["GBps"], "frac": e["frac"], "traffic": e["traffic"],
+                       "algorithmic_bytes": e["algorithmic_bytes"], "us_per_launch": e["us_per_call"]}
+                      for e in per_m]}
+    what = (f"{args.workload}: {wl.desc}, M in {{{','.join(map(str, Ms))}}}, "
+            + ("NVFP4 weights (E2M1, E4M3 scale per 16)" if nv else "group 128"))
     out = {
         "metric": METRIC_NVFP4 if nv else METRIC,
-        "value": round(r["gbs"], 1),
+        "value": round(gbs, 1),
         "unit": "GB/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(r["ms_per_step"], 6),
+        "ms_per_step": round(total_ms, 6),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
         "config": {
-            "workload": (f"{args.workload}: {wl.desc}, M={M}, NVFP4 weights (E2M1, E4M3 scale per 16)"
-                         if nv else f"{args.workload}: {wl.desc}, M={M}, group 128"),
-            "M": M, "K": wl.K, "N": wl.N, "group": 16 if nv else 128,
-            "us_per_call": round(r["us_per_call"], 3),
-            "pct_of_peak_hbm": round(100 * r["gbs"] / PEAK_HBM_GBS, 2),
-            "algorithmic_bytes_per_call": r["bytes"],
+            "workload": what,
+            "K": wl.K, "N": wl.N, "group": 16 if nv else 128, "Ms": Ms,
+            "step": "one call at each M (one kernel launch each); value = bytes of the step / summed call times",
+            "per_m": per_m,
             "buffer_sets": sets,
-            "plan": plan,
-            "timing": "HIP events around one graph replay of `steps` dependent calls on the launch stream",
+            "timing": ("per M: HIP events around one graph replay of `steps` calls on the launch stream, "
+                       "call i on buffer set i % buffer_sets, every set last touched >= 1 GiB of weights earlier"),
             "device": name,
         },
         "roofline": roof,
     }
-    if M == 16:
-        out["config"]["mfma_util"] = round(r["tflops"] / PEAK_BF16_TFLOPS, 4)
     if not args.no_cpu:
         log("bench: timing the CPU oracle ...")
-        out["cpu_baseline"] = cpu_baseline(prob, M, args.cpu_seconds)
+        out["cpu_baseline"] = cpu_baseline(prob, Ms[0], args.cpu_seconds)
     else:
         out["cpu_baseline"] = None
+    del prob
+    torch.cuda.empty_cache()
+    if not args.no_extras and not nv and args.m == 0 and args.workload == "down":
+        out["config"]["extras"] = extras(torch, w4, args)
     print(json.dumps(out), flush=True)
+
+
+def extras(torch, w4, args):
+    """Further keys of the default line: the other decoder shapes and the
+    full decode step, each timed the same way (graph replay, rotating sets)."""
+    res = {}
+    for wname, Ms in (("qkv", (1, 4, 8, 16)), ("attn_out", (1, 8)), ("gate_up", (1, 8)), ("lm_head", (1, 8, 16))):
+        wl = synth.WORKLOADS[wname]
+        sets = sets_for(wl.K, wl.N, 1)
+        prob = Problem(torch, w4, wl.K, wl.N, wl.seed, wl.act, sets)
+        for M in Ms:
+            steps = graph_steps(args, prob.bytes(M))
+            r = measure(torch, w4, prob, M, steps, min(args.warmup, 10))
+            res[f"{wname}_m{M}"] = {"K": wl.K, "N": wl.N, "us_per_call": round(r["us_per_call"], 3),
+                                    "GBps": round(r["gbs"], 1), "pct_of_peak_hbm": round(100 * r["gbs"] / PEAK_HBM_GBS, 2)}
+            log(f"bench: {wname} M={M} {r['us_per_call']:.3f} us/call {r['gbs']:.0f} GB/s")
+        del prob
+        torch.cuda.empty_cache()
+    for rec in stack(torch, w4, args, quiet=True):
+        res[f"stack_m{rec['M']}"] = {k: rec[k] for k in ("calls", "bytes", "ms_per_step", "GBps", "pct_peak")}
+        log(f"bench: stack M={rec['M']} {rec['ms_per_step']:.3f} ms {rec['GBps']:.0f} GB/s")
+    return res
 
 
 def nvfp4_sweep(torch, w4, args):
@@ -570,38 +645,45 @@ def tp_shards(torch, w4, args):
             torch.cuda.empty_cache()
 
 
-def stack(torch, w4, args):
-    """One decode step: 64 layers x (attn-in, attn-out, gate/up, down) + lm_head, all resident."""
-    dev = torch.device("cuda:0")
+def stack(torch, w4, args, quiet=False):
+    """One decode step: 64 layers x (attn-in, attn-out, gate/up, down) + lm_head, all resident.
+
+    Every layer has its own weights (11.9 GB in all, far beyond the 256 MiB
+    last-level cache); one step is the 257 calls in order, at M = 1 and 8.
+    Returns one record per M (and prints it unless quiet).
+    """
+    probs = {}
+    for (K, N) in set(synth.STACK_LAYER_SHAPES) | {synth.LM_HEAD_SHAPE}:
+        probs[(K, N)] = Problem(torch, w4, K, N, K + N, "normal", 1)
+    layers = []
+    for li in range(synth.STACK_LAYERS):
+        for (K, N) in synth.STACK_LAYER_SHAPES:
+            p = probs[(K, N)]
+            blob = p.blobs[0] if li == 0 else p.blobs[0].clone()
+            sc = p.scales[0] if li == 0 else p.scales[0].clone()
+            layers.append((K, N, blob, sc, p.acts[0], p.outs[0]))
+    K, N = synth.LM_HEAD_SHAPE
+    p = probs[(K, N)]
+    layers.append((K, N, p.blobs[0], p.scales[0], p.acts[0], p.outs[0]))
+    recs = []
     for M in (1, 8):
-        probs = {}
-        for (K, N) in set(synth.STACK_LAYER_SHAPES) | {synth.LM_HEAD_SHAPE}:
-            probs[(K, N)] = Problem(torch, w4, K, N, K + N, "normal", 1)
-        # every layer gets its own weights: 64 copies of each layer shape
-        layers = []
-        for li in range(synth.STACK_LAYERS):
-            for (K, N) in synth.STACK_LAYER_SHAPES:
-                p = probs[(K, N)]
-                blob = p.blobs[0] if li == 0 else p.blobs[0].clone()
-                sc = p.scales[0] if li == 0 else p.scales[0].clone()
-                layers.append((K, N, blob, sc, p.acts[0], p.outs[0]))
-        K, N = synth.LM_HEAD_SHAPE
-        p = probs[(K, N)]
-        layers.append((K, N, p.blobs[0], p.scales[0], p.acts[0], p.outs[0]))
         total = sum(synth.algorithmic_bytes(M, N, K) for (K, N, *_ ) in layers)
 
-        def step(_i):
+        def step(_i, M=M):
             for (K, N, blob, sc, a, o) in layers:
                 w4.gemm(a[:M], blob, sc, N, out=o[:M])
 
         ms = time_graph(torch, step, 3, 2)
-        print(json.dumps({"stack": "64 layers x 4 linear shapes + lm_head", "M": M, "calls": len(layers),
-                          "bytes": total, "ms_per_step": round(ms, 4),
-                          "GBps": round(total / (ms * 1e-3) / 1e9, 1),
-                          "pct_peak": round(100 * total / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 2)}), flush=True)
-        del layers, probs, p
-        torch.cuda.empty_cache()
-    _ = dev
+        rec = {"stack": "64 layers x 4 linear shapes + lm_head", "M": M, "calls": len(layers),
+               "bytes": total, "ms_per_step": round(ms, 4),
+               "GBps": round(total / (ms * 1e-3) / 1e9, 1),
+               "pct_peak": round(100 * total / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 2)}
+        recs.append(rec)
+        if not quiet:
+            print(json.dumps(rec), flush=True)
+    del layers, probs, p
+    torch.cuda.empty_cache()
+    return recs
 
 
 if __name__ == "__main__":

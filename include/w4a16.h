@@ -214,6 +214,25 @@ int w4a16_gemm_plan(const void *A, const void *wq_repacked, const void *scales, 
                     const w4a16_plan_t *plan, void *stream);
 
 /*
+ * Allocation-free form of w4a16_gemm_plan (plan == NULL: the plan w4a16_gemm
+ * chooses), for callers that cannot allocate device memory: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid allocation.
+ * Instead of a caller's workspace, the split-K counters and partials live in
+ * a static device array of W4A16_NOALLOC_SCRATCH_BYTES that each GPU the
+ * library runs on holds until the process ends.  The call allocates and
+ * frees nothing.  Its first call on a GPU finds the array's address and
+ * clears its counter region with a kernel on `stream`; every call leaves the
+ * counters zero.  All calls on one GPU share the one array, so calls that
+ * overlap in time on one GPU (different streams, concurrent graph replays)
+ * race and must not be issued.  A plan whose workspace would exceed the
+ * array returns W4A16_ERR_WORKSPACE; other arguments and errors as
+ * w4a16_gemm_plan.
+ */
+#define W4A16_NOALLOC_SCRATCH_BYTES (W4A16_SPLIT_COUNTER_BYTES + (4 << 20))
+int w4a16_gemm_noalloc(const void *A, const void *wq_repacked, const void *scales, void *C,
+                       int M, int N, int K, int group, const w4a16_plan_t *plan, void *stream);
+
+/*
  * Gate/up matmul with the MLP activation in its epilogue:
  *
  *     C = A . dequant(blob, scales)              (C[M][N], never stored)

@@ -11,6 +11,7 @@
 #include <atomic>
 #include <cstdint>
 #include <cstring>
+#include <mutex>
 
 #include "w4a16.h"
 #include "w4a16_kernels.hpp"
@@ -605,6 +606,49 @@ int run_gemm(const void *A, const void *wq, const void *scales, void *C, int M, 
     return e == hipSuccess ? W4A16_OK : W4A16_ERR_LAUNCH;
 }
 
+// ---------------------------------------------------------------- allocation-free calls
+// The workspace of w4a16_gemm_noalloc: a static device array, one copy per
+// GPU the library runs on, held until the process ends.  Host code never
+// passes the array's name to a kernel (on the host it is only a stand-in
+// for the symbol); it passes the device address found for the current GPU.
+__device__ __align__(256) uint8_t scratch[W4A16_NOALLOC_SCRATCH_BYTES];
+
+__global__ void __launch_bounds__(256) clear_words_kernel(uint32_t *__restrict__ p, int n) {
+    const int i = (int)blockIdx.x * 256 + (int)threadIdx.x;
+    if (i < n) p[i] = 0u;
+}
+
+// The scratch array's address on the current device.  The first call on a
+// device looks it up with that device current and clears the counter region
+// with a kernel on `stream` (calls leave that region zero after that).
+void *scratch_for_device(hipStream_t stream, int *status) {
+    static std::mutex mu;
+    static void *addr[64];
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) {
+        *status = W4A16_ERR_DEVICE;
+        return nullptr;
+    }
+    std::lock_guard<std::mutex> lock(mu);
+    if (!addr[dev]) {
+        void *p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) {
+            *status = W4A16_ERR_DEVICE;
+            return nullptr;
+        }
+        const int n = W4A16_SPLIT_COUNTER_BYTES / 4;
+        hipLaunchKernelGGL(clear_words_kernel, dim3((n + 255) / 256), dim3(256), 0, stream,
+                           static_cast<uint32_t *>(p), n);
+        if (hipGetLastError() != hipSuccess) {
+            *status = W4A16_ERR_LAUNCH;
+            return nullptr;
+        }
+        addr[dev] = p;
+    }
+    *status = W4A16_OK;
+    return addr[dev];
+}
+
 }  // namespace
 
 extern "C" {
@@ -690,6 +734,31 @@ int w4a16_gemm_plan(const void *A, const void *wq_repacked, const void *scales, 
                     const w4a16_plan_t *plan, void *stream) {
     return run_gemm(A, wq_repacked, scales, C, M, N, K, group, workspace, workspace_bytes, plan,
                     stream);
+}
+
+int w4a16_gemm_noalloc(const void *A, const void *wq_repacked, const void *scales, void *C, int M,
+                       int N, int K, int group, const w4a16_plan_t *plan, void *stream) {
+    // every check that needs no device comes first, so a rejected call
+    // touches neither the device nor the scratch array
+    if (!A || !wq_repacked || !scales || !C) return W4A16_ERR_NULL;
+    int st = check_shape(M, N, K);
+    if (st != W4A16_OK) return st;
+    if (group != W4A16_GROUP) return W4A16_ERR_GROUP;
+    if (!aligned16(A) || !aligned16(wq_repacked) || !aligned16(scales) || !aligned16(C)) return W4A16_ERR_ALIGN;
+    w4a16_plan_t p{};
+    if (plan) {
+        p = *plan;
+        st = validate_plan(p, M, N, K);
+        if (st != W4A16_OK) return st;
+    } else {
+        auto_plan(M, N, K, &p);
+    }
+    if (workspace_for(p, M, N) > (size_t)W4A16_NOALLOC_SCRATCH_BYTES) return W4A16_ERR_WORKSPACE;
+    st = check_device();
+    if (st != W4A16_OK) return st;
+    void *ws = scratch_for_device(static_cast<hipStream_t>(stream), &st);
+    if (st != W4A16_OK) return st;
+    return run_gemm(A, wq_repacked, scales, C, M, N, K, group, ws, W4A16_NOALLOC_SCRATCH_BYTES, plan, stream);
 }
 
 int w4a16_gemm_f32(const void *A, const void *wq_repacked, const void *scales, float *C, int M,

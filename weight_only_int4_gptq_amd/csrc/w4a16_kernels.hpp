@@ -579,11 +579,14 @@ __global__ void __launch_bounds__(64 * KW) gemm_kernel(GemmArgs p) {
 
     // Work unit of this workgroup.  Units below nwhole are whole strips; the
     // others are the S pieces (contiguous K ranges) of the remaining strips.
-    // With whole strips the units keep launch order, so the hardware's
-    // round-robin placement gives each CU one whole strip and one piece of
-    // the remainder; with every strip split, each XCD gets one contiguous
-    // range of units, so the pieces of a strip meet in one L2.
-    const int u = p.nwhole > 0 ? (int)blockIdx.x : xcd_unit(blockIdx.x, p.nunits);
+    // Each XCD gets one contiguous range of units, so neighbouring strips
+    // (which share the 128-byte lines of the scales) and the pieces of a
+    // strip meet in one L2.  With whole strips, the first nwhole workgroups
+    // (nwhole a multiple of 8) take them and the rest take the pieces, so
+    // the hardware's placement gives each CU one whole strip and one piece.
+    const int u = blockIdx.x < (unsigned)p.nwhole
+                      ? xcd_unit(blockIdx.x, p.nwhole)
+                      : p.nwhole + xcd_unit(blockIdx.x - p.nwhole, p.nunits - p.nwhole);
     const bool whole = u < p.nwhole;
     const bool split = !whole && p.S > 1;                     // this workgroup writes a partial sum
     const int ur = u - p.nwhole;

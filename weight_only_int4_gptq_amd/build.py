@@ -96,6 +96,13 @@ def _compile(out: str, sources: list, verbose: bool, reuse: bool = False) -> str
             print(err)
     if errs:
         raise RuntimeError("\n".join(errs))
+    if reuse:                       # keep the three newest cached objects of each unit
+        for src in sources:
+            unit = os.path.basename(src) + "."
+            cached = sorted((os.path.join(CACHE, f) for f in os.listdir(CACHE)
+                             if f.startswith(unit) and f.endswith(".o")), key=os.path.getmtime)
+            for old in cached[:-3]:
+                os.remove(old)
     tmp = out + ".tmp"
     _run([hipcc()] + FLAGS + ["-shared", "-o", tmp] + objs, "link")
     os.replace(tmp, out)

@@ -102,6 +102,19 @@ extern const int kNumPlainCt, kNumPlainRt, kNumEpiCt, kNumEpiRt;
     W4A16_NV_MFMA(X, 1, ASRC_LDS) W4A16_NV_MFMA(X, 2, ASRC_LDS) W4A16_NV_MFMA(X, 3, ASRC_LDS)     \
     W4A16_NV_MFMA(X, 4, ASRC_LDS) W4A16_NV_MFMA(X, 2, ASRC_GLOBAL) W4A16_NV_MFMA(X, 4, ASRC_GLOBAL)
 
+// W4A16_VARIANT_SUBSET: a handful of shapes per table instead of all of
+// them, for quick builds of the host side under the address and
+// undefined-behaviour sanitizers (the planner then falls back where a shape
+// is missing; the library itself is always built with every shape).
+#ifdef W4A16_VARIANT_SUBSET
+#undef W4A16_VARIANT_LIST_CT
+#undef W4A16_VARIANT_LIST_RT
+#undef W4A16_NV_VARIANT_LIST
+#define W4A16_VARIANT_LIST_CT(X) X(PATH_GEMV, 1, 1, 8, 2, ASRC_LDS) X(PATH_MFMA, 2, 2, 4, 4, ASRC_LDS)
+#define W4A16_VARIANT_LIST_RT(X) X(PATH_MFMA, 0, 2, 4, 2, ASRC_RING) X(PATH_MFMA, 0, 2, 4, 4, ASRC_LDS)
+#define W4A16_NV_VARIANT_LIST(X) X(PATH_GEMV, 1, 1, 8, 2, ASRC_LDS) X(PATH_MFMA, 0, 2, 4, 2, ASRC_RING)
+#endif
+
 extern const Variant kVariantsNv[], kVariantsNvEpi[];   // plain, and with the epilogue modes
 extern const int kNumVariantsNv, kNumVariantsNvEpi;
 

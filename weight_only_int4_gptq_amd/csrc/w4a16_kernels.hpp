@@ -1183,18 +1183,31 @@ __global__ void __launch_bounds__(64 * KW) gemm_kernel(GemmArgs p) {
 
     if (split) {
         // Hand-off between the S workgroups of a strip without flushing any
-        // L2: partials go out with device-coherent stores, every thread waits
-        // for its own stores to complete, then one counter increment per
-        // workgroup; the last to arrive reads the S partials with
-        // device-coherent loads and adds them in the fixed order z = 0..S-1.
+        // L2.  Every partial is written with an agent-scope atomic store,
+        // which gfx950 writes through its XCD's L2 to the device-coherent
+        // level; the wait for vmcnt 0 returns once each of this thread's
+        // stores is acknowledged there.  Only then, after the workgroup
+        // barrier, does one thread increment the strip's counter (an
+        // agent-scope RMW, performed at that same level).  The last to
+        // arrive reads the S partials with agent-scope atomic loads, which
+        // do not take a stale line from its own L2, and adds them in the
+        // fixed order z = 0..S-1.  An agent-scope release/acquire pair would
+        // add a write-back of this XCD's whole L2 and an invalidate of it,
+        // both of which only matter for data written or read with ordinary
+        // (non-atomic) accesses, and there is none in this exchange.  The
+        // signal fences keep the compiler from moving memory accesses across
+        // the wait and the counter; they emit no instruction.
         __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
         __builtin_amdgcn_s_barrier();
         if (threadIdx.x == 0) {
+            __atomic_signal_fence(__ATOMIC_SEQ_CST);
             const uint32_t prev = __hip_atomic_fetch_add(&p.count[strip], 1u, __ATOMIC_RELAXED,
                                                          __HIP_MEMORY_SCOPE_AGENT);
             s_last = (prev == (uint32_t)(p.S - 1));
         }
-        lds_barrier();
+        wg_barrier();
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
         if (s_last) {
             auto summed = [&](int t, int m, int cc) {
                 float s = 0.0f;

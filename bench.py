@@ -343,6 +343,93 @@ def summarize_profiles(args):
     print(json.dumps(rec[tag]))
 
 
+# Hardware-counter passes of one matmul call shape (each its own rocprofv3 run;
+# at most 8 SQ, 4 TCP and 4 TCC counters per pass).
+COUNTER_PASSES = [
+    "SQ_WAVES SQ_BUSY_CYCLES SQ_WAVE_CYCLES SQ_WAIT_ANY SQ_ACTIVE_INST_VALU SQ_INSTS_VALU SQ_INSTS_MFMA "
+    "SQ_VALU_MFMA_BUSY_CYCLES",
+    "SQ_INSTS_SALU SQ_INSTS_VMEM SQ_INSTS_LDS SQ_ACTIVE_INST_LDS SQ_LDS_BANK_CONFLICT SQ_WAIT_INST_ANY",
+    "TCP_TCC_READ_REQ_LATENCY_sum TCP_TCC_READ_REQ_sum TCC_HIT_sum TCC_MISS_sum",
+]
+CHIP_SES, CHIP_CUS, CHIP_SIMDS, CLOCK_GHZ = 32, 256, 1024, 2.4
+
+
+def summarize_counters(args):
+    """profiles/gemm_kernel_<workload>_m<M>_counters.md from rocprofv3 --pmc runs.
+
+    Each directory holds one pass of COUNTER_PASSES (any order).  Values are
+    the median over the matmul kernel's dispatches, summed over the chip.
+    Derived figures: waves per SIMD; the share of wave-cycles spent waiting
+    and issuing VALU instructions; instructions per (16-column tile,
+    128-row group) unit; MFMA busy share of all SIMD-cycles of the call;
+    the mean L1 -> L2 read latency.
+    """
+    import statistics as st
+    wname, M = args.workload, args.m
+    wl = synth.WORKLOADS[wname]
+    nv = args.format == "nvfp4"
+    tag = f"{'nvfp4_' if nv else ''}{wname}_m{M}"
+    fmt_flag = " --format nvfp4" if nv else ""
+    vals, cmds, kname = {}, [], None
+    for d in args.summarize_counters:
+        per = {}
+        for r in _csv_rows(os.path.join(d, "run_counter_collection.csv")):
+            if "gemm_kernel" not in r["Kernel_Name"]:
+                continue
+            kname = kname or r["Kernel_Name"]
+            per.setdefault(r["Counter_Name"], {}).setdefault(r["Dispatch_Id"], 0.0)
+            per[r["Counter_Name"]][r["Dispatch_Id"]] += float(r["Counter_Value"])
+        for c, by_dispatch in per.items():
+            vals[c] = (st.median(by_dispatch.values()), len(by_dispatch))
+        cmds.append(f"rocprofv3 --pmc {' '.join(sorted(per))} -d {d} -o run --output-format csv -- "
+                    f"python3 bench.py --workload {wname} --m {M}{fmt_flag} --steps 20 --warmup 5 --no-cpu")
+    v = {c: x[0] for c, x in vals.items()}
+    units = (wl.N // 16) * (wl.K // 128)
+    kshort = kname.split("(")[0].replace("void ", "").replace("w4a16::", "")
+    out = [f"# Hardware counters: {kshort}, {wl.desc}, M={M}{', NVFP4' if nv else ''}\n",
+           "Commands (repo root, TMPDIR=/tmp), one pass each:\n"]
+    out += [f"    {c}" for c in cmds]
+    out += ["", "Median over the matmul kernel's dispatches (warm-up, flush and graph-replayed calls, all "
+            "on cold weights) of each counter summed over the chip:", "",
+            "| counter | value | dispatches |", "|---|---|---|"]
+    out += [f"| {c} | {v[c]:.0f} | {vals[c][1]} |" for c in sorted(v)]
+    derived = []
+
+    def add(name, f):
+        try:
+            derived.append((name, f()))
+        except (KeyError, ZeroDivisionError):
+            pass
+
+    busy = lambda: v["SQ_BUSY_CYCLES"] / CHIP_SES          # cycles the shader engines held waves
+    add("waves per launch", lambda: f"{v['SQ_WAVES']:.0f} ({v['SQ_WAVES'] / CHIP_SIMDS:.2f} per SIMD)")
+    add("shader-engine busy time", lambda: f"{busy():.0f} cycles = {busy() / CLOCK_GHZ / 1000:.2f} us at "
+        f"{CLOCK_GHZ} GHz")
+    add("mean wave lifetime", lambda: f"{4 * v['SQ_WAVE_CYCLES'] / v['SQ_WAVES']:.0f} cycles "
+        f"({4 * v['SQ_WAVE_CYCLES'] / v['SQ_WAVES'] / busy():.2f} of the busy time)")
+    add("wave-cycles waiting (any cause)", lambda: f"{v['SQ_WAIT_ANY'] / v['SQ_WAVE_CYCLES']:.1%}")
+    add("wave-cycles issuing VALU", lambda: f"{v['SQ_ACTIVE_INST_VALU'] / v['SQ_WAVE_CYCLES']:.1%}")
+    add("wave-cycles waiting to issue", lambda: f"{v['SQ_WAIT_INST_ANY'] / v['SQ_WAVE_CYCLES']:.1%}")
+    add("VALU instructions per (tile, group)", lambda: f"{v['SQ_INSTS_VALU'] / units:.1f}")
+    add("MFMA instructions per (tile, group)", lambda: f"{v['SQ_INSTS_MFMA'] / units:.2f}")
+    add("SALU instructions per (tile, group)", lambda: f"{v['SQ_INSTS_SALU'] / units:.1f}")
+    add("VMEM instructions per (tile, group)", lambda: f"{v['SQ_INSTS_VMEM'] / units:.2f}")
+    add("LDS instructions per (tile, group)", lambda: f"{v['SQ_INSTS_LDS'] / units:.2f}")
+    add("MFMA busy, share of all SIMD-cycles", lambda: f"{v['SQ_VALU_MFMA_BUSY_CYCLES'] / (CHIP_SIMDS * busy()):.1%}")
+    add("LDS bank-conflict cycles per LDS-active cycle",
+        lambda: f"{v['SQ_LDS_BANK_CONFLICT'] / (4 * v['SQ_ACTIVE_INST_LDS']):.2f}")
+    add("mean L1 -> L2 read latency", lambda: f"{v['TCP_TCC_READ_REQ_LATENCY_sum'] / v['TCP_TCC_READ_REQ_sum']:.0f} cycles")
+    add("L2 hit rate", lambda: f"{v['TCC_HIT_sum'] / (v['TCC_HIT_sum'] + v['TCC_MISS_sum']):.1%}")
+    out += ["", f"Derived ({units} units of one 16-column tile x 128 rows; {CHIP_SES} shader engines, "
+            f"{CHIP_SIMDS} SIMDs):", "", "| figure | value |", "|---|---|"]
+    out += [f"| {a} | {b} |" for a, b in derived]
+    out += ["", f"Kernel source hash: {kernel_source_hash()}", ""]
+    path = os.path.join(ROOT, "profiles", f"gemm_kernel_{tag}_counters.md")
+    with open(path, "w") as f:
+        f.write("\n".join(out))
+    print(path)
+
+
 def synth_bytes(nv, M, wl):
     return (synth.algorithmic_bytes_nvfp4 if nv else synth.algorithmic_bytes)(M, wl.N, wl.K)
 
@@ -371,9 +458,13 @@ def main():
                     help="after timing, copy MIB MiB a few times (reference for byte counters)")
     ap.add_argument("--summarize", nargs=3, metavar=("TRACE_DIR", "FETCH_DIR", "WRITE_DIR"),
                     help="write profiles/ from rocprofv3 output of the bench (no GPU use)")
+    ap.add_argument("--summarize-counters", nargs="+", metavar="PMC_DIR",
+                    help="write profiles/..._counters.md from rocprofv3 --pmc runs of the bench (no GPU use)")
     args = ap.parse_args()
     if args.summarize:
         return summarize_profiles(args)
+    if args.summarize_counters:
+        return summarize_counters(args)
 
     if args.gpus != 1:
         print(f"bench.py: measures one GPU; --gpus {args.gpus} is not supported "

@@ -215,7 +215,9 @@ int w4a16_gemm_plan(const void *A, const void *wq_repacked, const void *scales, 
 
 /*
  * Allocation-free form of w4a16_gemm_plan (plan == NULL: the plan w4a16_gemm
- * chooses), for callers that cannot allocate device memory: code under HIP
+ * chooses, or, where that plan's split-K partials would not fit the array
+ * below, the same plan with every strip whole), for callers that cannot
+ * allocate device memory: code under HIP
  * graph capture, tight serving loops, harnesses that forbid allocation.
  * Instead of a caller's workspace, the split-K counters and partials live in
  * a static device array of W4A16_NOALLOC_SCRATCH_BYTES that each GPU the

@@ -159,19 +159,27 @@ def test_row_count_dispatch():
     for M in range(1, 17):
         p = w4.get_plan(M, 34816, 5120)
         assert p.path == (w4.PATH_GEMV if M == 1 else w4.PATH_MFMA), (M, p)
-        assert p.splits == 1
-        # wide N: A through the LDS ring from two to 8 rows, two tiles;
-        # above, four wavefronts split the columns (one tile each) around a
-        # shared ring
-        if 2 <= M <= 8:
-            assert p.asrc == w4.ASRC_RING and p.tiles == 2, (M, p)
-        elif M >= 9:
-            assert p.asrc == w4.ASRC_SPLITN and (p.tiles, p.kwaves, p.depth) == (1, 4, 4), (M, p)
-    # QKV width: all of A in LDS up to 7 rows, the ring above
-    assert w4.get_plan(4, 8192, 5120).asrc == w4.ASRC_LDS
-    assert w4.get_plan(7, 8192, 5120).asrc == w4.ASRC_LDS
-    assert w4.get_plan(8, 8192, 5120).asrc == w4.ASRC_RING
-    assert w4.get_plan(16, 8192, 5120).asrc == w4.ASRC_RING
+        # gate/up width: one tile and eight shallow wavefronts at one row;
+        # A through the LDS ring from two to 4 rows, two tiles; from five
+        # rows four wavefronts split the columns (one tile each up to 8 rows,
+        # two above) around a shared ring, and the 32 (16) strips beyond two
+        # (one) per CU are split four ways along K
+        if M == 1:
+            assert (p.tiles, p.kwaves, p.depth, p.splits) == (1, 8, 2, 1), (M, p)
+        elif M <= 4:
+            assert p.asrc == w4.ASRC_RING and p.tiles == 2 and p.splits == 1, (M, p)
+        elif M <= 8:
+            assert p.asrc == w4.ASRC_SPLITN and (p.tiles, p.kwaves, p.depth, p.splits, p.whole) == (1, 4, 4, 4, 512), (M, p)
+        else:
+            assert p.asrc == w4.ASRC_SPLITN and (p.tiles, p.kwaves, p.depth, p.splits, p.whole) == (2, 4, 3, 4, 256), (M, p)
+    # QKV and attention-out widths (one to two two-tile strips per CU, 40 and
+    # 48 groups): eight wavefronts, two tiles; A whole in LDS at 2-3 rows,
+    # the ring from 4
+    for N, K in ((8192, 5120), (5120, 6144)):
+        for M in range(2, 17):
+            p = w4.get_plan(M, N, K)
+            assert (p.path, p.tiles, p.kwaves, p.splits) == (w4.PATH_MFMA, 2, 8, 1), (N, M, p)
+            assert (p.asrc, p.depth) == ((w4.ASRC_LDS, 4) if M <= 3 else (w4.ASRC_RING, 2)), (N, M, p)
     # very wide N: LDS A at 3-4 rows, the ring at 2, split-N from 5 rows
     # (two tiles per wavefront up to 8 rows, four above)
     assert w4.get_plan(4, 248320, 5120).asrc == w4.ASRC_LDS
@@ -183,21 +191,17 @@ def test_row_count_dispatch():
     assert w4.nvfp4_get_plan(5, 248320, 5120).asrc == w4.ASRC_SPLITN
     assert w4.nvfp4_get_plan(9, 34816, 5120).asrc == w4.ASRC_SPLITN
     assert w4.nvfp4_get_plan(8, 34816, 5120).asrc == w4.ASRC_RING
-    # long K with few column strips: split K (two rows and more)
-    # the down projection (320 tiles, 136 groups) up to 8 rows: 256 whole
-    # one-tile strips and 64 strips in four K pieces, eight wavefronts
-    assert w4.get_plan(2, 5120, 17408).splits == 1           # the whole K of A in LDS
-    for M in (1, 4, 6, 8):
+    # the down projection (320 tiles, 136 groups) at one row and from five:
+    # 256 whole one-tile strips and 64 strips in four K pieces, eight
+    # wavefronts; two to four rows keep the whole K of A in LDS, unsplit
+    for M in (2, 3, 4):
+        p = w4.get_plan(M, 5120, 17408)
+        assert (p.splits, p.asrc, p.tiles, p.kwaves) == (1, w4.ASRC_LDS, 2, 8), (M, p)
+    for M in (1, 5, 8, 9, 16):
         p = w4.get_plan(M, 5120, 17408)
         assert (p.tiles, p.kwaves, p.splits, p.whole) == (1, 8, 4, 256), (M, p)
         assert p.path == (w4.PATH_GEMV if M == 1 else w4.PATH_MFMA), (M, p)
         assert M == 1 or p.asrc == w4.ASRC_RING, (M, p)
-    assert w4.get_plan(16, 5120, 17408).splits == 1           # ring A
-    assert w4.get_plan(16, 5120, 17408).asrc == w4.ASRC_RING
-    # the attention output (6144 x 5120) from two rows: ring A, two tiles, eight wavefronts
-    for M in range(2, 17):
-        p = w4.get_plan(M, 5120, 6144)
-        assert (p.path, p.asrc, p.tiles, p.kwaves, p.depth, p.splits) == (w4.PATH_MFMA, w4.ASRC_RING, 2, 8, 2, 1), (M, p)
     # a K shard of it (68 groups) and the attention output (48 groups) are not split
     assert w4.get_plan(1, 5120, 8704).splits == 1
     assert w4.get_plan(1, 5120, 6144).splits == 1

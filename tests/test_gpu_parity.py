@@ -181,12 +181,13 @@ def test_gemm_remainder_split_parity(K, N, seed):
     Cref, Dref = oracle.gemm(A, qw, sc, 16, N, K)
     shapes = [(w4.PATH_GEMV, 1, 8, 2, w4.ASRC_LDS), (w4.PATH_GEMV, 2, 4, 3, w4.ASRC_LDS),
               (w4.PATH_MFMA, 1, 8, 2, w4.ASRC_RING), (w4.PATH_MFMA, 2, 4, 4, w4.ASRC_LDS),
-              (w4.PATH_MFMA, 2, 4, 4, w4.ASRC_GLOBAL), (w4.PATH_MFMA, 2, 4, 2, w4.ASRC_RING)]
+              (w4.PATH_MFMA, 2, 4, 4, w4.ASRC_GLOBAL), (w4.PATH_MFMA, 2, 4, 2, w4.ASRC_RING),
+              (w4.PATH_MFMA, 1, 4, 4, w4.ASRC_SPLITN), (w4.PATH_MFMA, 2, 4, 3, w4.ASRC_SPLITN)]
     ws = torch.zeros(65536 + 4 * 16 * N * 4, dtype=torch.uint8, device=DEV)
     ran = 0
     for M in (1, 3, 4, 8, 13, 16):
         for (path, t, kw, d, asrc) in shapes:
-            nstrips = -(-(N // 16) // t)
+            nstrips = -(-(N // 16) // (t * (kw if asrc == w4.ASRC_SPLITN else 1)))
             for S in (2, 4):
                 for whole in sorted({0, 1, nstrips // 2, nstrips - 1, nstrips}):
                     p = w4.make_plan(path, t, kw, S, asrc, d, whole)
@@ -412,6 +413,41 @@ def test_silu_mul_split_k(splits):
             torch.cuda.synchronize()
             silu_mul_check(H1, Href[:M], E[:M], (M, p))
             assert torch.equal(H1.view(torch.int16), H2.view(torch.int16))
+
+
+def test_epilogue_modes_remainder_split():
+    # gate/up activation and fp32 output with the leading strips whole and
+    # the rest split along K (the automatic plans of the gate/up width from
+    # five rows): split-N, ring and GEMV strips; repeated calls bitwise equal
+    K, N = 1280, 1088
+    A, qw, sc = synth.gen_problem(K, N, 37)
+    q, s, a = to_dev(qw, sc, A)
+    blob = w4.repack_weights(q, K, N)
+    Href, E = oracle.gemm_silu_mul(A, qw, sc, 16, N, K)
+    C16, D16 = oracle.gemm(A, qw, sc, 16, N, K)
+    ws = torch.zeros(65536 + 4 * 16 * N * 4, dtype=torch.uint8, device=DEV)
+    ran = 0
+    for M in (1, 4, 9, 16):
+        for (path, t, kw, d, asrc) in ((w4.PATH_MFMA, 2, 4, 3, w4.ASRC_SPLITN), (w4.PATH_MFMA, 2, 4, 2, w4.ASRC_RING),
+                                       (w4.PATH_MFMA, 2, 8, 2, w4.ASRC_RING), (w4.PATH_GEMV, 2, 8, 2, w4.ASRC_LDS)):
+            nstrips = -(-(N // 16) // (t * (kw if asrc == w4.ASRC_SPLITN else 1)))
+            for S in (2, 4):
+                for whole in sorted({1, nstrips // 2, nstrips - 1}):
+                    p = w4.make_plan(path, t, kw, S, asrc, d, whole)
+                    if not w4.plan_ok(M, N, K, p):
+                        continue
+                    H1 = w4.gemm_silu_mul(a[:M].contiguous(), blob, s, N, plan=p, workspace=ws)
+                    H2 = w4.gemm_silu_mul(a[:M].contiguous(), blob, s, N, plan=p, workspace=ws)
+                    C = w4.gemm_f32(a[:M].contiguous(), blob, s, N, plan=p, workspace=ws)
+                    torch.cuda.synchronize()
+                    silu_mul_check(H1, Href[:M], E[:M], (M, p))
+                    assert torch.equal(H1.view(torch.int16), H2.view(torch.int16)), (M, p)
+                    e = oracle.normalized_error(C.cpu().numpy().astype(np.float64), C16[:M], D16[:M])
+                    assert e.max() <= TOL, (M, p, float(e.max()))
+                    ran += 1
+    note(f"[epilogue remainder split] {ran} plans")
+    assert ran >= 40
+    assert int(ws[:65536].view(torch.int32).abs().sum()) == 0
 
 
 def test_silu_mul_zero_gate_is_exact_zero_and_odd_tiles_rejected():

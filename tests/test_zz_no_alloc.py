@@ -58,6 +58,32 @@ def with_workspace(a, blob, s, N, M, plan):
     return C
 
 
+def test_noalloc_automatic_plan_too_large_for_the_array_runs_unsplit():
+    # a gate/up-width call at 8 rows: the automatic plan splits the strips
+    # beyond two per CU four ways, and those partials (4.5 MB) exceed the
+    # array; without a plan the call runs the same plan with every strip
+    # whole, bitwise equal to the workspace call with that plan
+    K, N, M = 4096, 34816, 8
+    A, qw, sc = synth.gen_problem(K, N, 31)
+    a = torch.from_numpy(A.view(np.int16)).to(DEV).view(torch.bfloat16)
+    blob = w4.repack_weights(torch.from_numpy(qw.view(np.int32)).to(DEV), K, N)
+    s = torch.from_numpy(sc.view(np.int16)).to(DEV).view(torch.bfloat16)
+    auto = w4.get_plan(M, N, K)
+    assert auto.splits > 1 and w4.workspace_bytes(M, N, K, auto) > SCRATCH
+    whole = w4.make_plan(auto.path, auto.tiles, auto.kwaves, 1, auto.asrc, auto.depth, 0)
+    st, C = noalloc(a[:M].contiguous(), blob, s, N, M, None)
+    assert st == 0, w4.status_string(st)
+    ref = with_workspace(a, blob, s, N, M, whole)
+    assert torch.equal(C.view(torch.int16), ref.view(torch.int16))
+    cols = np.arange(0, N, 97, dtype=np.int32)
+    Cref, Dref = oracle.gemm(A, qw, sc, M, N, K, cols=cols)
+    got = oracle.bf16_bits_to_f64(C.view(torch.int16).cpu().numpy().view(np.uint16))[:, cols]
+    assert float(oracle.normalized_error(got, Cref, Dref).max()) <= 2e-3
+    # an explicit split plan of that size is still rejected
+    st, _ = noalloc(a[:M].contiguous(), blob, s, N, M, auto)
+    assert st == -5
+
+
 def test_noalloc_matches_the_workspace_call_on_consecutive_calls():
     cases = []
     # the down projection at 8 rows: the automatic plan splits 64 of its

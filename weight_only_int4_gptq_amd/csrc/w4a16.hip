@@ -209,7 +209,10 @@ void auto_plan(int M, int N, int K, w4a16_plan_t *out) {
         // wavefronts per SIMD, one's dequantization overlaps the other's wait
         p.path = W4A16_PATH_GEMV;
         p.kwaves = 8;
-        if (wide) {
+        if (wide && !vwide && !deep) {         // gate/up width: one tile, eight shallow wavefronts
+            p.tiles = 1;
+            p.depth = 2;
+        } else if (wide) {
             p.tiles = 2;
             p.kwaves = deep ? 8 : 4;
             p.depth = deep ? 4 : 5;
@@ -264,6 +267,16 @@ void auto_plan(int M, int N, int K, w4a16_plan_t *out) {
             p.asrc = W4A16_ASRC_SPLITN;
             p.tiles = M <= 8 ? 2 : 4;
             p.depth = 2;
+        } else if (wide && G >= 32) {          // four wavefronts split 4 (8 above 8 rows) tiles, shared A
+            p.asrc = W4A16_ASRC_SPLITN;
+            p.tiles = M <= 8 ? 1 : 2;
+            p.depth = M <= 8 ? 4 : 3;
+            // strips beyond a whole number per CU: split four ways along K
+            const int ns = (NT + 4 * p.tiles - 1) / (4 * p.tiles), R = ns % kPlanCUs;
+            if (ns > kPlanCUs && R != 0 && 4 * R <= kPlanCUs) {
+                p.splits = 4;
+                p.whole = ns - R;
+            }
         } else if (wide && M >= 9) {           // four wavefronts split 4 tiles, shared A, depth 4
             p.asrc = W4A16_ASRC_SPLITN;
             p.tiles = 1;
@@ -295,24 +308,26 @@ void auto_plan(int M, int N, int K, w4a16_plan_t *out) {
             p.depth = (narrow && G >= 32) ? 4 : 2;
         }
     }
-    // Narrow N above one strip per CU with 32 to 127 groups (the attention
-    // output projection, 6144 x 5120) from two rows: A through the ring,
-    // two tiles, eight wavefronts (two per SIMD), shallow rings.
-    if (M >= 2 && narrow && NT > kPlanCUs && G >= 32 && !deep) {
+    // Between one and two strips of two tiles per CU with 32 to 127 groups
+    // (the attention output projection 6144 x 5120 and QKV 5120 x 8192):
+    // two tiles, eight wavefronts (two per SIMD); A staged whole in LDS
+    // (depth 4) for two and three rows, through the ring (depth 2) from four.
+    if (M >= 2 && NT > kPlanCUs && NT <= 2 * kPlanCUs && G >= 32 && !deep) {
         p.path = W4A16_PATH_MFMA;
-        p.asrc = W4A16_ASRC_RING;
+        p.asrc = M >= 4 ? W4A16_ASRC_RING : W4A16_ASRC_LDS;
         p.tiles = 2;
         p.kwaves = 8;
-        p.depth = 2;
+        p.depth = M >= 4 ? 2 : 4;
         p.splits = 1;
+        p.whole = 0;
     }
-    // Narrow N with long K, up to 8 rows: one tile per strip, eight
-    // wavefronts along K, and the strips beyond one per CU split into K
-    // pieces, so that every CU gets one whole strip and one piece
+    // Narrow N with long K, one row or five and more: one tile per strip,
+    // eight wavefronts along K, and the strips beyond one per CU split into
+    // K pieces, so that every CU gets one whole strip and one piece
     // (17408 x 5120: 256 whole strips and 64 strips in four pieces).  The
-    // pieces' hand-off finishes long before the whole strips do.  (Two
-    // rows keep the whole K range of A in LDS, which measures faster.)
-    if (narrow && deep && M <= 8 && M != 2 && NT > kPlanCUs && NT % kPlanCUs != 0) {
+    // pieces' hand-off finishes long before the whole strips do.  (Two to
+    // four rows keep the whole K range of A in LDS, which measures faster.)
+    if (narrow && deep && (M == 1 || M >= 5) && NT > kPlanCUs && NT % kPlanCUs != 0) {
         const int R = NT % kPlanCUs;
         int S = 1;
         while (S * 2 * R <= kPlanCUs && S * 2 <= G / 16) S *= 2;
@@ -752,13 +767,17 @@ int w4a16_gemm_noalloc(const void *A, const void *wq_repacked, const void *scale
         if (st != W4A16_OK) return st;
     } else {
         auto_plan(M, N, K, &p);
+        if (workspace_for(p, M, N) > (size_t)W4A16_NOALLOC_SCRATCH_BYTES) {
+            p.splits = 1;                      // partials too large: every strip whole
+            p.whole = 0;
+        }
     }
     if (workspace_for(p, M, N) > (size_t)W4A16_NOALLOC_SCRATCH_BYTES) return W4A16_ERR_WORKSPACE;
     st = check_device();
     if (st != W4A16_OK) return st;
     void *ws = scratch_for_device(static_cast<hipStream_t>(stream), &st);
     if (st != W4A16_OK) return st;
-    return run_gemm(A, wq_repacked, scales, C, M, N, K, group, ws, W4A16_NOALLOC_SCRATCH_BYTES, plan, stream);
+    return run_gemm(A, wq_repacked, scales, C, M, N, K, group, ws, W4A16_NOALLOC_SCRATCH_BYTES, &p, stream);
 }
 
 int w4a16_gemm_f32(const void *A, const void *wq_repacked, const void *scales, float *C, int M,

@@ -401,7 +401,11 @@ static __global__ void __launch_bounds__(256) repack_kernel(const uint32_t *__re
 }
 
 // Test exports: the same words_to_bf16x8 the GEMM kernels use, and the
-// checkpoint's scales [K/128][N].
+// checkpoint's scales [K/128][N].  Both instruction forms run (the shared
+// 64-bit shift of the GEMV kernels and the compiler's shifts of the
+// matrix-core kernels); where they disagree the export writes a value no
+// exact dequantization has (NaN, or code 255), so an export that matches
+// the oracle pins both.
 template <bool CODES>
 __global__ void __launch_bounds__(256) export_kernel(const u32x4 *__restrict__ blob,
                                                      const uint16_t *__restrict__ scales,
@@ -417,22 +421,25 @@ __global__ void __launch_bounds__(256) export_kernel(const u32x4 *__restrict__ b
     const u32x4 w = blob[pc];
     const DequantConsts kc = dequant_consts();
     const float s = CODES ? 0.0f : bf16_bits_to_f32(scales[(long long)g * N + n]);
-    uint32_t bw[4][4];
+    uint32_t bw[4][4], bx[4][4];
     words_to_bf16x8<true>(w[0], w[1], kc, bw[0], bw[1]);
     words_to_bf16x8<true>(w[2], w[3], kc, bw[2], bw[3]);
+    words_to_bf16x8<false>(w[0], w[1], kc, bx[0], bx[1]);
+    words_to_bf16x8<false>(w[2], w[3], kc, bx[2], bx[3]);
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
         const uint32_t (&b)[4] = bw[r];
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
             const long long k = (long long)g * kGroup + h * 32 + r * 8 + 2 * v;
+            const bool same = b[v] == bx[r][v];
             const float lo = pair_lo(b[v]), hi = pair_hi(b[v]);
             if (CODES) {
-                codes[k * N + n] = (uint8_t)(int)(lo - 128.0f);
-                codes[(k + 1) * N + n] = (uint8_t)(int)(hi - 128.0f);
+                codes[k * N + n] = same ? (uint8_t)(int)(lo - 128.0f) : (uint8_t)255;
+                codes[(k + 1) * N + n] = same ? (uint8_t)(int)(hi - 128.0f) : (uint8_t)255;
             } else {
-                W[k * N + n] = (lo - kBias) * s;
-                W[(k + 1) * N + n] = (hi - kBias) * s;
+                W[k * N + n] = same ? (lo - kBias) * s : __builtin_nanf("");
+                W[(k + 1) * N + n] = same ? (hi - kBias) * s : __builtin_nanf("");
             }
         }
     }
@@ -831,7 +838,9 @@ __global__ void __launch_bounds__(64 * KW) gemm_kernel(GemmArgs p) {
 #pragma unroll
         for (int i = 0; i < NACC; ++i) acc[t][i] = 0.0f;
 
-    auto compute_group = [&](auto jc, int g, auto final_) {
+    // later_c: how many younger groups have their loads in flight when this
+    // slot is computed (the explicit waits for DMA loads count on it)
+    auto compute_group = [&](auto jc, int g, auto later_c) {
         constexpr int j = decltype(jc)::value;
         const int gl = g - gw0;
         if constexpr (kNv) {
@@ -849,7 +858,7 @@ __global__ void __launch_bounds__(64 * KW) gemm_kernel(GemmArgs p) {
                     // as for GPTQ: wait for this slot's DMA loads explicitly;
                     // rows 16b + 4h .. +3 are bytes 32b + 8h of row c, in
                     // logical piece 2b + h/2, stored at piece (2b + h/2) ^ c
-                    constexpr int later = decltype(final_)::value ? D - 1 - j : D - 1;
+                    constexpr int later = decltype(later_c)::value;
                     __builtin_amdgcn_s_waitcnt(waitcnt_vm(2 * T + later * (2 * T + 1)));
                     if constexpr (kSplitN) wg_barrier();   // every wavefront's rows have landed
                     const uint8_t *slot = smem + (kSplitN ? shared_slot(g) : ring_slot(j)) + c * (kGroup * 2) +
@@ -925,7 +934,7 @@ __global__ void __launch_bounds__(64 * KW) gemm_kernel(GemmArgs p) {
                     // the compiler does not see the DMA loads: wait for this
                     // slot's explicitly (every load issued after them counted
                     // as if each later group had one DMA load: never fewer)
-                    constexpr int later = decltype(final_)::value ? D - 1 - j : D - 1;
+                    constexpr int later = decltype(later_c)::value;
                     __builtin_amdgcn_s_waitcnt(waitcnt_vm(2 * T + later * (2 * T + 1)));
                     if constexpr (kSplitN) wg_barrier();   // every wavefront's rows have landed
                     const uint8_t *slot = smem + (kSplitN ? shared_slot(g) : ring_slot(j)) + c * (kGroup * 2);
@@ -1001,28 +1010,62 @@ __global__ void __launch_bounds__(64 * KW) gemm_kernel(GemmArgs p) {
         }
     };
 
+    using Full = std::integral_constant<int, D - 1>;   // every younger slot in flight
+    // One full round: compute each slot, refill it with the group D ahead.
+    auto full_round = [&](int base) {
+        [&]<int... J>(std::integer_sequence<int, J...>) {
+            ((compute_group(std::integral_constant<int, J>{}, gat(base + J), Full{}),
+              load_group(std::integral_constant<int, J>{}, gat(base + J + D)),
+              __builtin_amdgcn_sched_barrier(0)),
+             ...);
+        }(std::make_integer_sequence<int, D>{});
+    };
+    // The last groups, with RT of the last round's refills still real
+    // (0 <= RT < D): the round computes its D slots and refills only the
+    // first RT of them, then those RT are computed.  Every load issued is a
+    // real group, and each wait count is still a compile-time constant.
+    auto tail = [&](auto rtc, int base) {
+        constexpr int RT = decltype(rtc)::value;
+        [&]<int... J>(std::integer_sequence<int, J...>) {
+            (([&] {
+                 // younger loads: slots J+1..D-1 of the previous round, and
+                 // this round's refills of slots 0..min(J, RT)-1
+                 compute_group(std::integral_constant<int, J>{}, gat(base + J),
+                               std::integral_constant<int, (D - 1 - J) + (J < RT ? J : RT)>{});
+                 if constexpr (J < RT) load_group(std::integral_constant<int, J>{}, gat(base + J + D));
+                 __builtin_amdgcn_sched_barrier(0);
+             }()),
+             ...);
+        }(std::make_integer_sequence<int, D>{});
+        [&]<int... J>(std::integer_sequence<int, J...>) {
+            (([&] {
+                 if constexpr (J < RT)
+                     compute_group(std::integral_constant<int, J>{}, gat(base + D + J),
+                                   std::integral_constant<int, RT - 1 - J>{});
+             }()),
+             ...);
+        }(std::make_integer_sequence<int, D>{});
+    };
+
     if (ng > 0) {
-        if (ng % D == 0) {
-            // exact: every refill is a real group; the last round loads nothing
+        if (ng % D == 0 || (D <= 4 && ng > D)) {
+            // exact: every refill is a real group.  Full rounds while two
+            // rounds' groups remain, then the tail for the remainder (one of
+            // D compiled tails; shallow rings only, for code size).
             int base = 0;
-            for (; base + D < ng; base += D) {
-                [&]<int... J>(std::integer_sequence<int, J...>) {
-                    ((compute_group(std::integral_constant<int, J>{}, gat(base + J), std::false_type{}),
-                      load_group(std::integral_constant<int, J>{}, gat(base + J + D)),
-                      __builtin_amdgcn_sched_barrier(0)),
-                     ...);
-                }(std::make_integer_sequence<int, D>{});
-            }
-            [&]<int... J>(std::integer_sequence<int, J...>) {
-                (compute_group(std::integral_constant<int, J>{}, gat(base + J), std::true_type{}), ...);
-            }(std::make_integer_sequence<int, D>{});
+            for (; base + 2 * D <= ng; base += D) full_round(base);
+            const int rt = ng - base - D;
+            [&]<int... R>(std::integer_sequence<int, R...>) {
+                ((rt == R ? tail(std::integral_constant<int, R>{}, base) : void()), ...);
+            }(std::make_integer_sequence<int, (D <= 4 ? D : 1)>{});
         } else {
-            // ragged: past the last group the refill re-reads the last group
-            // (clamped; it is in flight or in L2 already), so every iteration
-            // issues the same loads and the wait counts stay static
+            // ragged (deep rings, or fewer groups than slots): past the last
+            // group the refill re-reads the last group (clamped; it is in
+            // flight or in L2 already), so every iteration issues the same
+            // loads and the wait counts stay static
             for (int base = 0; base < ng; base += D) {
                 [&]<int... J>(std::integer_sequence<int, J...>) {
-                    ((base + J < ng ? compute_group(std::integral_constant<int, J>{}, gat(base + J), std::false_type{})
+                    ((base + J < ng ? compute_group(std::integral_constant<int, J>{}, gat(base + J), Full{})
                                     : void(),
                       load_group(std::integral_constant<int, J>{}, gidx(base + J + D)),
                       __builtin_amdgcn_sched_barrier(0)),

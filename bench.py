@@ -227,7 +227,20 @@ def cpu_baseline(prob, M, seconds=10.0):
     return {"value": round(nbytes / el / 1e9, 3), "unit": "GB/s", "cores": nthreads, "kind": "oracle",
             "sample": f"{reps} full calls of the same workload (M={M}, K={prob.K}, N={prob.N}), "
                       f"{el:.1f} s wall, fp64 C oracle with OpenMP over columns; "
-                      f"{el / reps * 1e6:.0f} us/call"}
+                      f"{el / reps * 1e6:.0f} us/call",
+            "host": {"cpu_model": cpu_model(), "logical_cpus": os.cpu_count(),
+                     "usable_cpus": len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else None}}
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
 
 
 def traffic_record(name):

@@ -187,10 +187,20 @@ def test_row_count_dispatch():
     assert w4.get_plan(8, 248320, 5120).asrc == w4.ASRC_SPLITN
     assert w4.get_plan(8, 248320, 5120).tiles == 2
     assert w4.get_plan(16, 248320, 5120).tiles == 4
-    # the same for NVFP4 weights from 5 rows; wide N from 9 rows
+    # the same for NVFP4 weights from 5 rows; the gate/up width from 5 rows
+    # with its strips beyond two per CU split four ways along K
     assert w4.nvfp4_get_plan(5, 248320, 5120).asrc == w4.ASRC_SPLITN
-    assert w4.nvfp4_get_plan(9, 34816, 5120).asrc == w4.ASRC_SPLITN
-    assert w4.nvfp4_get_plan(8, 34816, 5120).asrc == w4.ASRC_RING
+    for M in (5, 8, 9, 16):
+        p = w4.nvfp4_get_plan(M, 34816, 5120)
+        assert (p.asrc, p.tiles, p.splits, p.whole) == (w4.ASRC_SPLITN, 1, 4, 512), (M, p)
+    # NVFP4 down projection: the remainder split at one and two rows
+    for M in (1, 2):
+        p = w4.nvfp4_get_plan(M, 5120, 17408)
+        assert (p.tiles, p.kwaves, p.splits, p.whole) == (1, 8, 4, 256), (M, p)
+    p = w4.nvfp4_get_plan(1, 34816, 5120)
+    assert (p.path, p.tiles, p.kwaves, p.depth) == (w4.PATH_GEMV, 1, 8, 2), p
+    p = w4.nvfp4_get_plan(8, 5120, 6144)
+    assert (p.asrc, p.tiles, p.kwaves, p.depth) == (w4.ASRC_LDS, 2, 8, 4), p
     # the down projection (320 tiles, 136 groups) at one row and from five:
     # 256 whole one-tile strips and 64 strips in four K pieces, eight
     # wavefronts; two to four rows keep the whole K of A in LDS, unsplit

@@ -161,6 +161,35 @@ def test_nvfp4_split_k_parity_and_reuse(splits):
                 assert int(ws[:65536].view(torch.int32).abs().sum()) == 0
 
 
+def test_nvfp4_remainder_split_parity():
+    # the leading strips whole, the rest split along K (the automatic NVFP4
+    # plans of the down projection at one and two rows and of the gate/up
+    # width from five rows): GEMV, staged, ring and split-N strips
+    K, N = 2048, 1040
+    A, packed, scales = synth.gen_nvfp4_problem(K, N, 22)
+    blob, sc, a = to_dev(packed, scales, A)
+    Cref, Dref = oracle.nvfp4_gemm(A, packed, scales, ALPHA, 16, N, K)
+    ws = torch.zeros(65536 + 4 * 16 * N * 4, dtype=torch.uint8, device=DEV)
+    ran = 0
+    for M in (1, 2, 5, 8, 16):
+        for (path, t, kw, d, asrc) in ((w4.PATH_GEMV, 1, 8, 2, w4.ASRC_LDS), (w4.PATH_MFMA, 1, 8, 4, w4.ASRC_LDS),
+                                       (w4.PATH_MFMA, 1, 4, 4, w4.ASRC_SPLITN), (w4.PATH_MFMA, 2, 4, 2, w4.ASRC_RING)):
+            nstrips = -(-(N // 16) // (t * (kw if asrc == w4.ASRC_SPLITN else 1)))
+            for S in (2, 4):
+                for whole in sorted({1, nstrips // 2, nstrips - 1}):
+                    p = w4.make_plan(path, t, kw, S, asrc, d, whole)
+                    if not w4.nvfp4_plan_ok(M, N, K, p):
+                        continue
+                    C1 = run(a, blob, sc, N, M, plan=p, ws=ws)
+                    C2 = run(a, blob, sc, N, M, plan=p, ws=ws)
+                    assert max_err(C1, Cref[:M], Dref[:M]) <= TOL, (M, p)
+                    assert torch.equal(C1.view(torch.int16), C2.view(torch.int16)), (M, p)
+                    ran += 1
+    note(f"[nvfp4 remainder split] {ran} plans")
+    assert ran >= 30
+    assert int(ws[:65536].view(torch.int32).abs().sum()) == 0
+
+
 # ------------------------------------------------------------- exact special inputs
 
 E2M1 = [0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0, -0.0, -0.5, -1.0, -1.5, -2.0, -3.0, -4.0, -6.0]

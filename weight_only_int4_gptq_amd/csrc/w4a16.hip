@@ -406,10 +406,19 @@ void auto_plan_nv(int M, int N, int K, w4a16_plan_t *out) {
     auto set = [&](int path, int t, int kw, int s, int asrc, int d) {
         p.path = path, p.tiles = t, p.kwaves = kw, p.splits = s, p.asrc = asrc, p.depth = d;
     };
+    // narrow N with long K and more one-tile strips than CUs (the down
+    // projection): the strips beyond one per CU split four ways along K
+    const int R = NT % kPlanCUs;
+    const bool remainder = narrow && deep && NT > kPlanCUs && R != 0 && 4 * R <= kPlanCUs && G >= 64;
     if (M == 1) {
-        if (wide) set(W4A16_PATH_GEMV, 2, 4, 1, W4A16_ASRC_LDS, 5);
+        if (wide && !vwide && !deep) set(W4A16_PATH_GEMV, 1, 8, 1, W4A16_ASRC_LDS, 2);
+        else if (wide) set(W4A16_PATH_GEMV, 2, 4, 1, W4A16_ASRC_LDS, 5);
+        else if (remainder) set(W4A16_PATH_GEMV, 1, 8, 4, W4A16_ASRC_LDS, 2), p.whole = NT - R;
         else if (deep) set(W4A16_PATH_GEMV, 2, 8, 1, W4A16_ASRC_LDS, 3);
         else set(W4A16_PATH_GEMV, 1, 8, 1, W4A16_ASRC_LDS, 2);
+    } else if (M == 2 && remainder) {
+        set(W4A16_PATH_MFMA, 1, 8, 4, W4A16_ASRC_LDS, 4);
+        p.whole = NT - R;
     } else if (M <= 4) {
         if (vwide) set(W4A16_PATH_MFMA, 4, 4, 1, W4A16_ASRC_LDS, 2);
         else if (deep) set(W4A16_PATH_MFMA, 2, 8, 1, W4A16_ASRC_LDS, 4);
@@ -422,13 +431,19 @@ void auto_plan_nv(int M, int N, int K, w4a16_plan_t *out) {
         if (vwide) {
             set(W4A16_PATH_MFMA, 2, 4, 1, W4A16_ASRC_SPLITN, 2);
         } else if (wide) {
-            if (M >= 9) set(W4A16_PATH_MFMA, 1, 4, 1, W4A16_ASRC_SPLITN, 4);
-            else set(W4A16_PATH_MFMA, 2, 4, 1, W4A16_ASRC_RING, 2);
+            // four wavefronts split 4 tiles around a shared ring; the
+            // strips beyond a whole number per CU split four ways along K
+            set(W4A16_PATH_MFMA, 1, 4, 1, W4A16_ASRC_SPLITN, 4);
+            const int ns = (NT + 3) / 4, r = ns % kPlanCUs;
+            if (G >= 32 && ns > kPlanCUs && r != 0 && 4 * r <= kPlanCUs) {
+                p.splits = 4;
+                p.whole = ns - r;
+            }
         } else if (deep) {
             if (M <= 7) set(W4A16_PATH_MFMA, 4, 4, 4, W4A16_ASRC_LDS, 2);
             else set(W4A16_PATH_MFMA, 2, 4, 2, W4A16_ASRC_RING, 2);
-        } else if (narrow && M <= 8) {         // one tile (two from 64 groups), eight wavefronts
-            set(W4A16_PATH_MFMA, G >= 64 ? 2 : 1, 8, 1, W4A16_ASRC_LDS, 4);
+        } else if (narrow && M <= 8) {         // one tile (two from 64 groups or past 256 tiles), eight wavefronts
+            set(W4A16_PATH_MFMA, (G >= 64 || NT > kPlanCUs) ? 2 : 1, 8, 1, W4A16_ASRC_LDS, 4);
         } else if (M <= 7) {
             set(W4A16_PATH_MFMA, 2, 8, 1, W4A16_ASRC_LDS, 4);
         } else {
@@ -440,6 +455,7 @@ void auto_plan_nv(int M, int N, int K, w4a16_plan_t *out) {
     // (one row: up to two wavefronts per group, the idle ones finish at once)
     const int kwmax = (M == 1) ? 2 * G : G;
     while (p.splits > 1 && p.splits * p.kwaves > G) p.splits >>= 1;
+    if (p.splits == 1) p.whole = 0;
     while (p.asrc != W4A16_ASRC_SPLITN && p.kwaves > 1 && p.kwaves > kwmax) p.kwaves >>= 1;
     // fallbacks: A from global memory; the LDS ring (its kernels take any
     // row count, so they also cover K ranges of A too long to stage); the

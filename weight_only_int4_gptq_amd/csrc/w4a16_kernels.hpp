@@ -1011,6 +1011,10 @@ __global__ void __launch_bounds__(64 * KW) gemm_kernel(GemmArgs p) {
     };
 
     using Full = std::integral_constant<int, D - 1>;   // every younger slot in flight
+    // (The NVFP4 matrix-core kernels keep the clamped refills for fewer
+    // groups than slots: the extra code path crashes this compiler's
+    // AGPR-copy rewrite pass on some of their shapes.)
+    constexpr bool kFewerThanSlots = !kNv || PATH == PATH_GEMV;
     // One full round: compute each slot, refill it with the group D ahead.
     auto full_round = [&](int base) {
         [&]<int... J>(std::integer_sequence<int, J...>) {
@@ -1058,11 +1062,20 @@ __global__ void __launch_bounds__(64 * KW) gemm_kernel(GemmArgs p) {
             [&]<int... R>(std::integer_sequence<int, R...>) {
                 ((rt == R ? tail(std::integral_constant<int, R>{}, base) : void()), ...);
             }(std::make_integer_sequence<int, (D <= 4 ? D : 1)>{});
+        } else if (kFewerThanSlots && ng < D) {
+            // fewer groups than slots: the prologue loaded every group (its
+            // slots past the last re-read the last group); compute them, no
+            // refills
+            [&]<int... J>(std::integer_sequence<int, J...>) {
+                ((J < ng ? compute_group(std::integral_constant<int, J>{}, gat(J),
+                                         std::integral_constant<int, D - 1 - J>{})
+                         : void()),
+                 ...);
+            }(std::make_integer_sequence<int, D>{});
         } else {
-            // ragged (deep rings, or fewer groups than slots): past the last
-            // group the refill re-reads the last group (clamped; it is in
-            // flight or in L2 already), so every iteration issues the same
-            // loads and the wait counts stay static
+            // ragged deep rings: past the last group the refill re-reads the
+            // last group (clamped; it is in flight or in L2 already), so every
+            // iteration issues the same loads and the wait counts stay static
             for (int base = 0; base < ng; base += D) {
                 [&]<int... J>(std::integer_sequence<int, J...>) {
                     ((base + J < ng ? compute_group(std::integral_constant<int, J>{}, gat(base + J), Full{})

@@ -212,6 +212,20 @@ def test_row_count_dispatch():
         assert (p.tiles, p.kwaves, p.splits, p.whole) == (1, 8, 4, 256), (M, p)
         assert p.path == (w4.PATH_GEMV if M == 1 else w4.PATH_MFMA), (M, p)
         assert M == 1 or p.asrc == w4.ASRC_RING, (M, p)
+    # one GPU's tensor-parallel shares at 8 rows: up to 256 tiles, one tile
+    # and eight wavefronts with A through the ring; the 544/1088-tile column
+    # shards split their strips beyond a whole number per CU four ways; the
+    # 68-group K shard of down takes the remainder split like down
+    p = w4.get_plan(8, 4096, 5120)
+    assert (p.asrc, p.tiles, p.kwaves, p.depth, p.splits) == (w4.ASRC_RING, 1, 8, 4, 1), p
+    p = w4.get_plan(8, 17408, 5120)
+    assert (p.asrc, p.tiles, p.splits, p.whole) == (w4.ASRC_RING, 2, 4, 512), p
+    p = w4.get_plan(8, 8704, 5120)
+    assert (p.asrc, p.tiles, p.splits, p.whole) == (w4.ASRC_RING, 2, 4, 256), p
+    p = w4.get_plan(8, 5120, 8704)
+    assert (p.tiles, p.kwaves, p.splits, p.whole) == (1, 8, 4, 256), p
+    p = w4.get_plan(8, 5120, 2176)
+    assert (p.asrc, p.tiles, p.depth) == (w4.ASRC_RING, 2, 4), p
     # a K shard of it (68 groups) and the attention output (48 groups) are not split
     assert w4.get_plan(1, 5120, 8704).splits == 1
     assert w4.get_plan(1, 5120, 6144).splits == 1

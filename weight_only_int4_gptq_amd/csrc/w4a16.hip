@@ -166,35 +166,36 @@ int validate_plan(const w4a16_plan_t &p, int M, int N, int K, int fmt = FMT_GPTQ
 // and third, K / 2, 4, 8 for the second and fourth), M = 1..16.
 // Widths: "narrow" up to 384 tiles of 16 columns, "mid" 513..2047, "wide"
 // from 2048, "very wide" from 8192; "long" K from 128 groups of 128.
-//  * M = 1: the GEMV kernel; wide N: two tiles, four wavefronts, depth 5
-//    (eight wavefronts, depth 4 for long K); from 1024 tiles: one tile, four
-//    wavefronts, each wavefront's groups loaded in one go; narrower N, eight
-//    wavefronts along K: from 64 groups two tiles and depth 3, up to 256
-//    tiles with 32 groups or more one tile and depth 4, from 16 groups one
-//    tile and depth 2, else two tiles and depth 2;
-//  * M = 2..4: matrix cores; long K: A staged in LDS, two tiles, eight
-//    wavefronts (the whole K range of A, up to the full 160 KiB of LDS, one
-//    workgroup per CU); very wide N: four tiles, depth 2, A in LDS (through
-//    the ring with two wavefronts at M = 2); wide and mid N: A through the
-//    per-wavefront LDS ring (contiguous DMA loads), two tiles, depth 2;
-//    narrow N from 16 groups: A in LDS, eight wavefronts, depth 4, one
-//    tile (two from 64 groups) (the tensor-parallel shards); otherwise A in
-//    LDS, two tiles, depth 4;
+//  * M = 1: the GEMV kernel; eight wavefronts with a ring of depth 2 and one
+//    tile per strip almost everywhere (two wavefronts or more per SIMD);
+//    two tiles for the attention output (257..384 tiles, 32..63 groups);
+//    two tiles, four wavefronts, depth 4 below 16 groups; the very wide
+//    output head keeps two tiles, four wavefronts, depth 5;
+//  * M = 2..4: matrix cores; long K: the whole K range of A staged in LDS,
+//    two tiles, eight wavefronts; very wide N: four tiles, depth 2, A in
+//    LDS (the ring with two wavefronts at M = 2); wide and mid N: A through
+//    the per-wavefront LDS ring, two tiles, depth 2; narrow N from 16
+//    groups: A in LDS, eight wavefronts, depth 4, one tile (two from 64
+//    groups); otherwise A in LDS, two tiles, depth 4;
 //  * M >= 5, matrix cores:
 //      - very wide N: four wavefronts split the columns (two tiles each up
 //        to 8 rows, four above) around one shared ring of A, depth 2;
-//      - wide N from 9 rows: the same with one tile each, depth 4;
-//      - wide (up to 8 rows) and mid N: A through the ring, depth 2, two
-//        tiles up to 8 rows, four above;
+//      - wide N from 32 groups: the same with one tile each (two above 8
+//        rows), the strips beyond a whole number per CU split four ways
+//        along K;
+//      - mid N: A through the ring, two tiles, depth 2, with the same
+//        remainder split;
 //      - long K: A through the ring from M = 8; below, a quarter of K of A
 //        staged in LDS (split four ways);
-//      - narrow N up to 256 tiles: one tile, all of A staged in LDS, eight
-//        wavefronts along K;
+//      - narrow N up to 256 tiles: one tile, eight wavefronts, A in LDS up
+//        to 7 rows, through the ring above;
+//      - narrow N with 8..31 groups: A through the ring, two tiles, depth 4;
 //      - otherwise two tiles: all of A in LDS up to 7 rows and from 64
 //        groups (depth 4, eight wavefronts from 64 groups), A through the
 //        ring otherwise (depth 2; depth 4 for narrow N from 32 groups).
-//  Staged A that does not fit in LDS goes through the ring with four
-//  wavefronts.
+//  Two rules override these (below): the QKV and attention-output widths,
+//  and the remainder split of narrow N with long K.  Staged A that does
+//  not fit in LDS goes through the ring with four wavefronts.
 void auto_plan(int M, int N, int K, w4a16_plan_t *out) {
     const int NT = N / 16, G = K / W4A16_GROUP;
     const bool wide = NT >= 2048, vwide = NT >= 8192, deep = G >= 128;
@@ -216,25 +217,16 @@ void auto_plan(int M, int N, int K, w4a16_plan_t *out) {
             p.tiles = 2;
             p.kwaves = deep ? 8 : 4;
             p.depth = deep ? 4 : 5;
-        } else if (NT >= 1024) {               // one tile, each wavefront's groups in one go
+        } else if (NT > 256 && NT <= 384 && G >= 32 && G < 64) {   // attention out: two tiles, shallow
+            p.tiles = 2;
+            p.depth = 2;
+        } else if (G >= 16) {                  // one tile, eight shallow wavefronts
             p.tiles = 1;
+            p.depth = 2;
+        } else {                               // few groups: two tiles, four wavefronts
+            p.tiles = 2;
             p.kwaves = 4;
-            p.depth = (G == 40) ? 10 : 8;
-        } else if (G >= 64) {
-            p.tiles = 2;
-            p.depth = 3;
-        } else if (NT <= 256 && G >= 32) {
-            p.tiles = 1;
             p.depth = 4;
-        } else if (NT > 256 && G >= 32) {     // attention in and out: two tiles, shallow
-            p.tiles = 2;
-            p.depth = 2;
-        } else if (G >= 16) {
-            p.tiles = 1;
-            p.depth = 2;
-        } else {
-            p.tiles = 2;
-            p.depth = 2;
         }
     } else if (M <= 4) {
         p.path = W4A16_PATH_MFMA;
@@ -281,10 +273,19 @@ void auto_plan(int M, int N, int K, w4a16_plan_t *out) {
             p.asrc = W4A16_ASRC_SPLITN;
             p.tiles = 1;
             p.depth = 4;
-        } else if (wide || mid) {              // A through the ring: two tiles up to 8 rows, four above
+        } else if (wide) {                     // A through the ring: two tiles up to 8 rows, four above
             p.asrc = W4A16_ASRC_RING;
             p.tiles = M <= 8 ? 2 : 4;
             p.depth = 2;
+        } else if (mid) {                      // A through the ring, two tiles; strips beyond a whole
+            p.asrc = W4A16_ASRC_RING;          // number per CU split four ways along K
+            p.tiles = 2;
+            p.depth = 2;
+            const int ns = (NT + 1) / 2, R = ns % kPlanCUs;
+            if (ns > kPlanCUs && R != 0 && 4 * R <= kPlanCUs && G >= 32) {
+                p.splits = 4;
+                p.whole = ns - R;
+            }
         } else if (deep) {
             p.tiles = 2;
             p.depth = 4;
@@ -294,9 +295,14 @@ void auto_plan(int M, int N, int K, w4a16_plan_t *out) {
                 p.asrc = W4A16_ASRC_LDS;
                 p.splits = 4;
             }
-        } else if (narrow && NT <= 256) {      // one tile, all of A in LDS
+        } else if (narrow && NT <= 256) {      // one tile, eight wavefronts: A in LDS to 7 rows, the ring above
             p.tiles = 1;
             p.kwaves = 8;
+            p.depth = 4;
+            if (M >= 8) p.asrc = W4A16_ASRC_RING;
+        } else if (narrow && G >= 8 && G < 32) {    // 8-31 groups: two tiles, ring A, depth 4
+            p.asrc = W4A16_ASRC_RING;
+            p.tiles = 2;
             p.depth = 4;
         } else if (M <= 7 || G >= 64) {       // all of A in LDS (eight wavefronts from 64 groups)
             p.tiles = 2;
@@ -327,7 +333,7 @@ void auto_plan(int M, int N, int K, w4a16_plan_t *out) {
     // (17408 x 5120: 256 whole strips and 64 strips in four pieces).  The
     // pieces' hand-off finishes long before the whole strips do.  (Two to
     // four rows keep the whole K range of A in LDS, which measures faster.)
-    if (narrow && deep && (M == 1 || M >= 5) && NT > kPlanCUs && NT % kPlanCUs != 0) {
+    if (narrow && (M == 1 ? deep : (M >= 5 && G >= 64)) && NT > kPlanCUs && NT % kPlanCUs != 0) {
         const int R = NT % kPlanCUs;
         int S = 1;
         while (S * 2 * R <= kPlanCUs && S * 2 <= G / 16) S *= 2;

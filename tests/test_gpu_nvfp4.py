@@ -161,6 +161,32 @@ def test_nvfp4_split_k_parity_and_reuse(splits):
                 assert int(ws[:65536].view(torch.int32).abs().sum()) == 0
 
 
+def test_nvfp4_ring_tail_every_remainder():
+    # as for GPTQ: K = 128 * G, one wavefront along K, so every remainder of
+    # the ring depth and every "fewer groups than slots" case occurs
+    N = 64
+    for G in range(1, 12):
+        K = 128 * G
+        A, packed, scales = synth.gen_nvfp4_problem(K, N, 70 + G)
+        blob, sc, a = to_dev(packed, scales, A)
+        Cref, Dref = oracle.nvfp4_gemm(A, packed, scales, ALPHA, 16, N, K)
+        ran = 0
+        for M in (1, 4, 9):
+            for path, asrc in ((w4.PATH_GEMV, w4.ASRC_LDS), (w4.PATH_MFMA, w4.ASRC_LDS), (w4.PATH_MFMA, w4.ASRC_RING)):
+                for t, kw in ((1, 1), (2, 1), (1, 4), (2, 4), (1, 8)):
+                    for d in (2, 3, 4, 5, 8, 10):
+                        p = w4.make_plan(path, t, kw, 1, asrc, d)
+                        if not w4.nvfp4_plan_ok(M, N, K, p):
+                            continue
+                        C1 = run(a, blob, sc, N, M, plan=p)
+                        C2 = run(a, blob, sc, N, M, plan=p)
+                        assert max_err(C1, Cref[:M], Dref[:M]) <= TOL, (G, M, p)
+                        assert torch.equal(C1.view(torch.int16), C2.view(torch.int16)), (G, M, p)
+                        ran += 1
+        note(f"[nvfp4 ring tail] G={G}: {ran} plans")
+        assert ran > 0
+
+
 def test_nvfp4_remainder_split_parity():
     # the leading strips whole, the rest split along K (the automatic NVFP4
     # plans of the down projection at one and two rows and of the gate/up

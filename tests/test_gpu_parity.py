@@ -125,6 +125,38 @@ def test_gemm_parity_every_plan_every_m(K, N, seed):
     note(f"  worst normalized error {worst:.3e}")
 
 
+def test_ring_tail_every_remainder():
+    # the ring driver's three ways to end: whole rounds, the exact tail with
+    # rt = ng mod D refills left (one compiled tail per rt, depths 2..4),
+    # and fewer groups than slots; K = 128 * G with G = 1..11 groups and one
+    # wavefront along K (ng = G), so every rt and every ng < D occurs for
+    # each depth; GEMV, staged, global and ring A; bitwise repeatable
+    N = 64
+    for G in range(1, 12):
+        K = 128 * G
+        A, qw, sc = synth.gen_problem(K, N, 60 + G)
+        q, s, a = to_dev(qw, sc, A)
+        blob = w4.repack_weights(q, K, N)
+        Cref, Dref = oracle.gemm(A, qw, sc, 16, N, K)
+        ran = 0
+        for M in (1, 3, 8, 16):
+            for path in (w4.PATH_GEMV, w4.PATH_MFMA):
+                for asrc in ((w4.ASRC_LDS,) if path == w4.PATH_GEMV else (w4.ASRC_LDS, w4.ASRC_GLOBAL, w4.ASRC_RING)):
+                    for t, kw in ((1, 1), (2, 1), (1, 4), (2, 4), (1, 8)):
+                        for d in (2, 3, 4, 5, 8, 10):
+                            p = w4.make_plan(path, t, kw, 1, asrc, d)
+                            if not w4.plan_ok(M, N, K, p):
+                                continue
+                            C1 = run_gemm(a, blob, s, N, M, plan=p)
+                            C2 = run_gemm(a, blob, s, N, M, plan=p)
+                            e = max_err(C1, Cref[:M], Dref[:M])
+                            assert e <= TOL, (G, M, p, e)
+                            assert torch.equal(C1.view(torch.int16), C2.view(torch.int16)), (G, M, p)
+                            ran += 1
+        note(f"[ring tail] G={G}: {ran} plans")
+        assert ran > 0
+
+
 @pytest.mark.parametrize("K,N,seed", [(5120, 96, 9), (17408, 48, 10)])
 def test_gemm_parity_every_plan_long_k(K, N, seed):
     # K = 5120 (40 groups) and 17408 (136 groups): wavefront group counts that

@@ -168,7 +168,8 @@ int validate_plan(const w4a16_plan_t &p, int M, int N, int K, int fmt = FMT_GPTQ
 // from 2048, "very wide" from 8192; "long" K from 128 groups of 128.
 //  * M = 1: the GEMV kernel; eight wavefronts with a ring of depth 2 and one
 //    tile per strip almost everywhere (two wavefronts or more per SIMD);
-//    two tiles for the attention output (257..384 tiles, 32..63 groups);
+//    two tiles for the attention output and QKV (257..512 tiles, 32..63
+//    groups);
 //    two tiles, four wavefronts, depth 4 below 16 groups; the very wide
 //    output head keeps two tiles, four wavefronts, depth 5;
 //  * M = 2..4: matrix cores; long K: the whole K range of A staged in LDS,
@@ -217,7 +218,7 @@ void auto_plan(int M, int N, int K, w4a16_plan_t *out) {
             p.tiles = 2;
             p.kwaves = deep ? 8 : 4;
             p.depth = deep ? 4 : 5;
-        } else if (NT > 256 && NT <= 384 && G >= 32 && G < 64) {   // attention out: two tiles, shallow
+        } else if (NT > 256 && NT <= 512 && G >= 32 && G < 64) {   // attention out, QKV: two tiles, shallow
             p.tiles = 2;
             p.depth = 2;
         } else if (G >= 16) {                  // one tile, eight shallow wavefronts

@@ -13,7 +13,7 @@
 
 #include "w4a16.h"
 
-// a valid call ends at the device check, or (a shape this build lacks) at the plan check
+// a valid call ends at the device check, or (a shape the library was compiled without) at the plan check
 static bool device_or_plan(int st) { return st == W4A16_ERR_DEVICE || st == W4A16_ERR_PLAN; }
 
 #define CHECK(c)                                                                 \

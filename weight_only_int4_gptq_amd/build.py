@@ -2,7 +2,7 @@
 
 libw4a16.so        the matmul path (repack, GEMV and MFMA kernels, C ABI)
 libw4a16_probe.so  a plain streaming-read kernel, used only by bench.py to
-                   measure the read bandwidth the box reaches at a byte count
+                   measure the read bandwidth the GPU reaches at a byte count
 """
 from __future__ import annotations
 

@@ -140,15 +140,19 @@ size_t w4a16_repacked_bytes(int K, int N);
 int w4a16_repack_weights(const void *qweight, void *wq_repacked, int K, int N, void *stream);
 
 /*
- * The plan w4a16_gemm uses for (M, N, K): fills *plan and returns W4A16_OK,
- * or returns an error status for invalid shapes.  Host-only, no device work.
+ * The plan w4a16_gemm uses for (M, N, K): the row-count dispatch of the page
+ * "Qwen3.8-27B on single DGX Spark ..." (section "How.": the matmuls are
+ * kernels dispatched by row count), extended here by the column and K
+ * shape.  Fills *plan and returns W4A16_OK, or returns an error status for
+ * invalid shapes.  Host-only, no device work.
  */
 int w4a16_get_plan(int M, int N, int K, w4a16_plan_t *plan);
 
 /*
  * W4A16_OK if the library can run `plan` for (M, N, K) (a kernel exists and
  * its LDS fits), W4A16_ERR_PLAN if not, W4A16_ERR_SHAPE for invalid shapes.
- * Host-only, no device work.
+ * A plan is one arm of the row-count dispatch (same page and section as
+ * w4a16_get_plan).  Host-only, no device work.
  */
 int w4a16_check_plan(int M, int N, int K, const w4a16_plan_t *plan);
 
@@ -171,7 +175,10 @@ int w4a16_check_plan(int M, int N, int K, const w4a16_plan_t *plan);
  * the counter region zero again and writes partials only after it, so one
  * workspace serves calls of any shape and plan issued one after another
  * (stream order); calls that share a workspace must not run concurrently.
- * Calls whose plan needs no workspace accept NULL.
+ * Calls whose plan needs no workspace accept NULL.  No page defines a
+ * workspace: it holds this library's split-K partials, which the row-count
+ * dispatch (page "Qwen3.8-27B on single DGX Spark ...", section "How.")
+ * uses for narrow matrices.
  */
 size_t w4a16_workspace_bytes(int M, int N, int K);
 
@@ -206,7 +213,9 @@ int w4a16_gemm(const void *A, const void *wq_repacked, const void *scales, void 
                void *stream);
 
 /*
- * As w4a16_gemm, with an explicit plan (plan == NULL: same as w4a16_gemm).
+ * As w4a16_gemm (same passages), with an explicit plan: one arm of the
+ * row-count dispatch of the page "Qwen3.8-27B on single DGX Spark ..."
+ * (section "How.") chosen by the caller (plan == NULL: same as w4a16_gemm).
  * Returns W4A16_ERR_PLAN when the library has no kernel for the plan.
  */
 int w4a16_gemm_plan(const void *A, const void *wq_repacked, const void *scales, void *C,
@@ -260,8 +269,9 @@ int w4a16_gemm_silu_mul(const void *A, const void *wq_repacked, const void *scal
                         void *stream);
 
 /*
- * As w4a16_gemm_silu_mul with an explicit plan, whose tile count must be
- * even (W4A16_ERR_PLAN otherwise).
+ * As w4a16_gemm_silu_mul (same passages) with an explicit plan of the
+ * row-count dispatch, whose tile count must be even (W4A16_ERR_PLAN
+ * otherwise).
  */
 int w4a16_gemm_silu_mul_plan(const void *A, const void *wq_repacked, const void *scales, void *H,
                              int M, int N, int K, int group, void *workspace,
@@ -281,7 +291,7 @@ int w4a16_gemm_silu_mul_plan(const void *A, const void *wq_repacked, const void 
 int w4a16_gemm_f32(const void *A, const void *wq_repacked, const void *scales, float *C, int M,
                    int N, int K, int group, void *workspace, size_t workspace_bytes, void *stream);
 
-/* As w4a16_gemm_f32 with an explicit plan. */
+/* As w4a16_gemm_f32 (same passages) with an explicit plan of the row-count dispatch. */
 int w4a16_gemm_f32_plan(const void *A, const void *wq_repacked, const void *scales, float *C, int M,
                         int N, int K, int group, void *workspace, size_t workspace_bytes,
                         const w4a16_plan_t *plan, void *stream);
@@ -315,7 +325,7 @@ int w4a16_gemm_argmax(const void *A, const void *wq_repacked, const void *scales
                       float *val, int M, int N, int K, int group, void *workspace,
                       size_t workspace_bytes, void *stream);
 
-/* As w4a16_gemm_argmax with an explicit plan (splits must be 1). */
+/* As w4a16_gemm_argmax (same passages) with an explicit plan of the row-count dispatch (splits must be 1). */
 int w4a16_gemm_argmax_plan(const void *A, const void *wq_repacked, const void *scales, int *idx,
                            float *val, int M, int N, int K, int group, void *workspace,
                            size_t workspace_bytes, const w4a16_plan_t *plan, void *stream);
@@ -332,7 +342,9 @@ int w4a16_dequant_debug(const void *wq_repacked, const void *scales, float *W, i
 
 /*
  * Test export of the device unpacking used by both GEMM paths:
- * codes[k][n] = q in [0, 15], device uint8 [K][N] (written).
+ * codes[k][n] = q in [0, 15], device uint8 [K][N] (written): the 4-bit codes
+ * of the checkpoint format (page "Qwen3.8-27B on single DGX Spark ...",
+ * section "Quality.").
  */
 int w4a16_unpack_debug(const void *wq_repacked, uint8_t *codes, int K, int N, void *stream);
 
@@ -373,15 +385,17 @@ size_t w4a16_nvfp4_repacked_bytes(int K, int N);
 size_t w4a16_nvfp4_repacked_scale_bytes(int K, int N);
 
 /*
- * One-time repacks into the layouts above (pure permutations of bytes).
+ * One-time repacks into the layouts above (pure permutations of bytes) of
+ * the checkpoint tensors the NVFP4 section above cites.
  *   packed / scales           device, as above (read only)
  *   wq_repacked / scales_repacked  device, the sizes above (written)
  */
 int w4a16_nvfp4_repack_weights(const void *packed, void *wq_repacked, int K, int N, void *stream);
 int w4a16_nvfp4_repack_scales(const void *scales, void *scales_repacked, int K, int N, void *stream);
 
-/* Planning for the NVFP4 calls: as w4a16_get_plan, w4a16_check_plan,
- * w4a16_workspace_bytes and w4a16_workspace_bytes_plan. */
+/* Planning for the NVFP4 calls (the same row-count dispatch, page
+ * "Qwen3.8-27B on single DGX Spark ...", section "How."): as w4a16_get_plan,
+ * w4a16_check_plan, w4a16_workspace_bytes and w4a16_workspace_bytes_plan. */
 int w4a16_nvfp4_get_plan(int M, int N, int K, w4a16_plan_t *plan);
 int w4a16_nvfp4_check_plan(int M, int N, int K, const w4a16_plan_t *plan);
 size_t w4a16_nvfp4_workspace_bytes(int M, int N, int K);
@@ -402,7 +416,7 @@ int w4a16_nvfp4_gemm(const void *A, const void *wq_repacked, const void *scales,
                      int M, int N, int K, int group, void *workspace, size_t workspace_bytes,
                      void *stream);
 
-/* As w4a16_nvfp4_gemm with an explicit plan. */
+/* As w4a16_nvfp4_gemm (same passages) with an explicit plan of the row-count dispatch. */
 int w4a16_nvfp4_gemm_plan(const void *A, const void *wq_repacked, const void *scales, float alpha,
                           void *C, int M, int N, int K, int group, void *workspace,
                           size_t workspace_bytes, const w4a16_plan_t *plan, void *stream);
@@ -441,7 +455,10 @@ int w4a16_nvfp4_gemm_f32_plan(const void *A, const void *wq_repacked, const void
 
 /*
  * Test export of the NVFP4 device dequantization: W[k][n] = e2m1 * e4m3 as
- * fp32 (exact; without alpha), device fp32 [K][N] (written).
+ * fp32 (exact; without alpha), device fp32 [K][N] (written), for the
+ * format the NVFP4 section above cites (compressed-tensors
+ * "nvfp4-pack-quantized", page "Qwen3.8 27B - NVFP4 for veloGB10", section
+ * "Specifications").
  */
 int w4a16_nvfp4_dequant(const void *wq_repacked, const void *scales, float *W, int K, int N,
                         void *stream);

@@ -48,16 +48,16 @@ HEADLINE_MS = {"down": (1, 4, 8, 16), "qkv": (1, 4, 8, 16), "attn_out": (1, 4, 8
 PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 LLC_BYTES = 256 << 20          # MI355X Infinity Cache
 ROTATE_BYTES = 1 << 30         # rotate over >= 1 GiB of buffer sets
-KERNEL_SOURCES = ["weight_only_int4_gptq_amd/csrc/w4a16.hip",
-                  "weight_only_int4_gptq_amd/csrc/w4a16_kernels.hpp",
-                  "weight_only_int4_gptq_amd/csrc/w4a16_variants.hpp",
-                  "weight_only_int4_gptq_amd/csrc/variants_plain.hip",
-                  "weight_only_int4_gptq_amd/csrc/variants_epi.hip",
-                  "weight_only_int4_gptq_amd/csrc/variants_plain_rt.hip",
-                  "weight_only_int4_gptq_amd/csrc/variants_epi_rt.hip",
-                  "weight_only_int4_gptq_amd/build.py",
-                  "weight_only_int4_gptq_amd/csrc/variants_nvfp4.hip",
-                  "weight_only_int4_gptq_amd/csrc/variants_nvfp4_epi.hip"]
+# the files the matmul kernels are built from (their hash ties counters to a build)
+KERNEL_SOURCES = (["weight_only_int4_gptq_amd/csrc/w4a16_kernels.hpp",
+                   "weight_only_int4_gptq_amd/csrc/w4a16_variants.hpp",
+                   "weight_only_int4_gptq_amd/build.py"] +
+                  ["weight_only_int4_gptq_amd/csrc/" + u for u in
+                   ("w4a16.hip",
+                    "variants_plain_gemv.hip", "variants_plain_mfma12.hip", "variants_plain_mfma34.hip",
+                    "variants_plain_rt.hip", "variants_epi_gemv.hip", "variants_epi_mfma12.hip",
+                    "variants_epi_mfma34.hip", "variants_epi_rt.hip", "variants_nvfp4_gemv.hip",
+                    "variants_nvfp4_mfma.hip", "variants_nvfp4_epi_gemv.hip", "variants_nvfp4_epi_mfma.hip")])
 
 
 def log(*a):

@@ -16,8 +16,11 @@ import pytest
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 OUT = os.path.join(ROOT, "_build", "sanitize")
 CSRC = os.path.join(ROOT, "weight_only_int4_gptq_amd", "csrc")
-HIP_UNITS = ["w4a16.hip", "variants_plain.hip", "variants_plain_rt.hip", "variants_epi.hip",
-             "variants_epi_rt.hip", "variants_nvfp4.hip", "variants_nvfp4_epi.hip"]
+HIP_UNITS = ["w4a16.hip",
+             "variants_plain_gemv.hip", "variants_plain_mfma12.hip", "variants_plain_mfma34.hip",
+             "variants_plain_rt.hip", "variants_epi_gemv.hip", "variants_epi_mfma12.hip",
+             "variants_epi_mfma34.hip", "variants_epi_rt.hip", "variants_nvfp4_gemv.hip",
+             "variants_nvfp4_mfma.hip", "variants_nvfp4_epi_gemv.hip", "variants_nvfp4_epi_mfma.hip"]
 ENV = dict(os.environ, ASAN_OPTIONS="detect_leaks=0:abort_on_error=1",
            UBSAN_OPTIONS="print_stacktrace=1:halt_on_error=1")
 

@@ -1,5 +1,5 @@
 // Matmul kernels that carry the epilogue modes (gate/up activation, row
-// argmax, fp32 output), compile-time row counts.
+// argmax, fp32 output): the matrix-core path for three or four rows.
 #include <hip/hip_runtime.h>
 
 #include "w4a16_variants.hpp"
@@ -7,7 +7,7 @@
 namespace w4a16 {
 
 #define W4A16_V(P, MM, T, KW, D, AS) {P, MM, T, KW, D, AS, gemm_kernel<P, MM, T, KW, D, AS, true>},
-const Variant kVariantsEpiCt[] = {W4A16_VARIANT_LIST_CT(W4A16_V)};
-const int kNumEpiCt = sizeof(kVariantsEpiCt) / sizeof(kVariantsEpiCt[0]);
+const Variant kVariantsEpiMfma34[] = {W4A16_VARIANT_LIST_CT_MFMA34(W4A16_V)};
+const int kNumEpiMfma34 = sizeof(kVariantsEpiMfma34) / sizeof(kVariantsEpiMfma34[0]);
 
 }  // namespace w4a16

@@ -1,0 +1,12 @@
+// NVFP4 weight-only matmul kernels, plain: the GEMV path.
+#include <hip/hip_runtime.h>
+
+#include "w4a16_variants.hpp"
+
+namespace w4a16 {
+
+#define W4A16_V(P, MM, T, KW, D, AS) {P, MM, T, KW, D, AS, gemm_kernel<P, MM, T, KW, D, AS, false, FMT_NVFP4>},
+const Variant kVariantsNvGemv[] = {W4A16_NV_VARIANT_LIST_GEMV(W4A16_V)};
+const int kNumNvGemv = sizeof(kVariantsNvGemv) / sizeof(kVariantsNvGemv[0]);
+
+}  // namespace w4a16

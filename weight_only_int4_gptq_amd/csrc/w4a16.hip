@@ -47,17 +47,14 @@ const Variant *find_variant(const w4a16_plan_t &p, int M, bool epi = false, int 
                        : 0;
     const int asrc = (p.path == W4A16_PATH_GEMV) ? ASRC_LDS : p.asrc;
     const int depth = p.depth ? p.depth : default_depth(p.tiles);
-    VariantTable tabs[2];
-    int ntabs = 0;
-    if (fmt == FMT_NVFP4) {
-        tabs[ntabs++] = epi ? VariantTable{kVariantsNvEpi, kNumVariantsNvEpi} : VariantTable{kVariantsNv, kNumVariantsNv};
-    } else if (epi) {
-        tabs[ntabs++] = {kVariantsEpiCt, kNumEpiCt};
-        tabs[ntabs++] = {kVariantsEpiRt, kNumEpiRt};
-    } else {
-        tabs[ntabs++] = {kVariantsPlainCt, kNumPlainCt};
-        tabs[ntabs++] = {kVariantsPlainRt, kNumPlainRt};
-    }
+    const VariantTable plain[] = {{kVariantsPlainGemv, kNumPlainGemv}, {kVariantsPlainMfma12, kNumPlainMfma12},
+                                  {kVariantsPlainMfma34, kNumPlainMfma34}, {kVariantsPlainRt, kNumPlainRt}};
+    const VariantTable with_epi[] = {{kVariantsEpiGemv, kNumEpiGemv}, {kVariantsEpiMfma12, kNumEpiMfma12},
+                                     {kVariantsEpiMfma34, kNumEpiMfma34}, {kVariantsEpiRt, kNumEpiRt}};
+    const VariantTable nv[] = {{kVariantsNvGemv, kNumNvGemv}, {kVariantsNvMfma, kNumNvMfma}};
+    const VariantTable nv_epi[] = {{kVariantsNvEpiGemv, kNumNvEpiGemv}, {kVariantsNvEpiMfma, kNumNvEpiMfma}};
+    const VariantTable *tabs = fmt == FMT_NVFP4 ? (epi ? nv_epi : nv) : (epi ? with_epi : plain);
+    const int ntabs = fmt == FMT_NVFP4 ? 2 : 4;
     for (int ti = 0; ti < ntabs; ++ti)
         for (int i = 0; i < tabs[ti].n; ++i) {
             const Variant &v = tabs[ti].v[i];
@@ -71,9 +68,12 @@ const Variant *find_variant(const w4a16_plan_t &p, int M, bool epi = false, int 
 // A dense index of a kernel over every table (for per-kernel host caches), or
 // -1 if it is in none.
 int variant_slot(const Variant *v) {
-    const VariantTable tabs[] = {{kVariantsPlainCt, kNumPlainCt}, {kVariantsPlainRt, kNumPlainRt},
-                                 {kVariantsEpiCt, kNumEpiCt},     {kVariantsEpiRt, kNumEpiRt},
-                                 {kVariantsNv, kNumVariantsNv},   {kVariantsNvEpi, kNumVariantsNvEpi}};
+    const VariantTable tabs[] = {{kVariantsPlainGemv, kNumPlainGemv},   {kVariantsPlainMfma12, kNumPlainMfma12},
+                                 {kVariantsPlainMfma34, kNumPlainMfma34}, {kVariantsPlainRt, kNumPlainRt},
+                                 {kVariantsEpiGemv, kNumEpiGemv},       {kVariantsEpiMfma12, kNumEpiMfma12},
+                                 {kVariantsEpiMfma34, kNumEpiMfma34},   {kVariantsEpiRt, kNumEpiRt},
+                                 {kVariantsNvGemv, kNumNvGemv},         {kVariantsNvMfma, kNumNvMfma},
+                                 {kVariantsNvEpiGemv, kNumNvEpiGemv},   {kVariantsNvEpiMfma, kNumNvEpiMfma}};
     int base = 0;
     for (const VariantTable &t : tabs) {
         if (v >= t.v && v < t.v + t.n) return base + (int)(v - t.v);

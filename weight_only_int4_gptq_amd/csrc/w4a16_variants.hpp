@@ -1,6 +1,6 @@
-// The compiled kernel shapes of the W4A16 matmul, shared by the two
-// instantiation units (variants_plain.hip, variants_epi.hip) and the host
-// code that picks a kernel for a plan.
+// The compiled kernel shapes of the W4A16 matmul, shared by the
+// instantiation units (variants_*.hip) and the host code that picks a kernel
+// for a plan.
 #pragma once
 
 #include "w4a16_kernels.hpp"
@@ -38,23 +38,29 @@ struct Variant {
 
 // Kernels with compile-time rows (GEMV, and matrix-core kernels for one to
 // four rows) and kernels that take the row count at run time (matrix cores,
-// five rows and more, and ring A): two instantiation units each, compiled
-// with different register choices for the matrix-core results (see build.py).
+// five rows and more, and ring A) sit in separate instantiation units,
+// compiled with different register choices for the matrix-core results
+// (build.py).
+
 // more wavefronts per SIMD for one row: shallow rings, eight or sixteen along K
 #define W4A16_MANYWAVE(X, P, MM, AS) \
     X(P, MM, 2, 8, 2, AS) X(P, MM, 2, 8, 3, AS) X(P, MM, 4, 8, 2, AS) X(P, MM, 2, 16, 2, AS) \
     X(P, MM, 1, 16, 2, AS) X(P, MM, 4, 4, 3, AS) X(P, MM, 2, 8, 5, AS) X(P, MM, 1, 8, 2, AS)
 
-#define W4A16_VARIANT_LIST_CT(X)                                                                    \
-    W4A16_MANYWAVE(X, PATH_GEMV, 1, ASRC_LDS)                                                       \
-    W4A16_ONESHOT(X, PATH_GEMV, 1, ASRC_LDS) W4A16_ONESHOT(X, PATH_MFMA, 1, ASRC_LDS)               \
-    W4A16_ONESHOT(X, PATH_MFMA, 1, ASRC_GLOBAL)                                                     \
+// The compile-time-row list in three parts, one instantiation unit each (the
+// units compile in parallel): GEMV kernels, matrix-core kernels for one or
+// two rows, and matrix-core kernels for three or four rows.
+#define W4A16_VARIANT_LIST_CT_GEMV(X)                                                               \
+    W4A16_MANYWAVE(X, PATH_GEMV, 1, ASRC_LDS) W4A16_ONESHOT(X, PATH_GEMV, 1, ASRC_LDS)              \
     W4A16_SHAPES(X, PATH_GEMV, 1, ASRC_LDS) W4A16_SHAPES(X, PATH_GEMV, 2, ASRC_LDS)                 \
-    W4A16_SHAPES(X, PATH_GEMV, 3, ASRC_LDS) W4A16_SHAPES(X, PATH_GEMV, 4, ASRC_LDS)                 \
-    W4A16_WIDE(X, PATH_MFMA, 2, ASRC_LDS) W4A16_WIDE(X, PATH_MFMA, 3, ASRC_LDS)                     \
-    W4A16_WIDE(X, PATH_MFMA, 4, ASRC_LDS)                                                           \
+    W4A16_SHAPES(X, PATH_GEMV, 3, ASRC_LDS) W4A16_SHAPES(X, PATH_GEMV, 4, ASRC_LDS)
+#define W4A16_VARIANT_LIST_CT_MFMA12(X)                                                             \
+    W4A16_ONESHOT(X, PATH_MFMA, 1, ASRC_LDS) W4A16_ONESHOT(X, PATH_MFMA, 1, ASRC_GLOBAL)            \
+    W4A16_WIDE(X, PATH_MFMA, 2, ASRC_LDS)                                                           \
     W4A16_SHAPES(X, PATH_MFMA, 1, ASRC_LDS) W4A16_SHAPES(X, PATH_MFMA, 1, ASRC_GLOBAL)              \
-    W4A16_SHAPES(X, PATH_MFMA, 2, ASRC_LDS) W4A16_SHAPES(X, PATH_MFMA, 2, ASRC_GLOBAL)              \
+    W4A16_SHAPES(X, PATH_MFMA, 2, ASRC_LDS) W4A16_SHAPES(X, PATH_MFMA, 2, ASRC_GLOBAL)
+#define W4A16_VARIANT_LIST_CT_MFMA34(X)                                                             \
+    W4A16_WIDE(X, PATH_MFMA, 3, ASRC_LDS) W4A16_WIDE(X, PATH_MFMA, 4, ASRC_LDS)                     \
     W4A16_SHAPES(X, PATH_MFMA, 3, ASRC_LDS) W4A16_SHAPES(X, PATH_MFMA, 3, ASRC_GLOBAL)              \
     W4A16_SHAPES(X, PATH_MFMA, 4, ASRC_LDS) W4A16_SHAPES(X, PATH_MFMA, 4, ASRC_GLOBAL)
 // four wavefronts splitting the columns around one shared ring of A
@@ -68,14 +74,16 @@ struct Variant {
     W4A16_SHAPES(X, PATH_MFMA, 0, ASRC_LDS) W4A16_SHAPES(X, PATH_MFMA, 0, ASRC_GLOBAL)
 
 // Kernel tables, one per instantiation unit: plain matmuls and kernels that
-// also carry the epilogue modes, each split into compile-time-row (Ct) and
-// run-time-row (Rt) shapes.
+// also carry the epilogue modes, each in the three compile-time-row parts
+// and one run-time-row (Rt) table.
 struct VariantTable {
     const Variant *v;
     int n;
 };
-extern const Variant kVariantsPlainCt[], kVariantsPlainRt[], kVariantsEpiCt[], kVariantsEpiRt[];
-extern const int kNumPlainCt, kNumPlainRt, kNumEpiCt, kNumEpiRt;
+extern const Variant kVariantsPlainGemv[], kVariantsPlainMfma12[], kVariantsPlainMfma34[], kVariantsPlainRt[];
+extern const Variant kVariantsEpiGemv[], kVariantsEpiMfma12[], kVariantsEpiMfma34[], kVariantsEpiRt[];
+extern const int kNumPlainGemv, kNumPlainMfma12, kNumPlainMfma34, kNumPlainRt;
+extern const int kNumEpiGemv, kNumEpiMfma12, kNumEpiMfma34, kNumEpiRt;
 
 // NVFP4 weight-only kernels (one table plain, one with the epilogue modes;
 // A staged in LDS, read from global memory or through the LDS ring): the
@@ -86,12 +94,14 @@ extern const int kNumPlainCt, kNumPlainRt, kNumEpiCt, kNumEpiRt;
 #define W4A16_NV_MFMA(X, MM, AS) \
     X(PATH_MFMA, MM, 1, 1, 8, AS) X(PATH_MFMA, MM, 1, 8, 4, AS) X(PATH_MFMA, MM, 2, 4, 4, AS) \
     X(PATH_MFMA, MM, 2, 8, 4, AS) X(PATH_MFMA, MM, 4, 4, 2, AS) X(PATH_MFMA, MM, 1, 4, 8, AS)
-#define W4A16_NV_VARIANT_LIST(X)                                                                  \
+// in two parts, one unit each: the GEMV kernels and the matrix-core kernels
+#define W4A16_NV_VARIANT_LIST_GEMV(X)                                                             \
     W4A16_NV_GEMV(X, 1) W4A16_NV_GEMV(X, 2) W4A16_NV_GEMV(X, 3) W4A16_NV_GEMV(X, 4)               \
     X(PATH_GEMV, 1, 2, 4, 5, ASRC_LDS) X(PATH_GEMV, 1, 1, 4, 10, ASRC_LDS)                         \
     X(PATH_GEMV, 1, 2, 8, 2, ASRC_LDS) X(PATH_GEMV, 1, 2, 2, 8, ASRC_LDS)                           \
     X(PATH_GEMV, 1, 1, 8, 2, ASRC_LDS) X(PATH_GEMV, 1, 1, 8, 3, ASRC_LDS)                           \
-    X(PATH_GEMV, 1, 1, 16, 2, ASRC_LDS) X(PATH_GEMV, 1, 2, 8, 3, ASRC_LDS)                          \
+    X(PATH_GEMV, 1, 1, 16, 2, ASRC_LDS) X(PATH_GEMV, 1, 2, 8, 3, ASRC_LDS)
+#define W4A16_NV_VARIANT_LIST_MFMA(X)                                                             \
     W4A16_NV_MFMA(X, 0, ASRC_LDS) W4A16_NV_MFMA(X, 0, ASRC_GLOBAL)                                 \
     X(PATH_MFMA, 0, 8, 1, 4, ASRC_GLOBAL) X(PATH_MFMA, 0, 8, 2, 2, ASRC_GLOBAL)                    \
     X(PATH_MFMA, 0, 8, 1, 2, ASRC_GLOBAL) X(PATH_MFMA, 0, 8, 1, 3, ASRC_GLOBAL)                    \
@@ -107,15 +117,22 @@ extern const int kNumPlainCt, kNumPlainRt, kNumEpiCt, kNumEpiRt;
 // undefined-behaviour sanitizers (the planner then falls back where a shape
 // is missing; the library itself is always built with every shape).
 #ifdef W4A16_VARIANT_SUBSET
-#undef W4A16_VARIANT_LIST_CT
+#undef W4A16_VARIANT_LIST_CT_GEMV
+#undef W4A16_VARIANT_LIST_CT_MFMA12
+#undef W4A16_VARIANT_LIST_CT_MFMA34
 #undef W4A16_VARIANT_LIST_RT
-#undef W4A16_NV_VARIANT_LIST
-#define W4A16_VARIANT_LIST_CT(X) X(PATH_GEMV, 1, 1, 8, 2, ASRC_LDS) X(PATH_MFMA, 2, 2, 4, 4, ASRC_LDS)
+#undef W4A16_NV_VARIANT_LIST_GEMV
+#undef W4A16_NV_VARIANT_LIST_MFMA
+#define W4A16_VARIANT_LIST_CT_GEMV(X) X(PATH_GEMV, 1, 1, 8, 2, ASRC_LDS)
+#define W4A16_VARIANT_LIST_CT_MFMA12(X) X(PATH_MFMA, 2, 2, 4, 4, ASRC_LDS)
+#define W4A16_VARIANT_LIST_CT_MFMA34(X) X(PATH_MFMA, 4, 2, 4, 4, ASRC_LDS)
 #define W4A16_VARIANT_LIST_RT(X) X(PATH_MFMA, 0, 2, 4, 2, ASRC_RING) X(PATH_MFMA, 0, 2, 4, 4, ASRC_LDS)
-#define W4A16_NV_VARIANT_LIST(X) X(PATH_GEMV, 1, 1, 8, 2, ASRC_LDS) X(PATH_MFMA, 0, 2, 4, 2, ASRC_RING)
+#define W4A16_NV_VARIANT_LIST_GEMV(X) X(PATH_GEMV, 1, 1, 8, 2, ASRC_LDS)
+#define W4A16_NV_VARIANT_LIST_MFMA(X) X(PATH_MFMA, 0, 2, 4, 2, ASRC_RING)
 #endif
 
-extern const Variant kVariantsNv[], kVariantsNvEpi[];   // plain, and with the epilogue modes
-extern const int kNumVariantsNv, kNumVariantsNvEpi;
+// plain, and with the epilogue modes; GEMV and matrix-core parts
+extern const Variant kVariantsNvGemv[], kVariantsNvMfma[], kVariantsNvEpiGemv[], kVariantsNvEpiMfma[];
+extern const int kNumNvGemv, kNumNvMfma, kNumNvEpiGemv, kNumNvEpiMfma;
 
 }  // namespace w4a16

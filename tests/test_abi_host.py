@@ -162,8 +162,8 @@ def test_row_count_dispatch():
         # gate/up width: one tile and eight shallow wavefronts at one row;
         # A through the LDS ring from two to 4 rows, two tiles; from five
         # rows four wavefronts split the columns (one tile each up to 8 rows,
-        # two above) around a shared ring, and the 32 (16) strips beyond two
-        # (one) per CU are split four ways along K
+        # two above) around a shared ring of depth 4, and the 32 (16) strips
+        # beyond two (one) per CU are split four ways along K
         if M == 1:
             assert (p.tiles, p.kwaves, p.depth, p.splits) == (1, 8, 2, 1), (M, p)
         elif M <= 4:
@@ -171,7 +171,7 @@ def test_row_count_dispatch():
         elif M <= 8:
             assert p.asrc == w4.ASRC_SPLITN and (p.tiles, p.kwaves, p.depth, p.splits, p.whole) == (1, 4, 4, 4, 512), (M, p)
         else:
-            assert p.asrc == w4.ASRC_SPLITN and (p.tiles, p.kwaves, p.depth, p.splits, p.whole) == (2, 4, 3, 4, 256), (M, p)
+            assert p.asrc == w4.ASRC_SPLITN and (p.tiles, p.kwaves, p.depth, p.splits, p.whole) == (2, 4, 4, 4, 256), (M, p)
     # QKV and attention-out widths (one to two two-tile strips per CU, 40 and
     # 48 groups): eight wavefronts, two tiles; A whole in LDS at 2-3 rows,
     # the ring from 4
@@ -201,17 +201,23 @@ def test_row_count_dispatch():
     assert (p.path, p.tiles, p.kwaves, p.depth) == (w4.PATH_GEMV, 1, 8, 2), p
     p = w4.nvfp4_get_plan(8, 5120, 6144)
     assert (p.asrc, p.tiles, p.kwaves, p.depth) == (w4.ASRC_LDS, 2, 8, 4), p
-    # the down projection (320 tiles, 136 groups) at one row and from five:
-    # 256 whole one-tile strips and 64 strips in four K pieces, eight
-    # wavefronts; two to four rows keep the whole K of A in LDS, unsplit
+    # the down projection (320 tiles, 136 groups) at one row and from five
+    # to twelve: 256 whole one-tile strips and 64 strips in four K pieces,
+    # eight wavefronts; two to four rows keep the whole K of A in LDS,
+    # unsplit; from 13 rows split-N (four one-tile wavefronts around a shared
+    # ring of A) with every strip in eight K pieces of 17 groups
     for M in (2, 3, 4):
         p = w4.get_plan(M, 5120, 17408)
         assert (p.splits, p.asrc, p.tiles, p.kwaves) == (1, w4.ASRC_LDS, 2, 8), (M, p)
-    for M in (1, 5, 8, 9, 16):
+    for M in (1, 5, 8, 9, 12):
         p = w4.get_plan(M, 5120, 17408)
         assert (p.tiles, p.kwaves, p.splits, p.whole) == (1, 8, 4, 256), (M, p)
         assert p.path == (w4.PATH_GEMV if M == 1 else w4.PATH_MFMA), (M, p)
         assert M == 1 or p.asrc == w4.ASRC_RING, (M, p)
+    for M in (13, 16):
+        p = w4.get_plan(M, 5120, 17408)
+        assert (p.path, p.asrc, p.tiles, p.kwaves, p.depth, p.splits, p.whole) == \
+            (w4.PATH_MFMA, w4.ASRC_SPLITN, 1, 4, 4, 8, 0), (M, p)
     # one GPU's tensor-parallel shares at 8 rows: up to 256 tiles, one tile
     # and eight wavefronts with A through the ring; the 544/1088-tile column
     # shards split their strips beyond a whole number per CU four ways; the

@@ -482,6 +482,50 @@ def test_epilogue_modes_remainder_split():
     assert int(ws[:65536].view(torch.int32).abs().sum()) == 0
 
 
+def test_deep_split_reduction():
+    # 16 and 32 pieces per strip: the last workgroup adds the partials in
+    # several batches of loads.  Ragged strips (33 tiles; 34 for gate/up):
+    # some split-N wavefronts of the last strip hold no tile.  Plain C, the
+    # gate/up activation and the fp32 output; repeated calls are bitwise
+    # equal and leave the counters zero.
+    K = 4096
+    ran = 0
+    for N in (528, 544):
+        A, qw, sc = synth.gen_problem(K, N, 38 + N)
+        q, s, a = to_dev(qw, sc, A)
+        blob = w4.repack_weights(q, K, N)
+        C16, D16 = oracle.gemm(A, qw, sc, 16, N, K)
+        Href, E = oracle.gemm_silu_mul(A, qw, sc, 16, N, K) if N == 544 else (None, None)
+        shapes = [(w4.PATH_MFMA, 1, 4, 4, w4.ASRC_SPLITN), (w4.PATH_MFMA, 2, 4, 2, w4.ASRC_SPLITN),
+                  (w4.PATH_MFMA, 1, 1, 8, w4.ASRC_LDS), (w4.PATH_GEMV, 1, 1, 8, w4.ASRC_LDS),
+                  (w4.PATH_MFMA, 1, 4, 4, w4.ASRC_RING)]
+        for M in (1, 5, 16):
+            for (path, t, kw, d, asrc) in shapes:
+                for S in (8, 16, 32):
+                    p = w4.make_plan(path, t, kw, S, asrc, d)
+                    if not w4.plan_ok(M, N, K, p):
+                        continue
+                    ws = torch.zeros(w4.workspace_bytes(M, N, K, p), dtype=torch.uint8, device=DEV)
+                    note(f"[deep split] N={N} M={M} plan={p}")
+                    C1 = run_gemm(a, blob, s, N, M, plan=p, ws=ws)
+                    C2 = run_gemm(a, blob, s, N, M, plan=p, ws=ws)
+                    e = max_err(C1, C16[:M], D16[:M])
+                    assert e <= TOL, (M, p, e)
+                    assert torch.equal(C1.view(torch.int16), C2.view(torch.int16)), (M, p)
+                    F = w4.gemm_f32(a[:M].contiguous(), blob, s, N, plan=p, workspace=ws)
+                    torch.cuda.synchronize()
+                    ef = oracle.normalized_error(F.cpu().numpy().astype(np.float64), C16[:M], D16[:M])
+                    assert ef.max() <= TOL, (M, p, float(ef.max()))
+                    if Href is not None and t % 2 == 0:
+                        H = w4.gemm_silu_mul(a[:M].contiguous(), blob, s, N, plan=p, workspace=ws)
+                        torch.cuda.synchronize()
+                        silu_mul_check(H, Href[:M], E[:M], (M, p))
+                    assert int(ws[:65536].view(torch.int32).abs().sum()) == 0
+                    ran += 1
+    note(f"[deep split] {ran} plans")
+    assert ran >= 40
+
+
 def test_silu_mul_zero_gate_is_exact_zero_and_odd_tiles_rejected():
     K, N = 512, 256
     A, qw, sc = synth.gen_problem(K, N, 35)

@@ -182,8 +182,8 @@ int validate_plan(const w4a16_plan_t &p, int M, int N, int K, int fmt = FMT_GPTQ
 //      - very wide N: four wavefronts split the columns (two tiles each up
 //        to 8 rows, four above) around one shared ring of A, depth 2;
 //      - wide N from 32 groups: the same with one tile each (two above 8
-//        rows), the strips beyond a whole number per CU split four ways
-//        along K;
+//        rows), depth 4, the strips beyond a whole number per CU split four
+//        ways along K;
 //      - mid N: A through the ring, two tiles, depth 2, with the same
 //        remainder split;
 //      - long K: A through the ring from M = 8; below, a quarter of K of A
@@ -194,8 +194,9 @@ int validate_plan(const w4a16_plan_t &p, int M, int N, int K, int fmt = FMT_GPTQ
 //      - otherwise two tiles: all of A in LDS up to 7 rows and from 64
 //        groups (depth 4, eight wavefronts from 64 groups), A through the
 //        ring otherwise (depth 2; depth 4 for narrow N from 32 groups).
-//  Two rules override these (below): the QKV and attention-output widths,
-//  and the remainder split of narrow N with long K.  Staged A that does
+//  Three rules override these (below): the QKV and attention-output widths,
+//  the remainder split of narrow N with long K, and split-N with K pieces
+//  for narrow N with long K from 13 rows.  Staged A that does
 //  not fit in LDS goes through the ring with four wavefronts.
 void auto_plan(int M, int N, int K, w4a16_plan_t *out) {
     const int NT = N / 16, G = K / W4A16_GROUP;
@@ -263,7 +264,7 @@ void auto_plan(int M, int N, int K, w4a16_plan_t *out) {
         } else if (wide && G >= 32) {          // four wavefronts split 4 (8 above 8 rows) tiles, shared A
             p.asrc = W4A16_ASRC_SPLITN;
             p.tiles = M <= 8 ? 1 : 2;
-            p.depth = M <= 8 ? 4 : 3;
+            p.depth = 4;
             // strips beyond a whole number per CU: split four ways along K
             const int ns = (NT + 4 * p.tiles - 1) / (4 * p.tiles), R = ns % kPlanCUs;
             if (ns > kPlanCUs && R != 0 && 4 * R <= kPlanCUs) {
@@ -347,6 +348,21 @@ void auto_plan(int M, int N, int K, w4a16_plan_t *out) {
             p.splits = S;
             p.whole = NT - R;
         }
+    }
+    // Narrow N with long K from 13 rows: four wavefronts split four
+    // one-tile columns around one shared ring of A (a quarter of the A
+    // traffic of the per-wavefront ring), every strip split along K into
+    // pieces of at least 16 groups, at most eight (17408 x 5120: 80 strips
+    // in eight pieces of 17 groups).
+    if (narrow && deep && M >= 13) {
+        p.path = W4A16_PATH_MFMA;
+        p.asrc = W4A16_ASRC_SPLITN;
+        p.tiles = 1;
+        p.kwaves = 4;
+        p.depth = 4;
+        p.splits = 1;
+        while (p.splits < 8 && G / (p.splits * 2) >= 16) p.splits *= 2;
+        p.whole = 0;
     }
     // short K: no more wavefronts along K than groups per workgroup
     // (split-N wavefronts split the columns)

@@ -1265,31 +1265,69 @@ __global__ void __launch_bounds__(64 * KW) gemm_kernel(GemmArgs p) {
         wg_barrier();
         __atomic_signal_fence(__ATOMIC_SEQ_CST);
         if (s_last) {
-            auto summed = [&](int t, int m, int cc) {
-                float s = 0.0f;
-                for (int zz = 0; zz < p.S; ++zz)
-                    s += __hip_atomic_load(&p.part[((size_t)zz * M + m) * p.N + col_of(t, cc)],
-                                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            // The S partials of an output are added in the fixed order
+            // z = 0..S-1.  Every load of a batch (eight partials of two
+            // outputs; past z = S-1 the index is clamped and the value
+            // unused) is issued before the first add, so the batch costs one
+            // round trip to the device-coherent level instead of one per
+            // partial.
+            constexpr int kB = 8;
+            const size_t zstride = (size_t)M * p.N;
+            auto load_b = [&](size_t col, int m, int z0, float (&v)[kB]) {
+                const float *src = p.part + (size_t)m * p.N + col;
+#pragma unroll
+                for (int i = 0; i < kB; ++i)
+                    v[i] = __hip_atomic_load(src + (size_t)min(z0 + i, p.S - 1) * zstride, __ATOMIC_RELAXED,
+                                             __HIP_MEMORY_SCOPE_AGENT);
+            };
+            auto add_b = [&](const float (&v)[kB], int z0, float s) {
+#pragma unroll
+                for (int i = 0; i < kB; ++i)
+                    if (z0 + i < p.S) s += v[i];
                 return s;
             };
             // split-N: each wavefront adds its own tiles
             const int mc0 = kSplitN ? lane : (int)threadIdx.x;
             constexpr int kMcStep = kSplitN ? 64 : 64 * KW;
-            if (fuse != 1) {
+            // outputs e = t * 16M + mc of this thread, two at a time; gate/up:
+            // the gate tile t and its up tile t + T/2 together
+            const int nT = fuse == 1 ? kHalfT : T;
+            const int ne = nT * M * 16;
+            for (int e0 = mc0; e0 < ne; e0 += 2 * kMcStep) {
+                int te[2], me[2], ce[2];
+                size_t col0[2], col1[2];   // plain (or gate) column, and the up column
+                bool live[2];
 #pragma unroll
-                for (int t = 0; t < T; ++t)
-                    for (int mc = mc0; mc < M * 16; mc += kMcStep) {
-                        if (!tile_ok(t)) continue;
-                        emit_c(t, mc >> 4, mc & 15, summed(t, mc >> 4, mc & 15));
-                    }
-            } else {
+                for (int q = 0; q < 2; ++q) {
+                    const int e = min(e0 + q * kMcStep, ne - 1);
+                    te[q] = e / (M * 16);
+                    me[q] = (e % (M * 16)) >> 4;
+                    ce[q] = e & 15;
+                    live[q] = e0 + q * kMcStep < ne && tile_ok(te[q]);
+                    // an output that is not written still loads, from column 0
+                    col0[q] = live[q] ? col_of(te[q], ce[q]) : 0;
+                    col1[q] = live[q] && fuse == 1 ? col_of(te[q] + kHalfT, ce[q]) : 0;
+                }
+                float s0[2] = {0.0f, 0.0f}, s1[2] = {0.0f, 0.0f};
+                for (int z0 = 0; z0 < p.S; z0 += kB) {
+                    float v0[2][kB], v1[2][kB];
 #pragma unroll
-                for (int t = 0; t < kHalfT; ++t)
-                    for (int mc = mc0; mc < M * 16; mc += kMcStep) {
-                        if (!tile_ok(t)) continue;
-                        const int m = mc >> 4, cc = mc & 15;
-                        emit_h(t, m, cc, summed(t, m, cc), summed(t + kHalfT, m, cc));
+                    for (int q = 0; q < 2; ++q) {
+                        load_b(col0[q], me[q], z0, v0[q]);
+                        if (fuse == 1) load_b(col1[q], me[q], z0, v1[q]);
                     }
+#pragma unroll
+                    for (int q = 0; q < 2; ++q) {
+                        s0[q] = add_b(v0[q], z0, s0[q]);
+                        if (fuse == 1) s1[q] = add_b(v1[q], z0, s1[q]);
+                    }
+                }
+#pragma unroll
+                for (int q = 0; q < 2; ++q) {
+                    if (!live[q]) continue;
+                    if (fuse == 1) emit_h(te[q], me[q], ce[q], s0[q], s1[q]);
+                    else emit_c(te[q], me[q], ce[q], s0[q]);
+                }
             }
             if (threadIdx.x == 0)
                 __hip_atomic_store(&p.count[strip], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);

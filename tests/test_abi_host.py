@@ -201,19 +201,20 @@ def test_row_count_dispatch():
     assert (p.path, p.tiles, p.kwaves, p.depth) == (w4.PATH_GEMV, 1, 8, 2), p
     p = w4.nvfp4_get_plan(8, 5120, 6144)
     assert (p.asrc, p.tiles, p.kwaves, p.depth) == (w4.ASRC_LDS, 2, 8, 4), p
-    # the down projection (320 tiles, 136 groups) at one row and from five
+    # the down projection (320 tiles, 136 groups) at one row and from three
     # to twelve: 256 whole one-tile strips and 64 strips in four K pieces,
-    # eight wavefronts; two to four rows keep the whole K of A in LDS,
-    # unsplit; from 13 rows split-N (four one-tile wavefronts around a shared
-    # ring of A) with every strip in eight K pieces of 17 groups
-    for M in (2, 3, 4):
-        p = w4.get_plan(M, 5120, 17408)
-        assert (p.splits, p.asrc, p.tiles, p.kwaves) == (1, w4.ASRC_LDS, 2, 8), (M, p)
-    for M in (1, 5, 8, 9, 12):
+    # eight wavefronts, ring depth 4 from three to eight rows; two rows keep
+    # the whole K of A in LDS, unsplit; from 13 rows split-N (four one-tile
+    # wavefronts around a shared ring of A) with every strip in eight K
+    # pieces of 17 groups
+    p = w4.get_plan(2, 5120, 17408)
+    assert (p.splits, p.asrc, p.tiles, p.kwaves) == (1, w4.ASRC_LDS, 2, 8), p
+    for M in (1, 3, 4, 5, 8, 9, 12):
         p = w4.get_plan(M, 5120, 17408)
         assert (p.tiles, p.kwaves, p.splits, p.whole) == (1, 8, 4, 256), (M, p)
         assert p.path == (w4.PATH_GEMV if M == 1 else w4.PATH_MFMA), (M, p)
         assert M == 1 or p.asrc == w4.ASRC_RING, (M, p)
+        assert p.depth == (4 if 3 <= M <= 8 else 2), (M, p)
     for M in (13, 16):
         p = w4.get_plan(M, 5120, 17408)
         assert (p.path, p.asrc, p.tiles, p.kwaves, p.depth, p.splits, p.whole) == \

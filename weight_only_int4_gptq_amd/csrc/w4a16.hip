@@ -329,13 +329,16 @@ void auto_plan(int M, int N, int K, w4a16_plan_t *out) {
         p.splits = 1;
         p.whole = 0;
     }
-    // Narrow N with long K, one row or five and more: one tile per strip,
-    // eight wavefronts along K, and the strips beyond one per CU split into
-    // K pieces, so that every CU gets one whole strip and one piece
-    // (17408 x 5120: 256 whole strips and 64 strips in four pieces).  The
-    // pieces' hand-off finishes long before the whole strips do.  (Two to
-    // four rows keep the whole K range of A in LDS, which measures faster.)
-    if (narrow && (M == 1 ? deep : (M >= 5 && G >= 64)) && NT > kPlanCUs && NT % kPlanCUs != 0) {
+    // Narrow N with long K, one row, from three rows with 128 groups and
+    // more, or from five rows with 64: one tile per strip, eight wavefronts
+    // along K, and the strips beyond one per CU split into K pieces, so that
+    // every CU gets one whole strip and one piece (17408 x 5120: 256 whole
+    // strips and 64 strips in four pieces).  The pieces' hand-off finishes
+    // long before the whole strips do.  Ring depth 4 up to 8 rows with 128
+    // groups (slots of one or two KiB), 2 otherwise.  (Two rows, and three
+    // and four below 128 groups, keep the whole K range of A in LDS.)
+    if (narrow && (M == 1 ? deep : (deep ? M >= 3 : (M >= 5 && G >= 64))) && NT > kPlanCUs &&
+        NT % kPlanCUs != 0) {
         const int R = NT % kPlanCUs;
         int S = 1;
         while (S * 2 * R <= kPlanCUs && S * 2 <= G / 16) S *= 2;
@@ -344,7 +347,7 @@ void auto_plan(int M, int N, int K, w4a16_plan_t *out) {
             p.asrc = (M == 1) ? W4A16_ASRC_LDS : W4A16_ASRC_RING;
             p.tiles = 1;
             p.kwaves = 8;
-            p.depth = 2;
+            p.depth = (deep && M >= 3 && M <= 8) ? 4 : 2;
             p.splits = S;
             p.whole = NT - R;
         }

@@ -45,7 +45,7 @@ constexpr uint32_t kBiasPair = 0x43084308u;    // bf16 pair (136.0, 136.0) = cod
 constexpr float kBias = 136.0f;                // 128 (magic) + 8 (code midpoint)
 constexpr int kXcds = 8;                       // MI355X: 8 XCDs, 32 CUs each
 constexpr int kRowPad = 16;                    // bytes of padding per staged A row
-constexpr int kRingSlotBytes = 16 * kGroup * 2; // one group of A, 16 rows, in the LDS ring
+constexpr int kRingSlotBytes = 16 * kGroup * 2; // one group of A, 16 rows, in the shared (split-N) LDS ring
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
@@ -97,7 +97,7 @@ constexpr int kArgmaxBinOffset = 256;
 // Shared by host (sizing) and device (carving).  Offsets in bytes.
 struct LdsLayout {
     int keys;   // row argmax: one 64-bit key per row [16]
-    int a;      // staged A rows [M][Gwg*128 bf16 + pad]; ring: [KW][D][16 rows][256 B]
+    int a;      // staged A rows [M][Gwg*128 bf16 + pad]; ring: [KW][D][4 ceil(M/4) rows][256 B] + pad
     int bias;   // GEMV: bias of each 32-row quarter [M][Gwg][4] fp32;
                 // MFMA with staged A: bias tile rows [Gwg][16] fp32
     int red;    // cross-wavefront reduction [KW][T*M*16] fp32
@@ -114,7 +114,13 @@ __host__ __device__ inline LdsLayout lds_layout(int path, int asrc, int M, int G
     off += 16 * 8;
     L.a = off;
     if (stage) off += M * L.row;
-    else if (path == PATH_MFMA && asrc == ASRC_RING) off += KW * D * kRingSlotBytes;
+    else if (path == PATH_MFMA && asrc == ASRC_RING) {
+        // ceil(M/4) KiB per slot (four rows per KiB); the matrix-core reads
+        // take 16 rows from a slot, so the last slot's reads of rows past
+        // 4 ceil(M/4) need (4 - ceil(M/4)) KiB after it
+        const int nd = (M + 3) / 4;
+        off += KW * D * nd * 1024 + (4 - nd) * 1024;
+    }
     else if (path == PATH_MFMA && asrc == ASRC_SPLITN) off += (D + 1) * kRingSlotBytes;
     L.bias = off;
     if (path == PATH_GEMV) off += M * Gwg * 4 * 4;
@@ -682,12 +688,15 @@ __global__ void __launch_bounds__(64 * KW) gemm_kernel(GemmArgs p) {
     uint32_t sv[D][T][kNv ? 2 : 1];
     u32x4 av[kGlobalA ? D : 1][4];   // NVFP4: av[j][q] = the A fragments of blocks 2q, 2q+1
 
-    // Ring A: the group's rows go to this wavefront's LDS slot as contiguous
-    // 1 KiB DMA loads (four rows each; rows >= M repeat row M-1).  Inside a
+    // Ring A: the group's rows go to this wavefront's LDS slot of ceil(M/4)
+    // KiB as contiguous 1 KiB DMA loads (four rows each; rows >= M repeat
+    // row M-1).  The matrix-core reads take rows 0..15 of the slot: rows
+    // past the slot's last are the next slot's bytes (or the padding after
+    // the last slot) and only reach output rows that are never stored.  Inside a
     // row the 16-byte pieces are XOR-swizzled by the row index, so the
     // matrix-core reads below (16 rows, one piece each) hit distinct banks.
     const int nd = (M + 3) >> 2;                             // DMA loads per group
-    auto ring_slot = [&](int j) { return L.a + (wave * D + j) * kRingSlotBytes; };
+    auto ring_slot = [&](int j) { return L.a + (wave * D + j) * (nd << 10); };
     // this lane's byte offset inside a group of A for DMA load i (rows
     // 4i + h, swizzled piece c), fixed for the whole loop
     uint32_t ring_off[4];

@@ -193,10 +193,25 @@ def test_row_count_dispatch():
     for M in (5, 8, 9, 16):
         p = w4.nvfp4_get_plan(M, 34816, 5120)
         assert (p.asrc, p.tiles, p.splits, p.whole) == (w4.ASRC_SPLITN, 1, 4, 512), (M, p)
-    # NVFP4 down projection: the remainder split at one and two rows
+    # NVFP4 down projection: the remainder split at one and two rows; from
+    # five rows split-N with every strip in eight K pieces
     for M in (1, 2):
         p = w4.nvfp4_get_plan(M, 5120, 17408)
         assert (p.tiles, p.kwaves, p.splits, p.whole) == (1, 8, 4, 256), (M, p)
+    for M in (5, 8, 16):
+        p = w4.nvfp4_get_plan(M, 5120, 17408)
+        assert (p.asrc, p.tiles, p.kwaves, p.splits, p.depth, p.whole) == (w4.ASRC_SPLITN, 1, 4, 8, 4, 0), (M, p)
+    # NVFP4 gate/up width at two to four rows: four-tile strips with A in
+    # LDS, the 32 strips beyond two per CU in eight K pieces
+    for M in (2, 3, 4):
+        p = w4.nvfp4_get_plan(M, 34816, 5120)
+        assert (p.asrc, p.tiles, p.kwaves, p.splits, p.depth, p.whole) == (w4.ASRC_LDS, 4, 4, 8, 2, 512), (M, p)
+    # NVFP4 QKV and attention-out widths at five and six rows: one tile,
+    # eight wavefronts, A in LDS
+    for N, K in ((8192, 5120), (5120, 6144)):
+        for M in (5, 6):
+            p = w4.nvfp4_get_plan(M, N, K)
+            assert (p.asrc, p.tiles, p.kwaves, p.splits) == (w4.ASRC_LDS, 1, 8, 1), (N, M, p)
     p = w4.nvfp4_get_plan(1, 34816, 5120)
     assert (p.path, p.tiles, p.kwaves, p.depth) == (w4.PATH_GEMV, 1, 8, 2), p
     p = w4.nvfp4_get_plan(8, 5120, 6144)

@@ -402,21 +402,28 @@ void auto_plan(int M, int N, int K, w4a16_plan_t *out) {
 // MI355X (cold weights) over the decoder shapes, M = 1..16.  The matrix-core
 // path pays one scale multiply per 16-row block and output, so it wins later
 // than for GPTQ on narrow N and favours split K for long K:
-//  * M = 1, GEMV: wide: two tiles, four wavefronts, depth 5; long K: two
-//    tiles, eight wavefronts, depth 3; otherwise one tile, eight
-//    wavefronts, depth 2 (QKV and every tensor-parallel shard);
-//  * M = 2..4: very wide N: four tiles, depth 2; long K: two tiles, eight
-//    wavefronts; narrow N: one tile, eight wavefronts; else two tiles, four
-//    wavefronts; A in LDS throughout;
+//  * M = 1, GEMV: the gate/up width: one tile, eight wavefronts, depth 2;
+//    other wide N: two tiles, four wavefronts, depth 5; narrow N with long
+//    K (the down projection): one tile, eight wavefronts, the strips beyond
+//    one per CU split four ways along K; other long K: two tiles, eight
+//    wavefronts, depth 3; otherwise one tile, eight wavefronts, depth 2;
+//  * M = 2 on the down projection: the same remainder split with matrix
+//    cores, A in LDS, depth 4;
+//  * M = 2..4, A in LDS: very wide N: four tiles, depth 2; long K: two
+//    tiles, eight wavefronts; the gate/up width: four tiles, four
+//    wavefronts, depth 2, the strips beyond a whole number per CU split
+//    eight ways along K; otherwise one tile, eight wavefronts;
 //  * M >= 5: very wide N: four wavefronts split the columns (two tiles
-//    each) around one shared ring of A, depth 2; wide N from 9 rows: the
-//    same with one tile each, depth 4.  Otherwise A through the LDS ring,
-//    two tiles, four wavefronts, depth 2: wide N up to 8 rows; long K
-//    from 8 rows, split two ways (below: four tiles split four ways, A in
-//    LDS); narrow N (the tensor-parallel shards) up to 8 rows: A in LDS,
-//    eight wavefronts, depth 4, one tile (two from 64 groups); otherwise
-//    from 8 rows, depth 4 for narrow N from 64 groups (below: two tiles,
-//    eight wavefronts, A in LDS).
+//    each) around one shared ring of A, depth 2; wide N: the same with one
+//    tile each, depth 4, the strips beyond a whole number per CU split four
+//    ways along K; narrow N with long K: the same with every strip in eight
+//    K pieces; other long K: four tiles split four ways with A in LDS up to
+//    7 rows, from 8 the ring (two tiles, split two ways); fewer than 64
+//    groups up to 6 rows (the QKV and attention-out widths): one tile,
+//    eight wavefronts, A in LDS, depth 4; narrow N up to 8 rows: the same
+//    with two tiles from 64 groups or past 256 tiles; otherwise two tiles,
+//    eight wavefronts, A in LDS up to 7 rows, and from 8 rows the ring, two
+//    tiles, four wavefronts, depth 2 (4 for narrow N from 64 groups).
 // The first of these that the library has a kernel for and that fits is taken, else
 // the first compiled fallback.
 void auto_plan_nv(int M, int N, int K, w4a16_plan_t *out) {
@@ -449,7 +456,16 @@ void auto_plan_nv(int M, int N, int K, w4a16_plan_t *out) {
         if (vwide) set(W4A16_PATH_MFMA, 4, 4, 1, W4A16_ASRC_LDS, 2);
         else if (deep) set(W4A16_PATH_MFMA, 2, 8, 1, W4A16_ASRC_LDS, 4);
         else if (!wide) set(W4A16_PATH_MFMA, 1, 8, 1, W4A16_ASRC_LDS, 4);
-        else set(W4A16_PATH_MFMA, 2, 4, 1, W4A16_ASRC_LDS, 4);
+        else {
+            // the gate/up width: four-tile strips, the strips beyond a whole
+            // number per CU split eight ways along K
+            set(W4A16_PATH_MFMA, 4, 4, 1, W4A16_ASRC_LDS, 2);
+            const int ns = (NT + 3) / 4, r = ns % kPlanCUs;
+            if (ns > kPlanCUs && r != 0 && 8 * r <= kPlanCUs) {
+                p.splits = 8;
+                p.whole = ns - r;
+            }
+        }
     } else {
         // A through the LDS ring (two tiles, depth 2) wherever it measured
         // best; four wavefronts splitting the columns around one shared ring
@@ -465,9 +481,15 @@ void auto_plan_nv(int M, int N, int K, w4a16_plan_t *out) {
                 p.splits = 4;
                 p.whole = ns - r;
             }
+        } else if (deep && narrow) {
+            // four wavefronts split four one-tile columns around a shared
+            // ring, every strip in eight K pieces
+            set(W4A16_PATH_MFMA, 1, 4, 8, W4A16_ASRC_SPLITN, 4);
         } else if (deep) {
             if (M <= 7) set(W4A16_PATH_MFMA, 4, 4, 4, W4A16_ASRC_LDS, 2);
             else set(W4A16_PATH_MFMA, 2, 4, 2, W4A16_ASRC_RING, 2);
+        } else if (M <= 6 && G < 64) {         // QKV and attention-out widths: one tile, eight wavefronts
+            set(W4A16_PATH_MFMA, 1, 8, 1, W4A16_ASRC_LDS, 4);
         } else if (narrow && M <= 8) {         // one tile (two from 64 groups or past 256 tiles), eight wavefronts
             set(W4A16_PATH_MFMA, (G >= 64 || NT > kPlanCUs) ? 2 : 1, 8, 1, W4A16_ASRC_LDS, 4);
         } else if (M <= 7) {

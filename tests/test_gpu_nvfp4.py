@@ -286,7 +286,7 @@ def test_nvfp4_determinism_and_row_prefix():
 def test_nvfp4_workload_parity_full(name):
     wl = synth.WORKLOADS[name]
     K, N = wl.K, wl.N
-    Ms = (1, 2, 4, 8, 9, 16)
+    Ms = (1, 2, 3, 4, 5, 6, 7, 8, 9, 16)
     note(f"[nvfp4 workload] {name} K={K} N={N} Ms={Ms}")
     A, packed, scales = synth.gen_nvfp4_workload(name)
     blob, sc, a = to_dev(packed, scales, A)

@@ -344,7 +344,7 @@ def test_determinism_and_row_prefix():
 # every row count the decode step and the verify batches call each shape
 # with, through the automatic plans (the plain kernels the full-stack timing runs)
 FULL_MS = {"tiny": (1,), "qkv": (1, 2, 4, 8, 9, 16), "attn_out": (1, 2, 4, 8, 9, 16),
-           "gate_up": (1, 2, 4, 8, 9, 16), "down": (1, 2, 4, 8, 9, 16)}
+           "gate_up": (1, 2, 4, 8, 9, 16), "down": (1, 2, 3, 4, 5, 8, 9, 12, 13, 16)}
 
 
 @pytest.mark.parametrize("name", ["tiny", "qkv", "attn_out", "gate_up", "down"])

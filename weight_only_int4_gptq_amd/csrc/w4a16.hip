@@ -55,14 +55,20 @@ const Variant *find_variant(const w4a16_plan_t &p, int M, bool epi = false, int 
     const VariantTable nv_epi[] = {{kVariantsNvEpiGemv, kNumNvEpiGemv}, {kVariantsNvEpiMfma, kNumNvEpiMfma}};
     const VariantTable *tabs = fmt == FMT_NVFP4 ? (epi ? nv_epi : nv) : (epi ? with_epi : plain);
     const int ntabs = fmt == FMT_NVFP4 ? 2 : 4;
-    for (int ti = 0; ti < ntabs; ++ti)
-        for (int i = 0; i < tabs[ti].n; ++i) {
-            const Variant &v = tabs[ti].v[i];
-            if (v.path == p.path && v.mm == mm && v.tiles == p.tiles && v.kwaves == p.kwaves &&
-                v.depth == depth && v.asrc == asrc)
-                return &v;
-        }
-    return nullptr;
+    auto find = [&](int want_mm) -> const Variant * {
+        for (int ti = 0; ti < ntabs; ++ti)
+            for (int i = 0; i < tabs[ti].n; ++i) {
+                const Variant &v = tabs[ti].v[i];
+                if (v.path == p.path && v.mm == want_mm && v.tiles == p.tiles && v.kwaves == p.kwaves &&
+                    v.depth == depth && v.asrc == asrc)
+                    return &v;
+            }
+        return nullptr;
+    };
+    // ring A: the kernel with this M's DMA count per group fixed, if compiled
+    if (p.path == W4A16_PATH_MFMA && asrc == ASRC_RING)
+        if (const Variant *v = find(-((M + 3) / 4))) return v;
+    return find(mm);
 }
 
 // A dense index of a kernel over every table (for per-kernel host caches), or

@@ -549,7 +549,9 @@ static __global__ void __launch_bounds__(256) nv_export_kernel(const u32x4 *__re
 //
 // MM is the row count when it is known at compile time (1..4; the GEMV path
 // always has it): then only the live rows are scaled and accumulated.  MM = 0
-// (MFMA only) takes M at run time, up to 16.
+// (MFMA only) takes M at run time, up to 16.  MM < 0 (ring A only) also takes
+// M at run time, with ceil(M/4) = -MM fixed: the group's DMA loads are then
+// issued without a run-time count.
 //
 // The partial sums of the KW wavefronts meet in LDS and are added in a fixed
 // order (split-N wavefronts hold whole sums of their own tiles); with S > 1 the workgroups of one strip meet in the workspace, where
@@ -695,7 +697,7 @@ __global__ void __launch_bounds__(64 * KW) gemm_kernel(GemmArgs p) {
     // the last slot) and only reach output rows that are never stored.  Inside a
     // row the 16-byte pieces are XOR-swizzled by the row index, so the
     // matrix-core reads below (16 rows, one piece each) hit distinct banks.
-    const int nd = (M + 3) >> 2;                             // DMA loads per group
+    const int nd = (MM < 0) ? -MM : (M + 3) >> 2;           // DMA loads per group
     auto ring_slot = [&](int j) { return L.a + (wave * D + j) * (nd << 10); };
     // this lane's byte offset inside a group of A for DMA load i (rows
     // 4i + h, swizzled piece c), fixed for the whole loop

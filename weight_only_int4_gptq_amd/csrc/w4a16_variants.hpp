@@ -10,7 +10,8 @@ namespace w4a16 {
 using KernelFn = void (*)(GemmArgs);
 
 struct Variant {
-    int path, mm, tiles, kwaves, depth, asrc;   // mm: compile-time row count (0: run time)
+    int path, mm, tiles, kwaves, depth, asrc;   // mm: compile-time row count (0: run time;
+                                                // < 0: run time, ceil(M/4) = -mm)
     KernelFn fn;
 };
 
@@ -20,11 +21,13 @@ struct Variant {
     X(P, MM, 2, 4, 4, AS) X(P, MM, 2, 8, 4, AS) X(P, MM, 2, 4, 8, AS) X(P, MM, 4, 4, 2, AS) \
     X(P, MM, 4, 4, 4, AS)
 
-// A streamed per group through a per-wavefront LDS ring (matrix-core path)
+// A streamed per group through a per-wavefront LDS ring (matrix-core path);
+// the two-tile depth-2 shapes are compiled only with their DMA count fixed
+// (W4A16_RINGS_ND, one kernel per ceil(M/4))
 #define W4A16_RINGS(X, P, MM, AS) \
-    X(P, MM, 1, 4, 4, AS) X(P, MM, 1, 8, 4, AS) X(P, MM, 2, 4, 2, AS) X(P, MM, 2, 4, 4, AS) \
+    X(P, MM, 1, 4, 4, AS) X(P, MM, 1, 8, 4, AS) X(P, MM, 2, 4, 4, AS) \
     X(P, MM, 4, 4, 2, AS) X(P, MM, 4, 2, 2, AS) X(P, MM, 4, 4, 4, AS) X(P, MM, 8, 1, 4, AS) \
-    X(P, MM, 8, 2, 2, AS) X(P, MM, 8, 4, 2, AS) X(P, MM, 1, 8, 2, AS) X(P, MM, 2, 8, 2, AS)
+    X(P, MM, 8, 2, 2, AS) X(P, MM, 8, 4, 2, AS) X(P, MM, 1, 8, 2, AS)
 
 // eight-tile strips: A read once per eight tiles (matrix-core paths)
 #define W4A16_WIDE(X, P, MM, AS) \
@@ -68,8 +71,17 @@ struct Variant {
     X(P, MM, 1, 4, 2, AS) X(P, MM, 1, 4, 4, AS) X(P, MM, 2, 4, 2, AS) X(P, MM, 2, 4, 3, AS) \
     X(P, MM, 2, 4, 4, AS) X(P, MM, 4, 4, 2, AS)
 
+// rings of depth 2 with the DMA count per group fixed (MM = -ceil(M/4)):
+// every two-tile one, and one tile for 9..12 rows (measured faster; the
+// one-tile depth-4 ring measured slower with its count fixed)
+#define W4A16_RINGS_ND(X, P, AS) \
+    X(P, -1, 2, 8, 2, AS) X(P, -2, 2, 8, 2, AS) X(P, -3, 2, 8, 2, AS) X(P, -4, 2, 8, 2, AS) \
+    X(P, -1, 2, 4, 2, AS) X(P, -2, 2, 4, 2, AS) X(P, -3, 2, 4, 2, AS) X(P, -4, 2, 4, 2, AS) \
+    X(P, -3, 1, 8, 2, AS)
+
 #define W4A16_VARIANT_LIST_RT(X)                                                                    \
     W4A16_RINGS(X, PATH_MFMA, 0, ASRC_RING) W4A16_SPLITN(X, PATH_MFMA, 0, ASRC_SPLITN)             \
+    W4A16_RINGS_ND(X, PATH_MFMA, ASRC_RING)                                                         \
     W4A16_WIDE(X, PATH_MFMA, 0, ASRC_LDS) W4A16_WIDE(X, PATH_MFMA, 0, ASRC_GLOBAL)                  \
     W4A16_SHAPES(X, PATH_MFMA, 0, ASRC_LDS) W4A16_SHAPES(X, PATH_MFMA, 0, ASRC_GLOBAL)
 

@@ -105,6 +105,15 @@ struct LdsLayout {
     int row;    // bytes per staged A row
 };
 
+// Slots of the shared split-N ring: D + 1 rounded up to a power of two, so
+// that a group's slot is its index masked (a modulo by D + 1 cost several
+// scalar instructions per group, twice)
+__host__ __device__ constexpr int shared_slots(int D) {
+    int n = 1;
+    while (n < D + 1) n <<= 1;
+    return n;
+}
+
 __host__ __device__ inline LdsLayout lds_layout(int path, int asrc, int M, int Gwg, int T, int KW, int D) {
     LdsLayout L;
     const bool stage = (path == PATH_GEMV) || (asrc == ASRC_LDS);
@@ -121,7 +130,7 @@ __host__ __device__ inline LdsLayout lds_layout(int path, int asrc, int M, int G
         const int nd = (M + 3) / 4;
         off += KW * D * nd * 1024 + (4 - nd) * 1024;
     }
-    else if (path == PATH_MFMA && asrc == ASRC_SPLITN) off += (D + 1) * kRingSlotBytes;
+    else if (path == PATH_MFMA && asrc == ASRC_SPLITN) off += shared_slots(D) * kRingSlotBytes;
     L.bias = off;
     if (path == PATH_GEMV) off += M * Gwg * 4 * 4;
     else if (stage) off += Gwg * 16 * 4;
@@ -707,14 +716,15 @@ __global__ void __launch_bounds__(64 * KW) gemm_kernel(GemmArgs p) {
         const int row = min(4 * i + h, M - 1);
         ring_off[i] = (uint32_t)row * (uint32_t)p.K * 2u + (uint32_t)((c ^ (row & 15)) << 4);
     }
-    // Split-N: one ring of D + 1 slots for the workgroup; group g (the i-th
-    // of the range) in slot i % (D + 1).  Wavefront w loads rows 4w .. 4w+3
-    // of every group (rows >= M repeat row M-1), so each wavefront issues
-    // exactly one DMA load per group and the wait counts stay static.  The
-    // refill issued after computing group i goes to the slot of group i - 1,
-    // which every wavefront has finished reading once it passed group i's
-    // barrier; hence the one spare slot.
-    auto shared_slot = [&](int g) { return L.a + ((g - gk0) % (D + 1)) * kRingSlotBytes; };
+    // Split-N: one ring of P = shared_slots(D) >= D + 1 slots for the
+    // workgroup; group g (the i-th of the range) in slot i % P.  Wavefront w
+    // loads rows 4w .. 4w+3 of every group (rows >= M repeat row M-1), so
+    // each wavefront issues exactly one DMA load per group and the wait
+    // counts stay static.  The refill issued after computing group i (group
+    // i + D) goes to the slot of group i + D - P <= i - 1, which every
+    // wavefront has finished reading once it passed group i's barrier;
+    // hence at least one spare slot.
+    auto shared_slot = [&](int g) { return L.a + ((g - gk0) & (shared_slots(D) - 1)) * kRingSlotBytes; };
     const int sh_row = min(4 * wave + h, M - 1);
     const uint32_t sh_off = (uint32_t)sh_row * (uint32_t)p.K * 2u + (uint32_t)((c ^ (sh_row & 15)) << 4);
 

@@ -173,13 +173,12 @@ def test_row_count_dispatch():
         else:
             assert p.asrc == w4.ASRC_SPLITN and (p.tiles, p.kwaves, p.depth, p.splits, p.whole) == (2, 4, 4, 4, 256), (M, p)
     # QKV and attention-out widths (one to two two-tile strips per CU, 40 and
-    # 48 groups): eight wavefronts, two tiles; A whole in LDS at 2-3 rows,
-    # the ring from 4
+    # 48 groups): eight wavefronts, two tiles, A through the ring, depth 2
     for N, K in ((8192, 5120), (5120, 6144)):
         for M in range(2, 17):
             p = w4.get_plan(M, N, K)
             assert (p.path, p.tiles, p.kwaves, p.splits) == (w4.PATH_MFMA, 2, 8, 1), (N, M, p)
-            assert (p.asrc, p.depth) == ((w4.ASRC_LDS, 4) if M <= 3 else (w4.ASRC_RING, 2)), (N, M, p)
+            assert (p.asrc, p.depth) == (w4.ASRC_RING, 2), (N, M, p)
     # very wide N: LDS A at 3-4 rows, the ring at 2, split-N from 5 rows
     # (two tiles per wavefront up to 8 rows, four above)
     assert w4.get_plan(4, 248320, 5120).asrc == w4.ASRC_LDS

@@ -324,14 +324,15 @@ void auto_plan(int M, int N, int K, w4a16_plan_t *out) {
     }
     // Between one and two strips of two tiles per CU with 32 to 127 groups
     // (the attention output projection 6144 x 5120 and QKV 5120 x 8192):
-    // two tiles, eight wavefronts (two per SIMD); A staged whole in LDS
-    // (depth 4) for two and three rows, through the ring (depth 2) from four.
+    // two tiles, eight wavefronts (two per SIMD), A through the ring, depth 2
+    // (its kernels with the DMA count fixed beat A staged whole in LDS from
+    // two rows).
     if (M >= 2 && NT > kPlanCUs && NT <= 2 * kPlanCUs && G >= 32 && !deep) {
         p.path = W4A16_PATH_MFMA;
-        p.asrc = M >= 4 ? W4A16_ASRC_RING : W4A16_ASRC_LDS;
+        p.asrc = W4A16_ASRC_RING;
         p.tiles = 2;
         p.kwaves = 8;
-        p.depth = M >= 4 ? 2 : 4;
+        p.depth = 2;
         p.splits = 1;
         p.whole = 0;
     }
